@@ -1,0 +1,31 @@
+"""The float64 oracle against facts other than itself (runs on the CPU)."""
+import numpy as np
+import pytest
+
+import oracle_pins as P
+from oracle import load_oracle
+from cfc_recurrent_cell_amd.workloads import TINY, make_cfc_inputs
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return load_oracle()
+
+
+@pytest.mark.parametrize("name", sorted(P.ALL_PINS))
+def test_pin(lib, name):
+    P.ALL_PINS[name](lib)
+
+
+def test_finite_differences_tiny_workload(lib):
+    """Every one of the 1600 parameters of the tiny workload (b = 0, h0 = 0)."""
+    inp = make_cfc_inputs(TINY)
+    err = P.pin_finite_differences(lib, inp, eps=1e-6, rtol=1e-6, atol=1e-8)
+    assert err < 1e-7
+
+
+def test_autograd_smoke_rows(lib):
+    """Autograd on two rows of the smoke-shaped workload (K=64, H=128)."""
+    from cfc_recurrent_cell_amd.workloads import SMOKE
+    inp = make_cfc_inputs(SMOKE, B=2)
+    P.pin_autograd(lib, inp)
