@@ -1,0 +1,201 @@
+"""Benchmark of the CfC K-loop hot path on one MI355X.
+
+One step = cfc_forward + cfc_backward (overwrite mode, so the scratch clear is
+part of the step) + reduce_axis0 over one batch of the training-scale
+workload (B=256, K=64, n_in=n_hid=128, dt=0.5), inputs resident in HBM.
+
+Prints ONE JSON line.  `value` is batch-steps/s = B*K / seconds per step.
+The roofline object describes the step's dominant kernel, timed with HIP
+events recorded around each launch on the stream the kernel runs on, inside
+the timed region.  The cpu_baseline object times the float64 oracle on the
+host (one thread) on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CfC fwd+BPTT batch-steps/s (B=256,K=64,H=128); reduce_axis0 HBM GB/s"
+PEAK_F64_TFLOPS = 78.6        # MI355X FP64 vector: 256 CU * 2.4 GHz * 64 FMA/clk * 2
+PEAK_HBM_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "cfc_recurrent_cell_amd", "csrc", "cfc.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_train_B256_K64_H128.json")
+
+
+def algorithmic_work(B, K, n_in, H):
+    """FLOPs and bytes per launch that the method itself needs (not what a
+    particular kernel happens to move).  FLOPs count multiply-adds of the
+    contractions as 2; the O(H) elementwise work is not counted."""
+    N = H * (n_in + H + 2)
+    rows = B * K
+    fwd_flops = rows * 2 * H * (n_in + H)
+    # bwd: recompute a, W_rec^T da, dW_in and dW_rec contractions
+    bwd_flops = rows * (2 * H * (n_in + H) + 2 * H * H + 2 * H * (n_in + H))
+    f = 4
+    fwd_bytes = f * (B * K * n_in + B * H + B * K * H + H * (n_in + H + 2))
+    bwd_bytes = f * (B * K * n_in + B * H + B * K * H + B * H + B * N + B + H * (n_in + H + 2))
+    red_bytes = f * (B * N + N)
+    return dict(fwd_flops=fwd_flops, bwd_flops=bwd_flops, fwd_bytes=fwd_bytes, bwd_bytes=bwd_bytes,
+                reduce_bytes=red_bytes)
+
+
+def source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, only if
+    it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256_16") != source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s=10.0):
+    from oracle import oracle as O
+    B, K = inp.x.shape[0], inp.x.shape[1]
+    rows = max(1, min(B, 32))
+    sub = type(inp)(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x[:rows], inp.h0[:rows], inp.y[:rows], inp.dt)
+    O.load_oracle()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        O.cfc_step(sub, threads=1)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": rows * K * n / el, "unit": "batch-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} x (forward+backward+reduce over {rows} of the {B} rows of the "
+                      f"same workload, K={K}), float64, one thread, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 256 MiB device copy (to scale PMC byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the CfC path has no cross-GPU step in this "
+              "library (rows shard over GPUs with one [N]-float exchange, not built here). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import cfc_recurrent_cell_amd as C
+    from cfc_recurrent_cell_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    C.load_library()
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        n = 64 * 1024 * 1024
+        a = torch.ones(n, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4}))
+        return
+
+    cfg = W.TRAIN
+    inp = W.make_cfc_inputs(cfg)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    w_in, w_rec, b, w_tau, x, h0, y = map(t, (inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x, inp.h0, inp.y))
+    dt = float(inp.dt)
+    B, K, n_in, H = cfg.B, cfg.K, cfg.n_in, cfg.n_hid
+    N = W.scratch_row_len(n_in, H)
+    h_seq = torch.empty((B, K, H), device=dev)
+    scratch = torch.empty((B, N), device=dev)
+    loss = torch.empty((B,), device=dev)
+    out = torch.empty((N,), device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        C.cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, h_seq=h_seq)
+        if ev is not None:
+            ev[1].record()
+        C.cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, scratch=scratch, loss=loss)
+        if ev is not None:
+            ev[2].record()
+        C.reduce_axis0(scratch, out=out)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    k_ms = {
+        "cfc_fwd_kernel": sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps,
+        "cfc_bwd_kernel": sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps,
+        "reduce_axis0_kernel": sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps,
+    }
+    work = algorithmic_work(B, K, n_in, H)
+    flops = {"cfc_fwd_kernel": work["fwd_flops"], "cfc_bwd_kernel": work["bwd_flops"]}
+    dom = max(k_ms, key=k_ms.get)
+    if dom == "reduce_axis0_kernel":
+        ach = work["reduce_bytes"] / (k_ms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBPS}
+    else:
+        ach = flops[dom] / (k_ms[dom] * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": ach, "peak": PEAK_F64_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_F64_TFLOPS}
+    roof["kernel"] = dom
+    roof["traffic"] = measured_traffic(dom)
+    red_gbps = work["reduce_bytes"] / (k_ms["reduce_axis0_kernel"] * 1e-3) / 1e9
+
+    value = B * K / (ms_per_step * 1e-3)
+    rec = {
+        "metric": METRIC, "value": value, "unit": "batch-steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "K": K, "n_in": n_in, "n_hid": H, "dt": dt,
+                   "scratch_N": N, "io_dtype": "f32", "seed": cfg.seed},
+        "roofline": roof,
+        "kernels_ms": k_ms,
+        "reduce_axis0": {"GB_per_s": red_gbps, "frac_hbm": red_gbps / PEAK_HBM_GBPS,
+                         "bytes": work["reduce_bytes"],
+                         "note": "scratch of this step (33.8 MB) may be served partly from the MALL"},
+        "kernel_source_sha256_16": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

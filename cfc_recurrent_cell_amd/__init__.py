@@ -1,0 +1,114 @@
+"""cfc_recurrent_cell_amd -- batched CfC cell K-loop on AMD MI355X (gfx950).
+
+Thin Python layer over the C ABI in ``include/cfc.h``: it checks tensor
+shapes, dtypes and devices, takes device pointers from torch tensors and the
+current torch stream, and calls the HIP library.  PyTorch provides device
+memory and streams only; every step of the computation runs in the library's
+kernels.  Importing works without a GPU; calling needs the built library
+(``python -m cfc_recurrent_cell_amd.build``) and raises if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+from ._lib import (  # noqa: F401
+    CFC_ACCUMULATE, CFC_ERR_DIM, CFC_ERR_DT, CFC_ERR_HIP, CFC_ERR_NULL, CFC_ERR_OVERLAP,
+    CFC_ERR_UNSUPPORTED, CFC_OK, CFC_OVERWRITE, CfcError, CfcParams, LIB_PATH, _check,
+    declared_symbols, load_library, status_string,
+)
+
+__all__ = ["cfc_forward", "cfc_backward", "reduce_axis0", "cfc_scratch_row_len", "CfcError",
+           "load_library"]
+
+
+def cfc_scratch_row_len(n_in: int, n_hid: int) -> int:
+    """N = n_hid * (n_in + n_hid + 2); -1 for invalid dimensions."""
+    return int(load_library().cfc_scratch_row_len(n_in, n_hid))
+
+
+def _dev_f32(t, name, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor on a GPU "
+                         f"(got {t.dtype}, {t.device}, contiguous={t.is_contiguous()})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _stream(device, stream):
+    import torch
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _params(w_in, w_rec, b, w_tau):
+    H, n_in = w_in.shape
+    _dev_f32(w_in, "w_in", (H, n_in))
+    _dev_f32(w_rec, "w_rec", (H, H))
+    _dev_f32(b, "b", (H,))
+    _dev_f32(w_tau, "w_tau", (H,))
+    return CfcParams(w_in.data_ptr(), w_rec.data_ptr(), b.data_ptr(), w_tau.data_ptr(), n_in, H)
+
+
+def cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt: float, h_seq=None, stream=None):
+    """h_seq [B, K, H] = forward K-loop of the cell (see include/cfc.h)."""
+    import torch
+    lib = load_library()
+    p = _params(w_in, w_rec, b, w_tau)
+    B, K, _ = x.shape
+    _dev_f32(x, "x", (B, K, p.n_in))
+    _dev_f32(h0, "h0", (B, p.n_hid))
+    if h_seq is None:
+        h_seq = torch.empty((B, K, p.n_hid), dtype=torch.float32, device=x.device)
+    _dev_f32(h_seq, "h_seq", (B, K, p.n_hid))
+    _check("cfc_forward", lib.cfc_forward(ctypes.byref(p), x.data_ptr(), h0.data_ptr(),
+                                          float(dt), B, K, h_seq.data_ptr(),
+                                          _stream(x.device, stream)))
+    return h_seq
+
+
+def cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, scratch=None,
+                 loss=None, accumulate: bool = False, want_loss: bool = True,
+                 stream=None) -> Tuple[object, Optional[object]]:
+    """(scratch [B, N], loss [B] or None): per-row parameter gradients of
+    L_b = 1/2 |h_K - y_b|^2 (see include/cfc.h for the row layout)."""
+    import torch
+    lib = load_library()
+    p = _params(w_in, w_rec, b, w_tau)
+    B, K, _ = x.shape
+    N = cfc_scratch_row_len(p.n_in, p.n_hid)
+    _dev_f32(x, "x", (B, K, p.n_in))
+    _dev_f32(h0, "h0", (B, p.n_hid))
+    _dev_f32(h_seq, "h_seq", (B, K, p.n_hid))
+    _dev_f32(y, "y", (B, p.n_hid))
+    if scratch is None:
+        scratch = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    _dev_f32(scratch, "scratch", (B, N))
+    if loss is None and want_loss:
+        loss = torch.empty((B,), dtype=torch.float32, device=x.device)
+    if loss is not None:
+        _dev_f32(loss, "loss", (B,))
+    flags = CFC_ACCUMULATE if accumulate else CFC_OVERWRITE
+    _check("cfc_backward", lib.cfc_backward(
+        ctypes.byref(p), x.data_ptr(), h0.data_ptr(), h_seq.data_ptr(), y.data_ptr(), float(dt),
+        B, K, scratch.data_ptr(), loss.data_ptr() if loss is not None else None, flags,
+        _stream(x.device, stream)))
+    return scratch, loss
+
+
+def reduce_axis0(per_batch, out=None, stream=None):
+    """out[N] = column sums of per_batch [B, N] (overwrites ``out``)."""
+    import torch
+    lib = load_library()
+    B, N = per_batch.shape
+    _dev_f32(per_batch, "per_batch", (B, N))
+    if out is None:
+        out = torch.empty((N,), dtype=torch.float32, device=per_batch.device)
+    _dev_f32(out, "out", (N,))
+    _check("reduce_axis0", lib.reduce_axis0(per_batch.data_ptr(), B, N, out.data_ptr(),
+                                            _stream(per_batch.device, stream)))
+    return out

@@ -1,0 +1,444 @@
+// cfc.hip -- gfx950 kernels and the C ABI of libcfc_amd (see include/cfc.h).
+//
+// Kernels
+//   cfc_fwd_kernel     one workgroup per batch row runs the whole forward
+//                      K-loop; the input projection of a window of steps is
+//                      computed off the serial chain, then the recurrence
+//                      steps through the window.
+//   cfc_bwd_kernel     one workgroup per batch row runs the whole reverse
+//                      K-loop: the serial delta chain keeps dL/da for every
+//                      step in LDS, then the weight gradients are formed as
+//                      contractions over k and each scratch element is
+//                      written exactly once (no per-step read-modify-write).
+//   reduce_axis0_kernel  column-tiled sum over the leading axis.
+//
+// The block-per-batch layout and the single-writer scratch come from the
+// "K-loop Parallelization Implementation Plan" (foxhunt, 2026-05-17), Tasks 2
+// and 3; the column-tiled reducer with a padded LDS tree from the ml-alpha
+// commit "NVIDIA-grade rewrite of CfC K-loop hot kernels" (b23f8f2efa).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "cfc.h"
+
+namespace {
+
+constexpr int kThreads = 256;             // 4 wave64 per workgroup
+constexpr int kMaxIn = CFC_MAX_N_IN;
+constexpr int kMaxHid = CFC_MAX_N_HID;
+constexpr size_t kLdsBytes = 160 * 1024;  // gfx950 LDS per workgroup
+
+// ------------------------------------------------------------------ math
+__device__ __forceinline__ double softplus_f64(double w) {
+    // log(1 + e^w) without overflow
+    return log1p(exp(-fabs(w))) + fmax(w, 0.0);
+}
+__device__ __forceinline__ double logistic_f64(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+// Threads per output of a matvec: the largest power of two G <= 64 with
+// G * rows <= 256, so a group of G consecutive lanes shares one output and
+// combines with butterfly shuffles inside one wavefront.
+__device__ __forceinline__ int group_size(int rows) {
+    int g = 1;
+    while (g < 64 && 2 * g * rows <= kThreads) g <<= 1;
+    return g;
+}
+
+// Sum over the G consecutive lanes of a group (every lane of the wave takes
+// part, so the shuffles are non-divergent).
+__device__ __forceinline__ double group_sum(double v, int G) {
+    for (int off = G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// ------------------------------------------------------------ forward
+// LDS: U [KW][H] f64 | h [2][H] f64 | sp [H] f64 | xs [KW][n_in] f32
+__global__ __launch_bounds__(kThreads) void cfc_fwd_kernel(
+    const float* __restrict__ w_in, const float* __restrict__ w_rec,
+    const float* __restrict__ bias, const float* __restrict__ w_tau,
+    const float* __restrict__ x, const float* __restrict__ h0, double dt, int K, int n_in,
+    int H, int KW, float* __restrict__ h_seq) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    double* U = reinterpret_cast<double*>(smem);
+    double* hbuf = U + (size_t)KW * H;
+    double* sp = hbuf + 2 * H;
+    float* xs = reinterpret_cast<float*>(sp + H);
+
+    const int t = threadIdx.x;
+    const long long b = blockIdx.x;
+    const int G = group_size(H);
+    const int i = t / G, sub = t % G;
+
+    for (int u = t; u < H; u += kThreads) {
+        sp[u] = softplus_f64((double)w_tau[u]);
+        hbuf[u] = (double)h0[b * H + u];
+    }
+    int cur = 0;
+    for (int k0 = 0; k0 < K; k0 += KW) {
+        const int kw = min(KW, K - k0);
+        __syncthreads();  // the previous window is done with xs and U
+        const float* xb = x + (b * K + k0) * (long long)n_in;
+        for (int e = t; e < kw * n_in; e += kThreads) xs[e] = xb[e];
+        __syncthreads();
+        // input projection of the window, off the serial chain
+        for (int e = t; e < kw * H; e += kThreads) {
+            const int kk = e / H, r = e - kk * H;
+            const float* wr = w_in + (long long)r * n_in;
+            const float* xr = xs + kk * n_in;
+            double s = (double)bias[r];
+            for (int j = 0; j < n_in; ++j) s = fma((double)wr[j], (double)xr[j], s);
+            U[e] = s;
+        }
+        __syncthreads();
+        for (int kk = 0; kk < kw; ++kk) {
+            const double* hv = hbuf + cur * H;
+            double part = 0.0;
+            if (i < H) {
+                const float* wr = w_rec + (long long)i * H;
+                for (int j = sub; j < H; j += G) part = fma((double)wr[j], hv[j], part);
+            }
+            part = group_sum(part, G);
+            if (i < H && sub == 0) {
+                const double a = U[kk * H + i] + part;
+                const double g = 1.0 / (1.0 + exp(sp[i] * a * dt));
+                const double c = tanh(a);
+                const double hn = g * hv[i] + (1.0 - g) * c;
+                hbuf[(cur ^ 1) * H + i] = hn;
+                h_seq[(b * K + k0 + kk) * (long long)H + i] = (float)hn;
+            }
+            cur ^= 1;
+            __syncthreads();
+        }
+    }
+}
+
+// ----------------------------------------------------------- backward
+// LDS: DA [K][H] f64 | delta [2][H] f64 | gate [H] f64 | sp [H] | sw [H] |
+//      red [256] f64 | xs [K][n_in] f32 | hp [K][H] f32   (hp[k] = h_k)
+__host__ __device__ inline size_t bwd_lds_bytes(int K, int n_in, int H) {
+    return (size_t)8 * K * H + (size_t)8 * 5 * H + 8 * kThreads + (size_t)4 * K * n_in +
+           (size_t)4 * K * H;
+}
+
+__device__ __forceinline__ void store_grad(float* p, double v, int accumulate) {
+    if (accumulate) v += (double)*p;
+    *p = (float)v;
+}
+
+__global__ __launch_bounds__(kThreads) void cfc_bwd_kernel(
+    const float* __restrict__ w_in, const float* __restrict__ w_rec,
+    const float* __restrict__ bias, const float* __restrict__ w_tau,
+    const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
+    const float* __restrict__ y, double dt, int K, int n_in, int H, float* __restrict__ scratch,
+    float* __restrict__ loss, int accumulate) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    double* DA = reinterpret_cast<double*>(smem);
+    double* delta = DA + (size_t)K * H;
+    double* gate = delta + 2 * H;
+    double* sp = gate + H;
+    double* sw = sp + H;
+    double* red = sw + H;
+    float* xs = reinterpret_cast<float*>(red + kThreads);
+    float* hp = xs + (size_t)K * n_in;
+
+    const int t = threadIdx.x;
+    const long long b = blockIdx.x;
+    const long long N = (long long)H * (n_in + H + 2);
+    const int G = group_size(H);
+    const int i = t / G, sub = t % G;
+
+    // per-unit constants, staged row inputs, loss seed
+    double lpart = 0.0;
+    for (int u = t; u < H; u += kThreads) {
+        const double w = (double)w_tau[u];
+        sp[u] = softplus_f64(w);
+        sw[u] = logistic_f64(w);
+        const double d = (double)h_seq[(b * K + (K - 1)) * (long long)H + u] - (double)y[b * H + u];
+        delta[u] = d;
+        lpart += 0.5 * d * d;
+    }
+    const float* xb = x + b * K * (long long)n_in;
+    for (int e = t; e < K * n_in; e += kThreads) xs[e] = xb[e];
+    for (int u = t; u < H; u += kThreads) hp[u] = h0[b * H + u];
+    const float* hsb = h_seq + b * K * (long long)H;
+    for (int e = t; e < (K - 1) * H; e += kThreads) hp[H + e] = hsb[e];
+    red[t] = lpart;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+        if (t < s) red[t] += red[t + s];
+        __syncthreads();
+    }
+    if (t == 0 && loss) loss[b] = (float)red[0];
+
+    // serial reverse chain: dL/da_k for every k, delta carried through W_rec^T
+    double gb = 0.0, gwt = 0.0;  // owned by the lane with sub == 0 of unit i
+    int cur = 0;
+    for (int k = K - 1; k >= 0; --k) {
+        const float* xk = xs + k * n_in;
+        const float* hk = hp + k * H;
+        double part = 0.0;
+        if (i < H) {
+            const float* wi = w_in + (long long)i * n_in;
+            const float* wr = w_rec + (long long)i * H;
+            for (int j = sub; j < n_in; j += G) part = fma((double)wi[j], (double)xk[j], part);
+            for (int j = sub; j < H; j += G) part = fma((double)wr[j], (double)hk[j], part);
+        }
+        part = group_sum(part, G);
+        if (i < H && sub == 0) {
+            const double a = (double)bias[i] + part;
+            const double g = 1.0 / (1.0 + exp(sp[i] * a * dt));
+            const double c = tanh(a);
+            const double d = delta[cur * H + i];
+            const double dz = d * ((double)hk[i] - c) * g * (1.0 - g);
+            const double da = d * (1.0 - g) * (1.0 - c * c) - dz * sp[i] * dt;
+            DA[k * H + i] = da;
+            gate[i] = g;
+            gb += da;
+            gwt += dz * (-a * dt) * sw[i];
+        }
+        __syncthreads();
+        // delta_k = delta_{k+1} * g + W_rec^T da ; here i indexes the column j
+        double p2 = 0.0;
+        if (i < H) {
+            const double* dak = DA + k * H;
+            for (int r = sub; r < H; r += G) p2 = fma((double)w_rec[(long long)r * H + i], dak[r], p2);
+        }
+        p2 = group_sum(p2, G);
+        if (i < H && sub == 0) delta[(cur ^ 1) * H + i] = delta[cur * H + i] * gate[i] + p2;
+        cur ^= 1;
+        __syncthreads();
+    }
+
+    // weight gradients as contractions over k; one store per scratch element
+    float* row = scratch + b * N;
+    for (int e = t; e < H * n_in; e += kThreads) {
+        const int r = e / n_in, j = e - r * n_in;
+        double s = 0.0;
+        for (int k = 0; k < K; ++k) s = fma(DA[k * H + r], (double)xs[k * n_in + j], s);
+        store_grad(row + e, s, accumulate);
+    }
+    float* rrec = row + (long long)H * n_in;
+    for (int e = t; e < H * H; e += kThreads) {
+        const int r = e / H, j = e - r * H;
+        double s = 0.0;
+        for (int k = 0; k < K; ++k) s = fma(DA[k * H + r], (double)hp[k * H + j], s);
+        store_grad(rrec + e, s, accumulate);
+    }
+    if (i < H && sub == 0) {
+        store_grad(rrec + (long long)H * H + i, gb, accumulate);
+        store_grad(rrec + (long long)H * H + H + i, gwt, accumulate);
+    }
+}
+
+// -------------------------------------------------------- reduce_axis0
+// Workgroup = 4 waves; a tile of 64 columns.  VEC=4: 16 lanes x float4 cover
+// the tile, 4 rows per wave, 16 row slots per workgroup.  VEC=1: 64 lanes x 1
+// float, 1 row per wave, 4 row slots.  Each slot sums its rows (b = slot,
+// slot + SLOTS, ...) in float64; the slots are then added in a fixed order.
+template <int VEC>
+__global__ __launch_bounds__(kThreads) void reduce_axis0_kernel(const float* __restrict__ in,
+                                                                long long B, long long N,
+                                                                float* __restrict__ out) {
+    constexpr int kLanesPerRow = 64 / VEC;        // 16 or 64
+    constexpr int kRowsPerWave = 64 / kLanesPerRow;  // 4 or 1
+    constexpr int kSlots = kRowsPerWave * (kThreads / 64);
+    __shared__ double part[kSlots][64 + 1];  // +1: rows of the tree start on distinct banks
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int slot = wave * kRowsPerWave + lane / kLanesPerRow;
+    const int c0 = (lane % kLanesPerRow) * VEC;  // first column of this lane inside the tile
+    const long long col = (long long)blockIdx.x * 64 + c0;
+
+    double acc[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.0;
+
+    if (VEC == 4) {
+        if (col < N) {  // N % 4 == 0 here, so col < N means all 4 columns are in range
+            const float* p = in + col;
+            long long bb = slot;
+            for (; bb + 3 * kSlots < B; bb += 4 * kSlots) {
+                float4 q0 = *reinterpret_cast<const float4*>(p + bb * N);
+                float4 q1 = *reinterpret_cast<const float4*>(p + (bb + kSlots) * N);
+                float4 q2 = *reinterpret_cast<const float4*>(p + (bb + 2 * kSlots) * N);
+                float4 q3 = *reinterpret_cast<const float4*>(p + (bb + 3 * kSlots) * N);
+                acc[0] += (double)q0.x; acc[1] += (double)q0.y; acc[2] += (double)q0.z; acc[3] += (double)q0.w;
+                acc[0] += (double)q1.x; acc[1] += (double)q1.y; acc[2] += (double)q1.z; acc[3] += (double)q1.w;
+                acc[0] += (double)q2.x; acc[1] += (double)q2.y; acc[2] += (double)q2.z; acc[3] += (double)q2.w;
+                acc[0] += (double)q3.x; acc[1] += (double)q3.y; acc[2] += (double)q3.z; acc[3] += (double)q3.w;
+            }
+            for (; bb < B; bb += kSlots) {
+                float4 q = *reinterpret_cast<const float4*>(p + bb * N);
+                acc[0] += (double)q.x; acc[1] += (double)q.y; acc[2] += (double)q.z; acc[3] += (double)q.w;
+            }
+        }
+    } else {
+        if (col < N) {
+            const float* p = in + col;
+            long long bb = slot;
+            for (; bb + 3 * kSlots < B; bb += 4 * kSlots) {
+                const float q0 = p[bb * N], q1 = p[(bb + kSlots) * N];
+                const float q2 = p[(bb + 2 * kSlots) * N], q3 = p[(bb + 3 * kSlots) * N];
+                acc[0] += (double)q0; acc[0] += (double)q1; acc[0] += (double)q2; acc[0] += (double)q3;
+            }
+            for (; bb < B; bb += kSlots) acc[0] += (double)p[bb * N];
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) part[slot][c0 + v] = acc[v];
+    __syncthreads();
+    if (t < 64) {
+        const long long j = (long long)blockIdx.x * 64 + t;
+        double s = 0.0;
+        for (int q = 0; q < kSlots; ++q) s += part[q][t];
+        if (j < N) out[j] = (float)s;
+    }
+}
+
+// ---------------------------------------------------------- host helpers
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+inline Range span(const void* p, long long elems) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + (uintptr_t)elems * sizeof(float)};
+}
+inline bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+// Checked a*b for non-negative operands; false on overflow of the byte count.
+inline bool mul_ok(long long a, long long b, long long* r) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > (LLONG_MAX / 4) / a) return false;
+    *r = a * b;
+    return true;
+}
+
+int check_params(const cfc_params_t* p) {
+    if (!p || !p->w_in || !p->w_rec || !p->b || !p->w_tau) return CFC_ERR_NULL;
+    if (p->n_in < 1 || p->n_hid < 1) return CFC_ERR_DIM;
+    if (p->n_in > kMaxIn || p->n_hid > kMaxHid) return CFC_ERR_UNSUPPORTED;
+    return CFC_OK;
+}
+
+std::once_flag g_attr_once;
+void set_kernel_attributes() {
+    std::call_once(g_attr_once, [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    });
+}
+
+inline int launch_status() { return hipGetLastError() == hipSuccess ? CFC_OK : CFC_ERR_HIP; }
+
+}  // namespace
+
+// ================================================================ C ABI
+extern "C" long long cfc_scratch_row_len(int n_in, int n_hid) {
+    if (n_in < 1 || n_hid < 1) return -1;
+    const long long w = (long long)n_in + (long long)n_hid + 2;
+    long long n;
+    if (!mul_ok(w, n_hid, &n)) return -1;
+    return n;
+}
+
+extern "C" const char* cfc_status_string(int code) {
+    switch (code) {
+        case CFC_OK: return "ok";
+        case CFC_ERR_NULL: return "null pointer argument";
+        case CFC_ERR_DIM: return "dimension out of range or size overflow";
+        case CFC_ERR_DT: return "dt is not finite";
+        case CFC_ERR_UNSUPPORTED: return "shape beyond the compiled kernel limits";
+        case CFC_ERR_OVERLAP: return "output range overlaps another argument";
+        case CFC_ERR_HIP: return "HIP launch error";
+        default: return "unknown status code";
+    }
+}
+
+extern "C" int cfc_forward(const cfc_params_t* params, const float* x, const float* h0, float dt,
+                           int B, int K, float* h_seq, hipStream_t stream) {
+    int rc = check_params(params);
+    if (rc) return rc;
+    if (!x || !h0 || !h_seq) return CFC_ERR_NULL;
+    if (B < 1 || K < 1) return CFC_ERR_DIM;
+    if (!std::isfinite(dt)) return CFC_ERR_DT;
+    const int n_in = params->n_in, H = params->n_hid;
+    long long nx, ns;
+    if (!mul_ok((long long)B * K, n_in, &nx) || !mul_ok((long long)B * K, H, &ns)) return CFC_ERR_DIM;
+    const Range out = span(h_seq, ns);
+    const Range ins[] = {span(x, nx), span(h0, (long long)B * H), span(params->w_in, (long long)H * n_in),
+                         span(params->w_rec, (long long)H * H), span(params->b, H), span(params->w_tau, H)};
+    for (const Range& r : ins)
+        if (overlap(out, r)) return CFC_ERR_OVERLAP;
+
+    // Window of steps whose projections are staged at once.
+    const size_t fixed = (size_t)8 * 3 * H;
+    const size_t per_k = (size_t)8 * H + (size_t)4 * n_in;
+    int KW = (int)std::min<size_t>((size_t)K, (kLdsBytes - fixed) / per_k);
+    if (KW > 64) KW = 64;
+    const size_t lds = fixed + per_k * (size_t)KW;
+    set_kernel_attributes();
+    hipLaunchKernelGGL(cfc_fwd_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
+                       params->w_rec, params->b, params->w_tau, x, h0, (double)dt, K, n_in, H, KW,
+                       h_seq);
+    return launch_status();
+}
+
+extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const float* h0,
+                            const float* h_seq, const float* y, float dt, int B, int K,
+                            float* scratch, float* loss, int flags, hipStream_t stream) {
+    int rc = check_params(params);
+    if (rc) return rc;
+    if (!x || !h0 || !h_seq || !y || !scratch) return CFC_ERR_NULL;
+    if (B < 1 || K < 1) return CFC_ERR_DIM;
+    if (flags != CFC_OVERWRITE && flags != CFC_ACCUMULATE) return CFC_ERR_DIM;
+    if (!std::isfinite(dt)) return CFC_ERR_DT;
+    const int n_in = params->n_in, H = params->n_hid;
+    const long long N = cfc_scratch_row_len(n_in, H);
+    long long nx, ns, nsc;
+    if (N < 0 || !mul_ok((long long)B * K, n_in, &nx) || !mul_ok((long long)B * K, H, &ns) ||
+        !mul_ok((long long)B, N, &nsc))
+        return CFC_ERR_DIM;
+    const size_t lds = bwd_lds_bytes(K, n_in, H);
+    if (lds > kLdsBytes) return CFC_ERR_UNSUPPORTED;
+    const Range outs[] = {span(scratch, nsc), span(loss, loss ? B : 0)};
+    const Range ins[] = {span(x, nx), span(h0, (long long)B * H), span(h_seq, ns), span(y, (long long)B * H),
+                         span(params->w_in, (long long)H * n_in), span(params->w_rec, (long long)H * H),
+                         span(params->b, H), span(params->w_tau, H)};
+    for (const Range& o : outs)
+        for (const Range& r : ins)
+            if (overlap(o, r)) return CFC_ERR_OVERLAP;
+    if (overlap(outs[0], outs[1])) return CFC_ERR_OVERLAP;
+    set_kernel_attributes();
+    hipLaunchKernelGGL(cfc_bwd_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
+                       params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, K, n_in,
+                       H, scratch, loss, flags == CFC_ACCUMULATE ? 1 : 0);
+    return launch_status();
+}
+
+extern "C" int reduce_axis0(const float* per_batch, long long B, long long N, float* out,
+                            hipStream_t stream) {
+    if (B < 0 || N < 0) return CFC_ERR_DIM;
+    long long n;
+    if (!mul_ok(B, N, &n)) return CFC_ERR_DIM;
+    if (N == 0) return CFC_OK;
+    if (!out || (B > 0 && !per_batch)) return CFC_ERR_NULL;
+    if (B > 0 && overlap(span(out, N), span(per_batch, n))) return CFC_ERR_OVERLAP;
+    const long long tiles = (N + 63) / 64;
+    if (tiles > INT_MAX) return CFC_ERR_DIM;
+    const bool vec4 = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(per_batch) % 16 == 0);
+    if (vec4)
+        hipLaunchKernelGGL(reduce_axis0_kernel<4>, dim3((unsigned)tiles), dim3(kThreads), 0, stream,
+                           per_batch, B, N, out);
+    else
+        hipLaunchKernelGGL(reduce_axis0_kernel<1>, dim3((unsigned)tiles), dim3(kThreads), 0, stream,
+                           per_batch, B, N, out);
+    return launch_status();
+}

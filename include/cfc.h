@@ -1,0 +1,141 @@
+/*
+ * cfc.h -- C ABI of libcfc_amd: a batched CfC (closed-form continuous-time)
+ * recurrent cell K-loop for AMD Instinct MI355X (gfx950).
+ *
+ * Three calls make one training step of the cell's parameter gradient:
+ *
+ *   cfc_forward   x [B,K,n_in], h0 [B,H]           -> h_seq [B,K,H]
+ *   cfc_backward  x, h0, h_seq, y [B,H]            -> scratch [B,N] (+ loss [B])
+ *   reduce_axis0  scratch [B,N]                    -> out [N]
+ *
+ * The structure -- one independent chain per batch row, a per-batch gradient
+ * scratch in which each row has a single writer and no atomics, and a
+ * separate column-sum reducer that overwrites its output -- follows the
+ * "K-loop Parallelization Implementation Plan" (foxhunt, 2026-05-17):
+ * Task 1 (the reduce_axis0 kernel), Task 2 (the block-per-batch forward),
+ * Task 3 (the block-per-batch backward writing per-batch scratch) and
+ * Task 5 (scratch zeroed once per step, K invocations accumulate, reducer
+ * before the optimizer).
+ *
+ * The cell (per unit i, elementwise; w_tau plays the per-unit role of the
+ * pages' tau[n_hid]):
+ *     a      = W_in x_k + W_rec h_k + b
+ *     g      = sigmoid(-softplus(w_tau) * a * dt)
+ *     h_k+1  = g * h_k + (1 - g) * tanh(a)
+ * and the loss of row b is  L_b = 1/2 |h_K - y_b|^2.
+ *
+ * Conventions shared by every call
+ *  - All tensors are float32, dense, row-major, in DEVICE memory owned by the
+ *    caller.  The library allocates nothing, never synchronises the device or
+ *    the stream and never copies to the host: every call only validates its
+ *    arguments on the host and enqueues kernels on `stream` (0 = the null
+ *    stream), so the calls may be captured into a HIP graph.
+ *  - Internal arithmetic of the cell and of the reducer is float64; inputs and
+ *    outputs are float32 (each output is the float32 rounding of a float64
+ *    value).
+ *  - Outputs must not overlap any input or each other (checked on the host
+ *    from the byte ranges the dimensions imply).
+ *  - Identical inputs give bitwise-identical outputs: fixed summation orders,
+ *    no atomics.
+ *  - Argument errors are reported BEFORE anything is enqueued.  A launch
+ *    failure is reported from hipGetLastError() without synchronising;
+ *    errors raised later by the device surface at the caller's next sync.
+ *  - Offsets are 64-bit: a scratch of more than 2^32 bytes is supported.
+ */
+#ifndef CFC_AMD_H
+#define CFC_AMD_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define CFC_OK 0
+#define CFC_ERR_NULL 1        /* a required pointer is NULL                          */
+#define CFC_ERR_DIM 2         /* a dimension is out of range, or a size overflows     */
+#define CFC_ERR_DT 3          /* dt is not finite                                     */
+#define CFC_ERR_UNSUPPORTED 4 /* valid but beyond what the compiled kernels support   */
+#define CFC_ERR_OVERLAP 5     /* an output range overlaps an input or another output  */
+#define CFC_ERR_HIP 6         /* the HIP runtime rejected a launch                    */
+
+/* cfc_backward flags. */
+#define CFC_OVERWRITE 0  /* scratch[b,:] = this call's gradient (no prior memset needed) */
+#define CFC_ACCUMULATE 1 /* scratch[b,:] += this call's gradient (caller zeroes first)   */
+
+/* Compiled limits: n_in and n_hid up to 256; the backward also needs
+ * K * (12 * n_hid + 4 * n_in) + 40 * n_hid + 2048 bytes of LDS <= 160 KiB,
+ * e.g. K <= 76 at n_in = n_hid = 128 and K <= 37 at n_in = n_hid = 256.
+ * The forward has no limit on K. */
+#define CFC_MAX_N_IN 256
+#define CFC_MAX_N_HID 256
+
+/* The cell's parameters, all device pointers:
+ *   w_in  [n_hid, n_in]  row-major     w_rec [n_hid, n_hid] row-major
+ *   b     [n_hid]                      w_tau [n_hid]                        */
+typedef struct cfc_params {
+    const float *w_in;
+    const float *w_rec;
+    const float *b;
+    const float *w_tau;
+    int n_in;
+    int n_hid;
+} cfc_params_t;
+
+/* Length N of one per-batch gradient row:  N = n_hid * (n_in + n_hid + 2).
+ * Row layout: [ dL/dW_in (n_hid x n_in, row-major) | dL/dW_rec (n_hid x n_hid,
+ * row-major) | dL/db (n_hid) | dL/dw_tau (n_hid) ] -- the pages' four scratch
+ * tensors (grad_w_in, grad_w_rec, grad_b, grad_tau; Task 4) laid end to end so
+ * one reducer launch covers them all.  Returns -1 if a dimension is < 1 or
+ * the product overflows. */
+long long cfc_scratch_row_len(int n_in, int n_hid);
+
+/* Forward K-loop ("K-loop Parallelization Implementation Plan", Task 2; here
+ * the whole K-loop runs in one launch instead of one launch per k).
+ *   params   cell parameters (see cfc_params_t); n_in, n_hid in [1, 256]
+ *   x        [B, K, n_in]  inputs, row b, step k at x + (b*K + k)*n_in
+ *   h0       [B, n_hid]    initial state
+ *   dt       step length (finite; 0 allowed)
+ *   B, K     batch rows >= 1, timesteps >= 1
+ *   h_seq    [B, K, n_hid] OUTPUT: h_1 ... h_K of every row (h0 not repeated)
+ * Returns a CFC_* status. */
+int cfc_forward(const cfc_params_t *params, const float *x, const float *h0, float dt,
+                int B, int K, float *h_seq, hipStream_t stream);
+
+/* Backward through time of L = sum_b L_b ("K-loop Parallelization
+ * Implementation Plan", Task 3: block-per-batch backward writing per-batch
+ * scratch, single writer per row, no atomics).
+ *   params, x, h0, dt, B, K   as for cfc_forward
+ *   h_seq    [B, K, n_hid] the forward's output for the same inputs
+ *   y        [B, n_hid]    targets
+ *   scratch  [B, N] OUTPUT, N = cfc_scratch_row_len(n_in, n_hid):
+ *            row b = dL_b / d(W_in, W_rec, b, w_tau) in the row layout above.
+ *            flags = CFC_OVERWRITE: each row is written once with this call's
+ *            gradient (equivalent to the pages' memset + K accumulating calls).
+ *            flags = CFC_ACCUMULATE: each row is read and this call's gradient
+ *            added (float64 add, one float32 rounding).
+ *   loss     [B] OUTPUT or NULL: L_b per row
+ * Returns a CFC_* status; CFC_ERR_UNSUPPORTED if the LDS bound above fails. */
+int cfc_backward(const cfc_params_t *params, const float *x, const float *h0,
+                 const float *h_seq, const float *y, float dt, int B, int K,
+                 float *scratch, float *loss, int flags, hipStream_t stream);
+
+/* Column sum ("K-loop Parallelization Implementation Plan", Task 1):
+ *   out[j] = sum_{b < B} per_batch[b, j]   for j < N, OVERWRITING out.
+ * Float64 accumulation in a fixed order (no atomics), one float32 rounding.
+ *   per_batch [B, N] float32, B >= 0, N >= 0 (B = 0 writes zeros; N = 0 is a
+ *             no-op that enqueues nothing)
+ *   out       [N] OUTPUT
+ * Returns a CFC_* status (CFC_ERR_DIM if B*N*4 overflows). */
+int reduce_axis0(const float *per_batch, long long B, long long N, float *out,
+                 hipStream_t stream);
+
+/* Static text for a status code (never NULL). */
+const char *cfc_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CFC_AMD_H */

@@ -1,0 +1,121 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects bad arguments with the documented codes before it
+touches the HIP runtime (so none of these calls enqueues anything)."""
+import ctypes
+import os
+
+import pytest
+
+import cfc_recurrent_cell_amd as C
+from cfc_recurrent_cell_amd import _lib
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libcfc_amd.so not built (run __graft_entry__.build())")
+
+FAKE = 0x10000          # never dereferenced: every call below fails validation first
+
+
+def _params(n_in=8, n_hid=16, base=FAKE):
+    return C.CfcParams(base, base + 0x100000, base + 0x200000, base + 0x300000, n_in, n_hid)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return C.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _lib.declared_symbols()
+    assert set(names) == {"cfc_scratch_row_len", "cfc_forward", "cfc_backward", "reduce_axis0",
+                          "cfc_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_scratch_row_len(lib):
+    assert lib.cfc_scratch_row_len(16, 32) == 32 * (16 + 32 + 2) == 1600
+    assert lib.cfc_scratch_row_len(128, 128) == 33024
+    assert lib.cfc_scratch_row_len(256, 256) == 131584
+    assert lib.cfc_scratch_row_len(0, 4) == -1
+    assert lib.cfc_scratch_row_len(4, -1) == -1
+    assert lib.cfc_scratch_row_len(2**31 - 1, 2**31 - 1) == -1     # overflow
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert lib.cfc_status_string(code)
+    assert lib.cfc_status_string(99) == b"unknown status code"
+
+
+def _fwd(lib, p, x=FAKE + 0x400000, h0=FAKE + 0x500000, dt=1.0, B=2, K=3, h_seq=FAKE + 0x600000):
+    return lib.cfc_forward(ctypes.byref(p) if p is not None else None, x, h0, dt, B, K, h_seq, None)
+
+
+def _bwd(lib, p, dt=1.0, B=2, K=3, flags=0, scratch=FAKE + 0x900000, loss=None, h_seq=FAKE + 0x600000):
+    return lib.cfc_backward(ctypes.byref(p) if p is not None else None, FAKE + 0x400000,
+                            FAKE + 0x500000, h_seq, FAKE + 0x700000, dt, B, K, scratch, loss,
+                            flags, None)
+
+
+def test_forward_validation(lib):
+    assert _fwd(lib, None) == C.CFC_ERR_NULL
+    p = _params()
+    p.w_rec = None
+    assert _fwd(lib, p) == C.CFC_ERR_NULL
+    assert _fwd(lib, _params(), x=None) == C.CFC_ERR_NULL
+    assert _fwd(lib, _params(), h_seq=None) == C.CFC_ERR_NULL
+    assert _fwd(lib, _params(n_in=0)) == C.CFC_ERR_DIM
+    assert _fwd(lib, _params(n_hid=-3)) == C.CFC_ERR_DIM
+    assert _fwd(lib, _params(), B=0) == C.CFC_ERR_DIM
+    assert _fwd(lib, _params(), K=0) == C.CFC_ERR_DIM
+    assert _fwd(lib, _params(), dt=float("nan")) == C.CFC_ERR_DT
+    assert _fwd(lib, _params(), dt=float("inf")) == C.CFC_ERR_DT
+    assert _fwd(lib, _params(n_in=257)) == C.CFC_ERR_UNSUPPORTED
+    assert _fwd(lib, _params(n_hid=300)) == C.CFC_ERR_UNSUPPORTED
+    # output overlapping an input: h_seq [2,3,16] starting inside x
+    assert _fwd(lib, _params(), h_seq=FAKE + 0x400000 + 8) == C.CFC_ERR_OVERLAP
+    # h_seq overlapping the weights
+    assert _fwd(lib, _params(), h_seq=FAKE + 0x100000 - 4) == C.CFC_ERR_OVERLAP
+
+
+def test_backward_validation(lib):
+    assert _bwd(lib, None) == C.CFC_ERR_NULL
+    assert _bwd(lib, _params(), scratch=None) == C.CFC_ERR_NULL
+    assert _bwd(lib, _params(), B=0) == C.CFC_ERR_DIM
+    assert _bwd(lib, _params(), flags=7) == C.CFC_ERR_DIM
+    assert _bwd(lib, _params(), dt=float("-inf")) == C.CFC_ERR_DT
+    assert _bwd(lib, _params(n_in=512)) == C.CFC_ERR_UNSUPPORTED
+    # LDS bound: K * (12 H + 4 n_in) + 40 H + 2048 <= 160 KiB
+    assert _bwd(lib, _params(n_in=128, n_hid=128), K=77) == C.CFC_ERR_UNSUPPORTED
+    assert _bwd(lib, _params(n_in=256, n_hid=256), K=38) == C.CFC_ERR_UNSUPPORTED
+    # scratch overlapping h_seq
+    assert _bwd(lib, _params(), scratch=FAKE + 0x600000 + 64) == C.CFC_ERR_OVERLAP
+    # loss overlapping scratch
+    assert _bwd(lib, _params(), loss=FAKE + 0x900000 + 4) == C.CFC_ERR_OVERLAP
+
+
+def test_backward_lds_limit_matches_header(lib):
+    """The documented K limits are exactly where the library starts refusing."""
+    def lds(K, n_in, H):
+        return K * (12 * H + 4 * n_in) + 40 * H + 2048
+    for n_in, H, kmax in ((128, 128, 76), (256, 256, 37)):
+        assert lds(kmax, n_in, H) <= 160 * 1024 < lds(kmax + 1, n_in, H)
+
+
+def test_reduce_validation(lib):
+    assert lib.reduce_axis0(FAKE, -1, 4, FAKE + 0x100000, None) == C.CFC_ERR_DIM
+    assert lib.reduce_axis0(FAKE, 4, -1, FAKE + 0x100000, None) == C.CFC_ERR_DIM
+    assert lib.reduce_axis0(FAKE, 2**40, 2**40, FAKE + 0x100000, None) == C.CFC_ERR_DIM
+    assert lib.reduce_axis0(FAKE, 4, 0, None, None) == C.CFC_OK          # N = 0: nothing to do
+    assert lib.reduce_axis0(None, 4, 8, FAKE, None) == C.CFC_ERR_NULL
+    assert lib.reduce_axis0(FAKE, 4, 8, None, None) == C.CFC_ERR_NULL
+    assert lib.reduce_axis0(FAKE, 4, 8, FAKE + 16, None) == C.CFC_ERR_OVERLAP
+
+
+def test_product_path_never_imports_the_oracle():
+    import sys
+    import subprocess
+    code = ("import sys, cfc_recurrent_cell_amd as C; C.load_library(); "
+            "assert not any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules)")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    subprocess.run([sys.executable, "-c", code], check=True, cwd=root)
