@@ -235,6 +235,399 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_kernel(
     }
 }
 
+// =====================================================================
+// Kernels for n_in <= 128 and n_hid <= 128 (the smoke and training-scale
+// workloads): every dimension is zero-padded to 128 inside the kernel, which
+// leaves the results unchanged (padded units keep a = 0, h = 0, delta = 0).
+//
+// One workgroup of 4 wave64 per batch row, as above, but
+//  * the three dense contractions -- the input projection U = X W_in^T + b
+//    (forward), the recomputed pre-activations A = [X | H_prev] [W_in | W_rec]^T
+//    + b (backward) and the weight gradients DA^T [X | H_prev] (backward) --
+//    run on the f64 matrix cores (v_mfma_f64_16x16x4f64);
+//  * the serial chain keeps its 128x128 slice of W_rec (or W_rec^T) in
+//    registers: thread (ib, jb) holds rows 4ib..4ib+3, columns 16jb..16jb+15,
+//    reads 16 values of the state from LDS, and the 8 threads of a row block
+//    combine with a reduce-scatter so that lanes jb and jb^1 both end with the
+//    total of one output unit;
+//  * those two lanes share the transcendental work: one evaluates
+//    exp(2a) -> tanh(a) = 1 - 2/(1+exp(2a)), the other exp(sp a dt) -> the gate
+//    1/(1+exp(sp a dt)), and they swap results.
+// =====================================================================
+typedef double dbl4 __attribute__((ext_vector_type(4)));
+
+// D(16x16) += A(16x4) B(4x16) in f64.  Lane l supplies A[l%16][l/16] and
+// B[l/16][l%16]; element v of lane l is D[l/16 + 4v][l%16] (checked on gfx950).
+__device__ __forceinline__ dbl4 mfma_f64(double a, double b, dbl4 c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// Lane exchange inside a quad by DPP quad_perm (xor 1 = 0xB1, xor 2 = 0x4E).
+template <int CTRL>
+__device__ __forceinline__ double quad_swap(double v) {
+    return __builtin_amdgcn_update_dpp(0.0, v, CTRL, 0xF, 0xF, false);
+}
+
+// p[r] is this lane's partial sum for output 4*ib + r; the 8 lanes jb = 0..7
+// (lane bits 0..2) of a group hold partials over disjoint column blocks.
+// Returns the full sum of output 4*ib + 2*b2 + b1 (b2 = jb bit 2, b1 = bit 1)
+// in both lanes jb and jb^1.  Fixed order, so the result is deterministic.
+__device__ __forceinline__ double reduce_scatter8(const double p[4], int jb) {
+    const bool b2 = jb & 4, b1 = jb & 2;
+    const double send0 = b2 ? p[0] : p[2], send1 = b2 ? p[1] : p[3];
+    const double keep0 = b2 ? p[2] : p[0], keep1 = b2 ? p[3] : p[1];
+    const double q0 = keep0 + __shfl_xor(send0, 4);
+    const double q1 = keep1 + __shfl_xor(send1, 4);
+    const double send = b1 ? q0 : q1, keep = b1 ? q1 : q0;
+    const double r = keep + quad_swap<0x4E>(send);
+    return r + quad_swap<0xB1>(r);
+}
+
+// tanh(a) and sigmoid(-sp*a*dt) for the unit owned by a lane pair; `gate_lane`
+// picks which of the two this lane evaluates.  Both lanes return both values.
+__device__ __forceinline__ void cell_gates(double a, double spdt, bool gate_lane, double& g,
+                                           double& c) {
+    const double z = gate_lane ? spdt * a : 2.0 * a;
+    const double r = 1.0 / (1.0 + exp(z));
+    const double val = gate_lane ? r : 1.0 - 2.0 * r;
+    const double other = quad_swap<0xB1>(val);
+    g = gate_lane ? val : other;
+    c = gate_lane ? other : val;
+}
+
+constexpr int kSmall = 128;          // padded n_in and n_hid of the small kernels
+constexpr int kSmallFwdKW = 64;      // forward steps per window
+constexpr int kSmallBwdMaxK = 64;    // backward: whole K-loop on chip
+constexpr int kSmallXS = kSmall + 2;             // padded LDS row stride (floats)
+constexpr int kSmallZW = 2 * kSmall;             // [x | h_prev] width
+constexpr int kSmallZS = kSmallZW + 2;
+
+__host__ __device__ constexpr size_t small_fwd_lds_bytes() {
+    return (size_t)8 * kSmallFwdKW * kSmall + (size_t)8 * 3 * kSmall +
+           (size_t)4 * kSmallFwdKW * kSmallXS;
+}
+__host__ __device__ inline size_t small_bwd_lds_bytes(int K) {
+    const size_t KP = (size_t)((K + 15) & ~15);
+    return 8 * KP * kSmall + (size_t)8 * 2 * kSmall + 8 * 8 + 4 * KP * kSmallZS;
+}
+
+__global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
+    const float* __restrict__ w_in, const float* __restrict__ w_rec,
+    const float* __restrict__ bias, const float* __restrict__ w_tau,
+    const float* __restrict__ x, const float* __restrict__ h0, double dt, int K, int n_in,
+    int H, float* __restrict__ h_seq) {
+    constexpr int HP = kSmall, NP = kSmall, KW = kSmallFwdKW, XS = kSmallXS;
+    extern __shared__ __align__(16) unsigned char smem[];
+    double* U = reinterpret_cast<double*>(smem);  // [KW][HP]
+    double* hb = U + KW * HP;                     // [2][HP]
+    double* spv = hb + 2 * HP;                    // [HP]
+    float* xs = reinterpret_cast<float*>(spv + HP);  // [KW][XS]
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const long long b = blockIdx.x;
+    const int jb = lane & 7;
+    const int ib = wave * 8 + (lane >> 3);
+    const int o = 4 * ib + ((jb & 4) ? 2 : 0) + ((jb & 2) ? 1 : 0);
+    const bool gate_lane = jb & 1;
+
+    for (int u = t; u < HP; u += kThreads) {
+        spv[u] = u < H ? softplus_f64((double)w_tau[u]) : 0.0;
+        hb[u] = u < H ? (double)h0[b * H + u] : 0.0;
+    }
+    int cur = 0;
+    for (int k0 = 0; k0 < K; k0 += KW) {
+        const int kw = min(KW, K - k0);
+        const int kwp = (kw + 15) & ~15;
+        __syncthreads();
+        for (int e = t; e < kwp * NP; e += kThreads) {
+            const int kk = e / NP, j = e - kk * NP;
+            float v = 0.f;
+            if (kk < kw && j < n_in) v = x[(b * K + k0 + kk) * (long long)n_in + j];
+            xs[kk * XS + j] = v;
+        }
+        __syncthreads();
+        // ---- input projection of the window on the matrix cores
+        {
+            const int KB = kwp >> 4;
+            const int ib0 = 2 * wave;
+            dbl4 acc[4][2];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) acc[kb][q] = dbl4{0.0, 0.0, 0.0, 0.0};
+            const int r0 = ib0 * 16 + (lane & 15), r1 = r0 + 16;
+            auto wload = [&](int row, int j) -> double {
+                return (row < H && j < n_in) ? (double)w_in[(long long)row * n_in + j] : 0.0;
+            };
+            int j = lane >> 4;
+            double bw0 = wload(r0, j), bw1 = wload(r1, j);
+            for (int jc = 0; jc < NP / 4; ++jc) {
+                const int jn = j + 4;
+                const double nb0 = wload(r0, jn), nb1 = wload(r1, jn);  // prefetch next chunk
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    if (kb < KB) {
+                        const double a = (double)xs[(kb * 16 + (lane & 15)) * XS + j];
+                        acc[kb][0] = mfma_f64(a, bw0, acc[kb][0]);
+                        acc[kb][1] = mfma_f64(a, bw1, acc[kb][1]);
+                    }
+                }
+                bw0 = nb0;
+                bw1 = nb1;
+                j = jn;
+            }
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                if (kb < KB) {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int i = (ib0 + q) * 16 + (lane & 15);
+                        const double bi = i < H ? (double)bias[i] : 0.0;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            U[(kb * 16 + (lane >> 4) + 4 * v) * HP + i] = acc[kb][q][v] + bi;
+                    }
+                }
+            }
+        }
+        // ---- W_rec slice into registers (rows 4ib.., columns 16jb..)
+        double wr[4][16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const int row = 4 * ib + r, col = 16 * jb + c;
+                wr[r][c] = (row < H && col < H) ? (double)w_rec[row * H + col] : 0.0;
+            }
+        const double spdt_o = spv[o] * dt;
+        __syncthreads();
+        // ---- serial recurrence through the window
+        for (int kk = 0; kk < kw; ++kk) {
+            const double* hv = hb + cur * HP;
+            double hj[16];
+#pragma unroll
+            for (int c = 0; c < 16; c += 2) {
+                const double2 v2 = *reinterpret_cast<const double2*>(hv + 16 * jb + c);
+                hj[c] = v2.x;
+                hj[c + 1] = v2.y;
+            }
+            double p[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) p[r] = fma(wr[r][c], hj[c], p[r]);
+            const double a = U[kk * HP + o] + reduce_scatter8(p, jb);
+            double g, c;
+            cell_gates(a, spdt_o, gate_lane, g, c);
+            if (!gate_lane) {
+                const double hn = g * hv[o] + (1.0 - g) * c;
+                hb[(cur ^ 1) * HP + o] = hn;
+                if (o < H) h_seq[(b * K + k0 + kk) * (long long)H + o] = (float)hn;
+            }
+            cur ^= 1;
+            __syncthreads();
+        }
+    }
+}
+
+__device__ __forceinline__ void store_grad_f(float* p, double v, int accumulate) {
+    if (accumulate) v += (double)*p;
+    *p = (float)v;
+}
+
+__global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
+    const float* __restrict__ w_in, const float* __restrict__ w_rec,
+    const float* __restrict__ bias, const float* __restrict__ w_tau,
+    const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
+    const float* __restrict__ y, double dt, int K, int n_in, int H, float* __restrict__ scratch,
+    float* __restrict__ loss, int accumulate) {
+    constexpr int HP = kSmall, NP = kSmall, ZW = kSmallZW, ZS = kSmallZS;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int KP = (K + 15) & ~15;
+    double* AD = reinterpret_cast<double*>(smem);  // [KP][HP]: a, then dL/da
+    double* spv = AD + KP * HP;                    // [HP]
+    double* swv = spv + HP;                        // [HP]
+    double* red = swv + HP;                        // [8]
+    float* zs = reinterpret_cast<float*>(red + 8);  // [KP][ZS] = [x_k | h_k]
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const long long b = blockIdx.x;
+    const long long N = (long long)H * (n_in + H + 2);
+    const int jb = lane & 7;
+    const int ib = wave * 8 + (lane >> 3);
+    const int o = 4 * ib + ((jb & 4) ? 2 : 0) + ((jb & 2) ? 1 : 0);
+    const bool gate_lane = jb & 1;
+
+    // ---- stage [x_k | h_k] for every step (h_0 = h0, h_k = h_seq[k-1])
+    for (int e = t; e < KP * ZW; e += kThreads) {
+        const int kk = e / ZW, j = e - kk * ZW;
+        float v = 0.f;
+        if (kk < K) {
+            if (j < NP) {
+                if (j < n_in) v = x[(b * K + kk) * (long long)n_in + j];
+            } else {
+                const int jj = j - NP;
+                if (jj < H) v = kk == 0 ? h0[b * H + jj] : h_seq[(b * K + kk - 1) * (long long)H + jj];
+            }
+        }
+        zs[kk * ZS + j] = v;
+    }
+    for (int u = t; u < HP; u += kThreads) {
+        const double w = u < H ? (double)w_tau[u] : 0.0;
+        spv[u] = u < H ? softplus_f64(w) : 0.0;
+        swv[u] = u < H ? logistic_f64(w) : 0.0;
+    }
+    __syncthreads();
+
+    // ---- recompute every step's pre-activation on the matrix cores
+    {
+        const int KB = KP >> 4;
+        const int ib0 = 2 * wave;
+        dbl4 acc[4][2];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) acc[kb][q] = dbl4{0.0, 0.0, 0.0, 0.0};
+        const int r0 = ib0 * 16 + (lane & 15), r1 = r0 + 16;
+        auto wload = [&](int row, int j) -> double {
+            if (row >= H) return 0.0;
+            if (j < NP) return j < n_in ? (double)w_in[(long long)row * n_in + j] : 0.0;
+            const int jj = j - NP;
+            return jj < H ? (double)w_rec[(long long)row * H + jj] : 0.0;
+        };
+        int j = lane >> 4;
+        double bw0 = wload(r0, j), bw1 = wload(r1, j);
+        for (int jc = 0; jc < ZW / 4; ++jc) {
+            const int jn = j + 4;
+            const double nb0 = jn < ZW ? wload(r0, jn) : 0.0;
+            const double nb1 = jn < ZW ? wload(r1, jn) : 0.0;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                if (kb < KB) {
+                    const double a = (double)zs[(kb * 16 + (lane & 15)) * ZS + j];
+                    acc[kb][0] = mfma_f64(a, bw0, acc[kb][0]);
+                    acc[kb][1] = mfma_f64(a, bw1, acc[kb][1]);
+                }
+            }
+            bw0 = nb0;
+            bw1 = nb1;
+            j = jn;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            if (kb < KB) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int i = (ib0 + q) * 16 + (lane & 15);
+                    const double bi = i < H ? (double)bias[i] : 0.0;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int kk = kb * 16 + (lane >> 4) + 4 * v;
+                        AD[kk * HP + i] = kk < K ? acc[kb][q][v] + bi : 0.0;
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- W_rec^T slice into registers: wt[r][c] = W_rec[16jb + c][4ib + r]
+    double wt[4][16];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const int row = 16 * jb + c, col = 4 * ib + r;
+            wt[r][c] = (row < H && col < H) ? (double)w_rec[row * H + col] : 0.0;
+        }
+
+    // ---- loss seed
+    double delta = o < H ? (double)h_seq[(b * K + K - 1) * (long long)H + o] - (double)y[b * H + o] : 0.0;
+    {
+        double l = gate_lane ? 0.0 : 0.5 * delta * delta;
+        for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+        if (lane == 0) red[wave] = l;
+    }
+    const double sp_o = spv[o], sw_o = swv[o], spdt_o = sp_o * dt;
+    __syncthreads();
+    if (t == 0 && loss) loss[b] = (float)(((red[0] + red[1]) + red[2]) + red[3]);
+
+    // ---- serial reverse chain
+    double gb = 0.0, gwt = 0.0;
+    for (int k = K - 1; k >= 0; --k) {
+        const double a = AD[k * HP + o];
+        double g, c;
+        cell_gates(a, spdt_o, gate_lane, g, c);
+        const double hk = (double)zs[k * ZS + NP + o];
+        const double dz = delta * (hk - c) * g * (1.0 - g);
+        const double da = delta * (1.0 - g) * (1.0 - c * c) - dz * spdt_o;
+        gb += da;
+        gwt += dz * (-a * dt) * sw_o;
+        if (!gate_lane) AD[k * HP + o] = da;
+        __syncthreads();
+        if (k == 0) break;
+        const double* dak = AD + k * HP + 16 * jb;
+        double dj[16];
+#pragma unroll
+        for (int cc = 0; cc < 16; cc += 2) {
+            const double2 v2 = *reinterpret_cast<const double2*>(dak + cc);
+            dj[cc] = v2.x;
+            dj[cc + 1] = v2.y;
+        }
+        double p[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = fma(wt[r][cc], dj[cc], p[r]);
+        delta = delta * g + reduce_scatter8(p, jb);
+    }
+
+    // ---- weight gradients on the matrix cores: G = DA^T [X | H_prev]
+    float* row = scratch + b * N;
+    float* rrec = row + (long long)H * n_in;
+    {
+        const int ib0 = 2 * wave;
+        const int KC = KP >> 2;
+        for (int jg = 0; jg < ZW / 64; ++jg) {
+            dbl4 acc[2][4];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) acc[q][jj] = dbl4{0.0, 0.0, 0.0, 0.0};
+            for (int kc = 0; kc < KC; ++kc) {
+                const int kk = 4 * kc + (lane >> 4);
+                const double a0 = AD[kk * HP + ib0 * 16 + (lane & 15)];
+                const double a1 = AD[kk * HP + (ib0 + 1) * 16 + (lane & 15)];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const double bz = (double)zs[kk * ZS + (jg * 4 + jj) * 16 + (lane & 15)];
+                    acc[0][jj] = mfma_f64(a0, bz, acc[0][jj]);
+                    acc[1][jj] = mfma_f64(a1, bz, acc[1][jj]);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int jcol = (jg * 4 + jj) * 16 + (lane & 15);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int i = (ib0 + q) * 16 + (lane >> 4) + 4 * v;
+                        if (i >= H) continue;
+                        if (jcol < NP) {
+                            if (jcol < n_in) store_grad_f(row + (long long)i * n_in + jcol, acc[q][jj][v], accumulate);
+                        } else if (jcol - NP < H) {
+                            store_grad_f(rrec + (long long)i * H + (jcol - NP), acc[q][jj][v], accumulate);
+                        }
+                    }
+                }
+        }
+    }
+    if (!gate_lane && o < H) {
+        store_grad_f(rrec + (long long)H * H + o, gb, accumulate);
+        store_grad_f(rrec + (long long)H * H + H + o, gwt, accumulate);
+    }
+}
+
 // -------------------------------------------------------- reduce_axis0
 // Workgroup = 4 waves; a tile of 64 columns.  VEC=4: 16 lanes x float4 cover
 // the tile, 4 rows per wave, 16 row slots per workgroup.  VEC=1: 64 lanes x 1
@@ -333,6 +726,10 @@ void set_kernel_attributes() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_small_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_small_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     });
 }
 
@@ -378,6 +775,13 @@ extern "C" int cfc_forward(const cfc_params_t* params, const float* x, const flo
     for (const Range& r : ins)
         if (overlap(out, r)) return CFC_ERR_OVERLAP;
 
+    set_kernel_attributes();
+    if (n_in <= kSmall && H <= kSmall) {
+        hipLaunchKernelGGL(cfc_fwd_small_kernel, dim3(B), dim3(kThreads), small_fwd_lds_bytes(), stream,
+                           params->w_in, params->w_rec, params->b, params->w_tau, x, h0, (double)dt, K,
+                           n_in, H, h_seq);
+        return launch_status();
+    }
     // Window of steps whose projections are staged at once.
     const size_t fixed = (size_t)8 * 3 * H;
     const size_t per_k = (size_t)8 * H + (size_t)4 * n_in;
@@ -406,7 +810,8 @@ extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const fl
     if (N < 0 || !mul_ok((long long)B * K, n_in, &nx) || !mul_ok((long long)B * K, H, &ns) ||
         !mul_ok((long long)B, N, &nsc))
         return CFC_ERR_DIM;
-    const size_t lds = bwd_lds_bytes(K, n_in, H);
+    const bool small = n_in <= kSmall && H <= kSmall && K <= kSmallBwdMaxK;
+    const size_t lds = small ? small_bwd_lds_bytes(K) : bwd_lds_bytes(K, n_in, H);
     if (lds > kLdsBytes) return CFC_ERR_UNSUPPORTED;
     const Range outs[] = {span(scratch, nsc), span(loss, loss ? B : 0)};
     const Range ins[] = {span(x, nx), span(h0, (long long)B * H), span(h_seq, ns), span(y, (long long)B * H),
@@ -417,6 +822,12 @@ extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const fl
             if (overlap(o, r)) return CFC_ERR_OVERLAP;
     if (overlap(outs[0], outs[1])) return CFC_ERR_OVERLAP;
     set_kernel_attributes();
+    if (small) {
+        hipLaunchKernelGGL(cfc_bwd_small_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
+                           params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, K,
+                           n_in, H, scratch, loss, flags == CFC_ACCUMULATE ? 1 : 0);
+        return launch_status();
+    }
     hipLaunchKernelGGL(cfc_bwd_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
                        params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, K, n_in,
                        H, scratch, loss, flags == CFC_ACCUMULATE ? 1 : 0);
