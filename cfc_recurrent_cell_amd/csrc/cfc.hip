@@ -244,12 +244,13 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_kernel(
 //  * the three dense contractions -- the input projection U = X W_in^T + b
 //    (forward), the recomputed pre-activations A = [X | H_prev] [W_in | W_rec]^T
 //    + b (backward) and the weight gradients DA^T [X | H_prev] (backward) --
-//    run on the f64 matrix cores (v_mfma_f64_16x16x4f64);
+//    run on the f64 matrix cores (v_mfma_f64_16x16x4f64); the weight operand
+//    of the first two is held in registers for the whole contraction;
 //  * the serial chain keeps its 128x128 slice of W_rec (or W_rec^T) in
 //    registers: thread (ib, jb) holds rows 4ib..4ib+3, columns 16jb..16jb+15,
 //    reads 16 values of the state from LDS, and the 8 threads of a row block
-//    combine with a reduce-scatter so that lanes jb and jb^1 both end with the
-//    total of one output unit;
+//    combine with a DPP reduce-scatter so that lanes jb and jb^1 both end with
+//    the total of one output unit;
 //  * those two lanes share the transcendental work: one evaluates
 //    exp(2a) -> tanh(a) = 1 - 2/(1+exp(2a)), the other exp(sp a dt) -> the gate
 //    1/(1+exp(sp a dt)), and they swap results.
@@ -262,35 +263,72 @@ __device__ __forceinline__ dbl4 mfma_f64(double a, double b, dbl4 c) {
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
 
-// Lane exchange inside a quad by DPP quad_perm (xor 1 = 0xB1, xor 2 = 0x4E).
+// DPP lane moves: quad_perm xor 1 (0xB1), quad_perm xor 2 (0x4E), and
+// row_half_mirror (0x141: lane i of each 8-lane half-row reads lane 7 - i).
 template <int CTRL>
-__device__ __forceinline__ double quad_swap(double v) {
+__device__ __forceinline__ double dpp_move(double v) {
     return __builtin_amdgcn_update_dpp(0.0, v, CTRL, 0xF, 0xF, false);
 }
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141;
 
 // p[r] is this lane's partial sum for output 4*ib + r; the 8 lanes jb = 0..7
 // (lane bits 0..2) of a group hold partials over disjoint column blocks.
-// Returns the full sum of output 4*ib + 2*b2 + b1 (b2 = jb bit 2, b1 = bit 1)
-// in both lanes jb and jb^1.  Fixed order, so the result is deterministic.
+// Returns the full sum of output 4*ib + 2*(jb>>2) + ((jb>>1)&1) in both lanes
+// jb and jb^1.  Stage 1 pairs jb with 7-jb (half-mirror), stage 2 with jb^2,
+// stage 3 with jb^1; each stage halves the values a lane carries.  Fixed
+// order, so the result is deterministic.
 __device__ __forceinline__ double reduce_scatter8(const double p[4], int jb) {
-    const bool b2 = jb & 4, b1 = jb & 2;
-    const double send0 = b2 ? p[0] : p[2], send1 = b2 ? p[1] : p[3];
-    const double keep0 = b2 ? p[2] : p[0], keep1 = b2 ? p[3] : p[1];
-    const double q0 = keep0 + __shfl_xor(send0, 4);
-    const double q1 = keep1 + __shfl_xor(send1, 4);
+    const bool hi = jb & 4, b1 = jb & 2;
+    const double send0 = hi ? p[0] : p[2], send1 = hi ? p[1] : p[3];
+    const double keep0 = hi ? p[2] : p[0], keep1 = hi ? p[3] : p[1];
+    const double q0 = keep0 + dpp_move<kDppHalfMirror>(send0);
+    const double q1 = keep1 + dpp_move<kDppHalfMirror>(send1);
     const double send = b1 ? q0 : q1, keep = b1 ? q1 : q0;
-    const double r = keep + quad_swap<0x4E>(send);
-    return r + quad_swap<0xB1>(r);
+    const double r = keep + dpp_move<kDppXor2>(send);
+    return r + dpp_move<kDppXor1>(r);
+}
+
+// e^x for |x| <= 700: x = n ln2 + r with the two-constant (Cody-Waite) split
+// of ln2, |r| <= ln2/2, e^r by its degree-13 Taylor polynomial (truncation
+// below 5e-18 relative) evaluated with Estrin's scheme for a short dependency
+// chain, then scaled by 2^n.
+__device__ __forceinline__ double exp_f64(double x) {
+    constexpr double kLog2e = 1.4426950408889634074;
+    constexpr double kLn2Hi = 6.93147180369123816490e-01;
+    constexpr double kLn2Lo = 1.90821492927058770002e-10;
+    const double n = __builtin_rint(x * kLog2e);
+    double r = fma(-n, kLn2Hi, x);
+    r = fma(-n, kLn2Lo, r);
+    constexpr double c2 = 1.0 / 2, c3 = 1.0 / 6, c4 = 1.0 / 24, c5 = 1.0 / 120, c6 = 1.0 / 720,
+                     c7 = 1.0 / 5040, c8 = 1.0 / 40320, c9 = 1.0 / 362880, c10 = 1.0 / 3628800,
+                     c11 = 1.0 / 39916800, c12 = 1.0 / 479001600, c13 = 1.0 / 6227020800.0;
+    const double r2 = r * r, r4 = r2 * r2, r8 = r4 * r4;
+    const double q0 = 1.0 + r, q1 = fma(c3, r, c2), q2 = fma(c5, r, c4), q3 = fma(c7, r, c6);
+    const double q4 = fma(c9, r, c8), q5 = fma(c11, r, c10), q6 = fma(c13, r, c12);
+    const double s0 = fma(q1, r2, q0), s1 = fma(q3, r2, q2), s2 = fma(q5, r2, q4);
+    const double t0 = fma(s1, r4, s0), t1 = fma(q6, r4, s2);
+    return ldexp(fma(t1, r8, t0), (int)n);
+}
+
+// 1 / (1 + e^z) for any finite z: |z| is clamped to 700 (beyond it the result
+// is 0 or 1 to double precision); reciprocal by v_rcp_f64 and two Newton steps.
+__device__ __forceinline__ double inv_one_plus_exp(double z) {
+    z = fmin(fmax(z, -700.0), 700.0);
+    const double d = 1.0 + exp_f64(z);
+    double y = __builtin_amdgcn_rcp(d);
+    double e = fma(-d, y, 1.0);
+    y = fma(y, e, y);
+    e = fma(-d, y, 1.0);
+    return fma(y, e, y);
 }
 
 // tanh(a) and sigmoid(-sp*a*dt) for the unit owned by a lane pair; `gate_lane`
 // picks which of the two this lane evaluates.  Both lanes return both values.
 __device__ __forceinline__ void cell_gates(double a, double spdt, bool gate_lane, double& g,
                                            double& c) {
-    const double z = gate_lane ? spdt * a : 2.0 * a;
-    const double r = 1.0 / (1.0 + exp(z));
-    const double val = gate_lane ? r : 1.0 - 2.0 * r;
-    const double other = quad_swap<0xB1>(val);
+    const double r = inv_one_plus_exp(gate_lane ? spdt * a : 2.0 * a);
+    const double val = gate_lane ? r : fma(-2.0, r, 1.0);
+    const double other = dpp_move<kDppXor1>(val);
     g = gate_lane ? val : other;
     c = gate_lane ? other : val;
 }
@@ -306,9 +344,52 @@ __host__ __device__ constexpr size_t small_fwd_lds_bytes() {
     return (size_t)8 * kSmallFwdKW * kSmall + (size_t)8 * 3 * kSmall +
            (size_t)4 * kSmallFwdKW * kSmallXS;
 }
-__host__ __device__ inline size_t small_bwd_lds_bytes(int K) {
-    const size_t KP = (size_t)((K + 15) & ~15);
-    return 8 * KP * kSmall + (size_t)8 * 2 * kSmall + 8 * 8 + 4 * KP * kSmallZS;
+// The backward always stages kSmallBwdMaxK rows (rows >= K are zero), so its
+// contractions run without row guards.
+__host__ __device__ constexpr size_t small_bwd_lds_bytes() {
+    return (size_t)8 * kSmallBwdMaxK * kSmall + (size_t)8 * 2 * kSmall + 8 * 8 +
+           (size_t)4 * kSmallBwdMaxK * kSmallZS;
+}
+
+// Copy `rows` rows of `width` floats (source rows contiguous, row stride
+// src_stride) into LDS rows of stride dst_stride, zero-filling columns
+// [width, pad_width) and rows [rows, pad_rows).  Vector path when the source is
+// 16-byte aligned and width == pad_width is a multiple of 4.
+__device__ __forceinline__ void stage_rows(float* dst, int dst_stride, const float* src,
+                                           long long src_stride, int rows, int width, int pad_rows,
+                                           int pad_width, int t) {
+    const bool vec = width == pad_width && (width & 3) == 0 && (src_stride & 3) == 0 &&
+                     (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+    if (vec) {
+        const int q = width >> 2;  // float4 per row
+        const int total = pad_rows * q;
+        for (int e0 = t; e0 < total; e0 += 4 * kThreads) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * kThreads;
+                const int r = e / q, c4 = e - r * q;
+                v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (e < total && r < rows)
+                    v[u] = *reinterpret_cast<const float4*>(src + r * src_stride + 4 * c4);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * kThreads;
+                if (e < total) {
+                    const int r = e / q, c4 = e - r * q;
+                    float2* d = reinterpret_cast<float2*>(dst + r * dst_stride + 4 * c4);
+                    d[0] = make_float2(v[u].x, v[u].y);
+                    d[1] = make_float2(v[u].z, v[u].w);
+                }
+            }
+        }
+    } else {
+        for (int e = t; e < pad_rows * pad_width; e += kThreads) {
+            const int r = e / pad_width, c = e - r * pad_width;
+            dst[r * dst_stride + c] = (r < rows && c < width) ? src[r * src_stride + c] : 0.f;
+        }
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
@@ -330,97 +411,102 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
     const int o = 4 * ib + ((jb & 4) ? 2 : 0) + ((jb & 2) ? 1 : 0);
     const bool gate_lane = jb & 1;
 
+    // weight operand of the input projection, kept in registers:
+    // wb[q][jc] = W_in[(2*wave + q)*16 + lane%16][4*jc + lane/16]
+    double wb[2][NP / 4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int row = (2 * wave + q) * 16 + (lane & 15);
+        const int rowc = min(row, H - 1);
+#pragma unroll
+        for (int jc = 0; jc < NP / 4; ++jc) {
+            const int col = 4 * jc + (lane >> 4);
+            const float v = w_in[(long long)rowc * n_in + min(col, n_in - 1)];
+            wb[q][jc] = (row < H && col < n_in) ? (double)v : 0.0;
+        }
+    }
+    // W_rec slice for the recurrence: wr[r][c] = W_rec[4ib + r][16jb + c]
+    double wr[4][16];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = 4 * ib + r, rowc = min(row, H - 1);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const int col = 16 * jb + c;
+            const float v = w_rec[(long long)rowc * H + min(col, H - 1)];
+            wr[r][c] = (row < H && col < H) ? (double)v : 0.0;
+        }
+    }
     for (int u = t; u < HP; u += kThreads) {
         spv[u] = u < H ? softplus_f64((double)w_tau[u]) : 0.0;
         hb[u] = u < H ? (double)h0[b * H + u] : 0.0;
     }
+    double hprev = o < H ? (double)h0[b * H + o] : 0.0;
+    const double bias_q0 = (2 * wave) * 16 + (lane & 15) < H ? (double)bias[(2 * wave) * 16 + (lane & 15)] : 0.0;
+    const double bias_q1 = (2 * wave + 1) * 16 + (lane & 15) < H ? (double)bias[(2 * wave + 1) * 16 + (lane & 15)] : 0.0;
+
     int cur = 0;
     for (int k0 = 0; k0 < K; k0 += KW) {
         const int kw = min(KW, K - k0);
-        const int kwp = (kw + 15) & ~15;
-        __syncthreads();
-        for (int e = t; e < kwp * NP; e += kThreads) {
-            const int kk = e / NP, j = e - kk * NP;
-            float v = 0.f;
-            if (kk < kw && j < n_in) v = x[(b * K + k0 + kk) * (long long)n_in + j];
-            xs[kk * XS + j] = v;
-        }
+        __syncthreads();  // the previous window is done with xs and U
+        stage_rows(xs, XS, x + (b * K + k0) * (long long)n_in, n_in, kw, n_in, KW, NP, t);
         __syncthreads();
         // ---- input projection of the window on the matrix cores
         {
-            const int KB = kwp >> 4;
-            const int ib0 = 2 * wave;
             dbl4 acc[4][2];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int q = 0; q < 2; ++q) acc[kb][q] = dbl4{0.0, 0.0, 0.0, 0.0};
-            const int r0 = ib0 * 16 + (lane & 15), r1 = r0 + 16;
-            auto wload = [&](int row, int j) -> double {
-                return (row < H && j < n_in) ? (double)w_in[(long long)row * n_in + j] : 0.0;
-            };
-            int j = lane >> 4;
-            double bw0 = wload(r0, j), bw1 = wload(r1, j);
+            const float* xa = xs + (lane & 15) * XS + (lane >> 4);
+#pragma unroll
             for (int jc = 0; jc < NP / 4; ++jc) {
-                const int jn = j + 4;
-                const double nb0 = wload(r0, jn), nb1 = wload(r1, jn);  // prefetch next chunk
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    if (kb < KB) {
-                        const double a = (double)xs[(kb * 16 + (lane & 15)) * XS + j];
-                        acc[kb][0] = mfma_f64(a, bw0, acc[kb][0]);
-                        acc[kb][1] = mfma_f64(a, bw1, acc[kb][1]);
-                    }
-                }
-                bw0 = nb0;
-                bw1 = nb1;
-                j = jn;
-            }
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                if (kb < KB) {
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const int i = (ib0 + q) * 16 + (lane & 15);
-                        const double bi = i < H ? (double)bias[i] : 0.0;
-#pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            U[(kb * 16 + (lane >> 4) + 4 * v) * HP + i] = acc[kb][q][v] + bi;
-                    }
+                    const double a = (double)xa[kb * 16 * XS + 4 * jc];
+                    acc[kb][0] = mfma_f64(a, wb[0][jc], acc[kb][0]);
+                    acc[kb][1] = mfma_f64(a, wb[1][jc], acc[kb][1]);
                 }
             }
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    double* urow = U + (kb * 16 + (lane >> 4) + 4 * v) * HP + (2 * wave) * 16 + (lane & 15);
+                    urow[0] = acc[kb][0][v] + bias_q0;
+                    urow[16] = acc[kb][1][v] + bias_q1;
+                }
         }
-        // ---- W_rec slice into registers (rows 4ib.., columns 16jb..)
-        double wr[4][16];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const int row = 4 * ib + r, col = 16 * jb + c;
-                wr[r][c] = (row < H && col < H) ? (double)w_rec[row * H + col] : 0.0;
-            }
         const double spdt_o = spv[o] * dt;
         __syncthreads();
         // ---- serial recurrence through the window
         for (int kk = 0; kk < kw; ++kk) {
-            const double* hv = hb + cur * HP;
+            const double u = U[kk * HP + o];
+            const double* hv = hb + cur * HP + 16 * jb;
             double hj[16];
 #pragma unroll
             for (int c = 0; c < 16; c += 2) {
-                const double2 v2 = *reinterpret_cast<const double2*>(hv + 16 * jb + c);
+                const double2 v2 = *reinterpret_cast<const double2*>(hv + c);
                 hj[c] = v2.x;
                 hj[c + 1] = v2.y;
             }
-            double p[4] = {0.0, 0.0, 0.0, 0.0};
+            double pe[4] = {0.0, 0.0, 0.0, 0.0}, po[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-            for (int c = 0; c < 16; ++c)
+            for (int c = 0; c < 16; c += 2)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) p[r] = fma(wr[r][c], hj[c], p[r]);
-            const double a = U[kk * HP + o] + reduce_scatter8(p, jb);
+                for (int r = 0; r < 4; ++r) {
+                    pe[r] = fma(wr[r][c], hj[c], pe[r]);
+                    po[r] = fma(wr[r][c + 1], hj[c + 1], po[r]);
+                }
+            double p[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = pe[r] + po[r];
+            const double a = u + reduce_scatter8(p, jb);
             double g, c;
             cell_gates(a, spdt_o, gate_lane, g, c);
+            const double hn = fma(g, hprev - c, c);  // g*h + (1-g)*c
+            hprev = hn;
             if (!gate_lane) {
-                const double hn = g * hv[o] + (1.0 - g) * c;
                 hb[(cur ^ 1) * HP + o] = hn;
                 if (o < H) h_seq[(b * K + k0 + kk) * (long long)H + o] = (float)hn;
             }
@@ -443,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     float* __restrict__ loss, int accumulate) {
     constexpr int HP = kSmall, NP = kSmall, ZW = kSmallZW, ZS = kSmallZS;
     extern __shared__ __align__(16) unsigned char smem[];
-    const int KP = (K + 15) & ~15;
+    constexpr int KP = kSmallBwdMaxK;
     double* AD = reinterpret_cast<double*>(smem);  // [KP][HP]: a, then dL/da
     double* spv = AD + KP * HP;                    // [HP]
     double* swv = spv + HP;                        // [HP]
@@ -458,74 +544,68 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     const int o = 4 * ib + ((jb & 4) ? 2 : 0) + ((jb & 2) ? 1 : 0);
     const bool gate_lane = jb & 1;
 
-    // ---- stage [x_k | h_k] for every step (h_0 = h0, h_k = h_seq[k-1])
-    for (int e = t; e < KP * ZW; e += kThreads) {
-        const int kk = e / ZW, j = e - kk * ZW;
-        float v = 0.f;
-        if (kk < K) {
-            if (j < NP) {
-                if (j < n_in) v = x[(b * K + kk) * (long long)n_in + j];
+    // weight operand of the recomputation, in registers:
+    // wb[q][jc] = [W_in | W_rec][(2*wave + q)*16 + lane%16][4*jc + lane/16]
+    double wb[2][ZW / 4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int row = (2 * wave + q) * 16 + (lane & 15);
+        const int rowc = min(row, H - 1);
+#pragma unroll
+        for (int jc = 0; jc < ZW / 4; ++jc) {
+            const int col = 4 * jc + (lane >> 4);
+            double v;
+            if (jc < NP / 4) {  // compile-time after unrolling
+                const float f = w_in[(long long)rowc * n_in + min(col, n_in - 1)];
+                v = (row < H && col < n_in) ? (double)f : 0.0;
             } else {
-                const int jj = j - NP;
-                if (jj < H) v = kk == 0 ? h0[b * H + jj] : h_seq[(b * K + kk - 1) * (long long)H + jj];
+                const int cr = col - NP;
+                const float f = w_rec[(long long)rowc * H + min(cr, H - 1)];
+                v = (row < H && cr < H) ? (double)f : 0.0;
             }
+            wb[q][jc] = v;
         }
-        zs[kk * ZS + j] = v;
     }
+
+    // ---- stage [x_k | h_k] for every step (h_0 = h0, h_k = h_seq[k-1])
+    stage_rows(zs, ZS, x + b * K * (long long)n_in, n_in, K, n_in, KP, NP, t);
+    stage_rows(zs + NP, ZS, h0 + b * H, H, 1, H, 1, HP, t);
+    if (K > 1) stage_rows(zs + ZS + NP, ZS, h_seq + b * K * (long long)H, H, K - 1, H, KP - 1, HP, t);
+    else stage_rows(zs + ZS + NP, ZS, h_seq, H, 0, H, KP - 1, HP, t);
     for (int u = t; u < HP; u += kThreads) {
         const double w = u < H ? (double)w_tau[u] : 0.0;
         spv[u] = u < H ? softplus_f64(w) : 0.0;
         swv[u] = u < H ? logistic_f64(w) : 0.0;
     }
+    const double bias_q0 = (2 * wave) * 16 + (lane & 15) < H ? (double)bias[(2 * wave) * 16 + (lane & 15)] : 0.0;
+    const double bias_q1 = (2 * wave + 1) * 16 + (lane & 15) < H ? (double)bias[(2 * wave + 1) * 16 + (lane & 15)] : 0.0;
     __syncthreads();
 
     // ---- recompute every step's pre-activation on the matrix cores
     {
-        const int KB = KP >> 4;
-        const int ib0 = 2 * wave;
         dbl4 acc[4][2];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int q = 0; q < 2; ++q) acc[kb][q] = dbl4{0.0, 0.0, 0.0, 0.0};
-        const int r0 = ib0 * 16 + (lane & 15), r1 = r0 + 16;
-        auto wload = [&](int row, int j) -> double {
-            if (row >= H) return 0.0;
-            if (j < NP) return j < n_in ? (double)w_in[(long long)row * n_in + j] : 0.0;
-            const int jj = j - NP;
-            return jj < H ? (double)w_rec[(long long)row * H + jj] : 0.0;
-        };
-        int j = lane >> 4;
-        double bw0 = wload(r0, j), bw1 = wload(r1, j);
-        for (int jc = 0; jc < ZW / 4; ++jc) {
-            const int jn = j + 4;
-            const double nb0 = jn < ZW ? wload(r0, jn) : 0.0;
-            const double nb1 = jn < ZW ? wload(r1, jn) : 0.0;
+        const float* za = zs + (lane & 15) * ZS + (lane >> 4);
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                if (kb < KB) {
-                    const double a = (double)zs[(kb * 16 + (lane & 15)) * ZS + j];
-                    acc[kb][0] = mfma_f64(a, bw0, acc[kb][0]);
-                    acc[kb][1] = mfma_f64(a, bw1, acc[kb][1]);
-                }
+        for (int jc = 0; jc < ZW / 4; ++jc) {
+#pragma unroll
+            for (int kb = 0; kb < KP / 16; ++kb) {
+                const double a = (double)za[kb * 16 * ZS + 4 * jc];
+                acc[kb][0] = mfma_f64(a, wb[0][jc], acc[kb][0]);
+                acc[kb][1] = mfma_f64(a, wb[1][jc], acc[kb][1]);
             }
-            bw0 = nb0;
-            bw1 = nb1;
-            j = jn;
         }
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            if (kb < KB) {
+        for (int kb = 0; kb < KP / 16; ++kb) {
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int i = (ib0 + q) * 16 + (lane & 15);
-                    const double bi = i < H ? (double)bias[i] : 0.0;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int kk = kb * 16 + (lane >> 4) + 4 * v;
-                        AD[kk * HP + i] = kk < K ? acc[kb][q][v] + bi : 0.0;
-                    }
-                }
+            for (int v = 0; v < 4; ++v) {
+                const int kk = kb * 16 + (lane >> 4) + 4 * v;
+                double* arow = AD + kk * HP + (2 * wave) * 16 + (lane & 15);
+                arow[0] = kk < K ? acc[kb][0][v] + bias_q0 : 0.0;
+                arow[16] = kk < K ? acc[kb][1][v] + bias_q1 : 0.0;
             }
         }
     }
@@ -533,12 +613,15 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     // ---- W_rec^T slice into registers: wt[r][c] = W_rec[16jb + c][4ib + r]
     double wt[4][16];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 4; ++r) {
+        const int col = 4 * ib + r, colc = min(col, H - 1);
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
-            const int row = 16 * jb + c, col = 4 * ib + r;
-            wt[r][c] = (row < H && col < H) ? (double)w_rec[row * H + col] : 0.0;
+            const int row = 16 * jb + c;
+            const float f = w_rec[(long long)min(row, H - 1) * H + colc];
+            wt[r][c] = (row < H && col < H) ? (double)f : 0.0;
         }
+    }
 
     // ---- loss seed
     double delta = o < H ? (double)h_seq[(b * K + K - 1) * (long long)H + o] - (double)y[b * H + o] : 0.0;
@@ -553,11 +636,16 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
 
     // ---- serial reverse chain
     double gb = 0.0, gwt = 0.0;
+    double a_next = AD[(K - 1) * HP + o];
+    double h_next = (double)zs[(K - 1) * ZS + NP + o];
     for (int k = K - 1; k >= 0; --k) {
-        const double a = AD[k * HP + o];
+        const double a = a_next, hk = h_next;
+        if (k > 0) {
+            a_next = AD[(k - 1) * HP + o];
+            h_next = (double)zs[(k - 1) * ZS + NP + o];
+        }
         double g, c;
         cell_gates(a, spdt_o, gate_lane, g, c);
-        const double hk = (double)zs[k * ZS + NP + o];
         const double dz = delta * (hk - c) * g * (1.0 - g);
         const double da = delta * (1.0 - g) * (1.0 - c * c) - dz * spdt_o;
         gb += da;
@@ -573,12 +661,18 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
             dj[cc] = v2.x;
             dj[cc + 1] = v2.y;
         }
-        double p[4] = {0.0, 0.0, 0.0, 0.0};
+        double pe[4] = {0.0, 0.0, 0.0, 0.0}, po[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int cc = 0; cc < 16; ++cc)
+        for (int cc = 0; cc < 16; cc += 2)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = fma(wt[r][cc], dj[cc], p[r]);
-        delta = delta * g + reduce_scatter8(p, jb);
+            for (int r = 0; r < 4; ++r) {
+                pe[r] = fma(wt[r][cc], dj[cc], pe[r]);
+                po[r] = fma(wt[r][cc + 1], dj[cc + 1], po[r]);
+            }
+        double p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = pe[r] + po[r];
+        delta = fma(delta, g, reduce_scatter8(p, jb));
     }
 
     // ---- weight gradients on the matrix cores: G = DA^T [X | H_prev]
@@ -586,23 +680,35 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     float* rrec = row + (long long)H * n_in;
     {
         const int ib0 = 2 * wave;
-        const int KC = KP >> 2;
+        constexpr int KC = KP / 4;
+        const double* ada = AD + (lane >> 4) * HP + ib0 * 16 + (lane & 15);
+        const float* zb = zs + (lane >> 4) * ZS + (lane & 15);
         for (int jg = 0; jg < ZW / 64; ++jg) {
             dbl4 acc[2][4];
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) acc[q][jj] = dbl4{0.0, 0.0, 0.0, 0.0};
+            // operands of chunk kc: rows 4kc + lane/16
+            double a0 = ada[0], a1 = ada[16];
+            double bz[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) bz[jj] = (double)zb[(jg * 4 + jj) * 16];
             for (int kc = 0; kc < KC; ++kc) {
-                const int kk = 4 * kc + (lane >> 4);
-                const double a0 = AD[kk * HP + ib0 * 16 + (lane & 15)];
-                const double a1 = AD[kk * HP + (ib0 + 1) * 16 + (lane & 15)];
+                const int kn = kc + 1 < KC ? kc + 1 : kc;
+                const double na0 = ada[4 * kn * HP], na1 = ada[4 * kn * HP + 16];
+                double nbz[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) nbz[jj] = (double)zb[4 * kn * ZS + (jg * 4 + jj) * 16];
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const double bz = (double)zs[kk * ZS + (jg * 4 + jj) * 16 + (lane & 15)];
-                    acc[0][jj] = mfma_f64(a0, bz, acc[0][jj]);
-                    acc[1][jj] = mfma_f64(a1, bz, acc[1][jj]);
+                    acc[0][jj] = mfma_f64(a0, bz[jj], acc[0][jj]);
+                    acc[1][jj] = mfma_f64(a1, bz[jj], acc[1][jj]);
                 }
+                a0 = na0;
+                a1 = na1;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) bz[jj] = nbz[jj];
             }
 #pragma unroll
             for (int q = 0; q < 2; ++q)
@@ -811,7 +917,7 @@ extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const fl
         !mul_ok((long long)B, N, &nsc))
         return CFC_ERR_DIM;
     const bool small = n_in <= kSmall && H <= kSmall && K <= kSmallBwdMaxK;
-    const size_t lds = small ? small_bwd_lds_bytes(K) : bwd_lds_bytes(K, n_in, H);
+    const size_t lds = small ? small_bwd_lds_bytes() : bwd_lds_bytes(K, n_in, H);
     if (lds > kLdsBytes) return CFC_ERR_UNSUPPORTED;
     const Range outs[] = {span(scratch, nsc), span(loss, loss ? B : 0)};
     const Range ins[] = {span(x, nx), span(h0, (long long)B * H), span(h_seq, ns), span(y, (long long)B * H),

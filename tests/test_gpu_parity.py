@@ -37,6 +37,16 @@ def _own_sum_check(out_gpu, scratch_gpu_host, what):
     assert bad.size == 0, f"{what}: reduce differs from the exact sum of its input by >1 ulp at {bad[:5]}"
 
 
+def _ulp_check(got_f32, want_f64, what):
+    """The forward is float64 inside from float32 inputs, so each h_seq element
+    must be within one float32 ulp of the float64 oracle value."""
+    want = np.asarray(want_f64, dtype=np.float64)
+    diff = np.abs(np.asarray(got_f32, dtype=np.float64) - want)
+    ulp = np.spacing(np.abs(want.astype(np.float32))).astype(np.float64)
+    bad = np.flatnonzero(diff.ravel() > ulp.ravel())
+    assert bad.size == 0, f"{what}: {bad.size} h_seq elements more than 1 float32 ulp from the oracle"
+
+
 def _full_check(inp, what, threads=None):
     threads = threads or oracle_threads()
     say(f"[parity] {what}: B={inp.x.shape[0]} K={inp.x.shape[1]} n_in={inp.x.shape[2]} "
@@ -46,6 +56,7 @@ def _full_check(inp, what, threads=None):
     g_h, g_s, g_l, g_o = host(h_seq), host(scratch), host(loss), host(out)
     ref = O.cfc_step(inp, threads=threads)
     assert_close(g_h, ref["h_seq"], what + " h_seq")
+    _ulp_check(g_h, ref["h_seq"], what)
     assert_close(g_s, ref["scratch"], what + " scratch")
     assert_close(g_l, ref["loss"], what + " loss")
     assert_close(g_o, ref["out"], what + " out")
@@ -94,6 +105,7 @@ def test_large_workload_all_rows():
     say(f"[parity] {cfg.name}: oracle forward ({threads} threads)")
     ref_h = O.cfc_forward(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x, inp.h0, inp.dt, threads=threads)
     assert_close(host(h_seq), ref_h, cfg.name + " h_seq")
+    _ulp_check(host(h_seq), ref_h, cfg.name)
     N = W.scratch_row_len(cfg.n_in, cfg.n_hid)
     ref_out = np.zeros(N)
     own_out = np.zeros(N)
@@ -151,6 +163,7 @@ def test_long_forward_only():
     h = C.cfc_forward(d["w_in"], d["w_rec"], d["b"], d["w_tau"], d["x"], d["h0"], d["dt"])
     ref = O.cfc_forward(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x, inp.h0, inp.dt)
     assert_close(host(h), ref, "forward K=300")
+    _ulp_check(host(h), ref, "forward K=300")
 
 
 def test_backward_rejects_k_beyond_lds():
