@@ -392,6 +392,26 @@ __device__ __forceinline__ void stage_rows(float* dst, int dst_stride, const flo
     }
 }
 
+// dst[c] = src[c] widened to double for c < valid, 0 beyond (src is read only
+// below `valid`).  Float4 loads when the whole span is valid and aligned.
+template <int COUNT>
+__device__ __forceinline__ void load_span_f64(double (&dst)[COUNT], const float* src, int valid) {
+    const bool vec = valid >= COUNT && (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+    if (vec) {
+#pragma unroll
+        for (int m = 0; m < COUNT / 4; ++m) {
+            const float4 v = reinterpret_cast<const float4*>(src)[m];
+            dst[4 * m] = v.x;
+            dst[4 * m + 1] = v.y;
+            dst[4 * m + 2] = v.z;
+            dst[4 * m + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < COUNT; ++c) dst[c] = c < valid ? (double)src[c] : 0.0;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
@@ -411,31 +431,25 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
     const int o = 4 * ib + ((jb & 4) ? 2 : 0) + ((jb & 2) ? 1 : 0);
     const bool gate_lane = jb & 1;
 
-    // weight operand of the input projection, kept in registers:
-    // wb[q][jc] = W_in[(2*wave + q)*16 + lane%16][4*jc + lane/16]
+    // Weight operand of the input projection, kept in registers.  The
+    // contraction index of chunk jc in k-slot s = lane/16 is j = 32*s + jc, so a
+    // lane's operands are one contiguous span of a W_in row:
+    // wb[q][jc] = W_in[(2*wave + q)*16 + lane%16][32*(lane/16) + jc]
+    const int slot = lane >> 4;
     double wb[2][NP / 4];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int row = (2 * wave + q) * 16 + (lane & 15);
-        const int rowc = min(row, H - 1);
-#pragma unroll
-        for (int jc = 0; jc < NP / 4; ++jc) {
-            const int col = 4 * jc + (lane >> 4);
-            const float v = w_in[(long long)rowc * n_in + min(col, n_in - 1)];
-            wb[q][jc] = (row < H && col < n_in) ? (double)v : 0.0;
-        }
+        const int valid = row < H ? min(max(n_in - 32 * slot, 0), NP / 4) : 0;
+        load_span_f64<NP / 4>(wb[q], w_in + (long long)min(row, H - 1) * n_in + min(32 * slot, n_in - 1), valid);
     }
     // W_rec slice for the recurrence: wr[r][c] = W_rec[4ib + r][16jb + c]
     double wr[4][16];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int row = 4 * ib + r, rowc = min(row, H - 1);
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            const int col = 16 * jb + c;
-            const float v = w_rec[(long long)rowc * H + min(col, H - 1)];
-            wr[r][c] = (row < H && col < H) ? (double)v : 0.0;
-        }
+        const int row = 4 * ib + r;
+        const int valid = row < H ? min(max(H - 16 * jb, 0), 16) : 0;
+        load_span_f64<16>(wr[r], w_rec + (long long)min(row, H - 1) * H + min(16 * jb, H - 1), valid);
     }
     for (int u = t; u < HP; u += kThreads) {
         spv[u] = u < H ? softplus_f64((double)w_tau[u]) : 0.0;
@@ -458,12 +472,12 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int q = 0; q < 2; ++q) acc[kb][q] = dbl4{0.0, 0.0, 0.0, 0.0};
-            const float* xa = xs + (lane & 15) * XS + (lane >> 4);
+            const float* xa = xs + (lane & 15) * XS + 32 * slot;
 #pragma unroll
             for (int jc = 0; jc < NP / 4; ++jc) {
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    const double a = (double)xa[kb * 16 * XS + 4 * jc];
+                    const double a = (double)xa[kb * 16 * XS + jc];
                     acc[kb][0] = mfma_f64(a, wb[0][jc], acc[kb][0]);
                     acc[kb][1] = mfma_f64(a, wb[1][jc], acc[kb][1]);
                 }
@@ -544,27 +558,23 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     const int o = 4 * ib + ((jb & 4) ? 2 : 0) + ((jb & 2) ? 1 : 0);
     const bool gate_lane = jb & 1;
 
-    // weight operand of the recomputation, in registers:
-    // wb[q][jc] = [W_in | W_rec][(2*wave + q)*16 + lane%16][4*jc + lane/16]
+    // Weight operand of the recomputation, in registers.  Chunk jc of k-slot
+    // s = lane/16 contracts index j = 64*s + jc of [x | h_prev], so a lane holds
+    // one contiguous 64-wide span of a row of W_in (s = 0, 1) or W_rec (s = 2, 3):
+    // wb[q][jc] = [W_in | W_rec][(2*wave + q)*16 + lane%16][64*s + jc]
+    const int slot = lane >> 4;
     double wb[2][ZW / 4];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int row = (2 * wave + q) * 16 + (lane & 15);
         const int rowc = min(row, H - 1);
-#pragma unroll
-        for (int jc = 0; jc < ZW / 4; ++jc) {
-            const int col = 4 * jc + (lane >> 4);
-            double v;
-            if (jc < NP / 4) {  // compile-time after unrolling
-                const float f = w_in[(long long)rowc * n_in + min(col, n_in - 1)];
-                v = (row < H && col < n_in) ? (double)f : 0.0;
-            } else {
-                const int cr = col - NP;
-                const float f = w_rec[(long long)rowc * H + min(cr, H - 1)];
-                v = (row < H && cr < H) ? (double)f : 0.0;
-            }
-            wb[q][jc] = v;
-        }
+        const bool in_part = slot < 2;
+        const int c0 = in_part ? 64 * slot : 64 * (slot - 2);
+        const int width = in_part ? n_in : H;
+        const int valid = row < H ? min(max(width - c0, 0), ZW / 4) : 0;
+        const float* src = in_part ? w_in + (long long)rowc * n_in + min(c0, n_in - 1)
+                                   : w_rec + (long long)rowc * H + min(c0, H - 1);
+        load_span_f64<ZW / 4>(wb[q], src, valid);
     }
 
     // ---- stage [x_k | h_k] for every step (h_0 = h0, h_k = h_seq[k-1])
@@ -588,12 +598,12 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int q = 0; q < 2; ++q) acc[kb][q] = dbl4{0.0, 0.0, 0.0, 0.0};
-        const float* za = zs + (lane & 15) * ZS + (lane >> 4);
+        const float* za = zs + (lane & 15) * ZS + 64 * slot;
 #pragma unroll
         for (int jc = 0; jc < ZW / 4; ++jc) {
 #pragma unroll
             for (int kb = 0; kb < KP / 16; ++kb) {
-                const double a = (double)za[kb * 16 * ZS + 4 * jc];
+                const double a = (double)za[kb * 16 * ZS + jc];
                 acc[kb][0] = mfma_f64(a, wb[0][jc], acc[kb][0]);
                 acc[kb][1] = mfma_f64(a, wb[1][jc], acc[kb][1]);
             }
@@ -613,14 +623,13 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     // ---- W_rec^T slice into registers: wt[r][c] = W_rec[16jb + c][4ib + r]
     double wt[4][16];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int col = 4 * ib + r, colc = min(col, H - 1);
+    for (int c = 0; c < 16; ++c) {
+        const int row = 16 * jb + c;
+        double w4[4];
+        const int valid = row < H ? min(max(H - 4 * ib, 0), 4) : 0;
+        load_span_f64<4>(w4, w_rec + (long long)min(row, H - 1) * H + min(4 * ib, H - 1), valid);
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            const int row = 16 * jb + c;
-            const float f = w_rec[(long long)min(row, H - 1) * H + colc];
-            wt[r][c] = (row < H && col < H) ? (double)f : 0.0;
-        }
+        for (int r = 0; r < 4; ++r) wt[r][c] = w4[r];
     }
 
     // ---- loss seed
