@@ -346,9 +346,10 @@ __host__ __device__ constexpr size_t small_fwd_lds_bytes() {
 }
 // The backward always stages kSmallBwdMaxK rows (rows >= K are zero), so its
 // contractions run without row guards.
+constexpr int kSmallGS = 64 + 4;  // row stride (floats) of a wave's gradient-tile buffer
 __host__ __device__ constexpr size_t small_bwd_lds_bytes() {
     return (size_t)8 * kSmallBwdMaxK * kSmall + (size_t)8 * 2 * kSmall + 8 * 8 +
-           (size_t)4 * kSmallBwdMaxK * kSmallZS;
+           (size_t)4 * kSmallBwdMaxK * kSmallZS + (size_t)4 * 4 * 16 * kSmallGS;
 }
 
 // Copy `rows` rows of `width` floats (source rows contiguous, row stride
@@ -363,10 +364,10 @@ __device__ __forceinline__ void stage_rows(float* dst, int dst_stride, const flo
     if (vec) {
         const int q = width >> 2;  // float4 per row
         const int total = pad_rows * q;
-        for (int e0 = t; e0 < total; e0 += 4 * kThreads) {
-            float4 v[4];
+        for (int e0 = t; e0 < total; e0 += 8 * kThreads) {
+            float4 v[8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 8; ++u) {
                 const int e = e0 + u * kThreads;
                 const int r = e / q, c4 = e - r * q;
                 v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -374,7 +375,7 @@ __device__ __forceinline__ void stage_rows(float* dst, int dst_stride, const flo
                     v[u] = *reinterpret_cast<const float4*>(src + r * src_stride + 4 * c4);
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 8; ++u) {
                 const int e = e0 + u * kThreads;
                 if (e < total) {
                     const int r = e / q, c4 = e - r * q;
@@ -551,6 +552,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     float* zs = reinterpret_cast<float*>(red + 8);  // [KP][ZS] = [x_k | h_k]
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    float* gst = zs + KP * ZS + wave * 16 * kSmallGS;  // this wave's [16][kSmallGS] tile buffer
     const long long b = blockIdx.x;
     const long long N = (long long)H * (n_in + H + 2);
     const int jb = lane & 7;
@@ -719,22 +721,59 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) bz[jj] = nbz[jj];
             }
+            if (accumulate) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+                for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int jcol = (jg * 4 + jj) * 16 + (lane & 15);
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int jcol = (jg * 4 + jj) * 16 + (lane & 15);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int i = (ib0 + q) * 16 + (lane >> 4) + 4 * v;
-                        if (i >= H) continue;
-                        if (jcol < NP) {
-                            if (jcol < n_in) store_grad_f(row + (long long)i * n_in + jcol, acc[q][jj][v], accumulate);
-                        } else if (jcol - NP < H) {
-                            store_grad_f(rrec + (long long)i * H + (jcol - NP), acc[q][jj][v], accumulate);
+                        for (int v = 0; v < 4; ++v) {
+                            const int i = (ib0 + q) * 16 + (lane >> 4) + 4 * v;
+                            if (i >= H) continue;
+                            if (jcol < NP) {
+                                if (jcol < n_in) store_grad_f(row + (long long)i * n_in + jcol, acc[q][jj][v], 1);
+                            } else if (jcol - NP < H) {
+                                store_grad_f(rrec + (long long)i * H + (jcol - NP), acc[q][jj][v], 1);
+                            }
+                        }
+                    }
+            } else {
+                // Through the wave's LDS buffer: each 16 x 64 block of G is
+                // transposed from the MFMA layout into rows, then stored as
+                // row-contiguous float4 (256 bytes per 16 lanes).
+                const int c4 = 4 * (lane & 15);       // first of this lane's 4 columns
+                const int jc0 = jg * 64 + c4;         // its column of [X | H_prev]
+                const bool in_part = jc0 < NP;
+                const int col = in_part ? jc0 : jc0 - NP;
+                const int width = in_part ? n_in : H;
+                float* base = in_part ? row : rrec;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            gst[((lane >> 4) + 4 * v) * kSmallGS + jj * 16 + (lane & 15)] = (float)acc[q][jj][v];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int r = (lane >> 4) + 4 * m;
+                        const float4 val = *reinterpret_cast<const float4*>(gst + r * kSmallGS + c4);
+                        const int i = (ib0 + q) * 16 + r;
+                        if (i < H) {
+                            float* dst = base + (long long)i * width + col;
+                            if (col + 4 <= width && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                                *reinterpret_cast<float4*>(dst) = val;
+                            } else {
+                                if (col < width) dst[0] = val.x;
+                                if (col + 1 < width) dst[1] = val.y;
+                                if (col + 2 < width) dst[2] = val.z;
+                                if (col + 3 < width) dst[3] = val.w;
+                            }
                         }
                     }
                 }
+            }
         }
     }
     if (!gate_lane && o < H) {
