@@ -83,6 +83,36 @@ def cpu_baseline(inp, budget_s=10.0):
                       f"same workload, K={K}), float64, one thread, {el:.1f} s"}
 
 
+def reduce_sweep(torch, C, W, dev, reps=20):
+    """reduce_axis0 alone at several [B, N], timed with HIP events per launch,
+    with a 512 MiB buffer overwritten between launches so that neither the L2
+    nor the 256 MB MALL holds the input (HBM-resident numbers)."""
+    flush = torch.empty(128 * 1024 * 1024, device=dev)
+    shapes = [(W.REDUCE.B, W.REDUCE.N), (256, 33024), (1024, 131584), (8192, 131584)]
+    out = []
+    for B, N in shapes:
+        a = torch.randn(B, N, device=dev)
+        o = torch.empty(N, device=dev)
+        C.reduce_axis0(a, out=o)
+        times = []
+        for _ in range(reps):
+            flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            C.reduce_axis0(a, out=o)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        med = times[len(times) // 2]
+        gbps = (B * N + N) * 4 / (med * 1e-3) / 1e9
+        out.append({"B": B, "N": N, "bytes": (B * N + N) * 4, "median_ms": med, "GB_per_s": gbps,
+                    "frac_hbm": gbps / PEAK_HBM_GBPS})
+        del a, o
+    del flush
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -92,6 +122,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (to scale PMC byte counters)")
+    ap.add_argument("--workload", default="train", choices=["train", "smoke", "tiny", "large"],
+                    help="which seeded workload one step runs (the metric is quoted on 'train')")
+    ap.add_argument("--reduce-sweep", action="store_true",
+                    help="also time reduce_axis0 alone, cache-flushed, over a range of sizes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the CfC path has no cross-GPU step in this "
@@ -119,7 +153,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4}))
         return
 
-    cfg = W.TRAIN
+    cfg = {"train": W.TRAIN, "smoke": W.SMOKE, "tiny": W.TINY, "large": W.LARGE}[args.workload]
     inp = W.make_cfc_inputs(cfg)
     t = lambda a: torch.from_numpy(a).to(dev)
     w_in, w_rec, b, w_tau, x, h0, y = map(t, (inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x, inp.h0, inp.y))
@@ -192,6 +226,8 @@ def main():
                          "note": "scratch of this step (33.8 MB) may be served partly from the MALL"},
         "kernel_source_sha256_16": source_hash(),
     }
+    if args.reduce_sweep:
+        rec["reduce_axis0_sweep"] = reduce_sweep(torch, C, W, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
     print(json.dumps(rec), flush=True)
