@@ -783,68 +783,78 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
 }
 
 // -------------------------------------------------------- reduce_axis0
-// Workgroup = 4 waves; a tile of 64 columns.  VEC=4: 16 lanes x float4 cover
-// the tile, 4 rows per wave, 16 row slots per workgroup.  VEC=1: 64 lanes x 1
-// float, 1 row per wave, 4 row slots.  Each slot sums its rows (b = slot,
-// slot + SLOTS, ...) in float64; the slots are then added in a fixed order.
-template <int VEC>
+// A workgroup (4 waves) owns a tile of TW = LPR * VEC consecutive columns.  A
+// row of the tile is read by LPR consecutive lanes (VEC floats each: 256 or
+// 512 contiguous bytes per row), so a wave covers 64 / LPR rows per load and
+// the workgroup has S = 4 * 64 / LPR row slots.  Slot s sums rows s, s + S,
+// s + 2S, ... in that order in float64, with 8 rows' loads in flight; the S
+// slot sums of each column are then added in slot order through LDS (rows of
+// the LDS array padded by one double).  One float32 store per column.  No
+// atomics, so the result is bitwise reproducible.
+template <int VEC, int LPR>
 __global__ __launch_bounds__(kThreads) void reduce_axis0_kernel(const float* __restrict__ in,
                                                                 long long B, long long N,
                                                                 float* __restrict__ out) {
-    constexpr int kLanesPerRow = 64 / VEC;        // 16 or 64
-    constexpr int kRowsPerWave = 64 / kLanesPerRow;  // 4 or 1
+    constexpr int TW = LPR * VEC;
+    constexpr int kRowsPerWave = 64 / LPR;
     constexpr int kSlots = kRowsPerWave * (kThreads / 64);
-    __shared__ double part[kSlots][64 + 1];  // +1: rows of the tree start on distinct banks
+    constexpr int kUnroll = 8;
+    __shared__ double part[kSlots][TW + 1];
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    const int slot = wave * kRowsPerWave + lane / kLanesPerRow;
-    const int c0 = (lane % kLanesPerRow) * VEC;  // first column of this lane inside the tile
-    const long long col = (long long)blockIdx.x * 64 + c0;
+    const int slot = wave * kRowsPerWave + lane / LPR;
+    const int c0 = (lane % LPR) * VEC;  // first column of this lane inside the tile
+    const long long col = (long long)blockIdx.x * TW + c0;
 
     double acc[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = 0.0;
 
-    if (VEC == 4) {
-        if (col < N) {  // N % 4 == 0 here, so col < N means all 4 columns are in range
-            const float* p = in + col;
-            long long bb = slot;
-            for (; bb + 3 * kSlots < B; bb += 4 * kSlots) {
-                float4 q0 = *reinterpret_cast<const float4*>(p + bb * N);
-                float4 q1 = *reinterpret_cast<const float4*>(p + (bb + kSlots) * N);
-                float4 q2 = *reinterpret_cast<const float4*>(p + (bb + 2 * kSlots) * N);
-                float4 q3 = *reinterpret_cast<const float4*>(p + (bb + 3 * kSlots) * N);
-                acc[0] += (double)q0.x; acc[1] += (double)q0.y; acc[2] += (double)q0.z; acc[3] += (double)q0.w;
-                acc[0] += (double)q1.x; acc[1] += (double)q1.y; acc[2] += (double)q1.z; acc[3] += (double)q1.w;
-                acc[0] += (double)q2.x; acc[1] += (double)q2.y; acc[2] += (double)q2.z; acc[3] += (double)q2.w;
-                acc[0] += (double)q3.x; acc[1] += (double)q3.y; acc[2] += (double)q3.z; acc[3] += (double)q3.w;
-            }
-            for (; bb < B; bb += kSlots) {
-                float4 q = *reinterpret_cast<const float4*>(p + bb * N);
-                acc[0] += (double)q.x; acc[1] += (double)q.y; acc[2] += (double)q.z; acc[3] += (double)q.w;
+    if (col < N) {  // with VEC == 4, N % 4 == 0, so all 4 columns are in range
+        const float* p = in + col;
+        long long bb = slot;
+        for (; bb + (kUnroll - 1) * kSlots < B; bb += kUnroll * kSlots) {
+            if constexpr (VEC == 4) {
+                float4 q[kUnroll];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u)
+                    q[u] = *reinterpret_cast<const float4*>(p + (bb + u * kSlots) * N);
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    acc[0] += (double)q[u].x;
+                    acc[1] += (double)q[u].y;
+                    acc[2] += (double)q[u].z;
+                    acc[3] += (double)q[u].w;
+                }
+            } else {
+                float q[kUnroll];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) q[u] = p[(bb + u * kSlots) * N];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) acc[0] += (double)q[u];
             }
         }
-    } else {
-        if (col < N) {
-            const float* p = in + col;
-            long long bb = slot;
-            for (; bb + 3 * kSlots < B; bb += 4 * kSlots) {
-                const float q0 = p[bb * N], q1 = p[(bb + kSlots) * N];
-                const float q2 = p[(bb + 2 * kSlots) * N], q3 = p[(bb + 3 * kSlots) * N];
-                acc[0] += (double)q0; acc[0] += (double)q1; acc[0] += (double)q2; acc[0] += (double)q3;
+        for (; bb < B; bb += kSlots) {
+            if constexpr (VEC == 4) {
+                const float4 q = *reinterpret_cast<const float4*>(p + bb * N);
+                acc[0] += (double)q.x;
+                acc[1] += (double)q.y;
+                acc[2] += (double)q.z;
+                acc[3] += (double)q.w;
+            } else {
+                acc[0] += (double)p[bb * N];
             }
-            for (; bb < B; bb += kSlots) acc[0] += (double)p[bb * N];
         }
     }
 #pragma unroll
     for (int v = 0; v < VEC; ++v) part[slot][c0 + v] = acc[v];
     __syncthreads();
-    if (t < 64) {
-        const long long j = (long long)blockIdx.x * 64 + t;
-        double s = 0.0;
-        for (int q = 0; q < kSlots; ++q) s += part[q][t];
-        if (j < N) out[j] = (float)s;
+    for (int c = t; c < TW; c += kThreads) {
+        const long long j = (long long)blockIdx.x * TW + c;
+        double sum = 0.0;
+        for (int q = 0; q < kSlots; ++q) sum += part[q][c];
+        if (j < N) out[j] = (float)sum;
     }
 }
 
@@ -996,14 +1006,20 @@ extern "C" int reduce_axis0(const float* per_batch, long long B, long long N, fl
     if (N == 0) return CFC_OK;
     if (!out || (B > 0 && !per_batch)) return CFC_ERR_NULL;
     if (B > 0 && overlap(span(out, N), span(per_batch, n))) return CFC_ERR_OVERLAP;
-    const long long tiles = (N + 63) / 64;
-    if (tiles > INT_MAX) return CFC_ERR_DIM;
     const bool vec4 = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(per_batch) % 16 == 0);
-    if (vec4)
-        hipLaunchKernelGGL(reduce_axis0_kernel<4>, dim3((unsigned)tiles), dim3(kThreads), 0, stream,
+    // 512-byte row segments when that still gives >= 4 workgroups per CU
+    const bool wide = vec4 && N / 128 >= 1024;
+    const long long tw = wide ? 128 : 64;
+    const long long tiles = (N + tw - 1) / tw;
+    if (tiles > INT_MAX) return CFC_ERR_DIM;
+    if (wide)
+        hipLaunchKernelGGL((reduce_axis0_kernel<4, 32>), dim3((unsigned)tiles), dim3(kThreads), 0, stream,
+                           per_batch, B, N, out);
+    else if (vec4)
+        hipLaunchKernelGGL((reduce_axis0_kernel<4, 16>), dim3((unsigned)tiles), dim3(kThreads), 0, stream,
                            per_batch, B, N, out);
     else
-        hipLaunchKernelGGL(reduce_axis0_kernel<1>, dim3((unsigned)tiles), dim3(kThreads), 0, stream,
+        hipLaunchKernelGGL((reduce_axis0_kernel<1, 64>), dim3((unsigned)tiles), dim3(kThreads), 0, stream,
                            per_batch, B, N, out);
     return launch_status();
 }
