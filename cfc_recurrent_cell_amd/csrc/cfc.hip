@@ -267,7 +267,12 @@ __device__ __forceinline__ dbl4 mfma_f64(double a, double b, dbl4 c) {
 // row_half_mirror (0x141: lane i of each 8-lane half-row reads lane 7 - i).
 template <int CTRL>
 __device__ __forceinline__ double dpp_move(double v) {
-    return __builtin_amdgcn_update_dpp(0.0, v, CTRL, 0xF, 0xF, false);
+    // two 32-bit DPP moves; every lane of the patterns used here has a valid
+    // source, so no fallback value is needed
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(unsigned)u, CTRL, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), CTRL, 0xF, 0xF, true);
+    return __builtin_bit_cast(double, ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141;
 
@@ -322,15 +327,24 @@ __device__ __forceinline__ double inv_one_plus_exp(double z) {
     return fma(y, e, y);
 }
 
-// tanh(a) and sigmoid(-sp*a*dt) for the unit owned by a lane pair; `gate_lane`
-// picks which of the two this lane evaluates.  Both lanes return both values.
-__device__ __forceinline__ void cell_gates(double a, double spdt, bool gate_lane, double& g,
-                                           double& c) {
-    const double r = inv_one_plus_exp(gate_lane ? spdt * a : 2.0 * a);
-    const double val = gate_lane ? r : fma(-2.0, r, 1.0);
+// Per-lane constants of cell_gates: the gate lane evaluates 1/(1+e^(sp*dt*a)),
+// the tanh lane 1 - 2/(1+e^(2a)).
+struct GateLane {
+    double zmul, vmul, vadd;
+    bool gate;
+};
+__device__ __forceinline__ GateLane gate_lane_consts(bool gate_lane, double spdt) {
+    return GateLane{gate_lane ? spdt : 2.0, gate_lane ? 1.0 : -2.0, gate_lane ? 0.0 : 1.0, gate_lane};
+}
+
+// tanh(a) and sigmoid(-sp*a*dt) for the unit owned by a lane pair; each lane
+// evaluates one of the two and they swap.  Both lanes return both values.
+__device__ __forceinline__ void cell_gates(double a, const GateLane& L, double& g, double& c) {
+    const double r = inv_one_plus_exp(L.zmul * a);
+    const double val = fma(r, L.vmul, L.vadd);
     const double other = dpp_move<kDppXor1>(val);
-    g = gate_lane ? val : other;
-    c = gate_lane ? other : val;
+    g = L.gate ? val : other;
+    c = L.gate ? other : val;
 }
 
 constexpr int kSmall = 128;          // padded n_in and n_hid of the small kernels
@@ -492,7 +506,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
                     urow[16] = acc[kb][1][v] + bias_q1;
                 }
         }
-        const double spdt_o = spv[o] * dt;
+        const GateLane gl = gate_lane_consts(gate_lane, spv[o] * dt);
         __syncthreads();
         // ---- serial recurrence through the window
         for (int kk = 0; kk < kw; ++kk) {
@@ -518,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
             for (int r = 0; r < 4; ++r) p[r] = pe[r] + po[r];
             const double a = u + reduce_scatter8(p, jb);
             double g, c;
-            cell_gates(a, spdt_o, gate_lane, g, c);
+            cell_gates(a, gl, g, c);
             const double hn = fma(g, hprev - c, c);  // g*h + (1-g)*c
             hprev = hn;
             if (!gate_lane) {
@@ -642,6 +656,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
         if (lane == 0) red[wave] = l;
     }
     const double sp_o = spv[o], sw_o = swv[o], spdt_o = sp_o * dt;
+    const GateLane gl = gate_lane_consts(gate_lane, spdt_o);
     __syncthreads();
     if (t == 0 && loss) loss[b] = (float)(((red[0] + red[1]) + red[2]) + red[3]);
 
@@ -656,7 +671,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
             h_next = (double)zs[(k - 1) * ZS + NP + o];
         }
         double g, c;
-        cell_gates(a, spdt_o, gate_lane, g, c);
+        cell_gates(a, gl, g, c);
         const double dz = delta * (hk - c) * g * (1.0 - g);
         const double da = delta * (1.0 - g) * (1.0 - c * c) - dz * spdt_o;
         gb += da;
