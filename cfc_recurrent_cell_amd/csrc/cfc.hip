@@ -1,15 +1,18 @@
 // cfc.hip -- gfx950 kernels and the C ABI of libcfc_amd (see include/cfc.h).
 //
 // Kernels
-//   cfc_fwd_kernel     one workgroup per batch row runs the whole forward
-//                      K-loop; the input projection of a window of steps is
-//                      computed off the serial chain, then the recurrence
-//                      steps through the window.
-//   cfc_bwd_kernel     one workgroup per batch row runs the whole reverse
-//                      K-loop: the serial delta chain keeps dL/da for every
-//                      step in LDS, then the weight gradients are formed as
-//                      contractions over k and each scratch element is
-//                      written exactly once (no per-step read-modify-write).
+//   cfc_fwd_small_kernel / cfc_bwd_small_kernel   n_in, n_hid <= 128: one
+//       workgroup per batch row runs the whole (reverse) K-loop; dense
+//       contractions on the f64 matrix cores, the serial chain on the vector
+//       units with W_rec held in registers.
+//   cfc_fwd_large_kernel / cfc_bwd_large_kernel   n_in or n_hid in (128, 256]:
+//       a workgroup owns 16 batch rows, so every step is a matrix-core product.
+//   cfc_bwd_kernel    general backward (any n_in, n_hid <= 256, and the
+//       accumulate mode at the larger sizes): one workgroup per row, matvecs on
+//       the vector units with the weights read from L2.
+//   Every backward keeps dL/da for all steps on chip (or parked in its own
+//   scratch row) and forms the weight gradients as contractions over k, so
+//   each scratch element is written once (no per-step read-modify-write).
 //   reduce_axis0_kernel  column-tiled sum over the leading axis.
 //
 // The block-per-batch layout and the single-writer scratch come from the
@@ -54,67 +57,6 @@ __device__ __forceinline__ int group_size(int rows) {
 __device__ __forceinline__ double group_sum(double v, int G) {
     for (int off = G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
     return v;
-}
-
-// ------------------------------------------------------------ forward
-// LDS: U [KW][H] f64 | h [2][H] f64 | sp [H] f64 | xs [KW][n_in] f32
-__global__ __launch_bounds__(kThreads) void cfc_fwd_kernel(
-    const float* __restrict__ w_in, const float* __restrict__ w_rec,
-    const float* __restrict__ bias, const float* __restrict__ w_tau,
-    const float* __restrict__ x, const float* __restrict__ h0, double dt, int K, int n_in,
-    int H, int KW, float* __restrict__ h_seq) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    double* U = reinterpret_cast<double*>(smem);
-    double* hbuf = U + (size_t)KW * H;
-    double* sp = hbuf + 2 * H;
-    float* xs = reinterpret_cast<float*>(sp + H);
-
-    const int t = threadIdx.x;
-    const long long b = blockIdx.x;
-    const int G = group_size(H);
-    const int i = t / G, sub = t % G;
-
-    for (int u = t; u < H; u += kThreads) {
-        sp[u] = softplus_f64((double)w_tau[u]);
-        hbuf[u] = (double)h0[b * H + u];
-    }
-    int cur = 0;
-    for (int k0 = 0; k0 < K; k0 += KW) {
-        const int kw = min(KW, K - k0);
-        __syncthreads();  // the previous window is done with xs and U
-        const float* xb = x + (b * K + k0) * (long long)n_in;
-        for (int e = t; e < kw * n_in; e += kThreads) xs[e] = xb[e];
-        __syncthreads();
-        // input projection of the window, off the serial chain
-        for (int e = t; e < kw * H; e += kThreads) {
-            const int kk = e / H, r = e - kk * H;
-            const float* wr = w_in + (long long)r * n_in;
-            const float* xr = xs + kk * n_in;
-            double s = (double)bias[r];
-            for (int j = 0; j < n_in; ++j) s = fma((double)wr[j], (double)xr[j], s);
-            U[e] = s;
-        }
-        __syncthreads();
-        for (int kk = 0; kk < kw; ++kk) {
-            const double* hv = hbuf + cur * H;
-            double part = 0.0;
-            if (i < H) {
-                const float* wr = w_rec + (long long)i * H;
-                for (int j = sub; j < H; j += G) part = fma((double)wr[j], hv[j], part);
-            }
-            part = group_sum(part, G);
-            if (i < H && sub == 0) {
-                const double a = U[kk * H + i] + part;
-                const double g = 1.0 / (1.0 + exp(sp[i] * a * dt));
-                const double c = tanh(a);
-                const double hn = g * hv[i] + (1.0 - g) * c;
-                hbuf[(cur ^ 1) * H + i] = hn;
-                h_seq[(b * K + k0 + kk) * (long long)H + i] = (float)hn;
-            }
-            cur ^= 1;
-            __syncthreads();
-        }
-    }
 }
 
 // ----------------------------------------------------------- backward
@@ -797,6 +739,368 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     }
 }
 
+// =====================================================================
+// Kernels for 128 < max(n_in, n_hid) <= 256 (the large-batch workload).  A
+// workgroup owns kLR = 16 batch rows, so each step's contraction
+// [W_in | W_rec] (256 x 512) x [x_k ; h_k] (512 x 16 rows) is a dense product
+// on the f64 matrix cores, as is the backward's W_rec^T x dL/da; dimensions
+// are zero-padded to 256.  Rows stay independent: the 16 rows only share the
+// weight operand of each product.
+// =====================================================================
+constexpr int kLarge = 256;  // padded n_in and n_hid
+constexpr int kLR = 16;      // batch rows per workgroup
+constexpr int kLargeBwdMaxK = 20;
+
+// Element (j, r) of a [256][16] LDS array, XOR-swizzled within each row of 16
+// so that an MFMA operand read (16 consecutive r) and a staging write (16
+// consecutive j) both touch distinct banks.
+__device__ __forceinline__ int zidx(int j, int r) { return j * kLR + (r ^ (j & 15)); }
+
+__host__ __device__ constexpr size_t large_fwd_lds_bytes() {
+    return (size_t)4 * kLarge * kLR + (size_t)8 * kLarge * kLR;
+}
+__host__ __device__ constexpr size_t large_bwd_lds_bytes() {
+    return (size_t)4 * kLarge * kLR + (size_t)8 * kLarge * kLR + (size_t)8 * kLarge * kLR +
+           (size_t)8 * 3 * kLarge;
+}
+
+// 4 consecutive floats row[col .. col+3] of a row with `width` valid columns
+// (zero beyond; the whole float4 is zero when `ok` is false).
+__device__ __forceinline__ float4 load4_masked(const float* row, int col, int width, bool ok) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!ok || col >= width) return v;
+    const float* p = row + col;
+    if (col + 4 <= width && (reinterpret_cast<uintptr_t>(p) & 15) == 0) return *reinterpret_cast<const float4*>(p);
+    v.x = p[0];
+    if (col + 1 < width) v.y = p[1];
+    if (col + 2 < width) v.z = p[2];
+    if (col + 3 < width) v.w = p[3];
+    return v;
+}
+__device__ __forceinline__ float f4_get(const float4& v, int c) {
+    return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+}
+
+// Stage rows r0..r0+15 of a [rows][width] matrix (row stride `stride` floats)
+// into a swizzled [256][16] LDS array, transposed; zero outside the matrix.
+template <typename T>
+__device__ __forceinline__ void stage_t(T* dst, const float* src, long long stride, long long r0, long long B,
+                                        int width, int t) {
+#pragma unroll 4
+    for (int m = 0; m < kLR; ++m) {
+        const int e = t + kThreads * m;
+        const int rr = e >> 8, j = e & 255;
+        const long long b = r0 + rr;
+        const float v = (b < B && j < width) ? src[b * stride + j] : 0.f;
+        dst[zidx(j, rr)] = (T)v;
+    }
+}
+
+// D[i][r] += sum_j [W_in | W_rec][i][j] * Z[j][r] for the wave's four 16-unit
+// blocks (units (4*wave + tb)*16 ..), Z = [zx ; zh].  Chunk jj of half g and
+// k-slot s contracts j = 256*g + 64*s + jj, so each lane's weight operands
+// are contiguous 64-float spans of one row (float4 loads) and every chunk
+// reads only one of zx / zh.
+__device__ __forceinline__ void large_preact(dbl4 acc[4], const float* __restrict__ w_in,
+                                             const float* __restrict__ w_rec, int n_in, int H,
+                                             const float* zx, const double* zh, int wave, int lane) {
+    const int s = lane >> 4, r = lane & 15;
+#pragma unroll 1
+    for (int g = 0; g < 2; ++g) {
+        const int width = g == 0 ? n_in : H;
+        const float* wbase = g == 0 ? w_in : w_rec;
+        const float* wrow[4];
+        bool rok[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const int i = (4 * wave + tb) * 16 + (lane & 15);
+            rok[tb] = i < H;
+            wrow[tb] = wbase + (long long)min(i, H - 1) * width;
+        }
+        float4 w4[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) w4[tb] = load4_masked(wrow[tb], 64 * s, width, rok[tb]);
+#pragma unroll 1
+        for (int jq = 0; jq < 16; ++jq) {
+            float4 nw4[4];
+            const int jn = jq + 1 < 16 ? jq + 1 : jq;  // prefetch the next chunk group
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) nw4[tb] = load4_masked(wrow[tb], 64 * s + 4 * jn, width, rok[tb]);
+            double bz[4];
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const int jl = 64 * s + 4 * jq + cc;
+                bz[cc] = g == 0 ? (double)zx[zidx(jl, r)] : zh[zidx(jl, r)];
+            }
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma_f64((double)f4_get(w4[tb], cc), bz[cc], acc[tb]);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) w4[tb] = nw4[tb];
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
+    const float* __restrict__ w_in, const float* __restrict__ w_rec,
+    const float* __restrict__ bias, const float* __restrict__ w_tau,
+    const float* __restrict__ x, const float* __restrict__ h0, double dt, int B, int K, int n_in,
+    int H, float* __restrict__ h_seq) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* zx = reinterpret_cast<float*>(smem);                        // [256][16] x_k
+    double* zh = reinterpret_cast<double*>(smem + 4 * kLarge * kLR);   // [256][16] h_k
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int s = lane >> 4, r = lane & 15;
+    const long long r0 = (long long)blockIdx.x * kLR;
+
+    // this lane's 16 accumulator elements: unit (4*wave + tb)*16 + s + 4v, row r
+    double bias_v[4][4], spdt_v[4][4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = (4 * wave + tb) * 16 + s + 4 * v;
+            bias_v[tb][v] = i < H ? (double)bias[i] : 0.0;
+            spdt_v[tb][v] = i < H ? softplus_f64((double)w_tau[i]) * dt : 0.0;
+        }
+    stage_t(zh, h0, H, r0, B, H, t);
+    stage_t(zx, x, (long long)K * n_in, r0, B, n_in, t);
+    __syncthreads();
+
+    for (int k = 0; k < K; ++k) {
+        // next step's inputs, loaded now and written to LDS after this step
+        float xn[kLR];
+#pragma unroll
+        for (int m = 0; m < kLR; ++m) {
+            const int e = t + kThreads * m;
+            const int rr = e >> 8, j = e & 255;
+            const long long b = r0 + rr;
+            xn[m] = (k + 1 < K && b < B && j < n_in) ? x[(b * K + k + 1) * (long long)n_in + j] : 0.f;
+        }
+        dbl4 acc[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
+        large_preact(acc, w_in, w_rec, n_in, H, zx, zh, wave, lane);
+        __syncthreads();  // every wave is done reading zx / zh of step k
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = (4 * wave + tb) * 16 + s + 4 * v;
+                const double a = acc[tb][v] + bias_v[tb][v];
+                const double g = inv_one_plus_exp(spdt_v[tb][v] * a);
+                const double c = fma(-2.0, inv_one_plus_exp(2.0 * a), 1.0);
+                double* hp = zh + zidx(i, r);
+                *hp = fma(g, *hp - c, c);  // g*h + (1-g)*c
+            }
+#pragma unroll
+        for (int m = 0; m < kLR; ++m) {
+            const int e = t + kThreads * m;
+            zx[zidx(e & 255, e >> 8)] = xn[m];
+        }
+        __syncthreads();
+        // h_k+1 of the 16 rows, row-contiguous stores
+#pragma unroll 4
+        for (int m = 0; m < kLR; ++m) {
+            const int e = t + kThreads * m;
+            const int rr = e >> 8, j = e & 255;
+            const long long b = r0 + rr;
+            if (b < B && j < H) h_seq[(b * K + k) * (long long)H + j] = (float)zh[zidx(j, rr)];
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
+    const float* __restrict__ w_in, const float* __restrict__ w_rec,
+    const float* __restrict__ bias, const float* __restrict__ w_tau,
+    const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
+    const float* __restrict__ y, double dt, int B, int K, int n_in, int H, float* __restrict__ scratch,
+    float* __restrict__ loss) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* zx = reinterpret_cast<float*>(smem);                             // [256][16] x_k
+    double* zh = reinterpret_cast<double*>(smem + 4 * kLarge * kLR);        // [256][16] h_k
+    double* dab = reinterpret_cast<double*>(smem + 12 * kLarge * kLR);      // [256][16] dL/da_k
+    double* ubias = reinterpret_cast<double*>(smem + 20 * kLarge * kLR);    // [256] per-unit b,
+    double* uspdt = ubias + kLarge;                                          // softplus(w_tau)*dt,
+    double* usw = uspdt + kLarge;                                            // sigmoid(w_tau)
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int s = lane >> 4, r = lane & 15;
+    const long long r0 = (long long)blockIdx.x * kLR;
+    const long long N = (long long)H * (n_in + H + 2);
+    const long long b_own = r0 + r;
+    const bool row_ok = b_own < B;
+    // dL/da of every step is parked in the tail of its row's scratch (as two
+    // 32-bit halves per double) until the row's weight gradients are formed;
+    // every element there is rewritten afterwards.
+    const long long tmp_off = N - 2LL * K * H;
+
+    for (int u = t; u < kLarge; u += kThreads) {
+        const bool ok = u < H;
+        const double w = ok ? (double)w_tau[u] : 0.0;
+        ubias[u] = ok ? (double)bias[u] : 0.0;
+        uspdt[u] = ok ? softplus_f64(w) * dt : 0.0;
+        usw[u] = ok ? logistic_f64(w) : 0.0;
+    }
+    double delta[4][4], gbv[4][4], gwtv[4][4];
+    double lsum = 0.0;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = (4 * wave + tb) * 16 + s + 4 * v;
+            const bool ok = i < H;
+            const double d = (ok && row_ok) ? (double)h_seq[(b_own * K + K - 1) * (long long)H + i] -
+                                                  (double)y[b_own * H + i]
+                                            : 0.0;
+            delta[tb][v] = d;
+            lsum += 0.5 * d * d;
+            gbv[tb][v] = 0.0;
+            gwtv[tb][v] = 0.0;
+        }
+    // loss of each row: lanes r, r+16, r+32, r+48 of every wave share row r
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (lane < 16) dab[wave * 16 + lane] = lsum;
+    __syncthreads();
+    if (t < kLR && loss && r0 + t < B)
+        loss[r0 + t] = (float)(((dab[t] + dab[16 + t]) + dab[32 + t]) + dab[48 + t]);
+
+    for (int k = K - 1; k >= 0; --k) {
+        __syncthreads();  // previous step is done with zx, zh, dab
+        stage_t(zx, x + (long long)k * n_in, (long long)K * n_in, r0, B, n_in, t);
+        if (k == 0) stage_t(zh, h0, H, r0, B, H, t);
+        else stage_t(zh, h_seq + (long long)(k - 1) * H, (long long)K * H, r0, B, H, t);
+        __syncthreads();
+        dbl4 acc[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
+        large_preact(acc, w_in, w_rec, n_in, H, zx, zh, wave, lane);
+        double gk[4][4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = (4 * wave + tb) * 16 + s + 4 * v;
+                const double spdt = uspdt[i];
+                const double a = acc[tb][v] + ubias[i];
+                const double g = inv_one_plus_exp(spdt * a);
+                const double c = fma(-2.0, inv_one_plus_exp(2.0 * a), 1.0);
+                const double hp = zh[zidx(i, r)];
+                const double d = delta[tb][v];
+                const double dz = d * (hp - c) * g * (1.0 - g);
+                const double da = d * (1.0 - g) * (1.0 - c * c) - dz * spdt;
+                gbv[tb][v] += da;
+                gwtv[tb][v] += dz * (-a * dt) * usw[i];
+                gk[tb][v] = g;
+                dab[zidx(i, r)] = da;
+                if (row_ok && i < H) {
+                    const unsigned long long u = __builtin_bit_cast(unsigned long long, da);
+                    unsigned* q = reinterpret_cast<unsigned*>(scratch + b_own * N + tmp_off) +
+                                  2 * ((long long)k * H + i);
+                    q[0] = (unsigned)u;
+                    q[1] = (unsigned)(u >> 32);
+                }
+            }
+        if (k == 0) break;
+        __syncthreads();  // dab of step k complete
+        // delta_k = delta_k+1 * g + W_rec^T dL/da: chunk ic of k-slot s
+        // contracts unit i = 64*s + ic
+        dbl4 acc2[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc2[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+        for (int ic = 0; ic < 64; ++ic) {
+            const int i = 64 * s + ic;
+            const double bz = dab[zidx(i, r)];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const int j = (4 * wave + tb) * 16 + (lane & 15);
+                const double w = (i < H && j < H) ? (double)w_rec[(long long)min(i, H - 1) * H + min(j, H - 1)] : 0.0;
+                acc2[tb] = mfma_f64(w, bz, acc2[tb]);
+            }
+        }
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) delta[tb][v] = fma(delta[tb][v], gk[tb][v], acc2[tb][v]);
+    }
+
+    // ---- per row: G = DA^T [X | H_prev] over the K steps, then db and dw_tau
+    __syncthreads();
+    const int KP = (K + 3) & ~3;
+    double* dak = reinterpret_cast<double*>(smem);                       // [KP][256] dL/da
+    float* zk = reinterpret_cast<float*>(smem + (size_t)8 * KP * kLarge);  // [KP][512] [x | h_prev]
+    for (int rr = 0; rr < kLR; ++rr) {
+        const long long b = r0 + rr;
+        if (b >= B) break;
+        const unsigned* tq = reinterpret_cast<const unsigned*>(scratch + b * N + tmp_off);
+        for (int e = t; e < KP * kLarge; e += kThreads) {
+            const int kk = e >> 8, i = e & 255;
+            double v = 0.0;
+            if (kk < K && i < H) {
+                const long long q = 2 * ((long long)kk * H + i);
+                v = __builtin_bit_cast(double, ((unsigned long long)tq[q + 1] << 32) | tq[q]);
+            }
+            dak[e] = v;
+        }
+        for (int e = t; e < KP * 2 * kLarge; e += kThreads) {
+            const int kk = e >> 9, j = e & 511;
+            float v = 0.f;
+            if (kk < K) {
+                if (j < kLarge) {
+                    if (j < n_in) v = x[(b * K + kk) * (long long)n_in + j];
+                } else {
+                    const int jj = j - kLarge;
+                    if (jj < H) v = kk == 0 ? h0[b * H + jj] : h_seq[(b * K + kk - 1) * (long long)H + jj];
+                }
+            }
+            zk[e] = v;
+        }
+        __syncthreads();
+        float* grow = scratch + b * N;
+        float* grec = grow + (long long)H * n_in;
+        for (int jt = 0; jt < 2 * kLarge / 16; ++jt) {
+            dbl4 acc[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) acc[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
+            for (int kc = 0; kc < KP / 4; ++kc) {
+                const int kk = 4 * kc + s;
+                const double bz = (double)zk[kk * 2 * kLarge + jt * 16 + (lane & 15)];
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    acc[tb] = mfma_f64(dak[kk * kLarge + (4 * wave + tb) * 16 + (lane & 15)], bz, acc[tb]);
+            }
+            const int jcol = jt * 16 + (lane & 15);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int i = (4 * wave + tb) * 16 + s + 4 * v;
+                    if (i >= H) continue;
+                    if (jcol < kLarge) {
+                        if (jcol < n_in) grow[(long long)i * n_in + jcol] = (float)acc[tb][v];
+                    } else if (jcol - kLarge < H) {
+                        grec[(long long)i * H + (jcol - kLarge)] = (float)acc[tb][v];
+                    }
+                }
+        }
+        if (r == rr) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int i = (4 * wave + tb) * 16 + s + 4 * v;
+                    if (i < H) {
+                        grec[(long long)H * H + i] = (float)gbv[tb][v];
+                        grec[(long long)H * H + H + i] = (float)gwtv[tb][v];
+                    }
+                }
+        }
+        __syncthreads();  // LDS reused by the next row
+    }
+}
+
 // -------------------------------------------------------- reduce_axis0
 // A workgroup (4 waves) owns a tile of TW = LPR * VEC consecutive columns.  A
 // row of the tile is read by LPR consecutive lanes (VEC floats each: 256 or
@@ -901,13 +1205,15 @@ int check_params(const cfc_params_t* p) {
 std::once_flag g_attr_once;
 void set_kernel_attributes() {
     std::call_once(g_attr_once, [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_small_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_small_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_large_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     });
 }
@@ -961,16 +1267,10 @@ extern "C" int cfc_forward(const cfc_params_t* params, const float* x, const flo
                            n_in, H, h_seq);
         return launch_status();
     }
-    // Window of steps whose projections are staged at once.
-    const size_t fixed = (size_t)8 * 3 * H;
-    const size_t per_k = (size_t)8 * H + (size_t)4 * n_in;
-    int KW = (int)std::min<size_t>((size_t)K, (kLdsBytes - fixed) / per_k);
-    if (KW > 64) KW = 64;
-    const size_t lds = fixed + per_k * (size_t)KW;
-    set_kernel_attributes();
-    hipLaunchKernelGGL(cfc_fwd_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
-                       params->w_rec, params->b, params->w_tau, x, h0, (double)dt, K, n_in, H, KW,
-                       h_seq);
+    const long long groups = ((long long)B + kLR - 1) / kLR;
+    hipLaunchKernelGGL(cfc_fwd_large_kernel, dim3((unsigned)groups), dim3(kThreads), large_fwd_lds_bytes(),
+                       stream, params->w_in, params->w_rec, params->b, params->w_tau, x, h0, (double)dt, B,
+                       K, n_in, H, h_seq);
     return launch_status();
 }
 
@@ -990,7 +1290,9 @@ extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const fl
         !mul_ok((long long)B, N, &nsc))
         return CFC_ERR_DIM;
     const bool small = n_in <= kSmall && H <= kSmall && K <= kSmallBwdMaxK;
-    const size_t lds = small ? small_bwd_lds_bytes() : bwd_lds_bytes(K, n_in, H);
+    const bool large = !small && (n_in > kSmall || H > kSmall) && K <= kLargeBwdMaxK &&
+                       flags == CFC_OVERWRITE;
+    const size_t lds = small ? small_bwd_lds_bytes() : large ? large_bwd_lds_bytes() : bwd_lds_bytes(K, n_in, H);
     if (lds > kLdsBytes) return CFC_ERR_UNSUPPORTED;
     const Range outs[] = {span(scratch, nsc), span(loss, loss ? B : 0)};
     const Range ins[] = {span(x, nx), span(h0, (long long)B * H), span(h_seq, ns), span(y, (long long)B * H),
@@ -1005,6 +1307,13 @@ extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const fl
         hipLaunchKernelGGL(cfc_bwd_small_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
                            params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, K,
                            n_in, H, scratch, loss, flags == CFC_ACCUMULATE ? 1 : 0);
+        return launch_status();
+    }
+    if (large) {
+        const long long groups = ((long long)B + kLR - 1) / kLR;
+        hipLaunchKernelGGL(cfc_bwd_large_kernel, dim3((unsigned)groups), dim3(kThreads), lds, stream,
+                           params->w_in, params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt,
+                           B, K, n_in, H, scratch, loss);
         return launch_status();
     }
     hipLaunchKernelGGL(cfc_bwd_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
