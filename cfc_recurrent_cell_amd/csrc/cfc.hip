@@ -759,9 +759,10 @@ __device__ __forceinline__ int zidx(int j, int r) { return j * kLR + (r ^ (j & 1
 __host__ __device__ constexpr size_t large_fwd_lds_bytes() {
     return (size_t)4 * kLarge * kLR + (size_t)8 * kLarge * kLR;
 }
+constexpr int kLargeGS = 64 + 4;  // row stride (floats) of a wave's gradient-tile buffer
 __host__ __device__ constexpr size_t large_bwd_lds_bytes() {
     return (size_t)4 * kLarge * kLR + (size_t)8 * kLarge * kLR + (size_t)8 * kLarge * kLR +
-           (size_t)8 * 3 * kLarge;
+           (size_t)8 * 3 * kLarge + (size_t)4 * 4 * 16 * kLargeGS;
 }
 
 // 4 consecutive floats row[col .. col+3] of a row with `width` valid columns
@@ -797,14 +798,21 @@ __device__ __forceinline__ void stage_t(T* dst, const float* src, long long stri
 }
 
 // D[i][r] += sum_j [W_in | W_rec][i][j] * Z[j][r] for the wave's four 16-unit
-// blocks (units (4*wave + tb)*16 ..), Z = [zx ; zh].  Chunk jj of half g and
-// k-slot s contracts j = 256*g + 64*s + jj, so each lane's weight operands
-// are contiguous 64-float spans of one row (float4 loads) and every chunk
-// reads only one of zx / zh.
+// blocks (units (4*wave + tb)*16 ..), Z = [zx ; zh].  Chunk (jq, cc) of half g
+// and k-slot s contracts j = 256*g + 16*jq + 4*s + cc: one float4 load gives a
+// lane its weights for the four chunks of a jq, the four k-slots of a row read
+// 64 contiguous bytes, every cache line is consumed within two jq, and every
+// chunk reads only one of zx / zh.
+// FULL: n_in == n_hid == 256 and 16-byte aligned weights, so the weight loads
+// are plain float4 loads with no masking.
+template <bool FULL>
 __device__ __forceinline__ void large_preact(dbl4 acc[4], const float* __restrict__ w_in,
                                              const float* __restrict__ w_rec, int n_in, int H,
                                              const float* zx, const double* zh, int wave, int lane) {
     const int s = lane >> 4, r = lane & 15;
+    dbl4 acc_odd[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) acc_odd[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll 1
     for (int g = 0; g < 2; ++g) {
         const int width = g == 0 ? n_in : H;
@@ -817,31 +825,45 @@ __device__ __forceinline__ void large_preact(dbl4 acc[4], const float* __restric
             rok[tb] = i < H;
             wrow[tb] = wbase + (long long)min(i, H - 1) * width;
         }
+        auto wload = [&](int tb, int col) -> float4 {
+            if constexpr (FULL) return *reinterpret_cast<const float4*>(wrow[tb] + col);
+            else return load4_masked(wrow[tb], col, width, rok[tb]);
+        };
         float4 w4[4];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) w4[tb] = load4_masked(wrow[tb], 64 * s, width, rok[tb]);
-#pragma unroll 1
+        for (int tb = 0; tb < 4; ++tb) w4[tb] = wload(tb, 4 * s);
+#pragma unroll 2
         for (int jq = 0; jq < 16; ++jq) {
             float4 nw4[4];
             const int jn = jq + 1 < 16 ? jq + 1 : jq;  // prefetch the next chunk group
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) nw4[tb] = load4_masked(wrow[tb], 64 * s + 4 * jn, width, rok[tb]);
-            double bz[4];
+            for (int tb = 0; tb < 4; ++tb) nw4[tb] = wload(tb, 16 * jn + 4 * s);
+            double bz[4], wa[4][4];
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
-                const int jl = 64 * s + 4 * jq + cc;
+                const int jl = 16 * jq + 4 * s + cc;
                 bz[cc] = g == 0 ? (double)zx[zidx(jl, r)] : zh[zidx(jl, r)];
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) wa[cc][tb] = (double)f4_get(w4[tb], cc);
             }
+            // even chunks into acc, odd chunks into acc_odd: a dependent MFMA
+            // is always eight issues behind its predecessor
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc)
+            for (int cc = 0; cc < 4; cc += 2) {
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma_f64((double)f4_get(w4[tb], cc), bz[cc], acc[tb]);
+                for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma_f64(wa[cc][tb], bz[cc], acc[tb]);
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) acc_odd[tb] = mfma_f64(wa[cc + 1][tb], bz[cc + 1], acc_odd[tb]);
+            }
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) w4[tb] = nw4[tb];
         }
     }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) acc[tb] += acc_odd[tb];
 }
 
+template <bool FULL>
 __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
@@ -881,7 +903,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
         dbl4 acc[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) acc[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
-        large_preact(acc, w_in, w_rec, n_in, H, zx, zh, wave, lane);
+        large_preact<FULL>(acc, w_in, w_rec, n_in, H, zx, zh, wave, lane);
         __syncthreads();  // every wave is done reading zx / zh of step k
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
@@ -911,6 +933,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
     }
 }
 
+template <bool FULL>
 __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
@@ -975,7 +998,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
         dbl4 acc[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) acc[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
-        large_preact(acc, w_in, w_rec, n_in, H, zx, zh, wave, lane);
+        large_preact<FULL>(acc, w_in, w_rec, n_in, H, zx, zh, wave, lane);
         double gk[4][4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
@@ -994,16 +1017,22 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                 gwtv[tb][v] += dz * (-a * dt) * usw[i];
                 gk[tb][v] = g;
                 dab[zidx(i, r)] = da;
-                if (row_ok && i < H) {
-                    const unsigned long long u = __builtin_bit_cast(unsigned long long, da);
-                    unsigned* q = reinterpret_cast<unsigned*>(scratch + b_own * N + tmp_off) +
-                                  2 * ((long long)k * H + i);
-                    q[0] = (unsigned)u;
-                    q[1] = (unsigned)(u >> 32);
-                }
             }
-        if (k == 0) break;
         __syncthreads();  // dab of step k complete
+        // park dL/da_k of the 16 rows in their scratch tails, row-contiguous
+#pragma unroll 4
+        for (int m = 0; m < kLR; ++m) {
+            const int e = t + kThreads * m;
+            const int rr = e >> 8, i = e & 255;
+            const long long b = r0 + rr;
+            if (b < B && i < H) {
+                const unsigned long long u = __builtin_bit_cast(unsigned long long, dab[zidx(i, rr)]);
+                unsigned* q = reinterpret_cast<unsigned*>(scratch + b * N + tmp_off) + 2 * ((long long)k * H + i);
+                q[0] = (unsigned)u;
+                q[1] = (unsigned)(u >> 32);
+            }
+        }
+        if (k == 0) break;
         // delta_k = delta_k+1 * g + W_rec^T dL/da: chunk ic of k-slot s
         // contracts unit i = 64*s + ic
         dbl4 acc2[4];
@@ -1016,7 +1045,9 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
                 const int j = (4 * wave + tb) * 16 + (lane & 15);
-                const double w = (i < H && j < H) ? (double)w_rec[(long long)min(i, H - 1) * H + min(j, H - 1)] : 0.0;
+                double w;
+                if constexpr (FULL) w = (double)w_rec[(long long)i * kLarge + j];
+                else w = (i < H && j < H) ? (double)w_rec[(long long)min(i, H - 1) * H + min(j, H - 1)] : 0.0;
                 acc2[tb] = mfma_f64(w, bz, acc2[tb]);
             }
         }
@@ -1031,6 +1062,8 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const int KP = (K + 3) & ~3;
     double* dak = reinterpret_cast<double*>(smem);                       // [KP][256] dL/da
     float* zk = reinterpret_cast<float*>(smem + (size_t)8 * KP * kLarge);  // [KP][512] [x | h_prev]
+    float* gst = reinterpret_cast<float*>(smem + large_bwd_lds_bytes() - (size_t)4 * 4 * 16 * kLargeGS) +
+                 wave * 16 * kLargeGS;  // this wave's [16][kLargeGS] tile buffer
     for (int rr = 0; rr < kLR; ++rr) {
         const long long b = r0 + rr;
         if (b >= B) break;
@@ -1060,30 +1093,50 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
         __syncthreads();
         float* grow = scratch + b * N;
         float* grec = grow + (long long)H * n_in;
-        for (int jt = 0; jt < 2 * kLarge / 16; ++jt) {
-            dbl4 acc[4];
+        // the wave's 64 units x 512 columns, in 16 x 64 blocks: 4 column tiles
+        // per block, transposed through LDS into float4 row stores
+        for (int ub = 0; ub < 4; ++ub) {
+            const int ib = 4 * wave + ub;
+            for (int jg = 0; jg < 2 * kLarge / 64; ++jg) {
+                dbl4 acc[4];
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
-            for (int kc = 0; kc < KP / 4; ++kc) {
-                const int kk = 4 * kc + s;
-                const double bz = (double)zk[kk * 2 * kLarge + jt * 16 + (lane & 15)];
+                for (int jj = 0; jj < 4; ++jj) acc[jj] = dbl4{0.0, 0.0, 0.0, 0.0};
+                for (int kc = 0; kc < KP / 4; ++kc) {
+                    const int kk = 4 * kc + s;
+                    const double a = dak[kk * kLarge + ib * 16 + (lane & 15)];
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
-                    acc[tb] = mfma_f64(dak[kk * kLarge + (4 * wave + tb) * 16 + (lane & 15)], bz, acc[tb]);
-            }
-            const int jcol = jt * 16 + (lane & 15);
+                    for (int jj = 0; jj < 4; ++jj)
+                        acc[jj] = mfma_f64(a, (double)zk[kk * 2 * kLarge + (4 * jg + jj) * 16 + (lane & 15)], acc[jj]);
+                }
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
+                for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int i = (4 * wave + tb) * 16 + s + 4 * v;
-                    if (i >= H) continue;
-                    if (jcol < kLarge) {
-                        if (jcol < n_in) grow[(long long)i * n_in + jcol] = (float)acc[tb][v];
-                    } else if (jcol - kLarge < H) {
-                        grec[(long long)i * H + (jcol - kLarge)] = (float)acc[tb][v];
+                    for (int v = 0; v < 4; ++v)
+                        gst[(s + 4 * v) * kLargeGS + jj * 16 + (lane & 15)] = (float)acc[jj][v];
+                const int c4 = 4 * (lane & 15);
+                const int jc0 = jg * 64 + c4;
+                const bool in_part = jc0 < kLarge;
+                const int col = in_part ? jc0 : jc0 - kLarge;
+                const int width = in_part ? n_in : H;
+                float* base = in_part ? grow : grec;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int rr2 = s + 4 * m;
+                    const float4 val = *reinterpret_cast<const float4*>(gst + rr2 * kLargeGS + c4);
+                    const int i = ib * 16 + rr2;
+                    if (i < H) {
+                        float* dst = base + (long long)i * width + col;
+                        if (col + 4 <= width && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                            *reinterpret_cast<float4*>(dst) = val;
+                        } else {
+                            if (col < width) dst[0] = val.x;
+                            if (col + 1 < width) dst[1] = val.y;
+                            if (col + 2 < width) dst[2] = val.z;
+                            if (col + 3 < width) dst[3] = val.w;
+                        }
                     }
                 }
+            }
         }
         if (r == rr) {
 #pragma unroll
@@ -1211,11 +1264,21 @@ void set_kernel_attributes() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_small_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_large_kernel),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     });
+}
+
+// The 16-row kernels' unmasked instance: exact 256 x 256 shapes, 16-byte aligned weights.
+inline bool large_full(const cfc_params_t* p) {
+    return p->n_in == kLarge && p->n_hid == kLarge && (reinterpret_cast<uintptr_t>(p->w_in) & 15) == 0 &&
+           (reinterpret_cast<uintptr_t>(p->w_rec) & 15) == 0;
 }
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? CFC_OK : CFC_ERR_HIP; }
@@ -1268,9 +1331,14 @@ extern "C" int cfc_forward(const cfc_params_t* params, const float* x, const flo
         return launch_status();
     }
     const long long groups = ((long long)B + kLR - 1) / kLR;
-    hipLaunchKernelGGL(cfc_fwd_large_kernel, dim3((unsigned)groups), dim3(kThreads), large_fwd_lds_bytes(),
-                       stream, params->w_in, params->w_rec, params->b, params->w_tau, x, h0, (double)dt, B,
-                       K, n_in, H, h_seq);
+    if (large_full(params))
+        hipLaunchKernelGGL(cfc_fwd_large_kernel<true>, dim3((unsigned)groups), dim3(kThreads), large_fwd_lds_bytes(),
+                           stream, params->w_in, params->w_rec, params->b, params->w_tau, x, h0, (double)dt, B,
+                           K, n_in, H, h_seq);
+    else
+        hipLaunchKernelGGL(cfc_fwd_large_kernel<false>, dim3((unsigned)groups), dim3(kThreads), large_fwd_lds_bytes(),
+                           stream, params->w_in, params->w_rec, params->b, params->w_tau, x, h0, (double)dt, B,
+                           K, n_in, H, h_seq);
     return launch_status();
 }
 
@@ -1311,9 +1379,14 @@ extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const fl
     }
     if (large) {
         const long long groups = ((long long)B + kLR - 1) / kLR;
-        hipLaunchKernelGGL(cfc_bwd_large_kernel, dim3((unsigned)groups), dim3(kThreads), lds, stream,
-                           params->w_in, params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt,
-                           B, K, n_in, H, scratch, loss);
+        if (large_full(params))
+            hipLaunchKernelGGL(cfc_bwd_large_kernel<true>, dim3((unsigned)groups), dim3(kThreads), lds, stream,
+                               params->w_in, params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt,
+                               B, K, n_in, H, scratch, loss);
+        else
+            hipLaunchKernelGGL(cfc_bwd_large_kernel<false>, dim3((unsigned)groups), dim3(kThreads), lds, stream,
+                               params->w_in, params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt,
+                               B, K, n_in, H, scratch, loss);
         return launch_status();
     }
     hipLaunchKernelGGL(cfc_bwd_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
