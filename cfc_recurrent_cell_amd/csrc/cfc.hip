@@ -756,13 +756,39 @@ constexpr int kLargeBwdMaxK = 20;
 // consecutive j) both touch distinct banks.
 __device__ __forceinline__ int zidx(int j, int r) { return j * kLR + (r ^ (j & 15)); }
 
+// Unit held at row m of a wave's output tile tb: the four tiles of a wave
+// interleave (units 64*wave + 4*m + tb), so the W_rec^T operand of all four
+// tiles is one float4 per lane.
+__device__ __forceinline__ int lunit(int wave, int tb, int m) { return 64 * wave + 4 * m + tb; }
+
+// Per-thread slice (16 elements) of rows r0..r0+15 of a [rows][width] matrix:
+// element m of thread t is (row (t + 256 m) / 256, column (t + 256 m) % 256).
+__device__ __forceinline__ void fetch_t(float (&v)[kLR], const float* src, long long stride, long long r0,
+                                        long long B, int width, int t) {
+#pragma unroll
+    for (int m = 0; m < kLR; ++m) {
+        const int e = t + kThreads * m;
+        const int rr = e >> 8, j = e & 255;
+        const long long b = r0 + rr;
+        v[m] = (b < B && j < width) ? src[b * stride + j] : 0.f;
+    }
+}
+template <typename T>
+__device__ __forceinline__ void store_t(T* dst, const float (&v)[kLR], int t) {
+#pragma unroll
+    for (int m = 0; m < kLR; ++m) {
+        const int e = t + kThreads * m;
+        dst[zidx(e & 255, e >> 8)] = (T)v[m];
+    }
+}
+
 __host__ __device__ constexpr size_t large_fwd_lds_bytes() {
     return (size_t)4 * kLarge * kLR + (size_t)8 * kLarge * kLR;
 }
 constexpr int kLargeGS = 64 + 4;  // row stride (floats) of a wave's gradient-tile buffer
 __host__ __device__ constexpr size_t large_bwd_lds_bytes() {
     return (size_t)4 * kLarge * kLR + (size_t)8 * kLarge * kLR + (size_t)8 * kLarge * kLR +
-           (size_t)8 * 3 * kLarge + (size_t)4 * 4 * 16 * kLargeGS;
+           (size_t)8 * 3 * kLarge + (size_t)8 * kLarge * kLR + (size_t)4 * 4 * 16 * kLargeGS;
 }
 
 // 4 consecutive floats row[col .. col+3] of a row with `width` valid columns
@@ -821,7 +847,7 @@ __device__ __forceinline__ void large_preact(dbl4 acc[4], const float* __restric
         bool rok[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-            const int i = (4 * wave + tb) * 16 + (lane & 15);
+            const int i = lunit(wave, tb, lane & 15);
             rok[tb] = i < H;
             wrow[tb] = wbase + (long long)min(i, H - 1) * width;
         }
@@ -882,7 +908,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int i = (4 * wave + tb) * 16 + s + 4 * v;
+            const int i = lunit(wave, tb, s + 4 * v);
             bias_v[tb][v] = i < H ? (double)bias[i] : 0.0;
             spdt_v[tb][v] = i < H ? softplus_f64((double)w_tau[i]) * dt : 0.0;
         }
@@ -909,7 +935,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int i = (4 * wave + tb) * 16 + s + 4 * v;
+                const int i = lunit(wave, tb, s + 4 * v);
                 const double a = acc[tb][v] + bias_v[tb][v];
                 const double g = inv_one_plus_exp(spdt_v[tb][v] * a);
                 const double c = fma(-2.0, inv_one_plus_exp(2.0 * a), 1.0);
@@ -947,6 +973,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     double* ubias = reinterpret_cast<double*>(smem + 20 * kLarge * kLR);    // [256] per-unit b,
     double* uspdt = ubias + kLarge;                                          // softplus(w_tau)*dt,
     double* usw = uspdt + kLarge;                                            // sigmoid(w_tau)
+    double* gwt = usw + kLarge;  // [256][16] dL/dw_tau sums; each element owned by one lane
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int s = lane >> 4, r = lane & 15;
     const long long r0 = (long long)blockIdx.x * kLR;
@@ -965,21 +992,20 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
         uspdt[u] = ok ? softplus_f64(w) * dt : 0.0;
         usw[u] = ok ? logistic_f64(w) : 0.0;
     }
-    double delta[4][4], gbv[4][4], gwtv[4][4];
+    double delta[4][4];
     double lsum = 0.0;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int i = (4 * wave + tb) * 16 + s + 4 * v;
+            const int i = lunit(wave, tb, s + 4 * v);
             const bool ok = i < H;
             const double d = (ok && row_ok) ? (double)h_seq[(b_own * K + K - 1) * (long long)H + i] -
                                                   (double)y[b_own * H + i]
                                             : 0.0;
             delta[tb][v] = d;
             lsum += 0.5 * d * d;
-            gbv[tb][v] = 0.0;
-            gwtv[tb][v] = 0.0;
+            gwt[zidx(i, r)] = 0.0;
         }
     // loss of each row: lanes r, r+16, r+32, r+48 of every wave share row r
     lsum += __shfl_xor(lsum, 16);
@@ -989,11 +1015,18 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     if (t < kLR && loss && r0 + t < B)
         loss[r0 + t] = (float)(((dab[t] + dab[16 + t]) + dab[32 + t]) + dab[48 + t]);
 
+    // inputs of step k (x_k and h_k-1 of the 16 rows), fetched one step ahead
+    float xr[kLR], hr[kLR];
+    auto fetch_step = [&](int k) {
+        fetch_t(xr, x + (long long)k * n_in, (long long)K * n_in, r0, B, n_in, t);
+        if (k == 0) fetch_t(hr, h0, H, r0, B, H, t);
+        else fetch_t(hr, h_seq + (long long)(k - 1) * H, (long long)K * H, r0, B, H, t);
+    };
+    fetch_step(K - 1);
     for (int k = K - 1; k >= 0; --k) {
         __syncthreads();  // previous step is done with zx, zh, dab
-        stage_t(zx, x + (long long)k * n_in, (long long)K * n_in, r0, B, n_in, t);
-        if (k == 0) stage_t(zh, h0, H, r0, B, H, t);
-        else stage_t(zh, h_seq + (long long)(k - 1) * H, (long long)K * H, r0, B, H, t);
+        store_t(zx, xr, t);
+        store_t(zh, hr, t);
         __syncthreads();
         dbl4 acc[4];
 #pragma unroll
@@ -1004,7 +1037,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int i = (4 * wave + tb) * 16 + s + 4 * v;
+                const int i = lunit(wave, tb, s + 4 * v);
                 const double spdt = uspdt[i];
                 const double a = acc[tb][v] + ubias[i];
                 const double g = inv_one_plus_exp(spdt * a);
@@ -1013,8 +1046,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                 const double d = delta[tb][v];
                 const double dz = d * (hp - c) * g * (1.0 - g);
                 const double da = d * (1.0 - g) * (1.0 - c * c) - dz * spdt;
-                gbv[tb][v] += da;
-                gwtv[tb][v] += dz * (-a * dt) * usw[i];
+                gwt[zidx(i, r)] += dz * (-a * dt) * usw[i];
                 gk[tb][v] = g;
                 dab[zidx(i, r)] = da;
             }
@@ -1033,28 +1065,31 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
             }
         }
         if (k == 0) break;
+        fetch_step(k - 1);
         // delta_k = delta_k+1 * g + W_rec^T dL/da: chunk ic of k-slot s
-        // contracts unit i = 64*s + ic
+        // contracts unit i = 64*s + ic; the four tiles' operands
+        // W_rec[i][lunit(wave, 0..3, lane%16)] are one float4
         dbl4 acc2[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) acc2[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
+        const int jw = 64 * wave + 4 * (lane & 15);
 #pragma unroll 4
         for (int ic = 0; ic < 64; ++ic) {
             const int i = 64 * s + ic;
             const double bz = dab[zidx(i, r)];
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const int j = (4 * wave + tb) * 16 + (lane & 15);
-                double w;
-                if constexpr (FULL) w = (double)w_rec[(long long)i * kLarge + j];
-                else w = (i < H && j < H) ? (double)w_rec[(long long)min(i, H - 1) * H + min(j, H - 1)] : 0.0;
-                acc2[tb] = mfma_f64(w, bz, acc2[tb]);
-            }
+            float4 w4;
+            if constexpr (FULL) w4 = *reinterpret_cast<const float4*>(w_rec + (long long)i * kLarge + jw);
+            else w4 = load4_masked(w_rec + (long long)min(i, H - 1) * H, jw, H, i < H);
+            acc2[0] = mfma_f64((double)w4.x, bz, acc2[0]);
+            acc2[1] = mfma_f64((double)w4.y, bz, acc2[1]);
+            acc2[2] = mfma_f64((double)w4.z, bz, acc2[2]);
+            acc2[3] = mfma_f64((double)w4.w, bz, acc2[3]);
         }
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) delta[tb][v] = fma(delta[tb][v], gk[tb][v], acc2[tb][v]);
+            for (int v = 0; v < 4; ++v)
+                delta[tb][v] = fma(delta[tb][v], gk[tb][v], acc2[tb][v]);
     }
 
     // ---- per row: G = DA^T [X | H_prev] over the K steps, then db and dw_tau
@@ -1138,17 +1173,13 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                 }
             }
         }
-        if (r == rr) {
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int i = (4 * wave + tb) * 16 + s + 4 * v;
-                    if (i < H) {
-                        grec[(long long)H * H + i] = (float)gbv[tb][v];
-                        grec[(long long)H * H + H + i] = (float)gwtv[tb][v];
-                    }
-                }
+        // db: the row's parked dL/da summed over k, last step first (the order
+        // of the per-step accumulation); dw_tau from the lane-owned LDS sums
+        if (t < H) {
+            double gb = 0.0;
+            for (int kk = K - 1; kk >= 0; --kk) gb += dak[kk * kLarge + t];
+            grec[(long long)H * H + t] = (float)gb;
+            grec[(long long)H * H + H + t] = (float)gwt[zidx(t, rr)];
         }
         __syncthreads();  // LDS reused by the next row
     }
