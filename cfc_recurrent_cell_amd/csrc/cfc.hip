@@ -1099,33 +1099,43 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     float* zk = reinterpret_cast<float*>(smem + (size_t)8 * KP * kLarge);  // [KP][512] [x | h_prev]
     float* gst = reinterpret_cast<float*>(smem + large_bwd_lds_bytes() - (size_t)4 * 4 * 16 * kLargeGS) +
                  wave * 16 * kLargeGS;  // this wave's [16][kLargeGS] tile buffer
+    // operands of one row, fetched into registers one row ahead: thread t
+    // holds dL/da_kk[t] (from the parked tail), x_kk[t] and h_kk-1[t]
+    double pd[kLargeBwdMaxK];
+    float px[kLargeBwdMaxK], ph[kLargeBwdMaxK];
+    auto fetch_row = [&](long long b) {
+        const unsigned* tq = reinterpret_cast<const unsigned*>(scratch + b * N + tmp_off);
+#pragma unroll
+        for (int kk = 0; kk < kLargeBwdMaxK; ++kk) {
+            double dv = 0.0;
+            float xv = 0.f, hv = 0.f;
+            if (kk < K) {
+                if (t < H) {
+                    const long long q = 2 * ((long long)kk * H + t);
+                    dv = __builtin_bit_cast(double, ((unsigned long long)tq[q + 1] << 32) | tq[q]);
+                    hv = kk == 0 ? h0[b * H + t] : h_seq[(b * K + kk - 1) * (long long)H + t];
+                }
+                if (t < n_in) xv = x[(b * K + kk) * (long long)n_in + t];
+            }
+            pd[kk] = dv;
+            px[kk] = xv;
+            ph[kk] = hv;
+        }
+    };
+    fetch_row(r0);  // r0 < B: the grid has no empty workgroup
     for (int rr = 0; rr < kLR; ++rr) {
         const long long b = r0 + rr;
         if (b >= B) break;
-        const unsigned* tq = reinterpret_cast<const unsigned*>(scratch + b * N + tmp_off);
-        for (int e = t; e < KP * kLarge; e += kThreads) {
-            const int kk = e >> 8, i = e & 255;
-            double v = 0.0;
-            if (kk < K && i < H) {
-                const long long q = 2 * ((long long)kk * H + i);
-                v = __builtin_bit_cast(double, ((unsigned long long)tq[q + 1] << 32) | tq[q]);
+#pragma unroll
+        for (int kk = 0; kk < kLargeBwdMaxK; ++kk) {
+            if (kk < KP) {
+                dak[kk * kLarge + t] = pd[kk];
+                zk[kk * 2 * kLarge + t] = px[kk];
+                zk[kk * 2 * kLarge + kLarge + t] = ph[kk];
             }
-            dak[e] = v;
-        }
-        for (int e = t; e < KP * 2 * kLarge; e += kThreads) {
-            const int kk = e >> 9, j = e & 511;
-            float v = 0.f;
-            if (kk < K) {
-                if (j < kLarge) {
-                    if (j < n_in) v = x[(b * K + kk) * (long long)n_in + j];
-                } else {
-                    const int jj = j - kLarge;
-                    if (jj < H) v = kk == 0 ? h0[b * H + jj] : h_seq[(b * K + kk - 1) * (long long)H + jj];
-                }
-            }
-            zk[e] = v;
         }
         __syncthreads();
+        if (rr + 1 < kLR && b + 1 < B) fetch_row(b + 1);
         float* grow = scratch + b * N;
         float* grec = grow + (long long)H * n_in;
         // the wave's 64 units x 512 columns, in 16 x 64 blocks: 4 column tiles
