@@ -1,8 +1,11 @@
 """Benchmark of the CfC K-loop hot path on one MI355X.
 
-One step = cfc_forward + cfc_backward (overwrite mode, so the scratch clear is
-part of the step) + reduce_axis0 over one batch of the training-scale
-workload (B=256, K=64, n_in=n_hid=128, dt=0.5), inputs resident in HBM.
+One step = forward + backward (overwrite mode, so the scratch clear is part of
+the step) + reduce_axis0 over one batch of the training-scale workload (B=256,
+K=64, n_in=n_hid=128, dt=0.5), inputs resident in HBM.  By default the
+forward and backward are one cfc_forward_backward call (one kernel at this
+shape); --path separate times cfc_forward + cfc_backward instead.  Both paths
+are timed in every run; the other one is reported in "other_path".
 
 Prints ONE JSON line.  `value` is batch-steps/s = B*K / seconds per step.
 The roofline object describes the step's dominant kernel, timed with HIP
@@ -32,18 +35,22 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_train_B256_K64_H128.json"
 def algorithmic_work(B, K, n_in, H):
     """FLOPs and bytes per launch that the method itself needs (not what a
     particular kernel happens to move).  FLOPs count multiply-adds of the
-    contractions as 2; the O(H) elementwise work is not counted."""
+    contractions as 2; the O(H) elementwise work is not counted.  The separate
+    backward must recompute the pre-activations from h_seq (its inputs hold no
+    a_k); the one-call path has them from its own forward."""
     N = H * (n_in + H + 2)
     rows = B * K
     fwd_flops = rows * 2 * H * (n_in + H)
-    # bwd: recompute a, W_rec^T da, dW_in and dW_rec contractions
-    bwd_flops = rows * (2 * H * (n_in + H) + 2 * H * H + 2 * H * (n_in + H))
+    # bwd: W_rec^T da, dW_in and dW_rec contractions (+ recomputing a)
+    grad_flops = rows * (2 * H * H + 2 * H * (n_in + H))
+    bwd_flops = rows * 2 * H * (n_in + H) + grad_flops
     f = 4
     fwd_bytes = f * (B * K * n_in + B * H + B * K * H + H * (n_in + H + 2))
     bwd_bytes = f * (B * K * n_in + B * H + B * K * H + B * H + B * N + B + H * (n_in + H + 2))
+    fb_bytes = f * (B * K * n_in + B * H + B * K * H + B * H + B * N + B + H * (n_in + H + 2))
     red_bytes = f * (B * N + N)
-    return dict(fwd_flops=fwd_flops, bwd_flops=bwd_flops, fwd_bytes=fwd_bytes, bwd_bytes=bwd_bytes,
-                reduce_bytes=red_bytes)
+    return dict(fwd_flops=fwd_flops, bwd_flops=bwd_flops, fb_flops=fwd_flops + grad_flops,
+                fwd_bytes=fwd_bytes, bwd_bytes=bwd_bytes, fb_bytes=fb_bytes, reduce_bytes=red_bytes)
 
 
 def source_hash():
@@ -126,6 +133,8 @@ def main():
                     help="which seeded workload one step runs (the metric is quoted on 'train')")
     ap.add_argument("--reduce-sweep", action="store_true",
                     help="also time reduce_axis0 alone, cache-flushed, over a range of sizes")
+    ap.add_argument("--path", default="fused", choices=["fused", "separate"],
+                    help="fused: one cfc_forward_backward call; separate: cfc_forward + cfc_backward")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the CfC path has no cross-GPU step in this "
@@ -165,7 +174,7 @@ def main():
     loss = torch.empty((B,), device=dev)
     out = torch.empty((N,), device=dev)
 
-    def step(ev=None):
+    def step_separate(ev=None):
         if ev is not None:
             ev[0].record()
         C.cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, h_seq=h_seq)
@@ -178,26 +187,46 @@ def main():
         if ev is not None:
             ev[3].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def step_fused(ev=None):
+        if ev is not None:
+            ev[0].record()
+        C.cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt, h_seq=h_seq, scratch=scratch, loss=loss)
+        if ev is not None:
+            ev[1].record()
+        C.reduce_axis0(scratch, out=out)
+        if ev is not None:
+            ev[2].record()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for s in range(args.steps):
-        step(evs[s])
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    k_ms = {
-        "cfc_fwd_kernel": sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps,
-        "cfc_bwd_kernel": sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps,
-        "reduce_axis0_kernel": sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps,
-    }
+    def timed(path):
+        """W warm-up steps, then K steps bracketed by a sync on both sides, with
+        HIP events around every launch on the stream the launches use."""
+        step = step_fused if path == "fused" else step_separate
+        nev = 3 if path == "fused" else 4
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+        t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_start.record()
+        for i in range(args.steps):
+            step(evs[i])
+        t_end.record()
+        torch.cuda.synchronize()
+        ms = t_start.elapsed_time(t_end) / args.steps
+        per = lambda a, c: sum(e[a].elapsed_time(e[c]) for e in evs) / args.steps
+        if path == "fused":
+            km = {"cfc_fb_kernel": per(0, 1), "reduce_axis0_kernel": per(1, 2)}
+        else:
+            km = {"cfc_fwd_kernel": per(0, 1), "cfc_bwd_kernel": per(1, 2), "reduce_axis0_kernel": per(2, 3)}
+        return ms, km
+
+    other = "separate" if args.path == "fused" else "fused"
+    ms_other, k_other = timed(other)
+    ms_per_step, k_ms = timed(args.path)
     work = algorithmic_work(B, K, n_in, H)
-    flops = {"cfc_fwd_kernel": work["fwd_flops"], "cfc_bwd_kernel": work["bwd_flops"]}
+    flops = {"cfc_fwd_kernel": work["fwd_flops"], "cfc_bwd_kernel": work["bwd_flops"],
+             "cfc_fb_kernel": work["fb_flops"]}
     dom = max(k_ms, key=k_ms.get)
     if dom == "reduce_axis0_kernel":
         ach = work["reduce_bytes"] / (k_ms[dom] * 1e-3) / 1e9
@@ -208,6 +237,7 @@ def main():
         roof = {"bound": "alu", "achieved": ach, "peak": PEAK_F64_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_F64_TFLOPS}
     roof["kernel"] = dom
+    roof["algorithmic_flops_per_launch"] = flops.get(dom)
     roof["traffic"] = measured_traffic(dom)
     red_gbps = work["reduce_bytes"] / (k_ms["reduce_axis0_kernel"] * 1e-3) / 1e9
 
@@ -220,7 +250,10 @@ def main():
         "config": {"workload": cfg.name, "B": B, "K": K, "n_in": n_in, "n_hid": H, "dt": dt,
                    "scratch_N": N, "io_dtype": "f32", "seed": cfg.seed},
         "roofline": roof,
+        "path": args.path,
         "kernels_ms": k_ms,
+        "other_path": {"path": other, "value": B * K / (ms_other * 1e-3), "ms_per_step": ms_other,
+                       "kernels_ms": k_other},
         "reduce_axis0": {"GB_per_s": red_gbps, "frac_hbm": red_gbps / PEAK_HBM_GBPS,
                          "bytes": work["reduce_bytes"],
                          "note": "scratch of this step (33.8 MB) may be served partly from the MALL"},

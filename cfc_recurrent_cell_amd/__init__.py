@@ -18,8 +18,8 @@ from ._lib import (  # noqa: F401
     declared_symbols, load_library, status_string,
 )
 
-__all__ = ["cfc_forward", "cfc_backward", "reduce_axis0", "cfc_scratch_row_len", "CfcError",
-           "load_library"]
+__all__ = ["cfc_forward", "cfc_backward", "cfc_forward_backward", "reduce_axis0",
+           "cfc_scratch_row_len", "CfcError", "load_library"]
 
 
 def cfc_scratch_row_len(n_in: int, n_hid: int) -> int:
@@ -98,6 +98,37 @@ def cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, scratch=None
         B, K, scratch.data_ptr(), loss.data_ptr() if loss is not None else None, flags,
         _stream(x.device, stream)))
     return scratch, loss
+
+
+def cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt: float, h_seq=None, scratch=None,
+                         loss=None, accumulate: bool = False, want_loss: bool = True,
+                         stream=None) -> Tuple[object, object, Optional[object]]:
+    """(h_seq [B, K, H], scratch [B, N], loss [B] or None): the forward and the
+    backward of the same inputs in one library call (see include/cfc.h)."""
+    import torch
+    lib = load_library()
+    p = _params(w_in, w_rec, b, w_tau)
+    B, K, _ = x.shape
+    N = cfc_scratch_row_len(p.n_in, p.n_hid)
+    _dev_f32(x, "x", (B, K, p.n_in))
+    _dev_f32(h0, "h0", (B, p.n_hid))
+    _dev_f32(y, "y", (B, p.n_hid))
+    if h_seq is None:
+        h_seq = torch.empty((B, K, p.n_hid), dtype=torch.float32, device=x.device)
+    _dev_f32(h_seq, "h_seq", (B, K, p.n_hid))
+    if scratch is None:
+        scratch = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    _dev_f32(scratch, "scratch", (B, N))
+    if loss is None and want_loss:
+        loss = torch.empty((B,), dtype=torch.float32, device=x.device)
+    if loss is not None:
+        _dev_f32(loss, "loss", (B,))
+    flags = CFC_ACCUMULATE if accumulate else CFC_OVERWRITE
+    _check("cfc_forward_backward", lib.cfc_forward_backward(
+        ctypes.byref(p), x.data_ptr(), h0.data_ptr(), y.data_ptr(), float(dt), B, K,
+        h_seq.data_ptr(), scratch.data_ptr(), loss.data_ptr() if loss is not None else None, flags,
+        _stream(x.device, stream)))
+    return h_seq, scratch, loss
 
 
 def reduce_axis0(per_batch, out=None, stream=None):

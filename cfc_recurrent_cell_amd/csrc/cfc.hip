@@ -492,92 +492,20 @@ __device__ __forceinline__ void store_grad_f(float* p, double v, int accumulate)
     *p = (float)v;
 }
 
-__global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
-    const float* __restrict__ w_in, const float* __restrict__ w_rec,
-    const float* __restrict__ bias, const float* __restrict__ w_tau,
-    const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
-    const float* __restrict__ y, double dt, int K, int n_in, int H, float* __restrict__ scratch,
-    float* __restrict__ loss, int accumulate) {
+// Second half of a row's backward pass, shared by cfc_bwd_small_kernel and
+// cfc_fb_small_kernel.  On entry (after a barrier): AD[k][*] holds a_k for
+// k < K and 0 beyond, zs[k] holds [x_k | h_k-1] (rows >= K zero), spv/swv hold
+// softplus(w_tau) and sigmoid(w_tau), and delta is h_K - y of this lane's unit o
+// (computed from the float32 h_K).  Seeds the row's loss, runs the reverse
+// chain (AD[k] becomes dL/da_k), forms G = DA^T [X | H_prev] on the matrix
+// cores and writes the row [dW_in | dW_rec | db | dw_tau].
+__device__ __forceinline__ void small_reverse_and_grads(
+    const float* __restrict__ w_rec, double dt, int K, int n_in, int H, double delta, double* AD,
+    const double* spv, const double* swv, double* red, const float* zs, float* gst,
+    float* __restrict__ row, float* __restrict__ loss_b, int accumulate, int lane, int wave, int jb,
+    int ib, int o, bool gate_lane) {
     constexpr int HP = kSmall, NP = kSmall, ZW = kSmallZW, ZS = kSmallZS;
-    extern __shared__ __align__(16) unsigned char smem[];
     constexpr int KP = kSmallBwdMaxK;
-    double* AD = reinterpret_cast<double*>(smem);  // [KP][HP]: a, then dL/da
-    double* spv = AD + KP * HP;                    // [HP]
-    double* swv = spv + HP;                        // [HP]
-    double* red = swv + HP;                        // [8]
-    float* zs = reinterpret_cast<float*>(red + 8);  // [KP][ZS] = [x_k | h_k]
-
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    float* gst = zs + KP * ZS + wave * 16 * kSmallGS;  // this wave's [16][kSmallGS] tile buffer
-    const long long b = blockIdx.x;
-    const long long N = (long long)H * (n_in + H + 2);
-    const int jb = lane & 7;
-    const int ib = wave * 8 + (lane >> 3);
-    const int o = 4 * ib + ((jb & 4) ? 2 : 0) + ((jb & 2) ? 1 : 0);
-    const bool gate_lane = jb & 1;
-
-    // Weight operand of the recomputation, in registers.  Chunk jc of k-slot
-    // s = lane/16 contracts index j = 64*s + jc of [x | h_prev], so a lane holds
-    // one contiguous 64-wide span of a row of W_in (s = 0, 1) or W_rec (s = 2, 3):
-    // wb[q][jc] = [W_in | W_rec][(2*wave + q)*16 + lane%16][64*s + jc]
-    const int slot = lane >> 4;
-    double wb[2][ZW / 4];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int row = (2 * wave + q) * 16 + (lane & 15);
-        const int rowc = min(row, H - 1);
-        const bool in_part = slot < 2;
-        const int c0 = in_part ? 64 * slot : 64 * (slot - 2);
-        const int width = in_part ? n_in : H;
-        const int valid = row < H ? min(max(width - c0, 0), ZW / 4) : 0;
-        const float* src = in_part ? w_in + (long long)rowc * n_in + min(c0, n_in - 1)
-                                   : w_rec + (long long)rowc * H + min(c0, H - 1);
-        load_span_f64<ZW / 4>(wb[q], src, valid);
-    }
-
-    // ---- stage [x_k | h_k] for every step (h_0 = h0, h_k = h_seq[k-1])
-    stage_rows(zs, ZS, x + b * K * (long long)n_in, n_in, K, n_in, KP, NP, t);
-    stage_rows(zs + NP, ZS, h0 + b * H, H, 1, H, 1, HP, t);
-    if (K > 1) stage_rows(zs + ZS + NP, ZS, h_seq + b * K * (long long)H, H, K - 1, H, KP - 1, HP, t);
-    else stage_rows(zs + ZS + NP, ZS, h_seq, H, 0, H, KP - 1, HP, t);
-    for (int u = t; u < HP; u += kThreads) {
-        const double w = u < H ? (double)w_tau[u] : 0.0;
-        spv[u] = u < H ? softplus_f64(w) : 0.0;
-        swv[u] = u < H ? logistic_f64(w) : 0.0;
-    }
-    const double bias_q0 = (2 * wave) * 16 + (lane & 15) < H ? (double)bias[(2 * wave) * 16 + (lane & 15)] : 0.0;
-    const double bias_q1 = (2 * wave + 1) * 16 + (lane & 15) < H ? (double)bias[(2 * wave + 1) * 16 + (lane & 15)] : 0.0;
-    __syncthreads();
-
-    // ---- recompute every step's pre-activation on the matrix cores
-    {
-        dbl4 acc[4][2];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int q = 0; q < 2; ++q) acc[kb][q] = dbl4{0.0, 0.0, 0.0, 0.0};
-        const float* za = zs + (lane & 15) * ZS + 64 * slot;
-#pragma unroll
-        for (int jc = 0; jc < ZW / 4; ++jc) {
-#pragma unroll
-            for (int kb = 0; kb < KP / 16; ++kb) {
-                const double a = (double)za[kb * 16 * ZS + jc];
-                acc[kb][0] = mfma_f64(a, wb[0][jc], acc[kb][0]);
-                acc[kb][1] = mfma_f64(a, wb[1][jc], acc[kb][1]);
-            }
-        }
-#pragma unroll
-        for (int kb = 0; kb < KP / 16; ++kb) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int kk = kb * 16 + (lane >> 4) + 4 * v;
-                double* arow = AD + kk * HP + (2 * wave) * 16 + (lane & 15);
-                arow[0] = kk < K ? acc[kb][0][v] + bias_q0 : 0.0;
-                arow[16] = kk < K ? acc[kb][1][v] + bias_q1 : 0.0;
-            }
-        }
-    }
-
     // ---- W_rec^T slice into registers: wt[r][c] = W_rec[16jb + c][4ib + r]
     double wt[4][16];
 #pragma unroll
@@ -591,7 +519,6 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     }
 
     // ---- loss seed
-    double delta = o < H ? (double)h_seq[(b * K + K - 1) * (long long)H + o] - (double)y[b * H + o] : 0.0;
     {
         double l = gate_lane ? 0.0 : 0.5 * delta * delta;
         for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
@@ -600,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     const double sp_o = spv[o], sw_o = swv[o], spdt_o = sp_o * dt;
     const GateLane gl = gate_lane_consts(gate_lane, spdt_o);
     __syncthreads();
-    if (t == 0 && loss) loss[b] = (float)(((red[0] + red[1]) + red[2]) + red[3]);
+    if (wave == 0 && lane == 0 && loss_b) *loss_b = (float)(((red[0] + red[1]) + red[2]) + red[3]);
 
     // ---- serial reverse chain
     double gb = 0.0, gwt = 0.0;
@@ -644,7 +571,6 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     }
 
     // ---- weight gradients on the matrix cores: G = DA^T [X | H_prev]
-    float* row = scratch + b * N;
     float* rrec = row + (long long)H * n_in;
     {
         const int ib0 = 2 * wave;
@@ -737,6 +663,237 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
         store_grad_f(rrec + (long long)H * H + o, gb, accumulate);
         store_grad_f(rrec + (long long)H * H + H + o, gwt, accumulate);
     }
+}
+
+__global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
+    const float* __restrict__ w_in, const float* __restrict__ w_rec,
+    const float* __restrict__ bias, const float* __restrict__ w_tau,
+    const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
+    const float* __restrict__ y, double dt, int K, int n_in, int H, float* __restrict__ scratch,
+    float* __restrict__ loss, int accumulate) {
+    constexpr int HP = kSmall, NP = kSmall, ZW = kSmallZW, ZS = kSmallZS;
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int KP = kSmallBwdMaxK;
+    double* AD = reinterpret_cast<double*>(smem);  // [KP][HP]: a, then dL/da
+    double* spv = AD + KP * HP;                    // [HP]
+    double* swv = spv + HP;                        // [HP]
+    double* red = swv + HP;                        // [8]
+    float* zs = reinterpret_cast<float*>(red + 8);  // [KP][ZS] = [x_k | h_k]
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    float* gst = zs + KP * ZS + wave * 16 * kSmallGS;  // this wave's [16][kSmallGS] tile buffer
+    const long long b = blockIdx.x;
+    const long long N = (long long)H * (n_in + H + 2);
+    const int jb = lane & 7;
+    const int ib = wave * 8 + (lane >> 3);
+    const int o = 4 * ib + ((jb & 4) ? 2 : 0) + ((jb & 2) ? 1 : 0);
+    const bool gate_lane = jb & 1;
+
+    // Weight operand of the recomputation, in registers.  Chunk jc of k-slot
+    // s = lane/16 contracts index j = 64*s + jc of [x | h_prev], so a lane holds
+    // one contiguous 64-wide span of a row of W_in (s = 0, 1) or W_rec (s = 2, 3):
+    // wb[q][jc] = [W_in | W_rec][(2*wave + q)*16 + lane%16][64*s + jc]
+    const int slot = lane >> 4;
+    double wb[2][ZW / 4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int row = (2 * wave + q) * 16 + (lane & 15);
+        const int rowc = min(row, H - 1);
+        const bool in_part = slot < 2;
+        const int c0 = in_part ? 64 * slot : 64 * (slot - 2);
+        const int width = in_part ? n_in : H;
+        const int valid = row < H ? min(max(width - c0, 0), ZW / 4) : 0;
+        const float* src = in_part ? w_in + (long long)rowc * n_in + min(c0, n_in - 1)
+                                   : w_rec + (long long)rowc * H + min(c0, H - 1);
+        load_span_f64<ZW / 4>(wb[q], src, valid);
+    }
+
+    // ---- stage [x_k | h_k] for every step (h_0 = h0, h_k = h_seq[k-1])
+    stage_rows(zs, ZS, x + b * K * (long long)n_in, n_in, K, n_in, KP, NP, t);
+    stage_rows(zs + NP, ZS, h0 + b * H, H, 1, H, 1, HP, t);
+    if (K > 1) stage_rows(zs + ZS + NP, ZS, h_seq + b * K * (long long)H, H, K - 1, H, KP - 1, HP, t);
+    else stage_rows(zs + ZS + NP, ZS, h_seq, H, 0, H, KP - 1, HP, t);
+    for (int u = t; u < HP; u += kThreads) {
+        const double w = u < H ? (double)w_tau[u] : 0.0;
+        spv[u] = u < H ? softplus_f64(w) : 0.0;
+        swv[u] = u < H ? logistic_f64(w) : 0.0;
+    }
+    const double bias_q0 = (2 * wave) * 16 + (lane & 15) < H ? (double)bias[(2 * wave) * 16 + (lane & 15)] : 0.0;
+    const double bias_q1 = (2 * wave + 1) * 16 + (lane & 15) < H ? (double)bias[(2 * wave + 1) * 16 + (lane & 15)] : 0.0;
+    __syncthreads();
+
+    // ---- recompute every step's pre-activation on the matrix cores
+    {
+        dbl4 acc[4][2];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) acc[kb][q] = dbl4{0.0, 0.0, 0.0, 0.0};
+        const float* za = zs + (lane & 15) * ZS + 64 * slot;
+#pragma unroll
+        for (int jc = 0; jc < ZW / 4; ++jc) {
+#pragma unroll
+            for (int kb = 0; kb < KP / 16; ++kb) {
+                const double a = (double)za[kb * 16 * ZS + jc];
+                acc[kb][0] = mfma_f64(a, wb[0][jc], acc[kb][0]);
+                acc[kb][1] = mfma_f64(a, wb[1][jc], acc[kb][1]);
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < KP / 16; ++kb) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int kk = kb * 16 + (lane >> 4) + 4 * v;
+                double* arow = AD + kk * HP + (2 * wave) * 16 + (lane & 15);
+                arow[0] = kk < K ? acc[kb][0][v] + bias_q0 : 0.0;
+                arow[16] = kk < K ? acc[kb][1][v] + bias_q1 : 0.0;
+            }
+        }
+    }
+
+    const double delta =
+        o < H ? (double)h_seq[(b * K + K - 1) * (long long)H + o] - (double)y[b * H + o] : 0.0;
+    small_reverse_and_grads(w_rec, dt, K, n_in, H, delta, AD, spv, swv, red, zs, gst, scratch + b * N,
+                            loss ? loss + b : nullptr, accumulate, lane, wave, jb, ib, o, gate_lane);
+}
+
+// Forward and backward of one row in one workgroup (n_in, n_hid <= 128,
+// K <= 64).  The forward's pre-activations a_k stay in LDS (in float64) for the
+// reverse chain and [x_k | h_k-1] is staged once for both directions, so
+// nothing is recomputed and nothing is read back from h_seq.
+__host__ __device__ constexpr size_t small_fb_lds_bytes() {
+    return small_bwd_lds_bytes() + (size_t)8 * 2 * kSmall;
+}
+
+__global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
+    const float* __restrict__ w_in, const float* __restrict__ w_rec,
+    const float* __restrict__ bias, const float* __restrict__ w_tau,
+    const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ y, double dt,
+    int K, int n_in, int H, float* __restrict__ h_seq, float* __restrict__ scratch,
+    float* __restrict__ loss, int accumulate) {
+    constexpr int HP = kSmall, NP = kSmall, ZS = kSmallZS, KP = kSmallBwdMaxK;
+    extern __shared__ __align__(16) unsigned char smem[];
+    double* AD = reinterpret_cast<double*>(smem);  // [KP][HP]: W_in x_k + b, then a_k, then dL/da_k
+    double* spv = AD + KP * HP;                    // [HP]
+    double* swv = spv + HP;                        // [HP]
+    double* red = swv + HP;                        // [8]
+    double* hb = red + 8;                          // [2][HP] h_k exchange
+    float* zs = reinterpret_cast<float*>(hb + 2 * HP);  // [KP][ZS] = [x_k | h_k-1]
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    float* gst = zs + KP * ZS + wave * 16 * kSmallGS;
+    const long long b = blockIdx.x;
+    const long long N = (long long)H * (n_in + H + 2);
+    const int jb = lane & 7;
+    const int ib = wave * 8 + (lane >> 3);
+    const int o = 4 * ib + ((jb & 4) ? 2 : 0) + ((jb & 2) ? 1 : 0);
+    const bool gate_lane = jb & 1;
+    const int slot = lane >> 4;
+
+    // ---- stage x (rows >= K zero), h0 as row 0 of the h_prev half (rows >= K
+    // zero; rows 1..K-1 are written by the chain), per-unit constants
+    stage_rows(zs, ZS, x + b * K * (long long)n_in, n_in, K, n_in, KP, NP, t);
+    stage_rows(zs + NP, ZS, h0 + b * H, H, 1, H, 1, HP, t);
+    stage_rows(zs + K * ZS + NP, ZS, h0, H, 0, H, KP - K, HP, t);
+    for (int u = t; u < HP; u += kThreads) {
+        const double w = u < H ? (double)w_tau[u] : 0.0;
+        spv[u] = u < H ? softplus_f64(w) : 0.0;
+        swv[u] = u < H ? logistic_f64(w) : 0.0;
+        hb[u] = u < H ? (double)h0[b * H + u] : 0.0;
+    }
+    const double bias_q0 = (2 * wave) * 16 + (lane & 15) < H ? (double)bias[(2 * wave) * 16 + (lane & 15)] : 0.0;
+    const double bias_q1 = (2 * wave + 1) * 16 + (lane & 15) < H ? (double)bias[(2 * wave + 1) * 16 + (lane & 15)] : 0.0;
+    __syncthreads();
+
+    // ---- input projection of all K steps on the matrix cores: chunk jc of
+    // k-slot s contracts j = 32*s + jc, a contiguous span of a W_in row
+    {
+        double wb[2][NP / 4];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int row = (2 * wave + q) * 16 + (lane & 15);
+            const int valid = row < H ? min(max(n_in - 32 * slot, 0), NP / 4) : 0;
+            load_span_f64<NP / 4>(wb[q], w_in + (long long)min(row, H - 1) * n_in + min(32 * slot, n_in - 1), valid);
+        }
+        dbl4 acc[KP / 16][2];
+#pragma unroll
+        for (int kb = 0; kb < KP / 16; ++kb)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) acc[kb][q] = dbl4{0.0, 0.0, 0.0, 0.0};
+        const float* xa = zs + (lane & 15) * ZS + 32 * slot;
+#pragma unroll
+        for (int jc = 0; jc < NP / 4; ++jc) {
+#pragma unroll
+            for (int kb = 0; kb < KP / 16; ++kb) {
+                const double a = (double)xa[kb * 16 * ZS + jc];
+                acc[kb][0] = mfma_f64(a, wb[0][jc], acc[kb][0]);
+                acc[kb][1] = mfma_f64(a, wb[1][jc], acc[kb][1]);
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < KP / 16; ++kb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int kk = kb * 16 + (lane >> 4) + 4 * v;
+                double* urow = AD + kk * HP + (2 * wave) * 16 + (lane & 15);
+                urow[0] = kk < K ? acc[kb][0][v] + bias_q0 : 0.0;
+                urow[16] = kk < K ? acc[kb][1][v] + bias_q1 : 0.0;
+            }
+    }
+
+    // ---- forward chain (as in cfc_fwd_small_kernel); a_k replaces the
+    // projection in AD, h_k goes to h_seq and to the h_prev half of row k+1
+    double wr[4][16];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = 4 * ib + r;
+        const int valid = row < H ? min(max(H - 16 * jb, 0), 16) : 0;
+        load_span_f64<16>(wr[r], w_rec + (long long)min(row, H - 1) * H + min(16 * jb, H - 1), valid);
+    }
+    double hprev = o < H ? (double)h0[b * H + o] : 0.0;
+    const GateLane gl = gate_lane_consts(gate_lane, spv[o] * dt);
+    __syncthreads();
+    int cur = 0;
+    for (int k = 0; k < K; ++k) {
+        const double u = AD[k * HP + o];
+        const double* hv = hb + cur * HP + 16 * jb;
+        double hj[16];
+#pragma unroll
+        for (int c = 0; c < 16; c += 2) {
+            const double2 v2 = *reinterpret_cast<const double2*>(hv + c);
+            hj[c] = v2.x;
+            hj[c + 1] = v2.y;
+        }
+        double pe[4] = {0.0, 0.0, 0.0, 0.0}, po[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int c = 0; c < 16; c += 2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pe[r] = fma(wr[r][c], hj[c], pe[r]);
+                po[r] = fma(wr[r][c + 1], hj[c + 1], po[r]);
+            }
+        double p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = pe[r] + po[r];
+        const double a = u + reduce_scatter8(p, jb);
+        double g, c;
+        cell_gates(a, gl, g, c);
+        const double hn = fma(g, hprev - c, c);
+        hprev = hn;
+        if (!gate_lane) {
+            AD[k * HP + o] = a;
+            hb[(cur ^ 1) * HP + o] = hn;
+            if (k + 1 < K) zs[(k + 1) * ZS + NP + o] = (float)hn;
+            if (o < H) h_seq[(b * K + k) * (long long)H + o] = (float)hn;
+        }
+        cur ^= 1;
+        __syncthreads();
+    }
+
+    // ---- backward from the float32 h_K, as the separate backward sees it
+    const double delta = o < H ? (double)(float)hprev - (double)y[b * H + o] : 0.0;
+    small_reverse_and_grads(w_rec, dt, K, n_in, H, delta, AD, spv, swv, red, zs, gst, scratch + b * N,
+                            loss ? loss + b : nullptr, accumulate, lane, wave, jb, ib, o, gate_lane);
 }
 
 // =====================================================================
@@ -1305,6 +1462,8 @@ void set_kernel_attributes() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_small_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fb_small_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<true>),
@@ -1434,6 +1593,48 @@ extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const fl
                        params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, K, n_in,
                        H, scratch, loss, flags == CFC_ACCUMULATE ? 1 : 0);
     return launch_status();
+}
+
+extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, const float* h0,
+                                    const float* y, float dt, int B, int K, float* h_seq, float* scratch,
+                                    float* loss, int flags, hipStream_t stream) {
+    int rc = check_params(params);
+    if (rc) return rc;
+    if (!x || !h0 || !y || !h_seq || !scratch) return CFC_ERR_NULL;
+    if (B < 1 || K < 1) return CFC_ERR_DIM;
+    if (flags != CFC_OVERWRITE && flags != CFC_ACCUMULATE) return CFC_ERR_DIM;
+    if (!std::isfinite(dt)) return CFC_ERR_DT;
+    const int n_in = params->n_in, H = params->n_hid;
+    const long long N = cfc_scratch_row_len(n_in, H);
+    long long nx, ns, nsc;
+    if (N < 0 || !mul_ok((long long)B * K, n_in, &nx) || !mul_ok((long long)B * K, H, &ns) ||
+        !mul_ok((long long)B, N, &nsc))
+        return CFC_ERR_DIM;
+    const Range outs[] = {span(h_seq, ns), span(scratch, nsc), span(loss, loss ? B : 0)};
+    const Range ins[] = {span(x, nx), span(h0, (long long)B * H), span(y, (long long)B * H),
+                         span(params->w_in, (long long)H * n_in), span(params->w_rec, (long long)H * H),
+                         span(params->b, H), span(params->w_tau, H)};
+    for (const Range& o : outs)
+        for (const Range& r : ins)
+            if (overlap(o, r)) return CFC_ERR_OVERLAP;
+    if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2]))
+        return CFC_ERR_OVERLAP;
+    if (n_in <= kSmall && H <= kSmall && K <= kSmallBwdMaxK) {
+        set_kernel_attributes();
+        hipLaunchKernelGGL(cfc_fb_small_kernel, dim3(B), dim3(kThreads), small_fb_lds_bytes(), stream,
+                           params->w_in, params->w_rec, params->b, params->w_tau, x, h0, y, (double)dt, K,
+                           n_in, H, h_seq, scratch, loss, flags == CFC_ACCUMULATE ? 1 : 0);
+        return launch_status();
+    }
+    // other shapes: the two directions as separate launches on the same stream;
+    // the backward's shape limits are checked before anything is launched
+    const bool large = (n_in > kSmall || H > kSmall) && K <= kLargeBwdMaxK && flags == CFC_OVERWRITE;
+    const bool small_bwd = n_in <= kSmall && H <= kSmall && K <= kSmallBwdMaxK;
+    const size_t lds = small_bwd ? small_bwd_lds_bytes() : large ? large_bwd_lds_bytes() : bwd_lds_bytes(K, n_in, H);
+    if (lds > kLdsBytes) return CFC_ERR_UNSUPPORTED;
+    rc = cfc_forward(params, x, h0, dt, B, K, h_seq, stream);
+    if (rc) return rc;
+    return cfc_backward(params, x, h0, h_seq, y, dt, B, K, scratch, loss, flags, stream);
 }
 
 extern "C" int reduce_axis0(const float* per_batch, long long B, long long N, float* out,

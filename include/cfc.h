@@ -8,6 +8,9 @@
  *   cfc_backward  x, h0, h_seq, y [B,H]            -> scratch [B,N] (+ loss [B])
  *   reduce_axis0  scratch [B,N]                    -> out [N]
  *
+ * cfc_forward_backward does the first two in one call (one launch where the
+ * shape allows it).
+ *
  * The structure -- one independent chain per batch row, a per-batch gradient
  * scratch in which each row has a single writer and no atomics, and a
  * separate column-sum reducer that overwrites its output -- follows the
@@ -120,6 +123,26 @@ int cfc_forward(const cfc_params_t *params, const float *x, const float *h0, flo
 int cfc_backward(const cfc_params_t *params, const float *x, const float *h0,
                  const float *h_seq, const float *y, float dt, int B, int K,
                  float *scratch, float *loss, int flags, hipStream_t stream);
+
+/* cfc_forward followed by cfc_backward on the same inputs, in one call
+ * ("K-loop Parallelization Implementation Plan", Tasks 2 and 3 back to back):
+ *   params, x, h0, dt, B, K   as for cfc_forward
+ *   y, scratch, loss, flags   as for cfc_backward
+ *   h_seq    [B, K, n_hid] OUTPUT, as cfc_forward writes it
+ * For n_in, n_hid <= 128 and K <= 64 this is ONE kernel per row that keeps the
+ * forward's float64 pre-activations and the staged [x_k | h_k-1] on chip for
+ * the reverse pass instead of recomputing them from the float32 h_seq.  The
+ * reverse pass then uses the unrounded pre-activations (the separate backward
+ * recomputes them from float32 h); every other input of the backward
+ * (h_K - y, h_k-1 in the gradients) is the float32 value written to h_seq.
+ * Other shapes run cfc_forward and cfc_backward as two launches on `stream`,
+ * after checking the backward's limits, so nothing is enqueued when either
+ * direction would be refused.
+ * Returns a CFC_* status; the same argument rules as the two calls, and no
+ * output (h_seq, scratch, loss) may overlap another. */
+int cfc_forward_backward(const cfc_params_t *params, const float *x, const float *h0,
+                         const float *y, float dt, int B, int K, float *h_seq, float *scratch,
+                         float *loss, int flags, hipStream_t stream);
 
 /* Column sum ("K-loop Parallelization Implementation Plan", Task 1):
  *   out[j] = sum_{b < B} per_batch[b, j]   for j < N, OVERWRITING out.

@@ -26,8 +26,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _lib.declared_symbols()
-    assert set(names) == {"cfc_scratch_row_len", "cfc_forward", "cfc_backward", "reduce_axis0",
-                          "cfc_status_string"}
+    assert set(names) == {"cfc_scratch_row_len", "cfc_forward", "cfc_backward",
+                          "cfc_forward_backward", "reduce_axis0", "cfc_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -92,6 +92,35 @@ def test_backward_validation(lib):
     assert _bwd(lib, _params(), scratch=FAKE + 0x600000 + 64) == C.CFC_ERR_OVERLAP
     # loss overlapping scratch
     assert _bwd(lib, _params(), loss=FAKE + 0x900000 + 4) == C.CFC_ERR_OVERLAP
+
+
+def _fb(lib, p, dt=1.0, B=2, K=3, flags=0, h_seq=FAKE + 0x600000, scratch=FAKE + 0x900000, loss=None,
+        y=FAKE + 0x700000):
+    return lib.cfc_forward_backward(ctypes.byref(p) if p is not None else None, FAKE + 0x400000,
+                                    FAKE + 0x500000, y, dt, B, K, h_seq, scratch, loss, flags, None)
+
+
+def test_forward_backward_validation(lib):
+    """The one-call path applies the rules of both directions before it
+    enqueues anything, including the backward's LDS limit on the shapes that
+    fall back to two launches."""
+    assert _fb(lib, None) == C.CFC_ERR_NULL
+    assert _fb(lib, _params(), y=None) == C.CFC_ERR_NULL
+    assert _fb(lib, _params(), h_seq=None) == C.CFC_ERR_NULL
+    assert _fb(lib, _params(), scratch=None) == C.CFC_ERR_NULL
+    assert _fb(lib, _params(), B=0) == C.CFC_ERR_DIM
+    assert _fb(lib, _params(), K=0) == C.CFC_ERR_DIM
+    assert _fb(lib, _params(), flags=2) == C.CFC_ERR_DIM
+    assert _fb(lib, _params(), dt=float("nan")) == C.CFC_ERR_DT
+    assert _fb(lib, _params(n_hid=257)) == C.CFC_ERR_UNSUPPORTED
+    assert _fb(lib, _params(n_in=128, n_hid=128), K=77) == C.CFC_ERR_UNSUPPORTED
+    assert _fb(lib, _params(n_in=256, n_hid=256), K=38) == C.CFC_ERR_UNSUPPORTED
+    # outputs against inputs, and against each other
+    assert _fb(lib, _params(), h_seq=FAKE + 0x400000 + 8) == C.CFC_ERR_OVERLAP
+    assert _fb(lib, _params(), scratch=FAKE + 0x700000) == C.CFC_ERR_OVERLAP
+    assert _fb(lib, _params(), scratch=FAKE + 0x600000 + 64) == C.CFC_ERR_OVERLAP
+    assert _fb(lib, _params(), loss=FAKE + 0x600000 + 4) == C.CFC_ERR_OVERLAP
+    assert _fb(lib, _params(), loss=FAKE + 0x900000 + 4) == C.CFC_ERR_OVERLAP
 
 
 def test_backward_lds_limit_matches_header(lib):

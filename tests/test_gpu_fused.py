@@ -1,0 +1,158 @@
+"""GPU parity of cfc_forward_backward (forward and backward in one call)
+against the float64 oracle, through the C ABI, at the same per-element
+tolerance as the separate calls; plus its relation to the separate calls:
+h_seq bitwise equal to cfc_forward's, scratch equal to cfc_backward's to
+float32 rounding of the pre-activations (the one-kernel path keeps them in
+float64 instead of recomputing them from the float32 h_seq).
+"""
+import numpy as np
+import pytest
+
+from parity_util import assert_close, host, oracle_threads, say, to_dev
+from oracle import oracle as O
+from cfc_recurrent_cell_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests selected but torch sees no GPU")
+    import cfc_recurrent_cell_amd as C
+    C.load_library()
+    return torch.device("cuda:0")
+
+
+def fused_step(d, h_seq=None, scratch=None, out=None, accumulate=False):
+    import cfc_recurrent_cell_amd as C
+    h_seq, scratch, loss = C.cfc_forward_backward(d["w_in"], d["w_rec"], d["b"], d["w_tau"], d["x"],
+                                                  d["h0"], d["y"], d["dt"], h_seq=h_seq,
+                                                  scratch=scratch, accumulate=accumulate)
+    out = C.reduce_axis0(scratch, out=out)
+    return h_seq, scratch, loss, out
+
+
+def separate_step(d):
+    import cfc_recurrent_cell_amd as C
+    h = C.cfc_forward(d["w_in"], d["w_rec"], d["b"], d["w_tau"], d["x"], d["h0"], d["dt"])
+    s, l = C.cfc_backward(d["w_in"], d["w_rec"], d["b"], d["w_tau"], d["x"], d["h0"], h, d["y"], d["dt"])
+    return h, s, l
+
+
+def _check(inp, what, compare_separate=True):
+    say(f"[fused] {what}: B={inp.x.shape[0]} K={inp.x.shape[1]} n_in={inp.x.shape[2]} "
+        f"H={inp.w_rec.shape[0]} dt={float(inp.dt)}")
+    d = to_dev(inp)
+    h, s, l, o = [host(t) for t in fused_step(d)]
+    ref = O.cfc_step(inp, threads=oracle_threads())
+    assert_close(h, ref["h_seq"], what + " h_seq")
+    assert_close(s, ref["scratch"], what + " scratch")
+    assert_close(l, ref["loss"], what + " loss")
+    assert_close(o, ref["out"], what + " out")
+    if compare_separate:
+        hs, ss, ls = [host(t) for t in separate_step(d)]
+        assert np.array_equal(h.view(np.uint32), hs.view(np.uint32)), what + ": h_seq differs from cfc_forward"
+        assert np.array_equal(l.view(np.uint32), ls.view(np.uint32)), what + ": loss differs from cfc_backward"
+        assert_close(s, ss, what + " scratch vs cfc_backward", rtol=1e-5, atol=1e-6)
+    return d, (h, s, l, o)
+
+
+def test_fused_tiny():
+    _check(W.make_cfc_inputs(W.TINY), W.TINY.name)
+
+
+def test_fused_smoke():
+    _check(W.make_cfc_inputs(W.SMOKE), W.SMOKE.name)
+
+
+def test_fused_train_ten_steps_bitwise():
+    """Training-scale workload through the one-call path: oracle parity, then
+    10 repeats with every output poisoned in between, all bitwise equal."""
+    import torch
+    cfg = W.TRAIN
+    d, first = _check(W.make_cfc_inputs(cfg), cfg.name)
+    N = W.scratch_row_len(cfg.n_in, cfg.n_hid)
+    h_seq = torch.empty((cfg.B, cfg.K, cfg.n_hid), device="cuda")
+    scratch = torch.empty((cfg.B, N), device="cuda")
+    out = torch.empty((N,), device="cuda")
+    for step in range(cfg.steps):
+        for t in (h_seq, scratch, out):
+            t.fill_(float("nan"))
+        got = [host(t) for t in fused_step(d, h_seq=h_seq, scratch=scratch, out=out)]
+        for a, b_, name in zip(got, first, ("h_seq", "scratch", "loss", "out")):
+            assert np.array_equal(a.view(np.uint32), b_.view(np.uint32)), f"step {step} {name} differs"
+
+
+FUSED_SHAPES = [
+    # (B, K, n_in, H, dt, seed): the one-kernel path ...
+    (1, 1, 1, 1, 0.7, 41),
+    (3, 5, 21, 37, 0.9, 42),
+    (2, 9, 5, 3, 1.3, 43),
+    (5, 64, 128, 128, 0.5, 44),    # its K limit at the maximum width
+    (4, 17, 128, 7, 1.1, 45),
+    (6, 4, 64, 100, 0.0, 46),      # dt = 0
+    # ... and the shapes that fall back to two launches
+    (3, 65, 16, 24, 0.6, 47),      # K above the one-kernel limit
+    (5, 7, 130, 129, 0.6, 48),     # wider than 128
+    (2, 6, 256, 256, 1.0, 49),
+]
+
+
+@pytest.mark.parametrize("shape", FUSED_SHAPES, ids=lambda s: "B{}_K{}_n{}_H{}_dt{}".format(*s[:5]))
+def test_fused_shapes(shape):
+    B, K, n_in, H, dt, seed = shape
+    inp = W.make_random_cfc_inputs(B, K, n_in, H, dt, seed)
+    _check(inp, f"fused B{B} K{K} n{n_in} H{H}")
+
+
+def test_fused_b1_rows_bitwise_equal_batched():
+    """Rows are independent: each row run alone (B=1) equals its row of the
+    batched run bitwise."""
+    inp = W.make_random_cfc_inputs(5, 12, 40, 56, 0.8, 50)
+    say("[fused] B=1 vs batched")
+    h, s, l, _ = [host(t) for t in fused_step(to_dev(inp))]
+    for r in range(5):
+        one = W.CfcInputs(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x[r:r + 1], inp.h0[r:r + 1],
+                          inp.y[r:r + 1], inp.dt)
+        h1, s1, l1, o1 = [host(t) for t in fused_step(to_dev(one))]
+        assert np.array_equal(h1[0].view(np.uint32), h[r].view(np.uint32))
+        assert np.array_equal(s1[0].view(np.uint32), s[r].view(np.uint32))
+        assert np.array_equal(l1.view(np.uint32), l[r:r + 1].view(np.uint32))
+        assert np.array_equal(o1.view(np.uint32), s[r].view(np.uint32))   # B=1 reduce is a copy
+
+
+def test_fused_overwrite_and_accumulate():
+    """Overwrite ignores a poisoned scratch; accumulate onto zeros equals
+    overwrite bitwise (same kernel); a second accumulate doubles."""
+    import torch
+    inp = W.make_random_cfc_inputs(4, 10, 24, 40, 0.7, 51)
+    d = to_dev(inp)
+    say("[fused] overwrite / accumulate")
+    _, s_ref, _, _ = fused_step(d)
+    s_ref = s_ref.clone()
+    poisoned = torch.full_like(s_ref, float("nan"))
+    _, s_p, _, _ = fused_step(d, scratch=poisoned)
+    assert torch.equal(s_p.view(torch.int32), s_ref.view(torch.int32))
+    z = torch.zeros_like(s_ref)
+    fused_step(d, scratch=z, accumulate=True)
+    assert torch.equal(z.view(torch.int32), s_ref.view(torch.int32))
+    fused_step(d, scratch=z, accumulate=True)
+    assert_close(host(z), 2.0 * host(s_ref).astype(np.float64), "accumulate twice", rtol=1e-6, atol=1e-7)
+
+
+def test_fused_refusal_enqueues_nothing():
+    """A shape the backward refuses (K = 77 at 128/128) is refused before the
+    forward runs: h_seq keeps its poison."""
+    import torch
+    import cfc_recurrent_cell_amd as C
+    inp = W.make_random_cfc_inputs(2, 77, 128, 128, 0.5, 52)
+    d = to_dev(inp)
+    h_seq = torch.full((2, 77, 128), float("nan"), device="cuda")
+    with pytest.raises(C.CfcError) as e:
+        C.cfc_forward_backward(d["w_in"], d["w_rec"], d["b"], d["w_tau"], d["x"], d["h0"], d["y"],
+                               d["dt"], h_seq=h_seq)
+    assert e.value.code == C.CFC_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.isnan(h_seq).all()
