@@ -29,7 +29,7 @@ METRIC = "CfC fwd+BPTT batch-steps/s (B=256,K=64,H=128); reduce_axis0 HBM GB/s"
 PEAK_F64_TFLOPS = 78.6        # MI355X FP64 vector: 256 CU * 2.4 GHz * 64 FMA/clk * 2
 PEAK_HBM_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "cfc_recurrent_cell_amd", "csrc", "cfc.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_train_B256_K64_H128.json")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def algorithmic_work(B, K, n_in, H):
@@ -58,11 +58,11 @@ def source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, only if
-    it was taken on the current kernel source."""
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary of this
+    workload, only if it was taken on the current kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(PROFILES, f"traffic_{workload}.json")) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
@@ -73,21 +73,40 @@ def measured_traffic(kernel):
 
 
 def cpu_baseline(inp, budget_s=10.0):
+    """The float64 oracle on the host, as it stands: one thread over 32 of the
+    rows, then all available cores (up to 16 threads, rows split between them)
+    over all rows; each leg repeats whole forward+backward+reduce passes for
+    about half the budget.  The all-cores leg is the headline object."""
     from oracle import oracle as O
     B, K = inp.x.shape[0], inp.x.shape[1]
-    rows = max(1, min(B, 32))
-    sub = type(inp)(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x[:rows], inp.h0[:rows], inp.y[:rows], inp.dt)
     O.load_oracle()
-    n, t0 = 0, time.perf_counter()
-    while True:
-        O.cfc_step(sub, threads=1)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": rows * K * n / el, "unit": "batch-steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} x (forward+backward+reduce over {rows} of the {B} rows of the "
-                      f"same workload, K={K}), float64, one thread, {el:.1f} s"}
+
+    def leg(rows, threads, budget):
+        sub = type(inp)(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x[:rows], inp.h0[:rows], inp.y[:rows],
+                        inp.dt)
+        n, t0 = 0, time.perf_counter()
+        while True:
+            O.cfc_step(sub, threads=threads)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                break
+        return rows * K * n / el, n, el
+
+    try:
+        ncores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncores = os.cpu_count() or 1
+    threads = max(1, min(16, ncores))
+    rows1 = max(1, min(B, 32))
+    v1, n1, e1 = leg(rows1, 1, budget_s / 2)
+    vn, nn, en = leg(B, threads, budget_s / 2)
+    return {"value": vn, "unit": "batch-steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nn} x (forward+backward+reduce over all {B} rows of the same workload, K={K}), "
+                      f"float64, rows split over {threads} threads, {en:.1f} s",
+            "single_thread": {"value": v1, "cores": 1,
+                              "sample": f"{n1} x ({rows1} of the {B} rows), one thread, {e1:.1f} s"},
+            "host_cores_available": ncores}
 
 
 def reduce_sweep(torch, C, W, dev, reps=20):
@@ -133,8 +152,12 @@ def main():
                     help="which seeded workload one step runs (the metric is quoted on 'train')")
     ap.add_argument("--reduce-sweep", action="store_true",
                     help="also time reduce_axis0 alone, cache-flushed, over a range of sizes")
-    ap.add_argument("--path", default="fused", choices=["fused", "separate"],
-                    help="fused: one cfc_forward_backward call; separate: cfc_forward + cfc_backward")
+    ap.add_argument("--main-only", action="store_true",
+                    help="time only the selected path in overwrite mode (no other-path or accumulate-mode "
+                         "timing): for profiler runs whose per-kernel averages must match one variant")
+    ap.add_argument("--path", default=None, choices=["fused", "separate"],
+                    help="fused: one cfc_forward_backward call; separate: cfc_forward + cfc_backward "
+                         "(default: fused where that call is one kernel, i.e. n_in, n_hid <= 128 and K <= 64)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the CfC path has no cross-GPU step in this "
@@ -174,6 +197,9 @@ def main():
     loss = torch.empty((B,), device=dev)
     out = torch.empty((N,), device=dev)
 
+    if args.path is None:
+        args.path = "fused" if (n_in <= 128 and H <= 128 and K <= 64) else "separate"
+
     def step_separate(ev=None):
         if ev is not None:
             ev[0].record()
@@ -197,11 +223,22 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    def step_fused_accumulate(ev=None):
+        # the pages' clear-then-accumulate form: explicit zero fill, then += gradient
+        if ev is not None:
+            ev[0].record()
+        scratch.zero_()
+        C.cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt, h_seq=h_seq, scratch=scratch, loss=loss,
+                               accumulate=True)
+        C.reduce_axis0(scratch, out=out)
+        if ev is not None:
+            ev[1].record()
+
     def timed(path):
         """W warm-up steps, then K steps bracketed by a sync on both sides, with
         HIP events around every launch on the stream the launches use."""
-        step = step_fused if path == "fused" else step_separate
-        nev = 3 if path == "fused" else 4
+        step = {"fused": step_fused, "separate": step_separate, "accumulate": step_fused_accumulate}[path]
+        nev = {"fused": 3, "separate": 4, "accumulate": 2}[path]
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
@@ -217,13 +254,19 @@ def main():
         per = lambda a, c: sum(e[a].elapsed_time(e[c]) for e in evs) / args.steps
         if path == "fused":
             km = {"cfc_fb_kernel": per(0, 1), "reduce_axis0_kernel": per(1, 2)}
-        else:
+        elif path == "separate":
             km = {"cfc_fwd_kernel": per(0, 1), "cfc_bwd_kernel": per(1, 2), "reduce_axis0_kernel": per(2, 3)}
-        return ms, km
+        else:
+            km = {}
+        steps_ms = sorted(e[0].elapsed_time(e[nev - 1]) for e in evs)
+        q = lambda f: steps_ms[min(len(steps_ms) - 1, int(f * len(steps_ms)))]
+        return ms, km, {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9)}
 
     other = "separate" if args.path == "fused" else "fused"
-    ms_other, k_other = timed(other)
-    ms_per_step, k_ms = timed(args.path)
+    if not args.main_only:
+        ms_other, k_other, _ = timed(other)
+        ms_acc, _, pct_acc = timed("accumulate")
+    ms_per_step, k_ms, pct = timed(args.path)
     work = algorithmic_work(B, K, n_in, H)
     flops = {"cfc_fwd_kernel": work["fwd_flops"], "cfc_bwd_kernel": work["bwd_flops"],
              "cfc_fb_kernel": work["fb_flops"]}
@@ -238,8 +281,19 @@ def main():
                 "frac": ach / PEAK_F64_TFLOPS}
     roof["kernel"] = dom
     roof["algorithmic_flops_per_launch"] = flops.get(dom)
-    roof["traffic"] = measured_traffic(dom)
+    roof["traffic"] = measured_traffic(cfg.name, dom)
     red_gbps = work["reduce_bytes"] / (k_ms["reduce_axis0_kernel"] * 1e-3) / 1e9
+    # floors of the whole step: algorithmic bytes at 8 TB/s, algorithmic f64
+    # flops at 78.6 TFLOP/s; frac = the larger floor / measured time
+    step_flops = work["fb_flops"] if args.path == "fused" else work["fwd_flops"] + work["bwd_flops"]
+    step_bytes = (work["fb_bytes"] if args.path == "fused" else work["fwd_bytes"] + work["bwd_bytes"]) + \
+        work["reduce_bytes"]
+    hbm_floor_ms = step_bytes / (PEAK_HBM_GBPS * 1e9) * 1e3
+    f64_floor_ms = step_flops / (PEAK_F64_TFLOPS * 1e12) * 1e3
+    floors = {"algorithmic_bytes": step_bytes, "algorithmic_f64_flops": step_flops,
+              "hbm_floor_ms": hbm_floor_ms, "f64_floor_ms": f64_floor_ms,
+              "frac_hbm": hbm_floor_ms / ms_per_step, "frac_f64": f64_floor_ms / ms_per_step,
+              "frac_of_max_floor": max(hbm_floor_ms, f64_floor_ms) / ms_per_step}
 
     value = B * K / (ms_per_step * 1e-3)
     rec = {
@@ -251,9 +305,15 @@ def main():
                    "scratch_N": N, "io_dtype": "f32", "seed": cfg.seed},
         "roofline": roof,
         "path": args.path,
+        "fused_call_is_one_kernel": n_in <= 128 and H <= 128 and K <= 64,
+        "step_ms_percentiles": pct,
+        "step_floors": floors,
         "kernels_ms": k_ms,
-        "other_path": {"path": other, "value": B * K / (ms_other * 1e-3), "ms_per_step": ms_other,
-                       "kernels_ms": k_other},
+        "accumulate_mode": None if args.main_only else {
+            "ms_per_step": ms_acc, "value": B * K / (ms_acc * 1e-3), "step_ms_percentiles": pct_acc,
+            "step": "scratch zero fill + cfc_forward_backward(CFC_ACCUMULATE) + reduce_axis0"},
+        "other_path": None if args.main_only else {
+            "path": other, "value": B * K / (ms_other * 1e-3), "ms_per_step": ms_other, "kernels_ms": k_other},
         "reduce_axis0": {"GB_per_s": red_gbps, "frac_hbm": red_gbps / PEAK_HBM_GBPS,
                          "bytes": work["reduce_bytes"],
                          "note": "scratch of this step (33.8 MB) may be served partly from the MALL"},
