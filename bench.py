@@ -269,10 +269,15 @@ def main():
     ms_per_step, k_ms, pct = timed(args.path)
     work = algorithmic_work(B, K, n_in, H)
     flops = {"cfc_fwd_kernel": work["fwd_flops"], "cfc_bwd_kernel": work["bwd_flops"],
-             "cfc_fb_kernel": work["fb_flops"]}
+             "cfc_fb_kernel": work["fb_flops"], "reduce_axis0_kernel": 0}
+    nbytes = {"cfc_fwd_kernel": work["fwd_bytes"], "cfc_bwd_kernel": work["bwd_bytes"],
+              "cfc_fb_kernel": work["fb_bytes"], "reduce_axis0_kernel": work["reduce_bytes"]}
     dom = max(k_ms, key=k_ms.get)
-    if dom == "reduce_axis0_kernel":
-        ach = work["reduce_bytes"] / (k_ms[dom] * 1e-3) / 1e9
+    # the bound is the roofline the kernel's algorithmic intensity falls under:
+    # below the f64 ridge (78.6 TFLOP/s / 8 TB/s = 9.8 FLOP/B) it is HBM
+    ridge = PEAK_F64_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    if flops[dom] / nbytes[dom] < ridge:
+        ach = nbytes[dom] / (k_ms[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": ach / PEAK_HBM_GBPS}
     else:
@@ -280,7 +285,8 @@ def main():
         roof = {"bound": "alu", "achieved": ach, "peak": PEAK_F64_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_F64_TFLOPS}
     roof["kernel"] = dom
-    roof["algorithmic_flops_per_launch"] = flops.get(dom)
+    roof["algorithmic_flops_per_launch"] = flops[dom]
+    roof["algorithmic_bytes_per_launch"] = nbytes[dom]
     roof["traffic"] = measured_traffic(cfg.name, dom)
     red_gbps = work["reduce_bytes"] / (k_ms["reduce_axis0_kernel"] * 1e-3) / 1e9
     # floors of the whole step: algorithmic bytes at 8 TB/s, algorithmic f64
