@@ -23,7 +23,7 @@
  *   backward  exact reverse-mode gradient of L_b, one "+=" into the per-row
  *             scratch per timestep, in descending k, after the row is zeroed
  *             ("zero once per step, K invocations accumulate": Task 3 kernel
- *             comment and Task 5 Step 3).
+ *             comment and Task 5 Step 3); optionally also dL/dx_k and dL/dh_0.
  *   scratch row layout  [ dW_in (H x n_in, row-major) | dW_rec (H x H) |
  *                         db (H) | dw_tau (H) ]
  *   reduce_axis0  out[j] = sum_b in[b, j], b ascending, overwrite
@@ -109,13 +109,22 @@ int oracle_cfc_forward(int B, int K, int n_in, int H, double dt,
 /* Backward through time for L = sum_b 1/2 |h_K - y_b|^2.
  * Inputs as for the forward plus h_seq [B,K,H] and y [B,H].
  * scratch [B, N] receives each row's parameter gradient (zeroed first, then
- * one += per timestep).  loss [B] (may be NULL) receives L_b. */
-int oracle_cfc_backward(int B, int K, int n_in, int H, double dt,
-                        const double *w_in, const double *w_rec,
-                        const double *bias, const double *w_tau,
-                        const double *x, const double *h0,
-                        const double *h_seq, const double *y,
-                        double *scratch, double *loss)
+ * one += per timestep).  loss [B] (may be NULL) receives L_b.
+ * The gradients with respect to the cell's inputs -- the per-step grad_x and
+ * grad_h_old outputs of the pages' backward ("K-loop Parallelization
+ * Implementation Plan", Task 3 kernel signature, grad_x nullable), carried
+ * through the whole K-loop -- are optional:
+ *   grad_x  [B,K,n_in] (may be NULL): dL/dx_k = W_in^T da_k for every k;
+ *   grad_h0 [B,H]      (may be NULL): dL/dh_0, the delta left after step 0
+ *                      (each step's grad_h_old is the next step's delta, so
+ *                      only step 0's leaves the loop). */
+int oracle_cfc_backward_inputs(int B, int K, int n_in, int H, double dt,
+                               const double *w_in, const double *w_rec,
+                               const double *bias, const double *w_tau,
+                               const double *x, const double *h0,
+                               const double *h_seq, const double *y,
+                               double *scratch, double *loss,
+                               double *grad_x, double *grad_h0)
 {
     if (B < 0 || K < 1 || n_in < 1 || H < 1)
         return -1;
@@ -175,6 +184,16 @@ int oracle_cfc_backward(int B, int K, int n_in, int H, double dt,
                 g_b[i] += da[i];
                 g_wtau[i] += dz[i] * (-a[i] * dt) * sw[i];
             }
+            /* dL/dx_k = W_in^T da */
+            if (grad_x) {
+                double *gx = grad_x + ((size_t)b * K + k) * n_in;
+                for (int j = 0; j < n_in; ++j) {
+                    double t = 0.0;
+                    for (int i = 0; i < H; ++i)
+                        t += w_in[(size_t)i * n_in + j] * da[i];
+                    gx[j] = t;
+                }
+            }
             /* dL/dh_k = delta * g (direct path) + W_rec^T da */
             for (int j = 0; j < H; ++j) {
                 double s = delta[j] * g[j];
@@ -184,10 +203,25 @@ int oracle_cfc_backward(int B, int K, int n_in, int H, double dt,
             }
             memcpy(delta, delta_prev, sizeof(double) * H);
         }
+        /* after step 0, delta is dL/dh_0 */
+        if (grad_h0)
+            memcpy(grad_h0 + (size_t)b * H, delta, sizeof(double) * H);
     }
     free(sp); free(sw); free(a); free(g); free(c); free(hn);
     free(delta); free(delta_prev); free(dz); free(da);
     return 0;
+}
+
+/* The backward without the input gradients. */
+int oracle_cfc_backward(int B, int K, int n_in, int H, double dt,
+                        const double *w_in, const double *w_rec,
+                        const double *bias, const double *w_tau,
+                        const double *x, const double *h0,
+                        const double *h_seq, const double *y,
+                        double *scratch, double *loss)
+{
+    return oracle_cfc_backward_inputs(B, K, n_in, H, dt, w_in, w_rec, bias, w_tau, x, h0,
+                                      h_seq, y, scratch, loss, NULL, NULL);
 }
 
 /* out[j] = sum_{b=0}^{B-1} in[b, j], b ascending; B = 0 gives zeros. */

@@ -42,6 +42,8 @@ def _bind(lib):
     lib.oracle_cfc_forward.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double] + [_dp] * 7
     lib.oracle_cfc_backward.restype = ctypes.c_int
     lib.oracle_cfc_backward.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double] + [_dp] * 10
+    lib.oracle_cfc_backward_inputs.restype = ctypes.c_int
+    lib.oracle_cfc_backward_inputs.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double] + [_dp] * 12
     lib.oracle_reduce_axis0.restype = ctypes.c_int
     lib.oracle_reduce_axis0.argtypes = [ctypes.c_longlong, ctypes.c_longlong, _dp, _dp]
     lib.oracle_reduce_axis0_f32.restype = ctypes.c_int
@@ -126,6 +128,31 @@ def cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, threads: int = 1,
     return scratch, loss
 
 
+def cfc_backward_inputs(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, threads: int = 1, lib=None):
+    """(scratch [B, N], loss [B], grad_x [B, K, n_in], grad_h0 [B, H]), float64:
+    the backward plus the gradients with respect to x and h0."""
+    lib = lib or load_oracle()
+    w_in, w_rec, b, w_tau, x, h0, h_seq, y = map(_d, (w_in, w_rec, b, w_tau, x, h0, h_seq, y))
+    B, K, n_in = x.shape
+    H = w_rec.shape[0]
+    N = scratch_row_len(n_in, H, lib)
+    scratch = np.empty((B, N), dtype=np.float64)
+    loss = np.empty(B, dtype=np.float64)
+    grad_x = np.empty((B, K, n_in), dtype=np.float64)
+    grad_h0 = np.empty((B, H), dtype=np.float64)
+
+    def run(r0, r1):
+        rc = lib.oracle_cfc_backward_inputs(
+            r1 - r0, K, n_in, H, float(dt), _ptr(w_in), _ptr(w_rec), _ptr(b), _ptr(w_tau),
+            _ptr(x, r0 * K * n_in), _ptr(h0, r0 * H), _ptr(h_seq, r0 * K * H), _ptr(y, r0 * H),
+            _ptr(scratch, r0 * N), _ptr(loss, r0), _ptr(grad_x, r0 * K * n_in), _ptr(grad_h0, r0 * H))
+        if rc != 0:
+            raise ValueError("oracle_cfc_backward_inputs rejected its arguments")
+
+    _run_rows(run, B, threads)
+    return scratch, loss, grad_x, grad_h0
+
+
 def reduce_axis0(per_batch, lib=None) -> np.ndarray:
     lib = lib or load_oracle()
     a = _d(per_batch)
@@ -148,17 +175,23 @@ def reduce_axis0_f32(per_batch_f32, lib=None) -> np.ndarray:
 
 
 def cfc_step(inp, threads: int = 1, lib=None, keep_scratch: bool = True,
-             row_block: int = 256):
+             row_block: int = 256, input_grads: bool = False):
     """One whole step over a workload's inputs: forward, backward, reduce.
 
-    Returns dict(h_seq, scratch (or None), loss, out), all float64.  With
-    ``keep_scratch=False`` rows are processed in blocks and only the column
-    sum (still b ascending) is kept, so memory stays O(row_block * N).
+    Returns dict(h_seq, scratch (or None), loss, out), all float64, plus
+    grad_x and grad_h0 with ``input_grads``.  With ``keep_scratch=False`` rows
+    are processed in blocks and only the column sum (still b ascending) is
+    kept, so memory stays O(row_block * N).
     """
     lib = lib or load_oracle()
     h_seq = cfc_forward(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x, inp.h0, inp.dt,
                         threads=threads, lib=lib)
     B = inp.x.shape[0]
+    if input_grads:
+        scratch, loss, gx, gh = cfc_backward_inputs(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x, inp.h0,
+                                                    h_seq, inp.y, inp.dt, threads=threads, lib=lib)
+        out = reduce_axis0(scratch, lib=lib)
+        return dict(h_seq=h_seq, scratch=scratch, loss=loss, out=out, grad_x=gx, grad_h0=gh)
     if keep_scratch:
         scratch, loss = cfc_backward(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x, inp.h0,
                                      h_seq, inp.y, inp.dt, threads=threads, lib=lib)

@@ -12,8 +12,10 @@ What pins what:
     implies, derived by hand;
   * dt = 0: gate exactly 1/2 and dw_tau exactly 0;
   * central finite differences of the oracle's own forward loss: pins the whole
-    backward (every gradient slot) to the forward without sharing a formula;
-  * float64 torch autograd of the forward: a second, independent gradient;
+    backward (every gradient slot, and the gradients with respect to x and
+    h0) to the forward without sharing a formula;
+  * float64 torch autograd of the forward: a second, independent gradient
+    (parameters, x and h0);
   * batch-row independence, scratch clearing, permutation equivariance;
   * reduce_axis0 against exact integer sums and math.fsum.
 """
@@ -72,6 +74,11 @@ def pin_hand_examples(lib) -> None:
         np.testing.assert_allclose(loss[0], _ev(ex["loss"]), rtol=1e-13, err_msg=ex["name"] + " loss")
         np.testing.assert_allclose(scratch, want_s, rtol=1e-12, atol=1e-15, err_msg=ex["name"] + " scratch")
         np.testing.assert_array_equal(out, scratch[0], err_msg=ex["name"] + " reduce at B=1 is a copy")
+        _, _, gx, gh = O.cfc_backward_inputs(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, lib=lib)
+        np.testing.assert_allclose(gx, arr("grad_x", (1, K, n_in)), rtol=1e-12, atol=1e-15,
+                                   err_msg=ex["name"] + " grad_x")
+        np.testing.assert_allclose(gh, arr("grad_h0", (1, H)), rtol=1e-12, atol=1e-15,
+                                   err_msg=ex["name"] + " grad_h0")
 
 
 # ------------------------------------------------------- zero-weight closed form
@@ -107,6 +114,10 @@ def pin_zero_weights(lib, K=6, n_in=3, H=4, dt=0.8, seed=5) -> None:
         np.testing.assert_allclose(scratch[r], want, rtol=1e-12, atol=1e-14)
         np.testing.assert_array_equal(scratch[r, -H:], np.zeros(H))
         np.testing.assert_allclose(loss[r], 0.5 * np.sum((hK - y[r]) ** 2), rtol=1e-14)
+    # input gradients: W_in = 0 gives dL/dx = 0; d_k = d_k+1 / 2 gives dL/dh_0 = 2^-K (h_K - y)
+    _, _, gx, gh = O.cfc_backward_inputs(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, lib=lib)
+    np.testing.assert_array_equal(gx, np.zeros_like(gx))
+    np.testing.assert_array_equal(gh, 2.0 ** -K * (h_seq[:, -1] - y))
 
 
 # ---------------------------------------------------------------------- dt = 0
@@ -156,6 +167,31 @@ def pin_finite_differences(lib, inp: CfcInputs = None, eps=1e-6, rtol=2e-6, atol
     return float(np.max(np.abs(out - fd)))
 
 
+def pin_input_grad_finite_differences(lib, inp: CfcInputs = None, eps=1e-6, rtol=2e-6, atol=1e-9):
+    """d(sum_b L_b)/dx and d(sum_b L_b)/dh0 by central differences of the
+    oracle's own forward, against the backward's grad_x and grad_h0."""
+    if inp is None:
+        inp = make_random_cfc_inputs(2, 4, 3, 5, 0.7, seed=13)
+    w = [np.array(a, dtype=np.float64) for a in (inp.w_in, inp.w_rec, inp.b, inp.w_tau)]
+    x, h0, y, dt = np.array(inp.x, np.float64), np.array(inp.h0, np.float64), inp.y, float(inp.dt)
+    h_seq = O.cfc_forward(*w, x, h0, dt, lib=lib)
+    _, _, gx, gh = O.cfc_backward_inputs(*w, x, h0, h_seq, y, dt, lib=lib)
+
+    def L(xv, hv):
+        return _loss_from_hseq(O.cfc_forward(*w, xv, hv, dt, lib=lib), y)
+
+    for arr, got, is_x in ((x, gx, True), (h0, gh, False)):
+        fd = np.empty(arr.size)
+        for idx in range(arr.size):
+            p = arr.copy()
+            p.ravel()[idx] += eps
+            lp = L(p, h0) if is_x else L(x, p)
+            p.ravel()[idx] -= 2 * eps
+            lm = L(p, h0) if is_x else L(x, p)
+            fd[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(got.ravel(), fd, rtol=rtol, atol=atol)
+
+
 # ---------------------------------------------------------------- torch autograd
 def pin_autograd(lib, inp: CfcInputs = None) -> None:
     """Independent float64 gradient: torch autograd of the forward definition."""
@@ -164,7 +200,7 @@ def pin_autograd(lib, inp: CfcInputs = None) -> None:
         inp = make_random_cfc_inputs(3, 5, 4, 6, 0.7, seed=8)
     t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=False)
     w_in, w_rec, b, w_tau = (t(a).requires_grad_(True) for a in (inp.w_in, inp.w_rec, inp.b, inp.w_tau))
-    x, h0, y = t(inp.x), t(inp.h0), t(inp.y)
+    x, h0, y = t(inp.x).requires_grad_(True), t(inp.h0).requires_grad_(True), t(inp.y)
     dt = float(inp.dt)
     h = h0
     hs = []
@@ -181,6 +217,10 @@ def pin_autograd(lib, inp: CfcInputs = None) -> None:
     np.testing.assert_allclose(h_seq, torch.stack(hs, 1).detach().numpy(), rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(lossv.sum(), loss.item(), rtol=1e-12)
     np.testing.assert_allclose(out, want, rtol=1e-10, atol=1e-13)
+    _, _, gx, gh = O.cfc_backward_inputs(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x, inp.h0, h_seq,
+                                         inp.y, dt, lib=lib)
+    np.testing.assert_allclose(gx, x.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(gh, h0.grad.numpy(), rtol=1e-10, atol=1e-13)
 
 
 # ------------------------------------------------------------ structural pins
@@ -247,6 +287,7 @@ ALL_PINS = {
     "zero_weights": pin_zero_weights,
     "dt_zero": pin_dt_zero,
     "finite_differences": pin_finite_differences,
+    "input_grad_finite_differences": pin_input_grad_finite_differences,
     "autograd": pin_autograd,
     "row_independence": pin_row_independence,
     "scratch_clears": pin_scratch_clears,

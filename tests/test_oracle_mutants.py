@@ -42,6 +42,14 @@ MUTANTS = {
                                "for (long long b = 1; b < B; ++b)\n        for (long long j = 0; j < N; ++j)\n            out[j] += in[b * N + j];"),
     "loss_seed_sign": ("delta[i] = hK[i] - y[(size_t)b * H + i];",
                        "delta[i] = y[(size_t)b * H + i] - hK[i];"),
+    "grad_x_transposed_w_in": ("t += w_in[(size_t)i * n_in + j] * da[i];",
+                               "t += w_in[(size_t)j * n_in + i] * da[i];"),
+    "grad_x_uses_dz": ("t += w_in[(size_t)i * n_in + j] * da[i];",
+                       "t += w_in[(size_t)i * n_in + j] * dz[i];"),
+    "grad_x_steps_reversed": ("double *gx = grad_x + ((size_t)b * K + k) * n_in;",
+                              "double *gx = grad_x + ((size_t)b * K + (K - 1 - k)) * n_in;"),
+    "grad_h0_before_last_step": ("            memcpy(delta, delta_prev, sizeof(double) * H);\n        }\n        /* after step 0",
+                                 "            if (k > 0) memcpy(delta, delta_prev, sizeof(double) * H);\n        }\n        /* after step 0"),
 }
 
 

@@ -29,3 +29,11 @@ def test_autograd_smoke_rows(lib):
     from cfc_recurrent_cell_amd.workloads import SMOKE
     inp = make_cfc_inputs(SMOKE, B=2)
     P.pin_autograd(lib, inp)
+
+
+def test_input_grad_finite_differences_tiny_workload(lib):
+    """dL/dx (512 entries) and dL/dh0 (128) of the tiny workload.  The loss is
+    about 67 here, so each central difference carries a rounding error of about
+    2 * 67 * 2^-53 / (2 * 1e-6) = 7e-9; atol is four times that."""
+    inp = make_cfc_inputs(TINY)
+    P.pin_input_grad_finite_differences(lib, inp, eps=1e-6, rtol=1e-6, atol=3e-8)
