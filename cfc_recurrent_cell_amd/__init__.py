@@ -71,11 +71,29 @@ def cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt: float, h_seq=None, stream=None
     return h_seq
 
 
+def _input_grad_buffers(x, p, grad_x, grad_h0, input_grads):
+    """Allocate (or check) the optional dL/dx [B, K, n_in] and dL/dh0 [B, H]."""
+    import torch
+    B, K, _ = x.shape
+    if input_grads and grad_x is None:
+        grad_x = torch.empty((B, K, p.n_in), dtype=torch.float32, device=x.device)
+    if input_grads and grad_h0 is None:
+        grad_h0 = torch.empty((B, p.n_hid), dtype=torch.float32, device=x.device)
+    if grad_x is not None:
+        _dev_f32(grad_x, "grad_x", (B, K, p.n_in))
+    if grad_h0 is not None:
+        _dev_f32(grad_h0, "grad_h0", (B, p.n_hid))
+    return grad_x, grad_h0
+
+
 def cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, scratch=None,
                  loss=None, accumulate: bool = False, want_loss: bool = True,
-                 stream=None) -> Tuple[object, Optional[object]]:
+                 input_grads: bool = False, grad_x=None, grad_h0=None,
+                 stream=None) -> Tuple[object, ...]:
     """(scratch [B, N], loss [B] or None): per-row parameter gradients of
-    L_b = 1/2 |h_K - y_b|^2 (see include/cfc.h for the row layout)."""
+    L_b = 1/2 |h_K - y_b|^2 (see include/cfc.h for the row layout).  With
+    ``input_grads`` (or explicit ``grad_x`` / ``grad_h0`` buffers) it returns
+    (scratch, loss, grad_x [B, K, n_in], grad_h0 [B, H]) instead."""
     import torch
     lib = load_library()
     p = _params(w_in, w_rec, b, w_tau)
@@ -92,19 +110,26 @@ def cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, scratch=None
         loss = torch.empty((B,), dtype=torch.float32, device=x.device)
     if loss is not None:
         _dev_f32(loss, "loss", (B,))
+    want_inputs = input_grads or grad_x is not None or grad_h0 is not None
+    grad_x, grad_h0 = _input_grad_buffers(x, p, grad_x, grad_h0, input_grads)
     flags = CFC_ACCUMULATE if accumulate else CFC_OVERWRITE
+    ptr = lambda t: t.data_ptr() if t is not None else None
     _check("cfc_backward", lib.cfc_backward(
         ctypes.byref(p), x.data_ptr(), h0.data_ptr(), h_seq.data_ptr(), y.data_ptr(), float(dt),
-        B, K, scratch.data_ptr(), loss.data_ptr() if loss is not None else None, flags,
+        B, K, scratch.data_ptr(), ptr(loss), ptr(grad_x), ptr(grad_h0), flags,
         _stream(x.device, stream)))
+    if want_inputs:
+        return scratch, loss, grad_x, grad_h0
     return scratch, loss
 
 
 def cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt: float, h_seq=None, scratch=None,
                          loss=None, accumulate: bool = False, want_loss: bool = True,
-                         stream=None) -> Tuple[object, object, Optional[object]]:
+                         input_grads: bool = False, grad_x=None, grad_h0=None,
+                         stream=None) -> Tuple[object, ...]:
     """(h_seq [B, K, H], scratch [B, N], loss [B] or None): the forward and the
-    backward of the same inputs in one library call (see include/cfc.h)."""
+    backward of the same inputs in one library call (see include/cfc.h).  With
+    ``input_grads`` (or explicit buffers) grad_x and grad_h0 are appended."""
     import torch
     lib = load_library()
     p = _params(w_in, w_rec, b, w_tau)
@@ -123,11 +148,16 @@ def cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt: float, h_seq=None,
         loss = torch.empty((B,), dtype=torch.float32, device=x.device)
     if loss is not None:
         _dev_f32(loss, "loss", (B,))
+    want_inputs = input_grads or grad_x is not None or grad_h0 is not None
+    grad_x, grad_h0 = _input_grad_buffers(x, p, grad_x, grad_h0, input_grads)
     flags = CFC_ACCUMULATE if accumulate else CFC_OVERWRITE
+    ptr = lambda t: t.data_ptr() if t is not None else None
     _check("cfc_forward_backward", lib.cfc_forward_backward(
         ctypes.byref(p), x.data_ptr(), h0.data_ptr(), y.data_ptr(), float(dt), B, K,
-        h_seq.data_ptr(), scratch.data_ptr(), loss.data_ptr() if loss is not None else None, flags,
+        h_seq.data_ptr(), scratch.data_ptr(), ptr(loss), ptr(grad_x), ptr(grad_h0), flags,
         _stream(x.device, stream)))
+    if want_inputs:
+        return h_seq, scratch, loss, grad_x, grad_h0
     return h_seq, scratch, loss
 
 

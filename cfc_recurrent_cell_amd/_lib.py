@@ -54,9 +54,10 @@ def load_library(path: str = LIB_PATH):
     lib.cfc_forward.restype = i
     lib.cfc_forward.argtypes = [ctypes.POINTER(CfcParams), vp, vp, f, i, i, vp, vp]
     lib.cfc_backward.restype = i
-    lib.cfc_backward.argtypes = [ctypes.POINTER(CfcParams), vp, vp, vp, vp, f, i, i, vp, vp, i, vp]
+    lib.cfc_backward.argtypes = [ctypes.POINTER(CfcParams), vp, vp, vp, vp, f, i, i, vp, vp, vp, vp, i, vp]
     lib.cfc_forward_backward.restype = i
-    lib.cfc_forward_backward.argtypes = [ctypes.POINTER(CfcParams), vp, vp, vp, f, i, i, vp, vp, vp, i, vp]
+    lib.cfc_forward_backward.argtypes = [ctypes.POINTER(CfcParams), vp, vp, vp, f, i, i, vp, vp, vp, vp, vp,
+                                         i, vp]
     lib.reduce_axis0.restype = i
     lib.reduce_axis0.argtypes = [vp, ll, ll, vp, vp]
     lib.cfc_status_string.restype = ctypes.c_char_p

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_kernel(
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
     const float* __restrict__ y, double dt, int K, int n_in, int H, float* __restrict__ scratch,
-    float* __restrict__ loss, int accumulate) {
+    float* __restrict__ loss, float* __restrict__ grad_x, float* __restrict__ grad_h0, int accumulate) {
     extern __shared__ __align__(16) unsigned char smem[];
     double* DA = reinterpret_cast<double*>(smem);
     double* delta = DA + (size_t)K * H;
@@ -174,6 +174,18 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_kernel(
     if (i < H && sub == 0) {
         store_grad(rrec + (long long)H * H + i, gb, accumulate);
         store_grad(rrec + (long long)H * H + H + i, gwt, accumulate);
+    }
+    // input gradients: dL/dh_0 is the delta left after step 0; dL/dx_k = W_in^T da_k
+    if (grad_h0)
+        for (int u = t; u < H; u += kThreads) grad_h0[b * H + u] = (float)delta[cur * H + u];
+    if (grad_x) {
+        float* gx = grad_x + b * K * (long long)n_in;
+        for (int e = t; e < K * n_in; e += kThreads) {
+            const int k = e / n_in, j = e - k * n_in;
+            double s = 0.0;
+            for (int r = 0; r < H; ++r) s = fma(DA[k * H + r], (double)w_in[(long long)r * n_in + j], s);
+            gx[e] = (float)s;
+        }
     }
 }
 
@@ -498,12 +510,16 @@ __device__ __forceinline__ void store_grad_f(float* p, double v, int accumulate)
 // softplus(w_tau) and sigmoid(w_tau), and delta is h_K - y of this lane's unit o
 // (computed from the float32 h_K).  Seeds the row's loss, runs the reverse
 // chain (AD[k] becomes dL/da_k), forms G = DA^T [X | H_prev] on the matrix
-// cores and writes the row [dW_in | dW_rec | db | dw_tau].
+// cores and writes the row [dW_in | dW_rec | db | dw_tau].  Optionally also
+// the input gradients of the row: gh0_row [H] = dL/dh_0 (the chain runs its
+// W_rec^T step once more, at k = 0) and gx_row [K][n_in] = DA W_in (a third
+// product on the matrix cores).
 __device__ __forceinline__ void small_reverse_and_grads(
-    const float* __restrict__ w_rec, double dt, int K, int n_in, int H, double delta, double* AD,
-    const double* spv, const double* swv, double* red, const float* zs, float* gst,
-    float* __restrict__ row, float* __restrict__ loss_b, int accumulate, int lane, int wave, int jb,
-    int ib, int o, bool gate_lane) {
+    const float* __restrict__ w_in, const float* __restrict__ w_rec, double dt, int K, int n_in, int H,
+    double delta, double* AD, const double* spv, const double* swv, double* red, const float* zs,
+    float* gst, float* __restrict__ row, float* __restrict__ loss_b, float* __restrict__ gx_row,
+    float* __restrict__ gh0_row, int accumulate, int lane, int wave, int jb, int ib, int o,
+    bool gate_lane) {
     constexpr int HP = kSmall, NP = kSmall, ZW = kSmallZW, ZS = kSmallZS;
     constexpr int KP = kSmallBwdMaxK;
     // ---- W_rec^T slice into registers: wt[r][c] = W_rec[16jb + c][4ib + r]
@@ -547,7 +563,7 @@ __device__ __forceinline__ void small_reverse_and_grads(
         gwt += dz * (-a * dt) * sw_o;
         if (!gate_lane) AD[k * HP + o] = da;
         __syncthreads();
-        if (k == 0) break;
+        if (k == 0 && !gh0_row) break;
         const double* dak = AD + k * HP + 16 * jb;
         double dj[16];
 #pragma unroll
@@ -569,6 +585,7 @@ __device__ __forceinline__ void small_reverse_and_grads(
         for (int r = 0; r < 4; ++r) p[r] = pe[r] + po[r];
         delta = fma(delta, g, reduce_scatter8(p, jb));
     }
+    if (gh0_row && !gate_lane && o < H) gh0_row[o] = (float)delta;  // dL/dh_0
 
     // ---- weight gradients on the matrix cores: G = DA^T [X | H_prev]
     float* rrec = row + (long long)H * n_in;
@@ -663,6 +680,37 @@ __device__ __forceinline__ void small_reverse_and_grads(
         store_grad_f(rrec + (long long)H * H + o, gb, accumulate);
         store_grad_f(rrec + (long long)H * H + H + o, gwt, accumulate);
     }
+
+    // ---- input gradient GX = DA W_in on the matrix cores: wave w owns the
+    // column tiles jt = 2w, 2w+1 of n_in for all four 16-step tiles; chunk c
+    // contracts i = 4c + lane/16 (A = DA[16kt + lane%16][i] from LDS,
+    // B = W_in[i][16jt + lane%16] from L2)
+    if (gx_row) {
+        const int m = lane & 15, q = lane >> 4;
+#pragma unroll 1
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = (2 * wave + jj) * 16 + m;
+            dbl4 acc[KP / 16];
+#pragma unroll
+            for (int kt = 0; kt < KP / 16; ++kt) acc[kt] = dbl4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+            for (int c = 0; c < HP / 4; ++c) {
+                const int i = 4 * c + q;
+                const double w = (i < H && j < n_in) ? (double)w_in[(long long)i * n_in + j] : 0.0;
+#pragma unroll
+                for (int kt = 0; kt < KP / 16; ++kt) acc[kt] = mfma_f64(AD[(kt * 16 + m) * HP + i], w, acc[kt]);
+            }
+            if (j < n_in) {
+#pragma unroll
+                for (int kt = 0; kt < KP / 16; ++kt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int k = kt * 16 + q + 4 * v;
+                        if (k < K) gx_row[(long long)k * n_in + j] = (float)acc[kt][v];
+                    }
+            }
+        }
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
@@ -670,7 +718,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
     const float* __restrict__ y, double dt, int K, int n_in, int H, float* __restrict__ scratch,
-    float* __restrict__ loss, int accumulate) {
+    float* __restrict__ loss, float* __restrict__ grad_x, float* __restrict__ grad_h0, int accumulate) {
     constexpr int HP = kSmall, NP = kSmall, ZW = kSmallZW, ZS = kSmallZS;
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int KP = kSmallBwdMaxK;
@@ -753,8 +801,9 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
 
     const double delta =
         o < H ? (double)h_seq[(b * K + K - 1) * (long long)H + o] - (double)y[b * H + o] : 0.0;
-    small_reverse_and_grads(w_rec, dt, K, n_in, H, delta, AD, spv, swv, red, zs, gst, scratch + b * N,
-                            loss ? loss + b : nullptr, accumulate, lane, wave, jb, ib, o, gate_lane);
+    small_reverse_and_grads(w_in, w_rec, dt, K, n_in, H, delta, AD, spv, swv, red, zs, gst, scratch + b * N,
+                            loss ? loss + b : nullptr, grad_x ? grad_x + b * K * (long long)n_in : nullptr,
+                            grad_h0 ? grad_h0 + b * H : nullptr, accumulate, lane, wave, jb, ib, o, gate_lane);
 }
 
 // Forward and backward of one row in one workgroup (n_in, n_hid <= 128,
@@ -770,7 +819,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ y, double dt,
     int K, int n_in, int H, float* __restrict__ h_seq, float* __restrict__ scratch,
-    float* __restrict__ loss, int accumulate) {
+    float* __restrict__ loss, float* __restrict__ grad_x, float* __restrict__ grad_h0, int accumulate) {
     constexpr int HP = kSmall, NP = kSmall, ZS = kSmallZS, KP = kSmallBwdMaxK;
     extern __shared__ __align__(16) unsigned char smem[];
     double* AD = reinterpret_cast<double*>(smem);  // [KP][HP]: W_in x_k + b, then a_k, then dL/da_k
@@ -892,8 +941,9 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
 
     // ---- backward from the float32 h_K, as the separate backward sees it
     const double delta = o < H ? (double)(float)hprev - (double)y[b * H + o] : 0.0;
-    small_reverse_and_grads(w_rec, dt, K, n_in, H, delta, AD, spv, swv, red, zs, gst, scratch + b * N,
-                            loss ? loss + b : nullptr, accumulate, lane, wave, jb, ib, o, gate_lane);
+    small_reverse_and_grads(w_in, w_rec, dt, K, n_in, H, delta, AD, spv, swv, red, zs, gst, scratch + b * N,
+                            loss ? loss + b : nullptr, grad_x ? grad_x + b * K * (long long)n_in : nullptr,
+                            grad_h0 ? grad_h0 + b * H : nullptr, accumulate, lane, wave, jb, ib, o, gate_lane);
 }
 
 // =====================================================================
@@ -1122,7 +1172,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
     const float* __restrict__ y, double dt, int B, int K, int n_in, int H, float* __restrict__ scratch,
-    float* __restrict__ loss) {
+    float* __restrict__ loss, float* __restrict__ grad_x, float* __restrict__ grad_h0) {
     extern __shared__ __align__(16) unsigned char smem[];
     float* zx = reinterpret_cast<float*>(smem);                             // [256][16] x_k
     double* zh = reinterpret_cast<double*>(smem + 4 * kLarge * kLR);        // [256][16] h_k
@@ -1221,32 +1271,71 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                 q[1] = (unsigned)(u >> 32);
             }
         }
-        if (k == 0) break;
-        fetch_step(k - 1);
-        // delta_k = delta_k+1 * g + W_rec^T dL/da: chunk ic of k-slot s
-        // contracts unit i = 64*s + ic; the four tiles' operands
-        // W_rec[i][lunit(wave, 0..3, lane%16)] are one float4
-        dbl4 acc2[4];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc2[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
+        if (k > 0) fetch_step(k - 1);
         const int jw = 64 * wave + 4 * (lane & 15);
+        if (k > 0 || grad_h0) {
+            // delta_k = delta_k+1 * g + W_rec^T dL/da: chunk ic of k-slot s
+            // contracts unit i = 64*s + ic; the four tiles' operands
+            // W_rec[i][lunit(wave, 0..3, lane%16)] are one float4
+            dbl4 acc2[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) acc2[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll 4
-        for (int ic = 0; ic < 64; ++ic) {
-            const int i = 64 * s + ic;
-            const double bz = dab[zidx(i, r)];
-            float4 w4;
-            if constexpr (FULL) w4 = *reinterpret_cast<const float4*>(w_rec + (long long)i * kLarge + jw);
-            else w4 = load4_masked(w_rec + (long long)min(i, H - 1) * H, jw, H, i < H);
-            acc2[0] = mfma_f64((double)w4.x, bz, acc2[0]);
-            acc2[1] = mfma_f64((double)w4.y, bz, acc2[1]);
-            acc2[2] = mfma_f64((double)w4.z, bz, acc2[2]);
-            acc2[3] = mfma_f64((double)w4.w, bz, acc2[3]);
+            for (int ic = 0; ic < 64; ++ic) {
+                const int i = 64 * s + ic;
+                const double bz = dab[zidx(i, r)];
+                float4 w4;
+                if constexpr (FULL) w4 = *reinterpret_cast<const float4*>(w_rec + (long long)i * kLarge + jw);
+                else w4 = load4_masked(w_rec + (long long)min(i, H - 1) * H, jw, H, i < H);
+                acc2[0] = mfma_f64((double)w4.x, bz, acc2[0]);
+                acc2[1] = mfma_f64((double)w4.y, bz, acc2[1]);
+                acc2[2] = mfma_f64((double)w4.z, bz, acc2[2]);
+                acc2[3] = mfma_f64((double)w4.w, bz, acc2[3]);
+            }
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    delta[tb][v] = fma(delta[tb][v], gk[tb][v], acc2[tb][v]);
         }
+        if (grad_x) {
+            // dL/dx_k = W_in^T dL/da, the same product with W_in's rows; the
+            // lane's elements are column lunit(wave, tb, s + 4v) of row r
+            dbl4 acc3[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) acc3[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+            for (int ic = 0; ic < 64; ++ic) {
+                const int i = 64 * s + ic;
+                const double bz = dab[zidx(i, r)];
+                float4 w4;
+                if constexpr (FULL) w4 = *reinterpret_cast<const float4*>(w_in + (long long)i * kLarge + jw);
+                else w4 = load4_masked(w_in + (long long)min(i, H - 1) * n_in, jw, n_in, i < H);
+                acc3[0] = mfma_f64((double)w4.x, bz, acc3[0]);
+                acc3[1] = mfma_f64((double)w4.y, bz, acc3[1]);
+                acc3[2] = mfma_f64((double)w4.z, bz, acc3[2]);
+                acc3[3] = mfma_f64((double)w4.w, bz, acc3[3]);
+            }
+            if (row_ok) {
+                float* gx = grad_x + (b_own * K + k) * (long long)n_in;
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int j = lunit(wave, tb, s + 4 * v);
+                        if (j < n_in) gx[j] = (float)acc3[tb][v];
+                    }
+            }
+        }
+    }
+    if (grad_h0 && row_ok) {  // after step 0, delta is dL/dh_0
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                delta[tb][v] = fma(delta[tb][v], gk[tb][v], acc2[tb][v]);
+            for (int v = 0; v < 4; ++v) {
+                const int j = lunit(wave, tb, s + 4 * v);
+                if (j < H) grad_h0[b_own * H + j] = (float)delta[tb][v];
+            }
     }
 
     // ---- per row: G = DA^T [X | H_prev] over the K steps, then db and dw_tau
@@ -1437,6 +1526,16 @@ inline Range span(const void* p, long long elems) {
     return Range{lo, lo + (uintptr_t)elems * sizeof(float)};
 }
 inline bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+// No output range overlaps an input range or another output range.
+inline bool outputs_disjoint(const Range* outs, int n_out, const Range* ins, int n_in) {
+    for (int o = 0; o < n_out; ++o) {
+        for (int i = 0; i < n_in; ++i)
+            if (overlap(outs[o], ins[i])) return false;
+        for (int p = o + 1; p < n_out; ++p)
+            if (overlap(outs[o], outs[p])) return false;
+    }
+    return true;
+}
 
 // Checked a*b for non-negative operands; false on overflow of the byte count.
 inline bool mul_ok(long long a, long long b, long long* r) {
@@ -1544,7 +1643,8 @@ extern "C" int cfc_forward(const cfc_params_t* params, const float* x, const flo
 
 extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const float* h0,
                             const float* h_seq, const float* y, float dt, int B, int K,
-                            float* scratch, float* loss, int flags, hipStream_t stream) {
+                            float* scratch, float* loss, float* grad_x, float* grad_h0, int flags,
+                            hipStream_t stream) {
     int rc = check_params(params);
     if (rc) return rc;
     if (!x || !h0 || !h_seq || !y || !scratch) return CFC_ERR_NULL;
@@ -1562,19 +1662,17 @@ extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const fl
                        flags == CFC_OVERWRITE;
     const size_t lds = small ? small_bwd_lds_bytes() : large ? large_bwd_lds_bytes() : bwd_lds_bytes(K, n_in, H);
     if (lds > kLdsBytes) return CFC_ERR_UNSUPPORTED;
-    const Range outs[] = {span(scratch, nsc), span(loss, loss ? B : 0)};
+    const Range outs[] = {span(scratch, nsc), span(loss, loss ? B : 0), span(grad_x, grad_x ? nx : 0),
+                          span(grad_h0, grad_h0 ? (long long)B * H : 0)};
     const Range ins[] = {span(x, nx), span(h0, (long long)B * H), span(h_seq, ns), span(y, (long long)B * H),
                          span(params->w_in, (long long)H * n_in), span(params->w_rec, (long long)H * H),
                          span(params->b, H), span(params->w_tau, H)};
-    for (const Range& o : outs)
-        for (const Range& r : ins)
-            if (overlap(o, r)) return CFC_ERR_OVERLAP;
-    if (overlap(outs[0], outs[1])) return CFC_ERR_OVERLAP;
+    if (!outputs_disjoint(outs, 4, ins, 8)) return CFC_ERR_OVERLAP;
     set_kernel_attributes();
     if (small) {
         hipLaunchKernelGGL(cfc_bwd_small_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
                            params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, K,
-                           n_in, H, scratch, loss, flags == CFC_ACCUMULATE ? 1 : 0);
+                           n_in, H, scratch, loss, grad_x, grad_h0, flags == CFC_ACCUMULATE ? 1 : 0);
         return launch_status();
     }
     if (large) {
@@ -1582,22 +1680,23 @@ extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const fl
         if (large_full(params))
             hipLaunchKernelGGL(cfc_bwd_large_kernel<true>, dim3((unsigned)groups), dim3(kThreads), lds, stream,
                                params->w_in, params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt,
-                               B, K, n_in, H, scratch, loss);
+                               B, K, n_in, H, scratch, loss, grad_x, grad_h0);
         else
             hipLaunchKernelGGL(cfc_bwd_large_kernel<false>, dim3((unsigned)groups), dim3(kThreads), lds, stream,
                                params->w_in, params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt,
-                               B, K, n_in, H, scratch, loss);
+                               B, K, n_in, H, scratch, loss, grad_x, grad_h0);
         return launch_status();
     }
     hipLaunchKernelGGL(cfc_bwd_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
                        params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, K, n_in,
-                       H, scratch, loss, flags == CFC_ACCUMULATE ? 1 : 0);
+                       H, scratch, loss, grad_x, grad_h0, flags == CFC_ACCUMULATE ? 1 : 0);
     return launch_status();
 }
 
 extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, const float* h0,
                                     const float* y, float dt, int B, int K, float* h_seq, float* scratch,
-                                    float* loss, int flags, hipStream_t stream) {
+                                    float* loss, float* grad_x, float* grad_h0, int flags,
+                                    hipStream_t stream) {
     int rc = check_params(params);
     if (rc) return rc;
     if (!x || !h0 || !y || !h_seq || !scratch) return CFC_ERR_NULL;
@@ -1610,20 +1709,17 @@ extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, 
     if (N < 0 || !mul_ok((long long)B * K, n_in, &nx) || !mul_ok((long long)B * K, H, &ns) ||
         !mul_ok((long long)B, N, &nsc))
         return CFC_ERR_DIM;
-    const Range outs[] = {span(h_seq, ns), span(scratch, nsc), span(loss, loss ? B : 0)};
+    const Range outs[] = {span(h_seq, ns), span(scratch, nsc), span(loss, loss ? B : 0),
+                          span(grad_x, grad_x ? nx : 0), span(grad_h0, grad_h0 ? (long long)B * H : 0)};
     const Range ins[] = {span(x, nx), span(h0, (long long)B * H), span(y, (long long)B * H),
                          span(params->w_in, (long long)H * n_in), span(params->w_rec, (long long)H * H),
                          span(params->b, H), span(params->w_tau, H)};
-    for (const Range& o : outs)
-        for (const Range& r : ins)
-            if (overlap(o, r)) return CFC_ERR_OVERLAP;
-    if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2]))
-        return CFC_ERR_OVERLAP;
+    if (!outputs_disjoint(outs, 5, ins, 7)) return CFC_ERR_OVERLAP;
     if (n_in <= kSmall && H <= kSmall && K <= kSmallBwdMaxK) {
         set_kernel_attributes();
         hipLaunchKernelGGL(cfc_fb_small_kernel, dim3(B), dim3(kThreads), small_fb_lds_bytes(), stream,
                            params->w_in, params->w_rec, params->b, params->w_tau, x, h0, y, (double)dt, K,
-                           n_in, H, h_seq, scratch, loss, flags == CFC_ACCUMULATE ? 1 : 0);
+                           n_in, H, h_seq, scratch, loss, grad_x, grad_h0, flags == CFC_ACCUMULATE ? 1 : 0);
         return launch_status();
     }
     // other shapes: the two directions as separate launches on the same stream;
@@ -1634,7 +1730,7 @@ extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, 
     if (lds > kLdsBytes) return CFC_ERR_UNSUPPORTED;
     rc = cfc_forward(params, x, h0, dt, B, K, h_seq, stream);
     if (rc) return rc;
-    return cfc_backward(params, x, h0, h_seq, y, dt, B, K, scratch, loss, flags, stream);
+    return cfc_backward(params, x, h0, h_seq, y, dt, B, K, scratch, loss, grad_x, grad_h0, flags, stream);
 }
 
 extern "C" int reduce_axis0(const float* per_batch, long long B, long long N, float* out,

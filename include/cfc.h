@@ -119,15 +119,25 @@ int cfc_forward(const cfc_params_t *params, const float *x, const float *h0, flo
  *            flags = CFC_ACCUMULATE: each row is read and this call's gradient
  *            added (float64 add, one float32 rounding).
  *   loss     [B] OUTPUT or NULL: L_b per row
+ *   grad_x   [B, K, n_in] OUTPUT or NULL: dL/dx_k = W_in^T dL/da_k for every
+ *            step (overwritten whatever the flags)
+ *   grad_h0  [B, n_hid] OUTPUT or NULL: dL/dh_0, the gradient carried past
+ *            step 0 (overwritten whatever the flags)
+ *            These two are the pages' per-step grad_x and grad_h_old outputs
+ *            (Task 3 kernel signature: overwrite, grad_x nullable) over the
+ *            whole K-loop: each step's grad_h_old is the next step's carry,
+ *            so only step 0's leaves the loop.  Requesting them does not
+ *            change the other outputs.
  * Returns a CFC_* status; CFC_ERR_UNSUPPORTED if the LDS bound above fails. */
 int cfc_backward(const cfc_params_t *params, const float *x, const float *h0,
                  const float *h_seq, const float *y, float dt, int B, int K,
-                 float *scratch, float *loss, int flags, hipStream_t stream);
+                 float *scratch, float *loss, float *grad_x, float *grad_h0, int flags,
+                 hipStream_t stream);
 
 /* cfc_forward followed by cfc_backward on the same inputs, in one call
  * ("K-loop Parallelization Implementation Plan", Tasks 2 and 3 back to back):
  *   params, x, h0, dt, B, K   as for cfc_forward
- *   y, scratch, loss, flags   as for cfc_backward
+ *   y, scratch, loss, grad_x, grad_h0, flags   as for cfc_backward
  *   h_seq    [B, K, n_hid] OUTPUT, as cfc_forward writes it
  * For n_in, n_hid <= 128 and K <= 64 this is ONE kernel per row that keeps the
  * forward's float64 pre-activations and the staged [x_k | h_k-1] on chip for
@@ -139,10 +149,11 @@ int cfc_backward(const cfc_params_t *params, const float *x, const float *h0,
  * after checking the backward's limits, so nothing is enqueued when either
  * direction would be refused.
  * Returns a CFC_* status; the same argument rules as the two calls, and no
- * output (h_seq, scratch, loss) may overlap another. */
+ * output (h_seq, scratch, loss, grad_x, grad_h0) may overlap another. */
 int cfc_forward_backward(const cfc_params_t *params, const float *x, const float *h0,
                          const float *y, float dt, int B, int K, float *h_seq, float *scratch,
-                         float *loss, int flags, hipStream_t stream);
+                         float *loss, float *grad_x, float *grad_h0, int flags,
+                         hipStream_t stream);
 
 /* Column sum ("K-loop Parallelization Implementation Plan", Task 1):
  *   out[j] = sum_{b < B} per_batch[b, j]   for j < N, OVERWRITING out.

@@ -51,10 +51,11 @@ def _fwd(lib, p, x=FAKE + 0x400000, h0=FAKE + 0x500000, dt=1.0, B=2, K=3, h_seq=
     return lib.cfc_forward(ctypes.byref(p) if p is not None else None, x, h0, dt, B, K, h_seq, None)
 
 
-def _bwd(lib, p, dt=1.0, B=2, K=3, flags=0, scratch=FAKE + 0x900000, loss=None, h_seq=FAKE + 0x600000):
+def _bwd(lib, p, dt=1.0, B=2, K=3, flags=0, scratch=FAKE + 0x900000, loss=None, h_seq=FAKE + 0x600000,
+         grad_x=None, grad_h0=None):
     return lib.cfc_backward(ctypes.byref(p) if p is not None else None, FAKE + 0x400000,
                             FAKE + 0x500000, h_seq, FAKE + 0x700000, dt, B, K, scratch, loss,
-                            flags, None)
+                            grad_x, grad_h0, flags, None)
 
 
 def test_forward_validation(lib):
@@ -92,12 +93,18 @@ def test_backward_validation(lib):
     assert _bwd(lib, _params(), scratch=FAKE + 0x600000 + 64) == C.CFC_ERR_OVERLAP
     # loss overlapping scratch
     assert _bwd(lib, _params(), loss=FAKE + 0x900000 + 4) == C.CFC_ERR_OVERLAP
+    # input gradients: grad_x [2,3,8] over x, over scratch; grad_h0 [2,16] over y, over grad_x
+    assert _bwd(lib, _params(), grad_x=FAKE + 0x400000) == C.CFC_ERR_OVERLAP
+    assert _bwd(lib, _params(), grad_x=FAKE + 0x900000 + 8) == C.CFC_ERR_OVERLAP
+    assert _bwd(lib, _params(), grad_h0=FAKE + 0x700000 + 4) == C.CFC_ERR_OVERLAP
+    assert _bwd(lib, _params(), grad_x=FAKE + 0xA00000, grad_h0=FAKE + 0xA00000 + 16) == C.CFC_ERR_OVERLAP
 
 
 def _fb(lib, p, dt=1.0, B=2, K=3, flags=0, h_seq=FAKE + 0x600000, scratch=FAKE + 0x900000, loss=None,
-        y=FAKE + 0x700000):
+        y=FAKE + 0x700000, grad_x=None, grad_h0=None):
     return lib.cfc_forward_backward(ctypes.byref(p) if p is not None else None, FAKE + 0x400000,
-                                    FAKE + 0x500000, y, dt, B, K, h_seq, scratch, loss, flags, None)
+                                    FAKE + 0x500000, y, dt, B, K, h_seq, scratch, loss, grad_x, grad_h0,
+                                    flags, None)
 
 
 def test_forward_backward_validation(lib):
@@ -121,6 +128,8 @@ def test_forward_backward_validation(lib):
     assert _fb(lib, _params(), scratch=FAKE + 0x600000 + 64) == C.CFC_ERR_OVERLAP
     assert _fb(lib, _params(), loss=FAKE + 0x600000 + 4) == C.CFC_ERR_OVERLAP
     assert _fb(lib, _params(), loss=FAKE + 0x900000 + 4) == C.CFC_ERR_OVERLAP
+    assert _fb(lib, _params(), grad_x=FAKE + 0x600000 + 4) == C.CFC_ERR_OVERLAP
+    assert _fb(lib, _params(), grad_h0=FAKE + 0x500000) == C.CFC_ERR_OVERLAP
 
 
 def test_backward_lds_limit_matches_header(lib):
