@@ -155,6 +155,8 @@ def main():
     ap.add_argument("--main-only", action="store_true",
                     help="time only the selected path in overwrite mode (no other-path or accumulate-mode "
                          "timing): for profiler runs whose per-kernel averages must match one variant")
+    ap.add_argument("--input-grads", action="store_true",
+                    help="the timed step also writes grad_x [B,K,n_in] and grad_h0 [B,H]")
     ap.add_argument("--path", default=None, choices=["fused", "separate"],
                     help="fused: one cfc_forward_backward call; separate: cfc_forward + cfc_backward "
                          "(default: fused where that call is one kernel, i.e. n_in, n_hid <= 128 and K <= 64)")
@@ -223,6 +225,35 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    grad_x = torch.empty((B, K, n_in), device=dev)
+    grad_h0 = torch.empty((B, H), device=dev)
+
+    def step_fused_ig(ev=None):
+        # the one-call path with the input gradients (dL/dx, dL/dh_0) requested too
+        if ev is not None:
+            ev[0].record()
+        C.cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt, h_seq=h_seq, scratch=scratch, loss=loss,
+                               grad_x=grad_x, grad_h0=grad_h0)
+        if ev is not None:
+            ev[1].record()
+        C.reduce_axis0(scratch, out=out)
+        if ev is not None:
+            ev[2].record()
+
+    def step_separate_ig(ev=None):
+        if ev is not None:
+            ev[0].record()
+        C.cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, h_seq=h_seq)
+        if ev is not None:
+            ev[1].record()
+        C.cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, scratch=scratch, loss=loss,
+                       grad_x=grad_x, grad_h0=grad_h0)
+        if ev is not None:
+            ev[2].record()
+        C.reduce_axis0(scratch, out=out)
+        if ev is not None:
+            ev[3].record()
+
     def step_fused_accumulate(ev=None):
         # the pages' clear-then-accumulate form: explicit zero fill, then += gradient
         if ev is not None:
@@ -237,8 +268,9 @@ def main():
     def timed(path):
         """W warm-up steps, then K steps bracketed by a sync on both sides, with
         HIP events around every launch on the stream the launches use."""
-        step = {"fused": step_fused, "separate": step_separate, "accumulate": step_fused_accumulate}[path]
-        nev = {"fused": 3, "separate": 4, "accumulate": 2}[path]
+        step = {"fused": step_fused, "separate": step_separate, "accumulate": step_fused_accumulate,
+                "fused_ig": step_fused_ig, "separate_ig": step_separate_ig}[path]
+        nev = {"fused": 3, "separate": 4, "accumulate": 2, "fused_ig": 3, "separate_ig": 4}[path]
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
@@ -252,9 +284,9 @@ def main():
         torch.cuda.synchronize()
         ms = t_start.elapsed_time(t_end) / args.steps
         per = lambda a, c: sum(e[a].elapsed_time(e[c]) for e in evs) / args.steps
-        if path == "fused":
+        if path in ("fused", "fused_ig"):
             km = {"cfc_fb_kernel": per(0, 1), "reduce_axis0_kernel": per(1, 2)}
-        elif path == "separate":
+        elif path in ("separate", "separate_ig"):
             km = {"cfc_fwd_kernel": per(0, 1), "cfc_bwd_kernel": per(1, 2), "reduce_axis0_kernel": per(2, 3)}
         else:
             km = {}
@@ -266,12 +298,17 @@ def main():
     if not args.main_only:
         ms_other, k_other, _ = timed(other)
         ms_acc, _, pct_acc = timed("accumulate")
-    ms_per_step, k_ms, pct = timed(args.path)
+        ms_ig, k_ig, pct_ig = timed(args.path + "_ig")
+    ms_per_step, k_ms, pct = timed(args.path + ("_ig" if args.input_grads else ""))
     work = algorithmic_work(B, K, n_in, H)
     flops = {"cfc_fwd_kernel": work["fwd_flops"], "cfc_bwd_kernel": work["bwd_flops"],
              "cfc_fb_kernel": work["fb_flops"], "reduce_axis0_kernel": 0}
     nbytes = {"cfc_fwd_kernel": work["fwd_bytes"], "cfc_bwd_kernel": work["bwd_bytes"],
               "cfc_fb_kernel": work["fb_bytes"], "reduce_axis0_kernel": work["reduce_bytes"]}
+    if args.input_grads:   # W_in^T dL/da per row-step, one more W_rec^T step per row; grad_x, grad_h0 out
+        for kname in ("cfc_bwd_kernel", "cfc_fb_kernel"):
+            flops[kname] += B * K * 2 * H * n_in + B * 2 * H * H
+            nbytes[kname] += 4 * (B * K * n_in + B * H)
     dom = max(k_ms, key=k_ms.get)
     # the bound is the roofline the kernel's algorithmic intensity falls under:
     # below the f64 ridge (78.6 TFLOP/s / 8 TB/s = 9.8 FLOP/B) it is HBM
@@ -287,13 +324,16 @@ def main():
     roof["kernel"] = dom
     roof["algorithmic_flops_per_launch"] = flops[dom]
     roof["algorithmic_bytes_per_launch"] = nbytes[dom]
-    roof["traffic"] = measured_traffic(cfg.name, dom)
+    roof["traffic"] = measured_traffic(cfg.name + ("_input_grads" if args.input_grads else ""), dom)
     red_gbps = work["reduce_bytes"] / (k_ms["reduce_axis0_kernel"] * 1e-3) / 1e9
     # floors of the whole step: algorithmic bytes at 8 TB/s, algorithmic f64
     # flops at 78.6 TFLOP/s; frac = the larger floor / measured time
     step_flops = work["fb_flops"] if args.path == "fused" else work["fwd_flops"] + work["bwd_flops"]
     step_bytes = (work["fb_bytes"] if args.path == "fused" else work["fwd_bytes"] + work["bwd_bytes"]) + \
         work["reduce_bytes"]
+    if args.input_grads:
+        step_flops += B * K * 2 * H * n_in + B * 2 * H * H
+        step_bytes += 4 * (B * K * n_in + B * H)
     hbm_floor_ms = step_bytes / (PEAK_HBM_GBPS * 1e9) * 1e3
     f64_floor_ms = step_flops / (PEAK_F64_TFLOPS * 1e12) * 1e3
     floors = {"algorithmic_bytes": step_bytes, "algorithmic_f64_flops": step_flops,
@@ -311,10 +351,16 @@ def main():
                    "scratch_N": N, "io_dtype": "f32", "seed": cfg.seed},
         "roofline": roof,
         "path": args.path,
+        "input_grads": args.input_grads,
         "fused_call_is_one_kernel": n_in <= 128 and H <= 128 and K <= 64,
         "step_ms_percentiles": pct,
         "step_floors": floors,
         "kernels_ms": k_ms,
+        "with_input_grads": None if args.main_only else {
+            "ms_per_step": ms_ig, "value": B * K / (ms_ig * 1e-3), "step_ms_percentiles": pct_ig,
+            "kernels_ms": k_ig,
+            "extra_algorithmic_flops": B * K * 2 * H * n_in + B * 2 * H * H,
+            "step": f"{args.path} path with grad_x [B,K,n_in] and grad_h0 [B,H] also written"},
         "accumulate_mode": None if args.main_only else {
             "ms_per_step": ms_acc, "value": B * K / (ms_acc * 1e-3), "step_ms_percentiles": pct_acc,
             "step": "scratch zero fill + cfc_forward_backward(CFC_ACCUMULATE) + reduce_axis0"},

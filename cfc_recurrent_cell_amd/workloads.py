@@ -42,6 +42,7 @@ class CfcConfig:
     h0_var: float = 0.0          # 0 => h0 = 0 (not drawn)
     x_feature_scale: bool = False  # x = s_f * z, s_f ~ U[0.5, 2] per feature
     steps: int = 1               # repeated steps over the same inputs
+    cell: str = "gated"          # "gated" or "tau_decay" (w_tau then holds tau ~ U[0.05, 2])
 
 
 @dataclasses.dataclass(frozen=True)
@@ -63,7 +64,15 @@ TRAIN = CfcConfig("train_B256_K64_H128", B=256, K=64, n_in=128, n_hid=128, dt=0.
 LARGE = CfcConfig("large_B8192_K8_H256", B=8192, K=8, n_in=256, n_hid=256, dt=1.0, seed=4,
                   h0_var=0.1)
 
-CFC_CONFIGS = {c.name: c for c in (TINY, SMOKE, TRAIN, LARGE)}
+# The tau-decay cell: the shape and dt of the pages' B=1 backward test (n_in=8,
+# n_hid=16, dt=0.02, tau ~ U[0.05, 2]) over a few rows and steps, and the
+# training-scale shape with the same dt and tau range.
+TAU_TINY = CfcConfig("tau_tiny_B4_K8_n8_H16", B=4, K=8, n_in=8, n_hid=16, dt=0.02, seed=20,
+                     h0_var=0.1, cell="tau_decay")
+TAU_TRAIN = CfcConfig("tau_train_B256_K64_H128", B=256, K=64, n_in=128, n_hid=128, dt=0.02, seed=21,
+                      x_feature_scale=True, cell="tau_decay")
+
+CFC_CONFIGS = {c.name: c for c in (TINY, SMOKE, TRAIN, LARGE, TAU_TINY, TAU_TRAIN)}
 
 
 def scratch_row_len(n_in: int, n_hid: int) -> int:
@@ -81,6 +90,7 @@ class CfcInputs:
     h0: np.ndarray      # [B, H]
     y: np.ndarray       # [B, H]
     dt: np.float32
+    cell: str = "gated"
 
 
 def make_cfc_inputs(cfg: CfcConfig, B: Optional[int] = None) -> CfcInputs:
@@ -91,7 +101,7 @@ def make_cfc_inputs(cfg: CfcConfig, B: Optional[int] = None) -> CfcInputs:
     w_in = rng.standard_normal((H, n_in)) * np.sqrt(1.0 / n_in)
     w_rec = rng.standard_normal((H, H)) * np.sqrt(1.0 / H)
     b = np.zeros(H)
-    w_tau = rng.standard_normal(H) * np.sqrt(0.1)
+    w_tau = _draw_w_tau(rng, H, cfg.cell)
     x = rng.standard_normal((B, K, n_in))
     if cfg.x_feature_scale:
         s = rng.uniform(0.5, 2.0, size=n_in)
@@ -102,23 +112,33 @@ def make_cfc_inputs(cfg: CfcConfig, B: Optional[int] = None) -> CfcInputs:
         h0 = np.zeros((B, H))
     y = rng.standard_normal((B, H))
     f = lambda a: np.ascontiguousarray(a, dtype=np.float32)
-    return CfcInputs(f(w_in), f(w_rec), f(b), f(w_tau), f(x), f(h0), f(y), np.float32(cfg.dt))
+    return CfcInputs(f(w_in), f(w_rec), f(b), f(w_tau), f(x), f(h0), f(y), np.float32(cfg.dt), cfg.cell)
+
+
+def _draw_w_tau(rng, H: int, cell: str) -> np.ndarray:
+    """The gated cell's w_tau ~ N(0, 0.1); the tau-decay cell's time constants
+    tau ~ U[0.05, 2] (the range of the pages' B=1 backward test)."""
+    if cell == "tau_decay":
+        return rng.uniform(0.05, 2.0, size=H)
+    if cell != "gated":
+        raise ValueError(f"unknown cell {cell!r}")
+    return rng.standard_normal(H) * np.sqrt(0.1)
 
 
 def make_random_cfc_inputs(B: int, K: int, n_in: int, n_hid: int, dt: float, seed: int,
                            w_scale: float = 1.0, b_std: float = 0.1,
-                           h0_std: float = 0.3) -> CfcInputs:
+                           h0_std: float = 0.3, cell: str = "gated") -> CfcInputs:
     """Generic seeded inputs for ragged / edge-case shapes (nonzero b and h0)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     w_in = rng.standard_normal((n_hid, n_in)) * (w_scale / np.sqrt(max(n_in, 1)))
     w_rec = rng.standard_normal((n_hid, n_hid)) * (w_scale / np.sqrt(max(n_hid, 1)))
     b = rng.standard_normal(n_hid) * b_std
-    w_tau = rng.standard_normal(n_hid) * np.sqrt(0.1)
+    w_tau = _draw_w_tau(rng, n_hid, cell)
     x = rng.standard_normal((B, K, n_in))
     h0 = rng.standard_normal((B, n_hid)) * h0_std
     y = rng.standard_normal((B, n_hid))
     f = lambda a: np.ascontiguousarray(a, dtype=np.float32)
-    return CfcInputs(f(w_in), f(w_rec), f(b), f(w_tau), f(x), f(h0), f(y), np.float32(dt))
+    return CfcInputs(f(w_in), f(w_rec), f(b), f(w_tau), f(x), f(h0), f(y), np.float32(dt), cell)
 
 
 def make_reduce_input(cfg: ReduceConfig = REDUCE, integer: bool = False) -> np.ndarray:

@@ -29,12 +29,25 @@
  *   reduce_axis0  out[j] = sum_b in[b, j], b ascending, overwrite
  *             ("K-loop Parallelization Implementation Plan", Task 1).
  *
+ * A second cell, the tau-decay cell the pages print ("K-loop
+ * Parallelization Implementation Plan", Task 2 forward kernel and Task 3
+ * backward kernel), replaces the gate with a per-unit constant:
+ *     decay  = exp(-dt / max(tau, 1e-6))           (w_tau holds tau)
+ *     h_k+1  = decay * h_k + (1 - decay) * tanh(a)
+ * so dL/da has no gate term, and dL/dtau = dL/ddecay * decay * dt / tau^2
+ * where tau > 1e-6, zero elsewhere (the pages' guard).  Its scratch row has
+ * the same layout, with dL/dtau in the last slot.
+ *
  * Everything is double precision.  The caller widens the float32 inputs.
  * Return value 0 = ok, -1 = bad argument.
  */
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+
+#define ORACLE_CELL_GATED 0
+#define ORACLE_CELL_TAU_DECAY 1
+#define ORACLE_TAU_EPS 1e-6
 
 /* softplus(w) = log(1 + e^w), written in the overflow-safe form
  * log1p(e^-|w|) + max(w, 0). */
@@ -49,9 +62,30 @@ static double oracle_sigmoid(double z)
     return 1.0 / (1.0 + exp(-z));
 }
 
+/* Per-unit constants of the gate, from w_tau:
+ *   gated cell:     sp = softplus(w_tau) (the rate), sw = sigmoid(w_tau)
+ *                   (d softplus / d w_tau);
+ *   tau-decay cell: sp = exp(-dt / max(tau, eps)) (the gate itself),
+ *                   sw = dt / tau^2 where tau > eps, else 0, so that
+ *                   d decay / d tau = decay * sw. */
+static void oracle_unit_consts(int cell, int H, double dt, const double *w_tau,
+                               double *sp, double *sw)
+{
+    for (int i = 0; i < H; ++i) {
+        if (cell == ORACLE_CELL_TAU_DECAY) {
+            const double tau_eff = w_tau[i] > ORACLE_TAU_EPS ? w_tau[i] : ORACLE_TAU_EPS;
+            sp[i] = exp(-dt / tau_eff);
+            sw[i] = w_tau[i] > ORACLE_TAU_EPS ? dt / (tau_eff * tau_eff) : 0.0;
+        } else {
+            sp[i] = oracle_softplus(w_tau[i]);
+            sw[i] = oracle_sigmoid(w_tau[i]);
+        }
+    }
+}
+
 /* One cell step for one row: given x_k [n_in] and h [H], fill a, g, c and
- * h_next (each [H]).  sp holds softplus(w_tau). */
-static void oracle_cell(int n_in, int H, double dt,
+ * h_next (each [H]).  sp holds the per-unit constants above. */
+static void oracle_cell(int cell, int n_in, int H, double dt,
                         const double *w_in, const double *w_rec,
                         const double *bias, const double *sp,
                         const double *xk, const double *h,
@@ -64,7 +98,10 @@ static void oracle_cell(int n_in, int H, double dt,
         for (int j = 0; j < H; ++j)
             s += w_rec[(size_t)i * H + j] * h[j];
         a[i] = s;
-        g[i] = oracle_sigmoid(-sp[i] * s * dt);
+        if (cell == ORACLE_CELL_TAU_DECAY)
+            g[i] = sp[i];   /* the unit's decay, independent of a */
+        else
+            g[i] = oracle_sigmoid(-sp[i] * s * dt);
         c[i] = tanh(s);
         h_next[i] = g[i] * h[i] + (1.0 - g[i]) * c[i];
     }
@@ -77,32 +114,33 @@ long long oracle_scratch_row_len(int n_in, int H)
     return (long long)H * ((long long)n_in + H + 2);
 }
 
-/* Forward K-loop.  x [B,K,n_in], h0 [B,H] -> h_seq [B,K,H] holding h_1..h_K. */
+/* Forward K-loop.  x [B,K,n_in], h0 [B,H] -> h_seq [B,K,H] holding h_1..h_K.
+ * cell: ORACLE_CELL_GATED or ORACLE_CELL_TAU_DECAY. */
 int oracle_cfc_forward(int B, int K, int n_in, int H, double dt,
                        const double *w_in, const double *w_rec,
                        const double *bias, const double *w_tau,
-                       const double *x, const double *h0, double *h_seq)
+                       const double *x, const double *h0, double *h_seq, int cell)
 {
-    if (B < 0 || K < 1 || n_in < 1 || H < 1)
+    if (B < 0 || K < 1 || n_in < 1 || H < 1 || (cell != ORACLE_CELL_GATED && cell != ORACLE_CELL_TAU_DECAY))
         return -1;
     double *sp = malloc(sizeof(double) * H);
+    double *sw = malloc(sizeof(double) * H);
     double *a = malloc(sizeof(double) * H);
     double *g = malloc(sizeof(double) * H);
     double *c = malloc(sizeof(double) * H);
     double *h = malloc(sizeof(double) * H);
     double *hn = malloc(sizeof(double) * H);
-    for (int i = 0; i < H; ++i)
-        sp[i] = oracle_softplus(w_tau[i]);
+    oracle_unit_consts(cell, H, dt, w_tau, sp, sw);
     for (int b = 0; b < B; ++b) {
         memcpy(h, h0 + (size_t)b * H, sizeof(double) * H);
         for (int k = 0; k < K; ++k) {
             const double *xk = x + ((size_t)b * K + k) * n_in;
-            oracle_cell(n_in, H, dt, w_in, w_rec, bias, sp, xk, h, a, g, c, hn);
+            oracle_cell(cell, n_in, H, dt, w_in, w_rec, bias, sp, xk, h, a, g, c, hn);
             memcpy(h, hn, sizeof(double) * H);
             memcpy(h_seq + ((size_t)b * K + k) * H, h, sizeof(double) * H);
         }
     }
-    free(sp); free(a); free(g); free(c); free(h); free(hn);
+    free(sp); free(sw); free(a); free(g); free(c); free(h); free(hn);
     return 0;
 }
 
@@ -124,13 +162,13 @@ int oracle_cfc_backward_inputs(int B, int K, int n_in, int H, double dt,
                                const double *x, const double *h0,
                                const double *h_seq, const double *y,
                                double *scratch, double *loss,
-                               double *grad_x, double *grad_h0)
+                               double *grad_x, double *grad_h0, int cell)
 {
-    if (B < 0 || K < 1 || n_in < 1 || H < 1)
+    if (B < 0 || K < 1 || n_in < 1 || H < 1 || (cell != ORACLE_CELL_GATED && cell != ORACLE_CELL_TAU_DECAY))
         return -1;
     const size_t N = (size_t)oracle_scratch_row_len(n_in, H);
     double *sp = malloc(sizeof(double) * H);
-    double *sw = malloc(sizeof(double) * H);   /* d softplus / d w = sigmoid(w) */
+    double *sw = malloc(sizeof(double) * H);   /* see oracle_unit_consts */
     double *a = malloc(sizeof(double) * H);
     double *g = malloc(sizeof(double) * H);
     double *c = malloc(sizeof(double) * H);
@@ -139,10 +177,7 @@ int oracle_cfc_backward_inputs(int B, int K, int n_in, int H, double dt,
     double *delta_prev = malloc(sizeof(double) * H);
     double *dz = malloc(sizeof(double) * H);
     double *da = malloc(sizeof(double) * H);
-    for (int i = 0; i < H; ++i) {
-        sp[i] = oracle_softplus(w_tau[i]);
-        sw[i] = oracle_sigmoid(w_tau[i]);
-    }
+    oracle_unit_consts(cell, H, dt, w_tau, sp, sw);
     for (int b = 0; b < B; ++b) {
         double *row = scratch + (size_t)b * N;
         double *g_win = row;                                  /* [H, n_in] */
@@ -169,12 +204,18 @@ int oracle_cfc_backward_inputs(int B, int K, int n_in, int H, double dt,
             const double *hp = (k == 0) ? h0 + (size_t)b * H
                                         : h_seq + ((size_t)b * K + (k - 1)) * H;
             /* recompute the step's pre-activation and gates from h_k */
-            oracle_cell(n_in, H, dt, w_in, w_rec, bias, sp, xk, hp, a, g, c, hn);
+            oracle_cell(cell, n_in, H, dt, w_in, w_rec, bias, sp, xk, hp, a, g, c, hn);
             for (int i = 0; i < H; ++i) {
-                /* dL/dz with z = -sp*a*dt the gate's argument */
-                dz[i] = delta[i] * (hp[i] - c[i]) * g[i] * (1.0 - g[i]);
-                /* dL/da through tanh and through the gate */
-                da[i] = delta[i] * (1.0 - g[i]) * (1.0 - c[i] * c[i]) - dz[i] * sp[i] * dt;
+                if (cell == ORACLE_CELL_TAU_DECAY) {
+                    /* dL/d(decay); the gate does not depend on a */
+                    dz[i] = delta[i] * (hp[i] - c[i]);
+                    da[i] = delta[i] * (1.0 - g[i]) * (1.0 - c[i] * c[i]);
+                } else {
+                    /* dL/dz with z = -sp*a*dt the gate's argument */
+                    dz[i] = delta[i] * (hp[i] - c[i]) * g[i] * (1.0 - g[i]);
+                    /* dL/da through tanh and through the gate */
+                    da[i] = delta[i] * (1.0 - g[i]) * (1.0 - c[i] * c[i]) - dz[i] * sp[i] * dt;
+                }
             }
             for (int i = 0; i < H; ++i) {
                 for (int j = 0; j < n_in; ++j)
@@ -182,7 +223,10 @@ int oracle_cfc_backward_inputs(int B, int K, int n_in, int H, double dt,
                 for (int j = 0; j < H; ++j)
                     g_wrec[(size_t)i * H + j] += da[i] * hp[j];
                 g_b[i] += da[i];
-                g_wtau[i] += dz[i] * (-a[i] * dt) * sw[i];
+                if (cell == ORACLE_CELL_TAU_DECAY)
+                    g_wtau[i] += dz[i] * g[i] * sw[i];   /* dL/dtau */
+                else
+                    g_wtau[i] += dz[i] * (-a[i] * dt) * sw[i];
             }
             /* dL/dx_k = W_in^T da */
             if (grad_x) {
@@ -212,17 +256,6 @@ int oracle_cfc_backward_inputs(int B, int K, int n_in, int H, double dt,
     return 0;
 }
 
-/* The backward without the input gradients. */
-int oracle_cfc_backward(int B, int K, int n_in, int H, double dt,
-                        const double *w_in, const double *w_rec,
-                        const double *bias, const double *w_tau,
-                        const double *x, const double *h0,
-                        const double *h_seq, const double *y,
-                        double *scratch, double *loss)
-{
-    return oracle_cfc_backward_inputs(B, K, n_in, H, dt, w_in, w_rec, bias, w_tau, x, h0,
-                                      h_seq, y, scratch, loss, NULL, NULL);
-}
 
 /* out[j] = sum_{b=0}^{B-1} in[b, j], b ascending; B = 0 gives zeros. */
 int oracle_reduce_axis0(long long B, long long N, const double *in, double *out)

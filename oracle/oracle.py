@@ -24,6 +24,7 @@ _lock = threading.Lock()
 _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)
+CELLS = {"gated": 0, "tau_decay": 1}   # the oracle's cell codes
 _fp = ctypes.POINTER(ctypes.c_float)
 
 
@@ -39,11 +40,9 @@ def _bind(lib):
     lib.oracle_scratch_row_len.restype = ctypes.c_longlong
     lib.oracle_scratch_row_len.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.oracle_cfc_forward.restype = ctypes.c_int
-    lib.oracle_cfc_forward.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double] + [_dp] * 7
-    lib.oracle_cfc_backward.restype = ctypes.c_int
-    lib.oracle_cfc_backward.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double] + [_dp] * 10
+    lib.oracle_cfc_forward.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double] + [_dp] * 7 + [ctypes.c_int]
     lib.oracle_cfc_backward_inputs.restype = ctypes.c_int
-    lib.oracle_cfc_backward_inputs.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double] + [_dp] * 12
+    lib.oracle_cfc_backward_inputs.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double] + [_dp] * 12 + [ctypes.c_int]
     lib.oracle_reduce_axis0.restype = ctypes.c_int
     lib.oracle_reduce_axis0.argtypes = [ctypes.c_longlong, ctypes.c_longlong, _dp, _dp]
     lib.oracle_reduce_axis0_f32.restype = ctypes.c_int
@@ -83,7 +82,8 @@ def _row_chunks(B: int, threads: int):
     return [(int(bounds[t]), int(bounds[t + 1])) for t in range(threads) if bounds[t + 1] > bounds[t]]
 
 
-def cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, threads: int = 1, lib=None) -> np.ndarray:
+def cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, threads: int = 1, lib=None,
+                cell: str = "gated") -> np.ndarray:
     """h_seq [B, K, H] in float64."""
     lib = lib or load_oracle()
     w_in, w_rec, b, w_tau, x, h0 = map(_d, (w_in, w_rec, b, w_tau, x, h0))
@@ -94,7 +94,7 @@ def cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, threads: int = 1, lib=None) ->
     def run(r0, r1):
         rc = lib.oracle_cfc_forward(r1 - r0, K, n_in, H, float(dt), _ptr(w_in), _ptr(w_rec),
                                     _ptr(b), _ptr(w_tau), _ptr(x, r0 * K * n_in),
-                                    _ptr(h0, r0 * H), _ptr(h_seq, r0 * K * H))
+                                    _ptr(h0, r0 * H), _ptr(h_seq, r0 * K * H), CELLS[cell])
         if rc != 0:
             raise ValueError("oracle_cfc_forward rejected its arguments")
 
@@ -103,7 +103,7 @@ def cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, threads: int = 1, lib=None) ->
 
 
 def cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, threads: int = 1,
-                 lib=None, scratch: Optional[np.ndarray] = None):
+                 lib=None, scratch: Optional[np.ndarray] = None, cell: str = "gated"):
     """(scratch [B, N] float64, loss [B] float64).  ``scratch`` may be a
     preallocated (possibly poisoned) float64 buffer; the oracle zeroes it."""
     lib = lib or load_oracle()
@@ -117,18 +117,19 @@ def cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, threads: int = 1,
     loss = np.empty(B, dtype=np.float64)
 
     def run(r0, r1):
-        rc = lib.oracle_cfc_backward(r1 - r0, K, n_in, H, float(dt), _ptr(w_in), _ptr(w_rec),
-                                     _ptr(b), _ptr(w_tau), _ptr(x, r0 * K * n_in),
-                                     _ptr(h0, r0 * H), _ptr(h_seq, r0 * K * H), _ptr(y, r0 * H),
-                                     _ptr(scratch, r0 * N), _ptr(loss, r0))
+        rc = lib.oracle_cfc_backward_inputs(r1 - r0, K, n_in, H, float(dt), _ptr(w_in), _ptr(w_rec),
+                                            _ptr(b), _ptr(w_tau), _ptr(x, r0 * K * n_in),
+                                            _ptr(h0, r0 * H), _ptr(h_seq, r0 * K * H), _ptr(y, r0 * H),
+                                            _ptr(scratch, r0 * N), _ptr(loss, r0), None, None, CELLS[cell])
         if rc != 0:
-            raise ValueError("oracle_cfc_backward rejected its arguments")
+            raise ValueError("oracle_cfc_backward_inputs rejected its arguments")
 
     _run_rows(run, B, threads)
     return scratch, loss
 
 
-def cfc_backward_inputs(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, threads: int = 1, lib=None):
+def cfc_backward_inputs(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, threads: int = 1, lib=None,
+                        cell: str = "gated"):
     """(scratch [B, N], loss [B], grad_x [B, K, n_in], grad_h0 [B, H]), float64:
     the backward plus the gradients with respect to x and h0."""
     lib = lib or load_oracle()
@@ -145,7 +146,8 @@ def cfc_backward_inputs(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, threads: int
         rc = lib.oracle_cfc_backward_inputs(
             r1 - r0, K, n_in, H, float(dt), _ptr(w_in), _ptr(w_rec), _ptr(b), _ptr(w_tau),
             _ptr(x, r0 * K * n_in), _ptr(h0, r0 * H), _ptr(h_seq, r0 * K * H), _ptr(y, r0 * H),
-            _ptr(scratch, r0 * N), _ptr(loss, r0), _ptr(grad_x, r0 * K * n_in), _ptr(grad_h0, r0 * H))
+            _ptr(scratch, r0 * N), _ptr(loss, r0), _ptr(grad_x, r0 * K * n_in), _ptr(grad_h0, r0 * H),
+            CELLS[cell])
         if rc != 0:
             raise ValueError("oracle_cfc_backward_inputs rejected its arguments")
 
@@ -184,17 +186,18 @@ def cfc_step(inp, threads: int = 1, lib=None, keep_scratch: bool = True,
     kept, so memory stays O(row_block * N).
     """
     lib = lib or load_oracle()
+    cell = getattr(inp, "cell", "gated")
     h_seq = cfc_forward(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x, inp.h0, inp.dt,
-                        threads=threads, lib=lib)
+                        threads=threads, lib=lib, cell=cell)
     B = inp.x.shape[0]
     if input_grads:
         scratch, loss, gx, gh = cfc_backward_inputs(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x, inp.h0,
-                                                    h_seq, inp.y, inp.dt, threads=threads, lib=lib)
+                                                    h_seq, inp.y, inp.dt, threads=threads, lib=lib, cell=cell)
         out = reduce_axis0(scratch, lib=lib)
         return dict(h_seq=h_seq, scratch=scratch, loss=loss, out=out, grad_x=gx, grad_h0=gh)
     if keep_scratch:
         scratch, loss = cfc_backward(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x, inp.h0,
-                                     h_seq, inp.y, inp.dt, threads=threads, lib=lib)
+                                     h_seq, inp.y, inp.dt, threads=threads, lib=lib, cell=cell)
         out = reduce_axis0(scratch, lib=lib)
         return dict(h_seq=h_seq, scratch=scratch, loss=loss, out=out)
     N = scratch_row_len(inp.x.shape[2], inp.w_rec.shape[0], lib)
@@ -203,7 +206,7 @@ def cfc_step(inp, threads: int = 1, lib=None, keep_scratch: bool = True,
     for r0 in range(0, B, row_block):
         r1 = min(B, r0 + row_block)
         s, l = cfc_backward(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x[r0:r1], inp.h0[r0:r1],
-                            h_seq[r0:r1], inp.y[r0:r1], inp.dt, threads=threads, lib=lib)
+                            h_seq[r0:r1], inp.y[r0:r1], inp.dt, threads=threads, lib=lib, cell=cell)
         loss[r0:r1] = l
         for r in range(r1 - r0):       # b ascending, one row at a time
             out += s[r]

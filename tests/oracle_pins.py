@@ -45,9 +45,9 @@ def _loss_from_hseq(h_seq, y) -> float:
     return float(0.5 * np.sum(d * d))
 
 
-def _full_step(lib, w_in, w_rec, b, w_tau, x, h0, y, dt):
-    h_seq = O.cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, lib=lib)
-    scratch, loss = O.cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, lib=lib)
+def _full_step(lib, w_in, w_rec, b, w_tau, x, h0, y, dt, cell="gated"):
+    h_seq = O.cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, lib=lib, cell=cell)
+    scratch, loss = O.cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, lib=lib, cell=cell)
     out = O.reduce_axis0(scratch, lib=lib)
     return h_seq, scratch, loss, out
 
@@ -67,14 +67,15 @@ def pin_hand_examples(lib) -> None:
         h0 = arr("h0", (1, H))
         y = arr("y", (1, H))
         dt = _ev(ex["dt"])
-        h_seq, scratch, loss, out = _full_step(lib, w_in, w_rec, b, w_tau, x, h0, y, dt)
+        cell = ex.get("cell", "gated")
+        h_seq, scratch, loss, out = _full_step(lib, w_in, w_rec, b, w_tau, x, h0, y, dt, cell)
         want_h = arr("h_seq", (1, K, H))
         want_s = arr("scratch", (1, H * (n_in + H + 2)))
         np.testing.assert_allclose(h_seq, want_h, rtol=1e-13, atol=1e-15, err_msg=ex["name"] + " h_seq")
         np.testing.assert_allclose(loss[0], _ev(ex["loss"]), rtol=1e-13, err_msg=ex["name"] + " loss")
         np.testing.assert_allclose(scratch, want_s, rtol=1e-12, atol=1e-15, err_msg=ex["name"] + " scratch")
         np.testing.assert_array_equal(out, scratch[0], err_msg=ex["name"] + " reduce at B=1 is a copy")
-        _, _, gx, gh = O.cfc_backward_inputs(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, lib=lib)
+        _, _, gx, gh = O.cfc_backward_inputs(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, lib=lib, cell=cell)
         np.testing.assert_allclose(gx, arr("grad_x", (1, K, n_in)), rtol=1e-12, atol=1e-15,
                                    err_msg=ex["name"] + " grad_x")
         np.testing.assert_allclose(gh, arr("grad_h0", (1, H)), rtol=1e-12, atol=1e-15,
@@ -143,12 +144,13 @@ def pin_finite_differences(lib, inp: CfcInputs = None, eps=1e-6, rtol=2e-6, atol
     every parameter, against the reduced gradient from its backward."""
     if inp is None:
         inp = make_random_cfc_inputs(2, 4, 3, 5, 0.7, seed=7)
+    cell = inp.cell
     w = [np.array(a, dtype=np.float64) for a in (inp.w_in, inp.w_rec, inp.b, inp.w_tau)]
     x, h0, y, dt = inp.x, inp.h0, inp.y, float(inp.dt)
-    _, _, _, out = _full_step(lib, *w, x, h0, y, dt)
+    _, _, _, out = _full_step(lib, *w, x, h0, y, dt, cell)
 
     def L(params):
-        return _loss_from_hseq(O.cfc_forward(*params, x, h0, dt, lib=lib), y)
+        return _loss_from_hseq(O.cfc_forward(*params, x, h0, dt, lib=lib, cell=cell), y)
 
     fd = []
     for t in range(4):
@@ -172,13 +174,14 @@ def pin_input_grad_finite_differences(lib, inp: CfcInputs = None, eps=1e-6, rtol
     oracle's own forward, against the backward's grad_x and grad_h0."""
     if inp is None:
         inp = make_random_cfc_inputs(2, 4, 3, 5, 0.7, seed=13)
+    cell = inp.cell
     w = [np.array(a, dtype=np.float64) for a in (inp.w_in, inp.w_rec, inp.b, inp.w_tau)]
     x, h0, y, dt = np.array(inp.x, np.float64), np.array(inp.h0, np.float64), inp.y, float(inp.dt)
-    h_seq = O.cfc_forward(*w, x, h0, dt, lib=lib)
-    _, _, gx, gh = O.cfc_backward_inputs(*w, x, h0, h_seq, y, dt, lib=lib)
+    h_seq = O.cfc_forward(*w, x, h0, dt, lib=lib, cell=cell)
+    _, _, gx, gh = O.cfc_backward_inputs(*w, x, h0, h_seq, y, dt, lib=lib, cell=cell)
 
     def L(xv, hv):
-        return _loss_from_hseq(O.cfc_forward(*w, xv, hv, dt, lib=lib), y)
+        return _loss_from_hseq(O.cfc_forward(*w, xv, hv, dt, lib=lib, cell=cell), y)
 
     for arr, got, is_x in ((x, gx, True), (h0, gh, False)):
         fd = np.empty(arr.size)
@@ -202,25 +205,93 @@ def pin_autograd(lib, inp: CfcInputs = None) -> None:
     w_in, w_rec, b, w_tau = (t(a).requires_grad_(True) for a in (inp.w_in, inp.w_rec, inp.b, inp.w_tau))
     x, h0, y = t(inp.x).requires_grad_(True), t(inp.h0).requires_grad_(True), t(inp.y)
     dt = float(inp.dt)
+    cell = inp.cell
     h = h0
     hs = []
     for k in range(x.shape[1]):
         a = x[:, k] @ w_in.T + h @ w_rec.T + b
-        g = torch.sigmoid(-torch.nn.functional.softplus(w_tau) * a * dt)
+        if cell == "tau_decay":    # the pages' cell: a per-unit decay from tau, clamped at 1e-6
+            g = torch.exp(-dt / torch.clamp(w_tau, min=1e-6))
+        else:
+            g = torch.sigmoid(-torch.nn.functional.softplus(w_tau) * a * dt)
         h = g * h + (1 - g) * torch.tanh(a)
         hs.append(h)
     loss = 0.5 * ((h - y) ** 2).sum()
     loss.backward()
     want = torch.cat([w_in.grad.ravel(), w_rec.grad.ravel(), b.grad, w_tau.grad]).numpy()
     h_seq, _, lossv, out = _full_step(lib, inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x, inp.h0,
-                                      inp.y, dt)
+                                      inp.y, dt, cell)
     np.testing.assert_allclose(h_seq, torch.stack(hs, 1).detach().numpy(), rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(lossv.sum(), loss.item(), rtol=1e-12)
     np.testing.assert_allclose(out, want, rtol=1e-10, atol=1e-13)
     _, _, gx, gh = O.cfc_backward_inputs(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x, inp.h0, h_seq,
-                                         inp.y, dt, lib=lib)
+                                         inp.y, dt, lib=lib, cell=cell)
     np.testing.assert_allclose(gx, x.grad.numpy(), rtol=1e-10, atol=1e-13)
     np.testing.assert_allclose(gh, h0.grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
+# ------------------------------------------------------------- tau-decay cell
+def pin_tau_zero_weights(lib, K=5, n_in=3, H=4, dt=0.3, seed=14) -> None:
+    """Tau-decay cell with W_in = W_rec = 0, b = 0: a = 0, c = 0, so
+    h_k+1 = d h_k with d = exp(-dt/tau) per unit; backward by hand:
+    da_k = (1 - d) delta_k+1, dtau += delta_k+1 h_k d dt / tau^2,
+    delta_k = d delta_k+1."""
+    rng = np.random.default_rng(seed)
+    w_in, w_rec, b = np.zeros((H, n_in)), np.zeros((H, H)), np.zeros(H)
+    tau = rng.uniform(0.05, 2.0, H)
+    x = rng.standard_normal((2, K, n_in))
+    h0 = rng.standard_normal((2, H))
+    y = rng.standard_normal((2, H))
+    h_seq, scratch, loss, _ = _full_step(lib, w_in, w_rec, b, tau, x, h0, y, dt, "tau_decay")
+    _, _, gx, gh = O.cfc_backward_inputs(w_in, w_rec, b, tau, x, h0, h_seq, y, dt, lib=lib, cell="tau_decay")
+    d = np.exp(-dt / tau)
+    for r in range(2):
+        hs = [h0[r]]
+        for k in range(K):
+            hs.append(d * hs[-1])
+        np.testing.assert_allclose(h_seq[r], np.array(hs[1:]), rtol=1e-14, atol=1e-300)
+        delta = hs[-1] - y[r]
+        gWin, gWrec, gb, gtau = np.zeros((H, n_in)), np.zeros((H, H)), np.zeros(H), np.zeros(H)
+        for k in range(K - 1, -1, -1):
+            da = (1 - d) * delta
+            gWin += np.outer(da, x[r, k])
+            gWrec += np.outer(da, hs[k])
+            gb += da
+            gtau += delta * hs[k] * d * dt / tau ** 2
+            delta = d * delta
+        want = np.concatenate([gWin.ravel(), gWrec.ravel(), gb, gtau])
+        np.testing.assert_allclose(scratch[r], want, rtol=1e-12, atol=1e-14)
+        np.testing.assert_array_equal(gx[r], np.zeros((K, n_in)))
+        np.testing.assert_allclose(gh[r], delta, rtol=1e-13, atol=1e-300)
+
+
+def pin_tau_guard(lib, seed=15) -> None:
+    """Units with tau <= 1e-6 (the pages' guard): the decay is exp(-dt/1e-6),
+    which is 0 in float64 for dt = 0.5, so h_k+1 = tanh(a) exactly, and their
+    dL/dtau slot is exactly 0; the other units are unaffected."""
+    inp = make_random_cfc_inputs(3, 4, 5, 6, 0.5, seed, cell="tau_decay")
+    tau = inp.w_tau.astype(np.float64).copy()
+    tau[[1, 4]] = [0.0, -0.3]
+    h_seq, scratch, _, _ = _full_step(lib, inp.w_in, inp.w_rec, inp.b, tau, inp.x, inp.h0, inp.y, 0.5,
+                                      "tau_decay")
+    H = 6
+    assert scratch[0, -H + 1] == 0.0 and scratch[0, -H + 4] == 0.0
+    assert np.all(scratch[:, -H:][:, [0, 2, 3, 5]] != 0.0)
+    prev = inp.h0.astype(np.float64)
+    for k in range(4):
+        a = inp.x[:, k].astype(np.float64) @ inp.w_in.T.astype(np.float64) + \
+            prev @ inp.w_rec.T.astype(np.float64) + inp.b
+        np.testing.assert_allclose(h_seq[:, k, [1, 4]], np.tanh(a[:, [1, 4]]), rtol=1e-14, atol=1e-16)
+        prev = h_seq[:, k]
+
+
+def pin_tau_finite_differences(lib) -> None:
+    pin_finite_differences(lib, make_random_cfc_inputs(2, 4, 3, 5, 0.4, seed=16, cell="tau_decay"))
+    pin_input_grad_finite_differences(lib, make_random_cfc_inputs(2, 4, 3, 5, 0.4, seed=17, cell="tau_decay"))
+
+
+def pin_tau_autograd(lib) -> None:
+    pin_autograd(lib, make_random_cfc_inputs(3, 5, 4, 6, 0.7, seed=18, cell="tau_decay"))
 
 
 # ------------------------------------------------------------ structural pins
@@ -293,4 +364,8 @@ ALL_PINS = {
     "scratch_clears": pin_scratch_clears,
     "permutation": pin_permutation,
     "reduce_exact": pin_reduce_exact,
+    "tau_zero_weights": pin_tau_zero_weights,
+    "tau_guard": pin_tau_guard,
+    "tau_finite_differences": pin_tau_finite_differences,
+    "tau_autograd": pin_tau_autograd,
 }

@@ -27,7 +27,7 @@ MUTANTS = {
     "backward_drops_gate_term": ("- dz[i] * sp[i] * dt;", ";"),
     "backward_dz_sign": ("dz[i] = delta[i] * (hp[i] - c[i]) * g[i] * (1.0 - g[i]);",
                          "dz[i] = delta[i] * (c[i] - hp[i]) * g[i] * (1.0 - g[i]);"),
-    "backward_tanh_derivative": ("(1.0 - c[i] * c[i])", "(1.0 - c[i])"),
+    "backward_tanh_derivative": ("(1.0 - c[i] * c[i]) - dz[i] * sp[i] * dt;", "(1.0 - c[i]) - dz[i] * sp[i] * dt;"),
     "backward_transposed_w_rec": ("s += w_rec[(size_t)i * H + j] * da[i];",
                                   "s += w_rec[(size_t)j * H + i] * da[i];"),
     "backward_drops_direct_path": ("double s = delta[j] * g[j];", "double s = 0.0;"),
@@ -48,6 +48,13 @@ MUTANTS = {
                        "t += w_in[(size_t)i * n_in + j] * dz[i];"),
     "grad_x_steps_reversed": ("double *gx = grad_x + ((size_t)b * K + k) * n_in;",
                               "double *gx = grad_x + ((size_t)b * K + (K - 1 - k)) * n_in;"),
+    "tau_decay_product": ("sp[i] = exp(-dt / tau_eff);", "sp[i] = exp(-dt * tau_eff);"),
+    "tau_guard_inverted": ("sw[i] = w_tau[i] > ORACLE_TAU_EPS ? dt / (tau_eff * tau_eff) : 0.0;",
+                           "sw[i] = w_tau[i] > ORACLE_TAU_EPS ? 0.0 : dt / (tau_eff * tau_eff);"),
+    "tau_da_drops_one_minus_decay": ("da[i] = delta[i] * (1.0 - g[i]) * (1.0 - c[i] * c[i]);\n",
+                                     "da[i] = delta[i] * (1.0 - c[i] * c[i]);\n"),
+    "tau_dtau_missing_decay": ("g_wtau[i] += dz[i] * g[i] * sw[i];", "g_wtau[i] += dz[i] * sw[i];"),
+    "tau_dz_sign": ("dz[i] = delta[i] * (hp[i] - c[i]);", "dz[i] = delta[i] * (c[i] - hp[i]);"),
     "grad_h0_before_last_step": ("            memcpy(delta, delta_prev, sizeof(double) * H);\n        }\n        /* after step 0",
                                  "            if (k > 0) memcpy(delta, delta_prev, sizeof(double) * H);\n        }\n        /* after step 0"),
 }

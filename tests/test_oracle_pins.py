@@ -37,3 +37,12 @@ def test_input_grad_finite_differences_tiny_workload(lib):
     2 * 67 * 2^-53 / (2 * 1e-6) = 7e-9; atol is four times that."""
     inp = make_cfc_inputs(TINY)
     P.pin_input_grad_finite_differences(lib, inp, eps=1e-6, rtol=1e-6, atol=3e-8)
+
+
+def test_tau_decay_tiny_workload_finite_differences(lib):
+    """Every parameter (416) and input (256 + 64) of the tau-decay tiny
+    workload: the shape and dt of the pages' B=1 backward test."""
+    from cfc_recurrent_cell_amd.workloads import TAU_TINY
+    inp = make_cfc_inputs(TAU_TINY)
+    P.pin_finite_differences(lib, inp, eps=1e-6, rtol=1e-6, atol=1e-8)
+    P.pin_input_grad_finite_differences(lib, inp, eps=1e-6, rtol=1e-6, atol=1e-8)
