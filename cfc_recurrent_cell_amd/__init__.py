@@ -13,7 +13,7 @@ import ctypes
 from typing import Optional, Tuple
 
 from ._lib import (  # noqa: F401
-    CFC_ACCUMULATE, CFC_ERR_DIM, CFC_ERR_DT, CFC_ERR_HIP, CFC_ERR_NULL, CFC_ERR_OVERLAP,
+    CELLS, CFC_CELL_GATED, CFC_CELL_TAU_DECAY, CFC_ACCUMULATE, CFC_ERR_DIM, CFC_ERR_DT, CFC_ERR_HIP, CFC_ERR_NULL, CFC_ERR_OVERLAP,
     CFC_ERR_UNSUPPORTED, CFC_OK, CFC_OVERWRITE, CfcError, CfcParams, LIB_PATH, _check,
     declared_symbols, load_library, status_string,
 )
@@ -45,20 +45,23 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _params(w_in, w_rec, b, w_tau):
+def _params(w_in, w_rec, b, w_tau, cell="gated"):
+    if cell not in CELLS:
+        raise ValueError(f"cell must be one of {sorted(CELLS)}, got {cell!r}")
     H, n_in = w_in.shape
     _dev_f32(w_in, "w_in", (H, n_in))
     _dev_f32(w_rec, "w_rec", (H, H))
     _dev_f32(b, "b", (H,))
     _dev_f32(w_tau, "w_tau", (H,))
-    return CfcParams(w_in.data_ptr(), w_rec.data_ptr(), b.data_ptr(), w_tau.data_ptr(), n_in, H)
+    return CfcParams(w_in.data_ptr(), w_rec.data_ptr(), b.data_ptr(), w_tau.data_ptr(), n_in, H, CELLS[cell])
 
 
-def cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt: float, h_seq=None, stream=None):
-    """h_seq [B, K, H] = forward K-loop of the cell (see include/cfc.h)."""
+def cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt: float, h_seq=None, stream=None, cell: str = "gated"):
+    """h_seq [B, K, H] = forward K-loop of the cell (see include/cfc.h);
+    ``cell`` is "gated" or "tau_decay" (w_tau then holds tau)."""
     import torch
     lib = load_library()
-    p = _params(w_in, w_rec, b, w_tau)
+    p = _params(w_in, w_rec, b, w_tau, cell)
     B, K, _ = x.shape
     _dev_f32(x, "x", (B, K, p.n_in))
     _dev_f32(h0, "h0", (B, p.n_hid))
@@ -89,14 +92,14 @@ def _input_grad_buffers(x, p, grad_x, grad_h0, input_grads):
 def cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, scratch=None,
                  loss=None, accumulate: bool = False, want_loss: bool = True,
                  input_grads: bool = False, grad_x=None, grad_h0=None,
-                 stream=None) -> Tuple[object, ...]:
+                 stream=None, cell: str = "gated") -> Tuple[object, ...]:
     """(scratch [B, N], loss [B] or None): per-row parameter gradients of
     L_b = 1/2 |h_K - y_b|^2 (see include/cfc.h for the row layout).  With
     ``input_grads`` (or explicit ``grad_x`` / ``grad_h0`` buffers) it returns
     (scratch, loss, grad_x [B, K, n_in], grad_h0 [B, H]) instead."""
     import torch
     lib = load_library()
-    p = _params(w_in, w_rec, b, w_tau)
+    p = _params(w_in, w_rec, b, w_tau, cell)
     B, K, _ = x.shape
     N = cfc_scratch_row_len(p.n_in, p.n_hid)
     _dev_f32(x, "x", (B, K, p.n_in))
@@ -126,13 +129,13 @@ def cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, scratch=None
 def cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt: float, h_seq=None, scratch=None,
                          loss=None, accumulate: bool = False, want_loss: bool = True,
                          input_grads: bool = False, grad_x=None, grad_h0=None,
-                         stream=None) -> Tuple[object, ...]:
+                         stream=None, cell: str = "gated") -> Tuple[object, ...]:
     """(h_seq [B, K, H], scratch [B, N], loss [B] or None): the forward and the
     backward of the same inputs in one library call (see include/cfc.h).  With
     ``input_grads`` (or explicit buffers) grad_x and grad_h0 are appended."""
     import torch
     lib = load_library()
-    p = _params(w_in, w_rec, b, w_tau)
+    p = _params(w_in, w_rec, b, w_tau, cell)
     B, K, _ = x.shape
     N = cfc_scratch_row_len(p.n_in, p.n_hid)
     _dev_f32(x, "x", (B, K, p.n_in))

@@ -24,9 +24,15 @@ CFC_OVERWRITE = 0
 CFC_ACCUMULATE = 1
 
 
+CFC_CELL_GATED = 0
+CFC_CELL_TAU_DECAY = 1
+CELLS = {"gated": CFC_CELL_GATED, "tau_decay": CFC_CELL_TAU_DECAY}
+
+
 class CfcParams(ctypes.Structure):
     _fields_ = [("w_in", ctypes.c_void_p), ("w_rec", ctypes.c_void_p), ("b", ctypes.c_void_p),
-                ("w_tau", ctypes.c_void_p), ("n_in", ctypes.c_int), ("n_hid", ctypes.c_int)]
+                ("w_tau", ctypes.c_void_p), ("n_in", ctypes.c_int), ("n_hid", ctypes.c_int),
+                ("cell", ctypes.c_int)]
 
 
 class CfcError(RuntimeError):

@@ -43,6 +43,17 @@ __device__ __forceinline__ double softplus_f64(double w) {
 }
 __device__ __forceinline__ double logistic_f64(double z) { return 1.0 / (1.0 + exp(-z)); }
 
+// The tau-decay cell ("K-loop Parallelization Implementation Plan", Tasks 2
+// and 3): a unit's gate is the constant decay = exp(-dt / max(tau, 1e-6)), and
+// d decay / d tau = decay * q with q = dt / tau^2 where tau > 1e-6, else 0
+// (the pages' zero-gradient guard).
+constexpr double kTauEps = 1e-6;
+__device__ __forceinline__ void tau_decay_consts(double tau, double dt, double& decay, double& q) {
+    const double tau_eff = fmax(tau, kTauEps);
+    decay = exp(-dt / tau_eff);
+    q = tau > kTauEps ? dt / (tau_eff * tau_eff) : 0.0;
+}
+
 // Threads per output of a matvec: the largest power of two G <= 64 with
 // G * rows <= 256, so a group of G consecutive lanes shares one output and
 // combines with butterfly shuffles inside one wavefront.
@@ -77,7 +88,8 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_kernel(
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
     const float* __restrict__ y, double dt, int K, int n_in, int H, float* __restrict__ scratch,
-    float* __restrict__ loss, float* __restrict__ grad_x, float* __restrict__ grad_h0, int accumulate) {
+    float* __restrict__ loss, float* __restrict__ grad_x, float* __restrict__ grad_h0, int accumulate,
+    int cell) {
     extern __shared__ __align__(16) unsigned char smem[];
     double* DA = reinterpret_cast<double*>(smem);
     double* delta = DA + (size_t)K * H;
@@ -98,8 +110,12 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_kernel(
     double lpart = 0.0;
     for (int u = t; u < H; u += kThreads) {
         const double w = (double)w_tau[u];
-        sp[u] = softplus_f64(w);
-        sw[u] = logistic_f64(w);
+        if (cell == CFC_CELL_TAU_DECAY) {
+            tau_decay_consts(w, dt, sp[u], sw[u]);  // sp = decay, sw = d decay / d tau / decay
+        } else {
+            sp[u] = softplus_f64(w);
+            sw[u] = logistic_f64(w);
+        }
         const double d = (double)h_seq[(b * K + (K - 1)) * (long long)H + u] - (double)y[b * H + u];
         delta[u] = d;
         lpart += 0.5 * d * d;
@@ -133,15 +149,23 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_kernel(
         part = group_sum(part, G);
         if (i < H && sub == 0) {
             const double a = (double)bias[i] + part;
-            const double g = 1.0 / (1.0 + exp(sp[i] * a * dt));
             const double c = tanh(a);
             const double d = delta[cur * H + i];
-            const double dz = d * ((double)hk[i] - c) * g * (1.0 - g);
-            const double da = d * (1.0 - g) * (1.0 - c * c) - dz * sp[i] * dt;
+            double g, da;
+            if (cell == CFC_CELL_TAU_DECAY) {
+                g = sp[i];
+                const double dg = d * ((double)hk[i] - c);  // dL/d(decay)
+                da = d * (1.0 - g) * (1.0 - c * c);
+                gwt += dg * g * sw[i];
+            } else {
+                g = 1.0 / (1.0 + exp(sp[i] * a * dt));
+                const double dz = d * ((double)hk[i] - c) * g * (1.0 - g);
+                da = d * (1.0 - g) * (1.0 - c * c) - dz * sp[i] * dt;
+                gwt += dz * (-a * dt) * sw[i];
+            }
             DA[k * H + i] = da;
             gate[i] = g;
             gb += da;
-            gwt += dz * (-a * dt) * sw[i];
         }
         __syncthreads();
         // delta_k = delta_{k+1} * g + W_rec^T da ; here i indexes the column j
@@ -281,18 +305,39 @@ __device__ __forceinline__ double inv_one_plus_exp(double z) {
     return fma(y, e, y);
 }
 
-// Per-lane constants of cell_gates: the gate lane evaluates 1/(1+e^(sp*dt*a)),
+// The gate of one unit for both cells, as constants of one set of formulas
+// (padding units get g = 1/2 and no gradient terms):
+//   g                 = vadd + vmul / (1 + e^(zmul a))
+//                       (gated: 1/(1+e^(softplus(w_tau) dt a)); tau-decay: decay)
+//   dz                = delta (h - c) g (1 - vmul g)
+//   dL/da             = delta (1 - g)(1 - c^2) - dz rho
+//   dL/dw_tau (dtau) += dz (beta - a alpha)
+struct UnitGate {
+    double zmul, vmul, vadd, rho, alpha, beta;
+};
+__device__ __forceinline__ UnitGate unit_gate(int cell, double w, double dt, bool valid) {
+    if (!valid) return UnitGate{0.0, 1.0, 0.0, 0.0, 0.0, 0.0};
+    if (cell == CFC_CELL_TAU_DECAY) {
+        double decay, q;
+        tau_decay_consts(w, dt, decay, q);
+        return UnitGate{0.0, 0.0, decay, 0.0, 0.0, q};
+    }
+    const double spdt = softplus_f64(w) * dt;
+    return UnitGate{spdt, 1.0, 0.0, spdt, dt * logistic_f64(w), 0.0};
+}
+
+// Per-lane constants of cell_gates: the gate lane evaluates the gate above,
 // the tanh lane 1 - 2/(1+e^(2a)).
 struct GateLane {
     double zmul, vmul, vadd;
     bool gate;
 };
-__device__ __forceinline__ GateLane gate_lane_consts(bool gate_lane, double spdt) {
-    return GateLane{gate_lane ? spdt : 2.0, gate_lane ? 1.0 : -2.0, gate_lane ? 0.0 : 1.0, gate_lane};
+__device__ __forceinline__ GateLane gate_lane_consts(bool gate_lane, const UnitGate& u) {
+    return GateLane{gate_lane ? u.zmul : 2.0, gate_lane ? u.vmul : -2.0, gate_lane ? u.vadd : 1.0, gate_lane};
 }
 
-// tanh(a) and sigmoid(-sp*a*dt) for the unit owned by a lane pair; each lane
-// evaluates one of the two and they swap.  Both lanes return both values.
+// tanh(a) and the gate for the unit owned by a lane pair; each lane evaluates
+// one of the two and they swap.  Both lanes return both values.
 __device__ __forceinline__ void cell_gates(double a, const GateLane& L, double& g, double& c) {
     const double r = inv_one_plus_exp(L.zmul * a);
     const double val = fma(r, L.vmul, L.vadd);
@@ -309,14 +354,14 @@ constexpr int kSmallZW = 2 * kSmall;             // [x | h_prev] width
 constexpr int kSmallZS = kSmallZW + 2;
 
 __host__ __device__ constexpr size_t small_fwd_lds_bytes() {
-    return (size_t)8 * kSmallFwdKW * kSmall + (size_t)8 * 3 * kSmall +
+    return (size_t)8 * kSmallFwdKW * kSmall + (size_t)8 * 2 * kSmall +
            (size_t)4 * kSmallFwdKW * kSmallXS;
 }
 // The backward always stages kSmallBwdMaxK rows (rows >= K are zero), so its
 // contractions run without row guards.
 constexpr int kSmallGS = 64 + 4;  // row stride (floats) of a wave's gradient-tile buffer
 __host__ __device__ constexpr size_t small_bwd_lds_bytes() {
-    return (size_t)8 * kSmallBwdMaxK * kSmall + (size_t)8 * 2 * kSmall + 8 * 8 +
+    return (size_t)8 * kSmallBwdMaxK * kSmall + 8 * 8 +
            (size_t)4 * kSmallBwdMaxK * kSmallZS + (size_t)4 * 4 * 16 * kSmallGS;
 }
 
@@ -385,13 +430,12 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, double dt, int K, int n_in,
-    int H, float* __restrict__ h_seq) {
+    int H, float* __restrict__ h_seq, int cell) {
     constexpr int HP = kSmall, NP = kSmall, KW = kSmallFwdKW, XS = kSmallXS;
     extern __shared__ __align__(16) unsigned char smem[];
     double* U = reinterpret_cast<double*>(smem);  // [KW][HP]
     double* hb = U + KW * HP;                     // [2][HP]
-    double* spv = hb + 2 * HP;                    // [HP]
-    float* xs = reinterpret_cast<float*>(spv + HP);  // [KW][XS]
+    float* xs = reinterpret_cast<float*>(hb + 2 * HP);  // [KW][XS]
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const long long b = blockIdx.x;
@@ -420,10 +464,8 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
         const int valid = row < H ? min(max(H - 16 * jb, 0), 16) : 0;
         load_span_f64<16>(wr[r], w_rec + (long long)min(row, H - 1) * H + min(16 * jb, H - 1), valid);
     }
-    for (int u = t; u < HP; u += kThreads) {
-        spv[u] = u < H ? softplus_f64((double)w_tau[u]) : 0.0;
-        hb[u] = u < H ? (double)h0[b * H + u] : 0.0;
-    }
+    for (int u = t; u < HP; u += kThreads) hb[u] = u < H ? (double)h0[b * H + u] : 0.0;
+    const UnitGate ug = unit_gate(cell, o < H ? (double)w_tau[o] : 0.0, dt, o < H);
     double hprev = o < H ? (double)h0[b * H + o] : 0.0;
     const double bias_q0 = (2 * wave) * 16 + (lane & 15) < H ? (double)bias[(2 * wave) * 16 + (lane & 15)] : 0.0;
     const double bias_q1 = (2 * wave + 1) * 16 + (lane & 15) < H ? (double)bias[(2 * wave + 1) * 16 + (lane & 15)] : 0.0;
@@ -460,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
                     urow[16] = acc[kb][1][v] + bias_q1;
                 }
         }
-        const GateLane gl = gate_lane_consts(gate_lane, spv[o] * dt);
+        const GateLane gl = gate_lane_consts(gate_lane, ug);
         __syncthreads();
         // ---- serial recurrence through the window
         for (int kk = 0; kk < kw; ++kk) {
@@ -506,17 +548,17 @@ __device__ __forceinline__ void store_grad_f(float* p, double v, int accumulate)
 
 // Second half of a row's backward pass, shared by cfc_bwd_small_kernel and
 // cfc_fb_small_kernel.  On entry (after a barrier): AD[k][*] holds a_k for
-// k < K and 0 beyond, zs[k] holds [x_k | h_k-1] (rows >= K zero), spv/swv hold
-// softplus(w_tau) and sigmoid(w_tau), and delta is h_K - y of this lane's unit o
-// (computed from the float32 h_K).  Seeds the row's loss, runs the reverse
+// k < K and 0 beyond, zs[k] holds [x_k | h_k-1] (rows >= K zero), ug is the
+// gate of this lane's unit o, and delta is h_K - y of unit o (computed from the
+// float32 h_K).  Seeds the row's loss, runs the reverse
 // chain (AD[k] becomes dL/da_k), forms G = DA^T [X | H_prev] on the matrix
 // cores and writes the row [dW_in | dW_rec | db | dw_tau].  Optionally also
 // the input gradients of the row: gh0_row [H] = dL/dh_0 (the chain runs its
 // W_rec^T step once more, at k = 0) and gx_row [K][n_in] = DA W_in (a third
 // product on the matrix cores).
 __device__ __forceinline__ void small_reverse_and_grads(
-    const float* __restrict__ w_in, const float* __restrict__ w_rec, double dt, int K, int n_in, int H,
-    double delta, double* AD, const double* spv, const double* swv, double* red, const float* zs,
+    const float* __restrict__ w_in, const float* __restrict__ w_rec, int K, int n_in, int H,
+    double delta, double* AD, const UnitGate& ug, double* red, const float* zs,
     float* gst, float* __restrict__ row, float* __restrict__ loss_b, float* __restrict__ gx_row,
     float* __restrict__ gh0_row, int accumulate, int lane, int wave, int jb, int ib, int o,
     bool gate_lane) {
@@ -540,8 +582,7 @@ __device__ __forceinline__ void small_reverse_and_grads(
         for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
         if (lane == 0) red[wave] = l;
     }
-    const double sp_o = spv[o], sw_o = swv[o], spdt_o = sp_o * dt;
-    const GateLane gl = gate_lane_consts(gate_lane, spdt_o);
+    const GateLane gl = gate_lane_consts(gate_lane, ug);
     __syncthreads();
     if (wave == 0 && lane == 0 && loss_b) *loss_b = (float)(((red[0] + red[1]) + red[2]) + red[3]);
 
@@ -557,10 +598,10 @@ __device__ __forceinline__ void small_reverse_and_grads(
         }
         double g, c;
         cell_gates(a, gl, g, c);
-        const double dz = delta * (hk - c) * g * (1.0 - g);
-        const double da = delta * (1.0 - g) * (1.0 - c * c) - dz * spdt_o;
+        const double dz = delta * (hk - c) * g * fma(-ug.vmul, g, 1.0);
+        const double da = delta * (1.0 - g) * (1.0 - c * c) - dz * ug.rho;
         gb += da;
-        gwt += dz * (-a * dt) * sw_o;
+        gwt += dz * fma(-a, ug.alpha, ug.beta);
         if (!gate_lane) AD[k * HP + o] = da;
         __syncthreads();
         if (k == 0 && !gh0_row) break;
@@ -718,14 +759,13 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
     const float* __restrict__ y, double dt, int K, int n_in, int H, float* __restrict__ scratch,
-    float* __restrict__ loss, float* __restrict__ grad_x, float* __restrict__ grad_h0, int accumulate) {
+    float* __restrict__ loss, float* __restrict__ grad_x, float* __restrict__ grad_h0, int accumulate,
+    int cell) {
     constexpr int HP = kSmall, NP = kSmall, ZW = kSmallZW, ZS = kSmallZS;
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int KP = kSmallBwdMaxK;
     double* AD = reinterpret_cast<double*>(smem);  // [KP][HP]: a, then dL/da
-    double* spv = AD + KP * HP;                    // [HP]
-    double* swv = spv + HP;                        // [HP]
-    double* red = swv + HP;                        // [8]
+    double* red = AD + KP * HP;                    // [8]
     float* zs = reinterpret_cast<float*>(red + 8);  // [KP][ZS] = [x_k | h_k]
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -761,11 +801,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     stage_rows(zs + NP, ZS, h0 + b * H, H, 1, H, 1, HP, t);
     if (K > 1) stage_rows(zs + ZS + NP, ZS, h_seq + b * K * (long long)H, H, K - 1, H, KP - 1, HP, t);
     else stage_rows(zs + ZS + NP, ZS, h_seq, H, 0, H, KP - 1, HP, t);
-    for (int u = t; u < HP; u += kThreads) {
-        const double w = u < H ? (double)w_tau[u] : 0.0;
-        spv[u] = u < H ? softplus_f64(w) : 0.0;
-        swv[u] = u < H ? logistic_f64(w) : 0.0;
-    }
+    const UnitGate ug = unit_gate(cell, o < H ? (double)w_tau[o] : 0.0, dt, o < H);
     const double bias_q0 = (2 * wave) * 16 + (lane & 15) < H ? (double)bias[(2 * wave) * 16 + (lane & 15)] : 0.0;
     const double bias_q1 = (2 * wave + 1) * 16 + (lane & 15) < H ? (double)bias[(2 * wave + 1) * 16 + (lane & 15)] : 0.0;
     __syncthreads();
@@ -801,7 +837,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
 
     const double delta =
         o < H ? (double)h_seq[(b * K + K - 1) * (long long)H + o] - (double)y[b * H + o] : 0.0;
-    small_reverse_and_grads(w_in, w_rec, dt, K, n_in, H, delta, AD, spv, swv, red, zs, gst, scratch + b * N,
+    small_reverse_and_grads(w_in, w_rec, K, n_in, H, delta, AD, ug, red, zs, gst, scratch + b * N,
                             loss ? loss + b : nullptr, grad_x ? grad_x + b * K * (long long)n_in : nullptr,
                             grad_h0 ? grad_h0 + b * H : nullptr, accumulate, lane, wave, jb, ib, o, gate_lane);
 }
@@ -819,13 +855,12 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ y, double dt,
     int K, int n_in, int H, float* __restrict__ h_seq, float* __restrict__ scratch,
-    float* __restrict__ loss, float* __restrict__ grad_x, float* __restrict__ grad_h0, int accumulate) {
+    float* __restrict__ loss, float* __restrict__ grad_x, float* __restrict__ grad_h0, int accumulate,
+    int cell) {
     constexpr int HP = kSmall, NP = kSmall, ZS = kSmallZS, KP = kSmallBwdMaxK;
     extern __shared__ __align__(16) unsigned char smem[];
     double* AD = reinterpret_cast<double*>(smem);  // [KP][HP]: W_in x_k + b, then a_k, then dL/da_k
-    double* spv = AD + KP * HP;                    // [HP]
-    double* swv = spv + HP;                        // [HP]
-    double* red = swv + HP;                        // [8]
+    double* red = AD + KP * HP;                    // [8]
     double* hb = red + 8;                          // [2][HP] h_k exchange
     float* zs = reinterpret_cast<float*>(hb + 2 * HP);  // [KP][ZS] = [x_k | h_k-1]
 
@@ -844,12 +879,8 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     stage_rows(zs, ZS, x + b * K * (long long)n_in, n_in, K, n_in, KP, NP, t);
     stage_rows(zs + NP, ZS, h0 + b * H, H, 1, H, 1, HP, t);
     stage_rows(zs + K * ZS + NP, ZS, h0, H, 0, H, KP - K, HP, t);
-    for (int u = t; u < HP; u += kThreads) {
-        const double w = u < H ? (double)w_tau[u] : 0.0;
-        spv[u] = u < H ? softplus_f64(w) : 0.0;
-        swv[u] = u < H ? logistic_f64(w) : 0.0;
-        hb[u] = u < H ? (double)h0[b * H + u] : 0.0;
-    }
+    for (int u = t; u < HP; u += kThreads) hb[u] = u < H ? (double)h0[b * H + u] : 0.0;
+    const UnitGate ug = unit_gate(cell, o < H ? (double)w_tau[o] : 0.0, dt, o < H);
     const double bias_q0 = (2 * wave) * 16 + (lane & 15) < H ? (double)bias[(2 * wave) * 16 + (lane & 15)] : 0.0;
     const double bias_q1 = (2 * wave + 1) * 16 + (lane & 15) < H ? (double)bias[(2 * wave + 1) * 16 + (lane & 15)] : 0.0;
     __syncthreads();
@@ -900,7 +931,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
         load_span_f64<16>(wr[r], w_rec + (long long)min(row, H - 1) * H + min(16 * jb, H - 1), valid);
     }
     double hprev = o < H ? (double)h0[b * H + o] : 0.0;
-    const GateLane gl = gate_lane_consts(gate_lane, spv[o] * dt);
+    const GateLane gl = gate_lane_consts(gate_lane, ug);
     __syncthreads();
     int cur = 0;
     for (int k = 0; k < K; ++k) {
@@ -941,7 +972,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
 
     // ---- backward from the float32 h_K, as the separate backward sees it
     const double delta = o < H ? (double)(float)hprev - (double)y[b * H + o] : 0.0;
-    small_reverse_and_grads(w_in, w_rec, dt, K, n_in, H, delta, AD, spv, swv, red, zs, gst, scratch + b * N,
+    small_reverse_and_grads(w_in, w_rec, K, n_in, H, delta, AD, ug, red, zs, gst, scratch + b * N,
                             loss ? loss + b : nullptr, grad_x ? grad_x + b * K * (long long)n_in : nullptr,
                             grad_h0 ? grad_h0 + b * H : nullptr, accumulate, lane, wave, jb, ib, o, gate_lane);
 }
@@ -1101,7 +1132,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, double dt, int B, int K, int n_in,
-    int H, float* __restrict__ h_seq) {
+    int H, float* __restrict__ h_seq, int cell) {
     extern __shared__ __align__(16) unsigned char smem[];
     float* zx = reinterpret_cast<float*>(smem);                        // [256][16] x_k
     double* zh = reinterpret_cast<double*>(smem + 4 * kLarge * kLR);   // [256][16] h_k
@@ -1117,7 +1148,10 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
         for (int v = 0; v < 4; ++v) {
             const int i = lunit(wave, tb, s + 4 * v);
             bias_v[tb][v] = i < H ? (double)bias[i] : 0.0;
-            spdt_v[tb][v] = i < H ? softplus_f64((double)w_tau[i]) * dt : 0.0;
+            // gated: softplus(w_tau) dt; tau-decay: the decay itself
+            double decay = 0.0, q;
+            if (cell == CFC_CELL_TAU_DECAY && i < H) tau_decay_consts((double)w_tau[i], dt, decay, q);
+            spdt_v[tb][v] = i >= H ? 0.0 : cell == CFC_CELL_TAU_DECAY ? decay : softplus_f64((double)w_tau[i]) * dt;
         }
     stage_t(zh, h0, H, r0, B, H, t);
     stage_t(zx, x, (long long)K * n_in, r0, B, n_in, t);
@@ -1144,7 +1178,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
             for (int v = 0; v < 4; ++v) {
                 const int i = lunit(wave, tb, s + 4 * v);
                 const double a = acc[tb][v] + bias_v[tb][v];
-                const double g = inv_one_plus_exp(spdt_v[tb][v] * a);
+                const double g = cell == CFC_CELL_TAU_DECAY ? spdt_v[tb][v] : inv_one_plus_exp(spdt_v[tb][v] * a);
                 const double c = fma(-2.0, inv_one_plus_exp(2.0 * a), 1.0);
                 double* hp = zh + zidx(i, r);
                 *hp = fma(g, *hp - c, c);  // g*h + (1-g)*c
@@ -1166,20 +1200,21 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
     }
 }
 
-template <bool FULL>
+template <bool FULL, bool TAU>
 __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
     const float* __restrict__ y, double dt, int B, int K, int n_in, int H, float* __restrict__ scratch,
     float* __restrict__ loss, float* __restrict__ grad_x, float* __restrict__ grad_h0) {
+    constexpr int cell = TAU ? CFC_CELL_TAU_DECAY : CFC_CELL_GATED;
     extern __shared__ __align__(16) unsigned char smem[];
     float* zx = reinterpret_cast<float*>(smem);                             // [256][16] x_k
     double* zh = reinterpret_cast<double*>(smem + 4 * kLarge * kLR);        // [256][16] h_k
     double* dab = reinterpret_cast<double*>(smem + 12 * kLarge * kLR);      // [256][16] dL/da_k
     double* ubias = reinterpret_cast<double*>(smem + 20 * kLarge * kLR);    // [256] per-unit b,
-    double* uspdt = ubias + kLarge;                                          // softplus(w_tau)*dt,
-    double* usw = uspdt + kLarge;                                            // sigmoid(w_tau)
+    double* uspdt = ubias + kLarge;  // softplus(w_tau)*dt (tau-decay: the decay),
+    double* usw = uspdt + kLarge;    // sigmoid(w_tau) (tau-decay: d decay / d tau / decay)
     double* gwt = usw + kLarge;  // [256][16] dL/dw_tau sums; each element owned by one lane
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int s = lane >> 4, r = lane & 15;
@@ -1196,8 +1231,15 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
         const bool ok = u < H;
         const double w = ok ? (double)w_tau[u] : 0.0;
         ubias[u] = ok ? (double)bias[u] : 0.0;
-        uspdt[u] = ok ? softplus_f64(w) * dt : 0.0;
-        usw[u] = ok ? logistic_f64(w) : 0.0;
+        if (cell == CFC_CELL_TAU_DECAY) {
+            double decay = 0.0, q = 0.0;
+            if (ok) tau_decay_consts(w, dt, decay, q);
+            uspdt[u] = decay;
+            usw[u] = q;
+        } else {
+            uspdt[u] = ok ? softplus_f64(w) * dt : 0.0;
+            usw[u] = ok ? logistic_f64(w) : 0.0;
+        }
     }
     double delta[4][4];
     double lsum = 0.0;
@@ -1241,22 +1283,30 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
         large_preact<FULL>(acc, w_in, w_rec, n_in, H, zx, zh, wave, lane);
         double gk[4][4];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+            for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int i = lunit(wave, tb, s + 4 * v);
-                const double spdt = uspdt[i];
-                const double a = acc[tb][v] + ubias[i];
-                const double g = inv_one_plus_exp(spdt * a);
-                const double c = fma(-2.0, inv_one_plus_exp(2.0 * a), 1.0);
-                const double hp = zh[zidx(i, r)];
-                const double d = delta[tb][v];
-                const double dz = d * (hp - c) * g * (1.0 - g);
-                const double da = d * (1.0 - g) * (1.0 - c * c) - dz * spdt;
-                gwt[zidx(i, r)] += dz * (-a * dt) * usw[i];
-                gk[tb][v] = g;
-                dab[zidx(i, r)] = da;
-            }
+                for (int v = 0; v < 4; ++v) {
+                    const int i = lunit(wave, tb, s + 4 * v);
+                    const double spdt = uspdt[i];
+                    const double a = acc[tb][v] + ubias[i];
+                    const double c = fma(-2.0, inv_one_plus_exp(2.0 * a), 1.0);
+                    const double hp = zh[zidx(i, r)];
+                    const double d = delta[tb][v];
+                    double g, da;
+                    if constexpr (TAU) {
+                        g = spdt;
+                        const double dg = d * (hp - c);  // dL/d(decay)
+                        da = d * (1.0 - g) * (1.0 - c * c);
+                        gwt[zidx(i, r)] += dg * g * usw[i];
+                    } else {
+                        g = inv_one_plus_exp(spdt * a);
+                        const double dz = d * (hp - c) * g * (1.0 - g);
+                        da = d * (1.0 - g) * (1.0 - c * c) - dz * spdt;
+                        gwt[zidx(i, r)] += dz * (-a * dt) * usw[i];
+                    }
+                    gk[tb][v] = g;
+                    dab[zidx(i, r)] = da;
+                }
         __syncthreads();  // dab of step k complete
         // park dL/da_k of the 16 rows in their scratch tails, row-contiguous
 #pragma unroll 4
@@ -1549,6 +1599,7 @@ int check_params(const cfc_params_t* p) {
     if (!p || !p->w_in || !p->w_rec || !p->b || !p->w_tau) return CFC_ERR_NULL;
     if (p->n_in < 1 || p->n_hid < 1) return CFC_ERR_DIM;
     if (p->n_in > kMaxIn || p->n_hid > kMaxHid) return CFC_ERR_UNSUPPORTED;
+    if (p->cell != CFC_CELL_GATED && p->cell != CFC_CELL_TAU_DECAY) return CFC_ERR_UNSUPPORTED;
     return CFC_OK;
 }
 
@@ -1567,10 +1618,11 @@ void set_kernel_attributes() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        for (const void* f : {reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, false>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, true>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true>)})
+            (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     });
 }
 
@@ -1626,18 +1678,18 @@ extern "C" int cfc_forward(const cfc_params_t* params, const float* x, const flo
     if (n_in <= kSmall && H <= kSmall) {
         hipLaunchKernelGGL(cfc_fwd_small_kernel, dim3(B), dim3(kThreads), small_fwd_lds_bytes(), stream,
                            params->w_in, params->w_rec, params->b, params->w_tau, x, h0, (double)dt, K,
-                           n_in, H, h_seq);
+                           n_in, H, h_seq, params->cell);
         return launch_status();
     }
     const long long groups = ((long long)B + kLR - 1) / kLR;
     if (large_full(params))
         hipLaunchKernelGGL(cfc_fwd_large_kernel<true>, dim3((unsigned)groups), dim3(kThreads), large_fwd_lds_bytes(),
                            stream, params->w_in, params->w_rec, params->b, params->w_tau, x, h0, (double)dt, B,
-                           K, n_in, H, h_seq);
+                           K, n_in, H, h_seq, params->cell);
     else
         hipLaunchKernelGGL(cfc_fwd_large_kernel<false>, dim3((unsigned)groups), dim3(kThreads), large_fwd_lds_bytes(),
                            stream, params->w_in, params->w_rec, params->b, params->w_tau, x, h0, (double)dt, B,
-                           K, n_in, H, h_seq);
+                           K, n_in, H, h_seq, params->cell);
     return launch_status();
 }
 
@@ -1672,24 +1724,23 @@ extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const fl
     if (small) {
         hipLaunchKernelGGL(cfc_bwd_small_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
                            params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, K,
-                           n_in, H, scratch, loss, grad_x, grad_h0, flags == CFC_ACCUMULATE ? 1 : 0);
+                           n_in, H, scratch, loss, grad_x, grad_h0, flags == CFC_ACCUMULATE ? 1 : 0,
+                           params->cell);
         return launch_status();
     }
     if (large) {
         const long long groups = ((long long)B + kLR - 1) / kLR;
-        if (large_full(params))
-            hipLaunchKernelGGL(cfc_bwd_large_kernel<true>, dim3((unsigned)groups), dim3(kThreads), lds, stream,
-                               params->w_in, params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt,
-                               B, K, n_in, H, scratch, loss, grad_x, grad_h0);
-        else
-            hipLaunchKernelGGL(cfc_bwd_large_kernel<false>, dim3((unsigned)groups), dim3(kThreads), lds, stream,
-                               params->w_in, params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt,
-                               B, K, n_in, H, scratch, loss, grad_x, grad_h0);
+        const bool tau = params->cell == CFC_CELL_TAU_DECAY;
+        auto kern = large_full(params) ? (tau ? &cfc_bwd_large_kernel<true, true> : &cfc_bwd_large_kernel<true, false>)
+                                       : (tau ? &cfc_bwd_large_kernel<false, true> : &cfc_bwd_large_kernel<false, false>);
+        hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kThreads), lds, stream, params->w_in, params->w_rec,
+                           params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, K, n_in, H, scratch, loss,
+                           grad_x, grad_h0);
         return launch_status();
     }
     hipLaunchKernelGGL(cfc_bwd_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
                        params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, K, n_in,
-                       H, scratch, loss, grad_x, grad_h0, flags == CFC_ACCUMULATE ? 1 : 0);
+                       H, scratch, loss, grad_x, grad_h0, flags == CFC_ACCUMULATE ? 1 : 0, params->cell);
     return launch_status();
 }
 
@@ -1719,7 +1770,8 @@ extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, 
         set_kernel_attributes();
         hipLaunchKernelGGL(cfc_fb_small_kernel, dim3(B), dim3(kThreads), small_fb_lds_bytes(), stream,
                            params->w_in, params->w_rec, params->b, params->w_tau, x, h0, y, (double)dt, K,
-                           n_in, H, h_seq, scratch, loss, grad_x, grad_h0, flags == CFC_ACCUMULATE ? 1 : 0);
+                           n_in, H, h_seq, scratch, loss, grad_x, grad_h0, flags == CFC_ACCUMULATE ? 1 : 0,
+                           params->cell);
         return launch_status();
     }
     // other shapes: the two directions as separate launches on the same stream;

@@ -20,11 +20,17 @@
  * Task 5 (scratch zeroed once per step, K invocations accumulate, reducer
  * before the optimizer).
  *
- * The cell (per unit i, elementwise; w_tau plays the per-unit role of the
- * pages' tau[n_hid]):
+ * The cell (per unit i, elementwise), one of two:
+ *   CFC_CELL_GATED (w_tau plays the per-unit role of the pages' tau[n_hid]):
  *     a      = W_in x_k + W_rec h_k + b
  *     g      = sigmoid(-softplus(w_tau) * a * dt)
  *     h_k+1  = g * h_k + (1 - g) * tanh(a)
+ *   CFC_CELL_TAU_DECAY, the cell the pages print ("K-loop Parallelization
+ *   Implementation Plan", Task 2 forward and Task 3 backward kernels; w_tau
+ *   holds tau):
+ *     g      = exp(-dt / max(tau, 1e-6))           (a per-unit constant)
+ *     h_k+1  = g * h_k + (1 - g) * tanh(a)
+ *     with dL/dtau = 0 where tau <= 1e-6 (the pages' guard)
  * and the loss of row b is  L_b = 1/2 |h_K - y_b|^2.
  *
  * Conventions shared by every call
@@ -74,9 +80,14 @@ extern "C" {
 #define CFC_MAX_N_IN 256
 #define CFC_MAX_N_HID 256
 
+/* Cell types (cfc_params_t.cell). */
+#define CFC_CELL_GATED 0
+#define CFC_CELL_TAU_DECAY 1
+
 /* The cell's parameters, all device pointers:
  *   w_in  [n_hid, n_in]  row-major     w_rec [n_hid, n_hid] row-major
- *   b     [n_hid]                      w_tau [n_hid]                        */
+ *   b     [n_hid]                      w_tau [n_hid] (tau for CFC_CELL_TAU_DECAY)
+ * and the cell type (any other value: CFC_ERR_UNSUPPORTED). */
 typedef struct cfc_params {
     const float *w_in;
     const float *w_rec;
@@ -84,13 +95,15 @@ typedef struct cfc_params {
     const float *w_tau;
     int n_in;
     int n_hid;
+    int cell;
 } cfc_params_t;
 
 /* Length N of one per-batch gradient row:  N = n_hid * (n_in + n_hid + 2).
  * Row layout: [ dL/dW_in (n_hid x n_in, row-major) | dL/dW_rec (n_hid x n_hid,
  * row-major) | dL/db (n_hid) | dL/dw_tau (n_hid) ] -- the pages' four scratch
  * tensors (grad_w_in, grad_w_rec, grad_b, grad_tau; Task 4) laid end to end so
- * one reducer launch covers them all.  Returns -1 if a dimension is < 1 or
+ * one reducer launch covers them all.  For CFC_CELL_TAU_DECAY the last slot
+ * holds dL/dtau.  Returns -1 if a dimension is < 1 or
  * the product overflows. */
 long long cfc_scratch_row_len(int n_in, int n_hid);
 

@@ -15,8 +15,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
 FAKE = 0x10000          # never dereferenced: every call below fails validation first
 
 
-def _params(n_in=8, n_hid=16, base=FAKE):
-    return C.CfcParams(base, base + 0x100000, base + 0x200000, base + 0x300000, n_in, n_hid)
+def _params(n_in=8, n_hid=16, base=FAKE, cell=0):
+    return C.CfcParams(base, base + 0x100000, base + 0x200000, base + 0x300000, n_in, n_hid, cell)
 
 
 @pytest.fixture(scope="module")
@@ -73,6 +73,9 @@ def test_forward_validation(lib):
     assert _fwd(lib, _params(), dt=float("inf")) == C.CFC_ERR_DT
     assert _fwd(lib, _params(n_in=257)) == C.CFC_ERR_UNSUPPORTED
     assert _fwd(lib, _params(n_hid=300)) == C.CFC_ERR_UNSUPPORTED
+    # unknown cell type
+    assert _fwd(lib, _params(cell=2)) == C.CFC_ERR_UNSUPPORTED
+    assert _fwd(lib, _params(cell=-1)) == C.CFC_ERR_UNSUPPORTED
     # output overlapping an input: h_seq [2,3,16] starting inside x
     assert _fwd(lib, _params(), h_seq=FAKE + 0x400000 + 8) == C.CFC_ERR_OVERLAP
     # h_seq overlapping the weights
@@ -86,6 +89,7 @@ def test_backward_validation(lib):
     assert _bwd(lib, _params(), flags=7) == C.CFC_ERR_DIM
     assert _bwd(lib, _params(), dt=float("-inf")) == C.CFC_ERR_DT
     assert _bwd(lib, _params(n_in=512)) == C.CFC_ERR_UNSUPPORTED
+    assert _bwd(lib, _params(cell=7)) == C.CFC_ERR_UNSUPPORTED
     # LDS bound: K * (12 H + 4 n_in) + 40 H + 2048 <= 160 KiB
     assert _bwd(lib, _params(n_in=128, n_hid=128), K=77) == C.CFC_ERR_UNSUPPORTED
     assert _bwd(lib, _params(n_in=256, n_hid=256), K=38) == C.CFC_ERR_UNSUPPORTED
@@ -120,6 +124,7 @@ def test_forward_backward_validation(lib):
     assert _fb(lib, _params(), flags=2) == C.CFC_ERR_DIM
     assert _fb(lib, _params(), dt=float("nan")) == C.CFC_ERR_DT
     assert _fb(lib, _params(n_hid=257)) == C.CFC_ERR_UNSUPPORTED
+    assert _fb(lib, _params(cell=3)) == C.CFC_ERR_UNSUPPORTED
     assert _fb(lib, _params(n_in=128, n_hid=128), K=77) == C.CFC_ERR_UNSUPPORTED
     assert _fb(lib, _params(n_in=256, n_hid=256), K=38) == C.CFC_ERR_UNSUPPORTED
     # outputs against inputs, and against each other
@@ -148,6 +153,14 @@ def test_reduce_validation(lib):
     assert lib.reduce_axis0(None, 4, 8, FAKE, None) == C.CFC_ERR_NULL
     assert lib.reduce_axis0(FAKE, 4, 8, None, None) == C.CFC_ERR_NULL
     assert lib.reduce_axis0(FAKE, 4, 8, FAKE + 16, None) == C.CFC_ERR_OVERLAP
+
+
+def test_python_binding_rejects_unknown_cell():
+    import torch
+    t = torch.zeros(4)
+    with pytest.raises(ValueError, match="cell must be one of"):
+        C.cfc_forward(t.view(2, 2), t.view(2, 2), t[:2], t[:2], t.view(1, 1, 4), t.view(2, 2)[:1], 1.0,
+                      cell="leaky")
 
 
 def test_product_path_never_imports_the_oracle():
