@@ -83,7 +83,7 @@ def cpu_baseline(inp, budget_s=10.0):
 
     def leg(rows, threads, budget):
         sub = type(inp)(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x[:rows], inp.h0[:rows], inp.y[:rows],
-                        inp.dt)
+                        inp.dt, inp.cell)
         n, t0 = 0, time.perf_counter()
         while True:
             O.cfc_step(sub, threads=threads)
@@ -148,7 +148,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (to scale PMC byte counters)")
-    ap.add_argument("--workload", default="train", choices=["train", "smoke", "tiny", "large"],
+    ap.add_argument("--workload", default="train",
+                    choices=["train", "smoke", "tiny", "large", "tau_train", "tau_tiny"],
                     help="which seeded workload one step runs (the metric is quoted on 'train')")
     ap.add_argument("--reduce-sweep", action="store_true",
                     help="also time reduce_axis0 alone, cache-flushed, over a range of sizes")
@@ -187,7 +188,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4}))
         return
 
-    cfg = {"train": W.TRAIN, "smoke": W.SMOKE, "tiny": W.TINY, "large": W.LARGE}[args.workload]
+    cfg = {"train": W.TRAIN, "smoke": W.SMOKE, "tiny": W.TINY, "large": W.LARGE, "tau_train": W.TAU_TRAIN,
+           "tau_tiny": W.TAU_TINY}[args.workload]
+    cell = cfg.cell
     inp = W.make_cfc_inputs(cfg)
     t = lambda a: torch.from_numpy(a).to(dev)
     w_in, w_rec, b, w_tau, x, h0, y = map(t, (inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x, inp.h0, inp.y))
@@ -205,10 +208,10 @@ def main():
     def step_separate(ev=None):
         if ev is not None:
             ev[0].record()
-        C.cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, h_seq=h_seq)
+        C.cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, h_seq=h_seq, cell=cell)
         if ev is not None:
             ev[1].record()
-        C.cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, scratch=scratch, loss=loss)
+        C.cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, scratch=scratch, loss=loss, cell=cell)
         if ev is not None:
             ev[2].record()
         C.reduce_axis0(scratch, out=out)
@@ -218,7 +221,8 @@ def main():
     def step_fused(ev=None):
         if ev is not None:
             ev[0].record()
-        C.cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt, h_seq=h_seq, scratch=scratch, loss=loss)
+        C.cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt, h_seq=h_seq, scratch=scratch, loss=loss,
+                               cell=cell)
         if ev is not None:
             ev[1].record()
         C.reduce_axis0(scratch, out=out)
@@ -233,7 +237,7 @@ def main():
         if ev is not None:
             ev[0].record()
         C.cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt, h_seq=h_seq, scratch=scratch, loss=loss,
-                               grad_x=grad_x, grad_h0=grad_h0)
+                               grad_x=grad_x, grad_h0=grad_h0, cell=cell)
         if ev is not None:
             ev[1].record()
         C.reduce_axis0(scratch, out=out)
@@ -243,11 +247,11 @@ def main():
     def step_separate_ig(ev=None):
         if ev is not None:
             ev[0].record()
-        C.cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, h_seq=h_seq)
+        C.cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, h_seq=h_seq, cell=cell)
         if ev is not None:
             ev[1].record()
         C.cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, scratch=scratch, loss=loss,
-                       grad_x=grad_x, grad_h0=grad_h0)
+                       grad_x=grad_x, grad_h0=grad_h0, cell=cell)
         if ev is not None:
             ev[2].record()
         C.reduce_axis0(scratch, out=out)
@@ -260,7 +264,7 @@ def main():
             ev[0].record()
         scratch.zero_()
         C.cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt, h_seq=h_seq, scratch=scratch, loss=loss,
-                               accumulate=True)
+                               accumulate=True, cell=cell)
         C.reduce_axis0(scratch, out=out)
         if ev is not None:
             ev[1].record()
@@ -347,7 +351,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "B": B, "K": K, "n_in": n_in, "n_hid": H, "dt": dt,
+        "config": {"workload": cfg.name, "cell": cell, "B": B, "K": K, "n_in": n_in, "n_hid": H, "dt": dt,
                    "scratch_N": N, "io_dtype": "f32", "seed": cfg.seed},
         "roofline": roof,
         "path": args.path,

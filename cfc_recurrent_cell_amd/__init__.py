@@ -19,7 +19,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["cfc_forward", "cfc_backward", "cfc_forward_backward", "reduce_axis0",
-           "cfc_scratch_row_len", "CfcError", "load_library"]
+           "reduce_axis0_split_workspace", "cfc_scratch_row_len", "CfcError", "load_library"]
 
 
 def cfc_scratch_row_len(n_in: int, n_hid: int) -> int:
@@ -164,15 +164,45 @@ def cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt: float, h_seq=None,
     return h_seq, scratch, loss
 
 
-def reduce_axis0(per_batch, out=None, stream=None):
-    """out[N] = column sums of per_batch [B, N] (overwrites ``out``)."""
+def reduce_axis0(per_batch, out=None, stream=None, leading_axes: int = 1, split: bool = False,
+                 workspace=None):
+    """Column sums over the leading axis (overwrites ``out``).
+
+    ``per_batch`` is contiguous float32 on the GPU.  Its first ``leading_axes``
+    dimensions are merged into the reduced axis B and the rest into the
+    column axis N -- e.g. a [B, heads, E, H, H] scratch reduced over batch and
+    heads is reduce_axis0(t, leading_axes=2) with B = B*heads and N = E*H*H
+    (sizing N from the wrong axes reads past the buffer; here both come from
+    the tensor's shape).  ``out`` gets shape per_batch.shape[leading_axes:].
+    ``split=True`` uses reduce_axis0_split (narrow rows over a long leading
+    axis); its workspace is allocated here unless given as a uint8 tensor."""
+    import math
     import torch
     lib = load_library()
-    B, N = per_batch.shape
-    _dev_f32(per_batch, "per_batch", (B, N))
+    if not 1 <= leading_axes <= per_batch.dim():
+        raise ValueError(f"leading_axes must be in [1, {per_batch.dim()}], got {leading_axes}")
+    _dev_f32(per_batch, "per_batch")
+    lead, tail = tuple(per_batch.shape[:leading_axes]), tuple(per_batch.shape[leading_axes:])
+    B, N = math.prod(lead), math.prod(tail)
     if out is None:
-        out = torch.empty((N,), dtype=torch.float32, device=per_batch.device)
-    _dev_f32(out, "out", (N,))
-    _check("reduce_axis0", lib.reduce_axis0(per_batch.data_ptr(), B, N, out.data_ptr(),
-                                            _stream(per_batch.device, stream)))
+        out = torch.empty(tail, dtype=torch.float32, device=per_batch.device)
+    _dev_f32(out, "out", tail)
+    s = _stream(per_batch.device, stream)
+    if not split:
+        _check("reduce_axis0", lib.reduce_axis0(per_batch.data_ptr(), B, N, out.data_ptr(), s))
+        return out
+    need = int(lib.reduce_axis0_split_workspace(B, N))
+    if need < 0:
+        raise ValueError(f"invalid reduce size B={B} N={N}")
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=per_batch.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("reduce_axis0_split", lib.reduce_axis0_split(per_batch.data_ptr(), B, N, out.data_ptr(), ws_ptr,
+                                                        ws_bytes, s))
     return out
+
+
+def reduce_axis0_split_workspace(B: int, N: int) -> int:
+    """Bytes of workspace reduce_axis0_split needs for [B, N] (0: none)."""
+    return int(load_library().reduce_axis0_split_workspace(B, N))

@@ -66,6 +66,10 @@ def load_library(path: str = LIB_PATH):
                                          i, vp]
     lib.reduce_axis0.restype = i
     lib.reduce_axis0.argtypes = [vp, ll, ll, vp, vp]
+    lib.reduce_axis0_split_workspace.restype = ll
+    lib.reduce_axis0_split_workspace.argtypes = [ll, ll]
+    lib.reduce_axis0_split.restype = i
+    lib.reduce_axis0_split.argtypes = [vp, ll, ll, vp, vp, ll, vp]
     lib.cfc_status_string.restype = ctypes.c_char_p
     lib.cfc_status_string.argtypes = [i]
     _lib = lib

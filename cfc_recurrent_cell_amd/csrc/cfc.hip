@@ -1567,6 +1567,53 @@ __global__ __launch_bounds__(kThreads) void reduce_axis0_kernel(const float* __r
     }
 }
 
+// Split reduce for narrow rows (N <= 256) over a long leading axis ("Custom
+// Kernel Optimization Implementation Plan", Tasks 4-5: a batch-parallel first
+// phase of block partial sums, then a final reduce of the partials; here both
+// phases keep a fixed summation order).  Workgroup p sums rows
+// [p R, min(B, (p+1) R)) of all N columns.  Threads t < T = (256 / N) N read
+// consecutive elements (consecutive floats for consecutive threads): thread t
+// owns column t % N and starts at row t / N of the chunk, stepping RP = T / N
+// rows, 8 rows' loads in flight, accumulating in float64.  The RP sums of each
+// column are then combined by a fixed pairwise tree through LDS, and thread
+// j < N writes the chunk's sum of column j.  Phase 1 reads the float32 input
+// and writes float64 partials [P][N]; phase 2 is the same kernel over the
+// partials as one chunk, writing float32.
+template <typename TIn, typename TOut>
+__global__ __launch_bounds__(kThreads) void reduce_rows_narrow_kernel(const TIn* __restrict__ in, long long B,
+                                                                      int N, long long R,
+                                                                      TOut* __restrict__ out) {
+    __shared__ double red[kThreads];
+    const int t = threadIdx.x;
+    const int RP = kThreads / N, T = RP * N;
+    const long long r0 = (long long)blockIdx.x * R;
+    const long long r1 = min(B, r0 + R);
+    double acc = 0.0;
+    if (t < T) {
+        const TIn* p = in + t % N;
+        long long r = r0 + t / N;
+        for (; r + 7LL * RP < r1; r += 8LL * RP) {
+            TIn q[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) q[u] = p[(r + (long long)u * RP) * N];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += (double)q[u];
+        }
+        for (; r < r1; r += RP) acc += (double)p[r * N];
+    }
+    red[t] = acc;
+    __syncthreads();
+    // slot q = t / N adds slot q + w when q is a multiple of 2w: a fixed tree
+    for (int w = 1; w < RP; w *= 2) {
+        if (t < T) {
+            const int q = t / N;
+            if (q % (2 * w) == 0 && q + w < RP) red[t] += red[t + w * N];
+        }
+        __syncthreads();
+    }
+    if (t < N) out[(long long)blockIdx.x * N + t] = (TOut)red[t];
+}
+
 // ---------------------------------------------------------- host helpers
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -1783,6 +1830,51 @@ extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, 
     rc = cfc_forward(params, x, h0, dt, B, K, h_seq, stream);
     if (rc) return rc;
     return cfc_backward(params, x, h0, h_seq, y, dt, B, K, scratch, loss, grad_x, grad_h0, flags, stream);
+}
+
+// Chunking of the split reduce; it depends only on (B, N), so the summation
+// order -- and the result -- is the same on every device.  At most 1024
+// chunks and 64 K partials (512 KB) for the one-workgroup second phase; each
+// chunk is at least 8 passes of RP rows.
+constexpr long long kSplitMaxChunks = 1024;
+constexpr long long kSplitMaxPartials = 65536;
+struct SplitPlan {
+    long long R, P;
+};
+inline SplitPlan split_plan(long long B, long long N) {
+    const long long RP = kThreads / N;
+    const long long chunks = std::min(kSplitMaxChunks, kSplitMaxPartials / N);
+    long long R = std::max((B + chunks - 1) / chunks, 8 * RP);
+    R = (R + RP - 1) / RP * RP;
+    return SplitPlan{R, B > 0 ? (B + R - 1) / R : 0};
+}
+
+extern "C" long long reduce_axis0_split_workspace(long long B, long long N) {
+    if (B < 0 || N < 0) return -1;
+    long long n;
+    if (!mul_ok(B, N, &n)) return -1;
+    if (N == 0 || N > kThreads) return 0;
+    const SplitPlan sp = split_plan(B, N);
+    return sp.P >= 2 ? sp.P * N * (long long)sizeof(double) : 0;
+}
+
+extern "C" int reduce_axis0_split(const float* per_batch, long long B, long long N, float* out,
+                                  void* workspace, long long workspace_bytes, hipStream_t stream) {
+    const long long need = reduce_axis0_split_workspace(B, N);
+    if (need < 0) return CFC_ERR_DIM;
+    if (need == 0) return reduce_axis0(per_batch, B, N, out, stream);
+    if (!out || !per_batch || !workspace) return CFC_ERR_NULL;
+    if (workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 7) != 0) return CFC_ERR_DIM;
+    const Range ws{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + (uintptr_t)need};
+    const Range in = span(per_batch, B * N), o = span(out, N);
+    if (overlap(o, in) || overlap(ws, in) || overlap(ws, o)) return CFC_ERR_OVERLAP;
+    const SplitPlan sp = split_plan(B, N);
+    double* part = static_cast<double*>(workspace);
+    hipLaunchKernelGGL((reduce_rows_narrow_kernel<float, double>), dim3((unsigned)sp.P), dim3(kThreads), 0, stream,
+                       per_batch, B, (int)N, sp.R, part);
+    hipLaunchKernelGGL((reduce_rows_narrow_kernel<double, float>), dim3(1), dim3(kThreads), 0, stream,
+                       (const double*)part, sp.P, (int)N, sp.P, out);
+    return launch_status();
 }
 
 extern "C" int reduce_axis0(const float* per_batch, long long B, long long N, float* out,

@@ -178,6 +178,31 @@ int cfc_forward_backward(const cfc_params_t *params, const float *x, const float
 int reduce_axis0(const float *per_batch, long long B, long long N, float *out,
                  hipStream_t stream);
 
+/* Bytes of workspace reduce_axis0_split needs for a [B, N] input: 0 when it
+ * runs the one-pass reduce_axis0 instead (N > 256, or too few rows to split),
+ * -1 if B or N is negative or B*N*4 overflows. */
+long long reduce_axis0_split_workspace(long long B, long long N);
+
+/* Column sum for narrow rows over a long leading axis -- e.g. N = 3 columns
+ * over B = 524288 rows, the pages' bias-gradient reduce ("Custom Kernel
+ * Optimization Implementation Plan", Tasks 4-5: batch-parallel partial sums,
+ * then a final reduce of the partials).  reduce_axis0 gives such a shape a
+ * single workgroup; here up to 1024 workgroups each sum a chunk of rows into
+ * float64 partials in `workspace`, and one more sums the partials, both in a
+ * fixed order that depends only on (B, N).
+ *   per_batch, B, N, out   as for reduce_axis0 (out is overwritten)
+ *   workspace  device memory of at least reduce_axis0_split_workspace(B, N)
+ *              bytes, 8-byte aligned, owned by the caller, not overlapping
+ *              per_batch or out; its contents on entry are ignored and on
+ *              return are unspecified.  May be NULL when that size is 0.
+ * The result is the float32 rounding of a float64 sum, bitwise reproducible
+ * for a given (B, N); its grouping differs from reduce_axis0's, so the two
+ * may differ in the last float32 bit.
+ * Returns a CFC_* status: CFC_ERR_DIM also when the workspace is too small
+ * or misaligned. */
+int reduce_axis0_split(const float *per_batch, long long B, long long N, float *out,
+                       void *workspace, long long workspace_bytes, hipStream_t stream);
+
 /* Static text for a status code (never NULL). */
 const char *cfc_status_string(int code);
 

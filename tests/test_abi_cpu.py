@@ -27,7 +27,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _lib.declared_symbols()
     assert set(names) == {"cfc_scratch_row_len", "cfc_forward", "cfc_backward",
-                          "cfc_forward_backward", "reduce_axis0", "cfc_status_string"}
+                          "cfc_forward_backward", "reduce_axis0", "reduce_axis0_split",
+                          "reduce_axis0_split_workspace", "cfc_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -153,6 +154,45 @@ def test_reduce_validation(lib):
     assert lib.reduce_axis0(None, 4, 8, FAKE, None) == C.CFC_ERR_NULL
     assert lib.reduce_axis0(FAKE, 4, 8, None, None) == C.CFC_ERR_NULL
     assert lib.reduce_axis0(FAKE, 4, 8, FAKE + 16, None) == C.CFC_ERR_OVERLAP
+
+
+def test_split_reduce_workspace_sizes(lib):
+    """Chunking depends only on (B, N): 256 // N rows per pass, at least 8
+    passes per chunk, at most 1024 chunks and 64 K partials."""
+    ws = lib.reduce_axis0_split_workspace
+    # N = 3: 85 rows per pass, chunks of max(ceil(524288/1024), 680) = 680 rows -> 772 chunks
+    assert ws(524288, 3) == 772 * 3 * 8
+    assert ws(10, 3) == 0                    # one chunk: the one-pass reduce runs
+    assert ws(100000, 300) == 0              # wider than 256: one pass
+    assert ws(100000, 0) == 0
+    assert ws(-1, 3) == -1 and ws(3, -1) == -1
+    assert ws(2**40, 2**40) == -1            # B*N*4 overflows
+    # N = 256: one row per pass, 8-row chunks, 256 chunks at most (64 K partials):
+    # 20000 rows -> chunks of ceil(20000/256) = 79 rows -> 254 chunks
+    assert ws(20000, 256) == 254 * 256 * 8
+    assert ws(2048, 256) == 256 * 256 * 8
+    assert ws(16, 256) == 2 * 256 * 8
+
+
+def test_split_reduce_validation(lib):
+    big = FAKE + 0x10000000
+    f = lib.reduce_axis0_split
+    assert f(FAKE, 524288, 3, big, None, 0, None) == C.CFC_ERR_NULL          # workspace needed
+    assert f(None, 524288, 3, big, big + 0x100000, 18528, None) == C.CFC_ERR_NULL
+    assert f(FAKE, 524288, 3, big, big + 0x100000, 18527, None) == C.CFC_ERR_DIM   # too small
+    assert f(FAKE, 524288, 3, big, big + 0x100004, 18528, None) == C.CFC_ERR_DIM   # misaligned
+    assert f(FAKE, 524288, 3, big, FAKE + 64, 18528, None) == C.CFC_ERR_OVERLAP    # over the input
+    assert f(FAKE, 524288, 3, big, big + 8, 18528, None) == C.CFC_ERR_OVERLAP      # over out
+    assert f(FAKE, -5, 3, big, None, 0, None) == C.CFC_ERR_DIM
+
+
+def test_reduce_binding_checks_leading_axes():
+    import torch
+    t = torch.zeros(2, 3, 4)
+    with pytest.raises(ValueError, match="leading_axes"):
+        C.reduce_axis0(t, leading_axes=0)
+    with pytest.raises(ValueError, match="leading_axes"):
+        C.reduce_axis0(t, leading_axes=4)
 
 
 def test_python_binding_rejects_unknown_cell():
