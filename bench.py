@@ -112,29 +112,37 @@ def cpu_baseline(inp, budget_s=10.0):
 def reduce_sweep(torch, C, W, dev, reps=20):
     """reduce_axis0 alone at several [B, N], timed with HIP events per launch,
     with a 512 MiB buffer overwritten between launches so that neither the L2
-    nor the 256 MB MALL holds the input (HBM-resident numbers)."""
+    nor the 256 MB MALL holds the input (HBM-resident numbers).  Narrow shapes
+    (N <= 256 over many rows) are timed with both the one-pass reduce_axis0
+    and the two-phase reduce_axis0_split (its two launches together)."""
     flush = torch.empty(128 * 1024 * 1024, device=dev)
-    shapes = [(W.REDUCE.B, W.REDUCE.N), (256, 33024), (1024, 131584), (8192, 131584)]
+    shapes = [(W.REDUCE.B, W.REDUCE.N, False), (256, 33024, False), (1024, 131584, False), (8192, 131584, False),
+              (524288, 3, False), (524288, 3, True), (262144, 64, False), (262144, 64, True),
+              (65536, 256, False), (65536, 256, True)]
     out = []
-    for B, N in shapes:
+    for B, N, split in shapes:
         a = torch.randn(B, N, device=dev)
         o = torch.empty(N, device=dev)
-        C.reduce_axis0(a, out=o)
+        ws = None
+        if split:
+            ws = torch.empty((C.reduce_axis0_split_workspace(B, N),), dtype=torch.uint8, device=dev)
+        run = lambda: C.reduce_axis0(a, out=o, split=split, workspace=ws)
+        run()
         times = []
         for _ in range(reps):
             flush.fill_(1.0)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            C.reduce_axis0(a, out=o)
+            run()
             e1.record()
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1))
         times.sort()
         med = times[len(times) // 2]
         gbps = (B * N + N) * 4 / (med * 1e-3) / 1e9
-        out.append({"B": B, "N": N, "bytes": (B * N + N) * 4, "median_ms": med, "GB_per_s": gbps,
-                    "frac_hbm": gbps / PEAK_HBM_GBPS})
-        del a, o
+        out.append({"B": B, "N": N, "entry": "reduce_axis0_split" if split else "reduce_axis0",
+                    "bytes": (B * N + N) * 4, "median_ms": med, "GB_per_s": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS})
+        del a, o, ws
     del flush
     return out
 

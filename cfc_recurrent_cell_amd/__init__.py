@@ -18,7 +18,8 @@ from ._lib import (  # noqa: F401
     declared_symbols, load_library, status_string,
 )
 
-__all__ = ["cfc_forward", "cfc_backward", "cfc_forward_backward", "reduce_axis0",
+__all__ = ["cfc_forward", "cfc_backward", "cfc_backward_window", "cfc_backward_windows",
+           "cfc_forward_backward", "reduce_axis0",
            "reduce_axis0_split_workspace", "cfc_scratch_row_len", "CfcError", "load_library"]
 
 
@@ -124,6 +125,66 @@ def cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, scratch=None
     if want_inputs:
         return scratch, loss, grad_x, grad_h0
     return scratch, loss
+
+
+def cfc_backward_window(w_in, w_rec, b, w_tau, x, h0, h_seq, dt: float, k_begin: int, k_end: int, scratch,
+                        y=None, delta_in=None, delta_out=None, loss=None, grad_x=None,
+                        accumulate: bool = False, stream=None, cell: str = "gated"):
+    """Backward over steps [k_begin, k_end) of the forward that produced
+    h_seq (see include/cfc.h): dL/dh_k_end comes in as ``delta_in`` (or, when
+    None, from the loss seed h_K - y), dL/dh_k_begin goes out in ``delta_out``
+    (may be ``delta_in`` itself), the window's parameter gradient goes into
+    ``scratch`` (overwritten, or added with ``accumulate``).  Returns
+    (scratch, loss, grad_x, delta_out)."""
+    lib = load_library()
+    p = _params(w_in, w_rec, b, w_tau, cell)
+    B, K, _ = x.shape
+    N = cfc_scratch_row_len(p.n_in, p.n_hid)
+    _dev_f32(x, "x", (B, K, p.n_in))
+    _dev_f32(h0, "h0", (B, p.n_hid))
+    _dev_f32(h_seq, "h_seq", (B, K, p.n_hid))
+    _dev_f32(scratch, "scratch", (B, N))
+    for t, name, shape in ((y, "y", (B, p.n_hid)), (delta_in, "delta_in", (B, p.n_hid)),
+                           (delta_out, "delta_out", (B, p.n_hid)), (loss, "loss", (B,)),
+                           (grad_x, "grad_x", (B, K, p.n_in))):
+        if t is not None:
+            _dev_f32(t, name, shape)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    flags = CFC_ACCUMULATE if accumulate else CFC_OVERWRITE
+    _check("cfc_backward_window", lib.cfc_backward_window(
+        ctypes.byref(p), x.data_ptr(), h0.data_ptr(), h_seq.data_ptr(), ptr(y), ptr(delta_in), float(dt), B, K,
+        int(k_begin), int(k_end), scratch.data_ptr(), ptr(loss), ptr(grad_x), ptr(delta_out), flags,
+        _stream(x.device, stream)))
+    return scratch, loss, grad_x, delta_out
+
+
+def cfc_backward_windows(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, window: int, scratch=None,
+                         loss=None, grad_x=None, grad_h0=None, stream=None, cell: str = "gated"):
+    """The whole backward as windows of ``window`` steps, from the last to the
+    first: the last window is seeded from y and overwrites the scratch, each
+    earlier one takes the carried dL/dh and accumulates.  For K beyond the
+    one-call backward's on-chip limit.  Returns (scratch, loss, grad_x,
+    grad_h0) with grad_h0 = dL/dh_0 (allocated here if not given)."""
+    import torch
+    B, K, _ = x.shape
+    if window < 1:
+        raise ValueError("window must be >= 1")
+    H = w_rec.shape[0]
+    if scratch is None:
+        scratch = torch.empty((B, cfc_scratch_row_len(w_in.shape[1], H)), dtype=torch.float32, device=x.device)
+    if loss is None:
+        loss = torch.empty((B,), dtype=torch.float32, device=x.device)
+    delta = grad_h0 if grad_h0 is not None else torch.empty((B, H), dtype=torch.float32, device=x.device)
+    k_end = K
+    while k_end > 0:
+        k_begin = max(0, k_end - window)
+        seeded = k_end == K
+        cfc_backward_window(w_in, w_rec, b, w_tau, x, h0, h_seq, dt, k_begin, k_end, scratch,
+                            y=y if seeded else None, delta_in=None if seeded else delta, delta_out=delta,
+                            loss=loss if seeded else None, grad_x=grad_x, accumulate=not seeded, stream=stream,
+                            cell=cell)
+        k_end = k_begin
+    return scratch, loss, grad_x, delta
 
 
 def cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt: float, h_seq=None, scratch=None,

@@ -61,6 +61,9 @@ def load_library(path: str = LIB_PATH):
     lib.cfc_forward.argtypes = [ctypes.POINTER(CfcParams), vp, vp, f, i, i, vp, vp]
     lib.cfc_backward.restype = i
     lib.cfc_backward.argtypes = [ctypes.POINTER(CfcParams), vp, vp, vp, vp, f, i, i, vp, vp, vp, vp, i, vp]
+    lib.cfc_backward_window.restype = i
+    lib.cfc_backward_window.argtypes = [ctypes.POINTER(CfcParams), vp, vp, vp, vp, vp, f, i, i, i, i, vp, vp, vp,
+                                        vp, i, vp]
     lib.cfc_forward_backward.restype = i
     lib.cfc_forward_backward.argtypes = [ctypes.POINTER(CfcParams), vp, vp, vp, f, i, i, vp, vp, vp, vp, vp,
                                          i, vp]

@@ -71,8 +71,22 @@ __device__ __forceinline__ double group_sum(double v, int G) {
 }
 
 // ----------------------------------------------------------- backward
-// LDS: DA [K][H] f64 | delta [2][H] f64 | gate [H] f64 | sp [H] | sw [H] |
-//      red [256] f64 | xs [K][n_in] f32 | hp [K][H] f32   (hp[k] = h_k)
+// The steps one backward launch covers: steps k0 .. k0 + Kw - 1 of a K-step
+// forward (row b's x_k at x + (b K + k) n_in, h_k+1 at h_seq + (b K + k) H,
+// h_0 in h0).  The gradient flowing into the window's last state h_k0+Kw is
+// delta_in [B, H], or, when delta_in is NULL (then k0 + Kw == K), the loss
+// seed h_K - y.  delta_out [B, H] (may be NULL; may be delta_in itself, since
+// each element is read before the one writer of that element writes it)
+// receives dL/dh_k0 -- dL/dh_0 for the first window.  Kernels index steps
+// relative to k0.
+struct BwdWindow {
+    int K, k0, Kw;
+    const float* delta_in;
+    float* delta_out;
+};
+
+// LDS: DA [Kw][H] f64 | delta [2][H] f64 | gate [H] f64 | sp [H] | sw [H] |
+//      red [256] f64 | xs [Kw][n_in] f32 | hp [Kw][H] f32   (hp[k] = h_k0+k)
 __host__ __device__ inline size_t bwd_lds_bytes(int K, int n_in, int H) {
     return (size_t)8 * K * H + (size_t)8 * 5 * H + 8 * kThreads + (size_t)4 * K * n_in +
            (size_t)4 * K * H;
@@ -87,9 +101,10 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
-    const float* __restrict__ y, double dt, int K, int n_in, int H, float* __restrict__ scratch,
-    float* __restrict__ loss, float* __restrict__ grad_x, float* __restrict__ grad_h0, int accumulate,
-    int cell) {
+    const float* __restrict__ y, double dt, BwdWindow win, int n_in, int H, float* __restrict__ scratch,
+    float* __restrict__ loss, float* __restrict__ grad_x, int accumulate, int cell) {
+    const int K = win.Kw;  // steps of this launch; indices below are relative to win.k0
+    const long long Kf = win.K, k0 = win.k0;
     extern __shared__ __align__(16) unsigned char smem[];
     double* DA = reinterpret_cast<double*>(smem);
     double* delta = DA + (size_t)K * H;
@@ -116,14 +131,19 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_kernel(
             sp[u] = softplus_f64(w);
             sw[u] = logistic_f64(w);
         }
-        const double d = (double)h_seq[(b * K + (K - 1)) * (long long)H + u] - (double)y[b * H + u];
-        delta[u] = d;
-        lpart += 0.5 * d * d;
+        if (win.delta_in) {
+            delta[u] = (double)win.delta_in[b * H + u];
+        } else {
+            const double d = (double)h_seq[(b * Kf + (Kf - 1)) * H + u] - (double)y[b * H + u];
+            delta[u] = d;
+            lpart += 0.5 * d * d;
+        }
     }
-    const float* xb = x + b * K * (long long)n_in;
+    const float* xb = x + (b * Kf + k0) * n_in;
     for (int e = t; e < K * n_in; e += kThreads) xs[e] = xb[e];
-    for (int u = t; u < H; u += kThreads) hp[u] = h0[b * H + u];
-    const float* hsb = h_seq + b * K * (long long)H;
+    const float* hstart = k0 == 0 ? h0 + b * H : h_seq + (b * Kf + k0 - 1) * H;
+    for (int u = t; u < H; u += kThreads) hp[u] = hstart[u];
+    const float* hsb = h_seq + (b * Kf + k0) * H;
     for (int e = t; e < (K - 1) * H; e += kThreads) hp[H + e] = hsb[e];
     red[t] = lpart;
     __syncthreads();
@@ -199,11 +219,12 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_kernel(
         store_grad(rrec + (long long)H * H + i, gb, accumulate);
         store_grad(rrec + (long long)H * H + H + i, gwt, accumulate);
     }
-    // input gradients: dL/dh_0 is the delta left after step 0; dL/dx_k = W_in^T da_k
-    if (grad_h0)
-        for (int u = t; u < H; u += kThreads) grad_h0[b * H + u] = (float)delta[cur * H + u];
+    // input gradients: dL/dh_k0 is the delta left after the window's first
+    // step; dL/dx_k = W_in^T da_k
+    if (win.delta_out)
+        for (int u = t; u < H; u += kThreads) win.delta_out[b * H + u] = (float)delta[cur * H + u];
     if (grad_x) {
-        float* gx = grad_x + b * K * (long long)n_in;
+        float* gx = grad_x + (b * Kf + k0) * n_in;
         for (int e = t; e < K * n_in; e += kThreads) {
             const int k = e / n_in, j = e - k * n_in;
             double s = 0.0;
@@ -758,10 +779,11 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
-    const float* __restrict__ y, double dt, int K, int n_in, int H, float* __restrict__ scratch,
-    float* __restrict__ loss, float* __restrict__ grad_x, float* __restrict__ grad_h0, int accumulate,
-    int cell) {
+    const float* __restrict__ y, double dt, BwdWindow win, int n_in, int H, float* __restrict__ scratch,
+    float* __restrict__ loss, float* __restrict__ grad_x, int accumulate, int cell) {
     constexpr int HP = kSmall, NP = kSmall, ZW = kSmallZW, ZS = kSmallZS;
+    const int K = win.Kw;  // steps of this launch; indices below are relative to win.k0
+    const long long Kf = win.K, k0 = win.k0;
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int KP = kSmallBwdMaxK;
     double* AD = reinterpret_cast<double*>(smem);  // [KP][HP]: a, then dL/da
@@ -796,10 +818,10 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
         load_span_f64<ZW / 4>(wb[q], src, valid);
     }
 
-    // ---- stage [x_k | h_k] for every step (h_0 = h0, h_k = h_seq[k-1])
-    stage_rows(zs, ZS, x + b * K * (long long)n_in, n_in, K, n_in, KP, NP, t);
-    stage_rows(zs + NP, ZS, h0 + b * H, H, 1, H, 1, HP, t);
-    if (K > 1) stage_rows(zs + ZS + NP, ZS, h_seq + b * K * (long long)H, H, K - 1, H, KP - 1, HP, t);
+    // ---- stage [x_k | h_k] for every step of the window (h_0 = h0, h_k = h_seq[k-1])
+    stage_rows(zs, ZS, x + (b * Kf + k0) * n_in, n_in, K, n_in, KP, NP, t);
+    stage_rows(zs + NP, ZS, k0 == 0 ? h0 + b * H : h_seq + (b * Kf + k0 - 1) * H, H, 1, H, 1, HP, t);
+    if (K > 1) stage_rows(zs + ZS + NP, ZS, h_seq + (b * Kf + k0) * H, H, K - 1, H, KP - 1, HP, t);
     else stage_rows(zs + ZS + NP, ZS, h_seq, H, 0, H, KP - 1, HP, t);
     const UnitGate ug = unit_gate(cell, o < H ? (double)w_tau[o] : 0.0, dt, o < H);
     const double bias_q0 = (2 * wave) * 16 + (lane & 15) < H ? (double)bias[(2 * wave) * 16 + (lane & 15)] : 0.0;
@@ -835,11 +857,14 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
         }
     }
 
-    const double delta =
-        o < H ? (double)h_seq[(b * K + K - 1) * (long long)H + o] - (double)y[b * H + o] : 0.0;
+    const double delta = o >= H ? 0.0
+                         : win.delta_in ? (double)win.delta_in[b * H + o]
+                                        : (double)h_seq[(b * Kf + Kf - 1) * H + o] - (double)y[b * H + o];
     small_reverse_and_grads(w_in, w_rec, K, n_in, H, delta, AD, ug, red, zs, gst, scratch + b * N,
-                            loss ? loss + b : nullptr, grad_x ? grad_x + b * K * (long long)n_in : nullptr,
-                            grad_h0 ? grad_h0 + b * H : nullptr, accumulate, lane, wave, jb, ib, o, gate_lane);
+                            loss && !win.delta_in ? loss + b : nullptr,
+                            grad_x ? grad_x + (b * Kf + k0) * n_in : nullptr,
+                            win.delta_out ? win.delta_out + b * H : nullptr, accumulate, lane, wave, jb, ib, o,
+                            gate_lane);
 }
 
 // Forward and backward of one row in one workgroup (n_in, n_hid <= 128,
@@ -1205,9 +1230,12 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
-    const float* __restrict__ y, double dt, int B, int K, int n_in, int H, float* __restrict__ scratch,
-    float* __restrict__ loss, float* __restrict__ grad_x, float* __restrict__ grad_h0) {
+    const float* __restrict__ y, double dt, int B, BwdWindow win, int n_in, int H, float* __restrict__ scratch,
+    float* __restrict__ loss, float* __restrict__ grad_x) {
     constexpr int cell = TAU ? CFC_CELL_TAU_DECAY : CFC_CELL_GATED;
+    const int K = win.Kw;  // steps of this launch; indices below are relative to win.k0
+    const long long Kf = win.K, k0 = win.k0;
+    float* __restrict__ grad_h0 = win.delta_out;
     extern __shared__ __align__(16) unsigned char smem[];
     float* zx = reinterpret_cast<float*>(smem);                             // [256][16] x_k
     double* zh = reinterpret_cast<double*>(smem + 4 * kLarge * kLR);        // [256][16] h_k
@@ -1249,9 +1277,10 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
         for (int v = 0; v < 4; ++v) {
             const int i = lunit(wave, tb, s + 4 * v);
             const bool ok = i < H;
-            const double d = (ok && row_ok) ? (double)h_seq[(b_own * K + K - 1) * (long long)H + i] -
-                                                  (double)y[b_own * H + i]
-                                            : 0.0;
+            double d = 0.0;
+            if (ok && row_ok)
+                d = win.delta_in ? (double)win.delta_in[b_own * H + i]
+                                 : (double)h_seq[(b_own * Kf + Kf - 1) * H + i] - (double)y[b_own * H + i];
             delta[tb][v] = d;
             lsum += 0.5 * d * d;
             gwt[zidx(i, r)] = 0.0;
@@ -1261,15 +1290,15 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     lsum += __shfl_xor(lsum, 32);
     if (lane < 16) dab[wave * 16 + lane] = lsum;
     __syncthreads();
-    if (t < kLR && loss && r0 + t < B)
+    if (t < kLR && loss && !win.delta_in && r0 + t < B)
         loss[r0 + t] = (float)(((dab[t] + dab[16 + t]) + dab[32 + t]) + dab[48 + t]);
 
     // inputs of step k (x_k and h_k-1 of the 16 rows), fetched one step ahead
     float xr[kLR], hr[kLR];
     auto fetch_step = [&](int k) {
-        fetch_t(xr, x + (long long)k * n_in, (long long)K * n_in, r0, B, n_in, t);
-        if (k == 0) fetch_t(hr, h0, H, r0, B, H, t);
-        else fetch_t(hr, h_seq + (long long)(k - 1) * H, (long long)K * H, r0, B, H, t);
+        fetch_t(xr, x + (k0 + k) * n_in, Kf * n_in, r0, B, n_in, t);
+        if (k0 + k == 0) fetch_t(hr, h0, H, r0, B, H, t);
+        else fetch_t(hr, h_seq + (k0 + k - 1) * H, Kf * H, r0, B, H, t);
     };
     fetch_step(K - 1);
     for (int k = K - 1; k >= 0; --k) {
@@ -1367,7 +1396,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                 acc3[3] = mfma_f64((double)w4.w, bz, acc3[3]);
             }
             if (row_ok) {
-                float* gx = grad_x + (b_own * K + k) * (long long)n_in;
+                float* gx = grad_x + (b_own * Kf + k0 + k) * n_in;
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
@@ -1378,7 +1407,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
             }
         }
     }
-    if (grad_h0 && row_ok) {  // after step 0, delta is dL/dh_0
+    if (grad_h0 && row_ok) {  // after the window's first step, delta is dL/dh_k0
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
@@ -1409,9 +1438,9 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                 if (t < H) {
                     const long long q = 2 * ((long long)kk * H + t);
                     dv = __builtin_bit_cast(double, ((unsigned long long)tq[q + 1] << 32) | tq[q]);
-                    hv = kk == 0 ? h0[b * H + t] : h_seq[(b * K + kk - 1) * (long long)H + t];
+                    hv = k0 + kk == 0 ? h0[b * H + t] : h_seq[(b * Kf + k0 + kk - 1) * H + t];
                 }
-                if (t < n_in) xv = x[(b * K + kk) * (long long)n_in + t];
+                if (t < n_in) xv = x[(b * Kf + k0 + kk) * n_in + t];
             }
             pd[kk] = dv;
             px[kk] = xv;
@@ -1740,39 +1769,51 @@ extern "C" int cfc_forward(const cfc_params_t* params, const float* x, const flo
     return launch_status();
 }
 
-extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const float* h0,
-                            const float* h_seq, const float* y, float dt, int B, int K,
-                            float* scratch, float* loss, float* grad_x, float* grad_h0, int flags,
-                            hipStream_t stream) {
+namespace {
+// Validation and dispatch shared by cfc_backward (one window covering all K
+// steps, seeded from y) and cfc_backward_window.
+int backward_window(const cfc_params_t* params, const float* x, const float* h0, const float* h_seq,
+                    const float* y, const float* delta_in, float dt, int B, int K, int k_begin, int k_end,
+                    float* scratch, float* loss, float* grad_x, float* delta_out, int flags, hipStream_t stream) {
     int rc = check_params(params);
     if (rc) return rc;
-    if (!x || !h0 || !h_seq || !y || !scratch) return CFC_ERR_NULL;
-    if (B < 1 || K < 1) return CFC_ERR_DIM;
+    if (!x || !h0 || !h_seq || !scratch) return CFC_ERR_NULL;
+    if (!delta_in && !y) return CFC_ERR_NULL;
+    if (B < 1 || K < 1 || k_begin < 0 || k_end > K || k_begin >= k_end) return CFC_ERR_DIM;
+    if (!delta_in && k_end != K) return CFC_ERR_DIM;  // the loss seed belongs to the last step
+    if (delta_in && loss) return CFC_ERR_DIM;          // the loss is the seeded window's
     if (flags != CFC_OVERWRITE && flags != CFC_ACCUMULATE) return CFC_ERR_DIM;
     if (!std::isfinite(dt)) return CFC_ERR_DT;
     const int n_in = params->n_in, H = params->n_hid;
+    const int Kw = k_end - k_begin;
     const long long N = cfc_scratch_row_len(n_in, H);
     long long nx, ns, nsc;
     if (N < 0 || !mul_ok((long long)B * K, n_in, &nx) || !mul_ok((long long)B * K, H, &ns) ||
         !mul_ok((long long)B, N, &nsc))
         return CFC_ERR_DIM;
-    const bool small = n_in <= kSmall && H <= kSmall && K <= kSmallBwdMaxK;
-    const bool large = !small && (n_in > kSmall || H > kSmall) && K <= kLargeBwdMaxK &&
+    const bool small = n_in <= kSmall && H <= kSmall && Kw <= kSmallBwdMaxK;
+    const bool large = !small && (n_in > kSmall || H > kSmall) && Kw <= kLargeBwdMaxK &&
                        flags == CFC_OVERWRITE;
-    const size_t lds = small ? small_bwd_lds_bytes() : large ? large_bwd_lds_bytes() : bwd_lds_bytes(K, n_in, H);
+    const size_t lds = small ? small_bwd_lds_bytes() : large ? large_bwd_lds_bytes() : bwd_lds_bytes(Kw, n_in, H);
     if (lds > kLdsBytes) return CFC_ERR_UNSUPPORTED;
+    const long long BH = (long long)B * H;
     const Range outs[] = {span(scratch, nsc), span(loss, loss ? B : 0), span(grad_x, grad_x ? nx : 0),
-                          span(grad_h0, grad_h0 ? (long long)B * H : 0)};
-    const Range ins[] = {span(x, nx), span(h0, (long long)B * H), span(h_seq, ns), span(y, (long long)B * H),
-                         span(params->w_in, (long long)H * n_in), span(params->w_rec, (long long)H * H),
-                         span(params->b, H), span(params->w_tau, H)};
-    if (!outputs_disjoint(outs, 4, ins, 8)) return CFC_ERR_OVERLAP;
+                          span(delta_out, delta_out && delta_out != delta_in ? BH : 0)};
+    const Range ins[] = {span(x, nx), span(h0, BH), span(h_seq, ns), span(y, y && !delta_in ? BH : 0),
+                         span(delta_in, delta_in ? BH : 0), span(params->w_in, (long long)H * n_in),
+                         span(params->w_rec, (long long)H * H), span(params->b, H), span(params->w_tau, H)};
+    if (!outputs_disjoint(outs, 4, ins, 9)) return CFC_ERR_OVERLAP;
+    if (delta_out && delta_out == delta_in) {  // in place: still disjoint from the other outputs
+        const Range d = span(delta_out, BH);
+        for (int o = 0; o < 3; ++o)
+            if (overlap(d, outs[o])) return CFC_ERR_OVERLAP;
+    }
+    const BwdWindow win{K, k_begin, Kw, delta_in, delta_out};
     set_kernel_attributes();
     if (small) {
         hipLaunchKernelGGL(cfc_bwd_small_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
-                           params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, K,
-                           n_in, H, scratch, loss, grad_x, grad_h0, flags == CFC_ACCUMULATE ? 1 : 0,
-                           params->cell);
+                           params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, win, n_in, H,
+                           scratch, loss, grad_x, flags == CFC_ACCUMULATE ? 1 : 0, params->cell);
         return launch_status();
     }
     if (large) {
@@ -1781,14 +1822,32 @@ extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const fl
         auto kern = large_full(params) ? (tau ? &cfc_bwd_large_kernel<true, true> : &cfc_bwd_large_kernel<true, false>)
                                        : (tau ? &cfc_bwd_large_kernel<false, true> : &cfc_bwd_large_kernel<false, false>);
         hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kThreads), lds, stream, params->w_in, params->w_rec,
-                           params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, K, n_in, H, scratch, loss,
-                           grad_x, grad_h0);
+                           params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, win, n_in, H, scratch, loss,
+                           grad_x);
         return launch_status();
     }
     hipLaunchKernelGGL(cfc_bwd_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
-                       params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, K, n_in,
-                       H, scratch, loss, grad_x, grad_h0, flags == CFC_ACCUMULATE ? 1 : 0, params->cell);
+                       params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, win, n_in,
+                       H, scratch, loss, grad_x, flags == CFC_ACCUMULATE ? 1 : 0, params->cell);
     return launch_status();
+}
+}  // namespace
+
+extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const float* h0,
+                            const float* h_seq, const float* y, float dt, int B, int K,
+                            float* scratch, float* loss, float* grad_x, float* grad_h0, int flags,
+                            hipStream_t stream) {
+    if (!y) return CFC_ERR_NULL;
+    return backward_window(params, x, h0, h_seq, y, nullptr, dt, B, K, 0, K, scratch, loss, grad_x, grad_h0,
+                           flags, stream);
+}
+
+extern "C" int cfc_backward_window(const cfc_params_t* params, const float* x, const float* h0,
+                                   const float* h_seq, const float* y, const float* delta_in, float dt,
+                                   int B, int K, int k_begin, int k_end, float* scratch, float* loss,
+                                   float* grad_x, float* delta_out, int flags, hipStream_t stream) {
+    return backward_window(params, x, h0, h_seq, y, delta_in, dt, B, K, k_begin, k_end, scratch, loss, grad_x,
+                           delta_out, flags, stream);
 }
 
 extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, const float* h0,

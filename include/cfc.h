@@ -75,7 +75,8 @@ extern "C" {
 
 /* Compiled limits: n_in and n_hid up to 256; the backward also needs
  * K * (12 * n_hid + 4 * n_in) + 40 * n_hid + 2048 bytes of LDS <= 160 KiB,
- * e.g. K <= 76 at n_in = n_hid = 128 and K <= 37 at n_in = n_hid = 256.
+ * e.g. K <= 76 at n_in = n_hid = 128 and K <= 37 at n_in = n_hid = 256
+ * (cfc_backward_window takes longer K in windows within that bound).
  * The forward has no limit on K. */
 #define CFC_MAX_N_IN 256
 #define CFC_MAX_N_HID 256
@@ -146,6 +147,40 @@ int cfc_backward(const cfc_params_t *params, const float *x, const float *h0,
                  const float *h_seq, const float *y, float dt, int B, int K,
                  float *scratch, float *loss, float *grad_x, float *grad_h0, int flags,
                  hipStream_t stream);
+
+/* The backward over a window of steps [k_begin, k_end) of a K-step forward,
+ * with the state gradient carried in and out -- for K beyond the backward's
+ * LDS bound (which then applies to k_end - k_begin), or to feed an upstream
+ * gradient dL/dh_K.  It generalises the pages' per-step backward ("K-loop
+ * Parallelization Implementation Plan", Task 3: grad_h_new in, grad_h_old
+ * out, parameter gradients accumulated into the scratch across the K calls
+ * of Task 5) from one step to a window of steps.
+ *   params, x, h0, h_seq, dt, B, K   as for cfc_backward (the whole forward)
+ *   0 <= k_begin < k_end <= K
+ *   delta_in  [B, n_hid] or NULL: dL/dh_k_end, the gradient flowing into the
+ *             window's last state.  NULL seeds it from the loss instead:
+ *             h_K - y, which needs k_end == K and y.
+ *   y         [B, n_hid], read only when delta_in is NULL (may be NULL otherwise)
+ *   scratch   [B, N]: this window's parameter gradient, CFC_OVERWRITE or
+ *             CFC_ACCUMULATE (flags); running the windows from the last to the
+ *             first, the first call overwriting and the others accumulating,
+ *             gives cfc_backward's scratch up to float32 rounding (each call
+ *             rounds once)
+ *   loss      [B] or NULL: L_b, only in the seeded window (must be NULL when
+ *             delta_in is given)
+ *   grad_x    [B, K, n_in] or NULL: dL/dx_k for the window's steps (the rest
+ *             of the array is not touched)
+ *   delta_out [B, n_hid] or NULL: dL/dh_k_begin -- the next window's
+ *             delta_in, or dL/dh_0 for k_begin = 0.  It may be the same buffer
+ *             as delta_in (every element is read before it is written).
+ * Windows of at most 64 steps at n_in, n_hid <= 128 (20 at wider shapes,
+ * overwrite mode) run the specialised kernels.
+ * Returns a CFC_* status: CFC_ERR_DIM for a bad window, a missing seed or a
+ * loss without one; CFC_ERR_UNSUPPORTED if the window exceeds the LDS bound. */
+int cfc_backward_window(const cfc_params_t *params, const float *x, const float *h0,
+                        const float *h_seq, const float *y, const float *delta_in, float dt,
+                        int B, int K, int k_begin, int k_end, float *scratch, float *loss,
+                        float *grad_x, float *delta_out, int flags, hipStream_t stream);
 
 /* cfc_forward followed by cfc_backward on the same inputs, in one call
  * ("K-loop Parallelization Implementation Plan", Tasks 2 and 3 back to back):

@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _lib.declared_symbols()
-    assert set(names) == {"cfc_scratch_row_len", "cfc_forward", "cfc_backward",
+    assert set(names) == {"cfc_scratch_row_len", "cfc_forward", "cfc_backward", "cfc_backward_window",
                           "cfc_forward_backward", "reduce_axis0", "reduce_axis0_split",
                           "reduce_axis0_split_workspace", "cfc_status_string"}
     for n in names:
@@ -136,6 +136,34 @@ def test_forward_backward_validation(lib):
     assert _fb(lib, _params(), loss=FAKE + 0x900000 + 4) == C.CFC_ERR_OVERLAP
     assert _fb(lib, _params(), grad_x=FAKE + 0x600000 + 4) == C.CFC_ERR_OVERLAP
     assert _fb(lib, _params(), grad_h0=FAKE + 0x500000) == C.CFC_ERR_OVERLAP
+
+
+def _win(lib, p, k_begin, k_end, K=6, y=FAKE + 0x700000, delta_in=None, delta_out=None, loss=None, flags=0,
+         scratch=FAKE + 0x900000):
+    return lib.cfc_backward_window(ctypes.byref(p), FAKE + 0x400000, FAKE + 0x500000, FAKE + 0x600000, y,
+                                   delta_in, 1.0, 2, K, k_begin, k_end, scratch, loss, None, delta_out, flags,
+                                   None)
+
+
+def test_backward_window_validation(lib):
+    p = _params()
+    D1, D2 = FAKE + 0xB00000, FAKE + 0xC00000
+    assert _win(lib, p, 2, 2) == C.CFC_ERR_DIM            # empty window
+    assert _win(lib, p, 3, 2) == C.CFC_ERR_DIM
+    assert _win(lib, p, -1, 6) == C.CFC_ERR_DIM
+    assert _win(lib, p, 0, 7) == C.CFC_ERR_DIM            # past K
+    assert _win(lib, p, 0, 4) == C.CFC_ERR_DIM            # seeded from y but not ending at K
+    assert _win(lib, p, 0, 6, y=None) == C.CFC_ERR_NULL   # no seed at all
+    assert _win(lib, p, 0, 4, y=None, delta_in=D1, loss=FAKE + 0xD00000) == C.CFC_ERR_DIM  # loss without seed
+    assert _win(lib, p, 0, 4, y=None, delta_in=D1, flags=5) == C.CFC_ERR_DIM
+    # delta_out partly over delta_in ([2,16] floats), or over the scratch
+    assert _win(lib, p, 0, 4, y=None, delta_in=D1, delta_out=D1 + 8) == C.CFC_ERR_OVERLAP
+    assert _win(lib, p, 0, 4, y=None, delta_in=D1, delta_out=FAKE + 0x900000 + 4) == C.CFC_ERR_OVERLAP
+    # delta_in over an output
+    assert _win(lib, p, 0, 4, y=None, delta_in=FAKE + 0x900000, delta_out=D2) == C.CFC_ERR_OVERLAP
+    # the window's own LDS bound: 64 steps of 128/128 fit, 77 do not
+    big = _params(n_in=128, n_hid=128)
+    assert _win(lib, big, 0, 77, K=200, y=None, delta_in=D1) == C.CFC_ERR_UNSUPPORTED
 
 
 def test_backward_lds_limit_matches_header(lib):
