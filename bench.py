@@ -157,7 +157,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (to scale PMC byte counters)")
     ap.add_argument("--workload", default="train",
-                    choices=["train", "smoke", "tiny", "large", "tau_train", "tau_tiny"],
+                    choices=["train", "smoke", "tiny", "large", "long", "tau_train", "tau_tiny"],
                     help="which seeded workload one step runs (the metric is quoted on 'train')")
     ap.add_argument("--reduce-sweep", action="store_true",
                     help="also time reduce_axis0 alone, cache-flushed, over a range of sizes")
@@ -166,7 +166,9 @@ def main():
                          "timing): for profiler runs whose per-kernel averages must match one variant")
     ap.add_argument("--input-grads", action="store_true",
                     help="the timed step also writes grad_x [B,K,n_in] and grad_h0 [B,H]")
-    ap.add_argument("--path", default=None, choices=["fused", "separate"],
+    ap.add_argument("--window", type=int, default=64,
+                    help="steps per window of the windows path")
+    ap.add_argument("--path", default=None, choices=["fused", "separate", "windows"],
                     help="fused: one cfc_forward_backward call; separate: cfc_forward + cfc_backward "
                          "(default: fused where that call is one kernel, i.e. n_in, n_hid <= 128 and K <= 64)")
     args = ap.parse_args()
@@ -196,8 +198,8 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4}))
         return
 
-    cfg = {"train": W.TRAIN, "smoke": W.SMOKE, "tiny": W.TINY, "large": W.LARGE, "tau_train": W.TAU_TRAIN,
-           "tau_tiny": W.TAU_TINY}[args.workload]
+    cfg = {"train": W.TRAIN, "smoke": W.SMOKE, "tiny": W.TINY, "large": W.LARGE, "long": W.LONG,
+           "tau_train": W.TAU_TRAIN, "tau_tiny": W.TAU_TINY}[args.workload]
     cell = cfg.cell
     inp = W.make_cfc_inputs(cfg)
     t = lambda a: torch.from_numpy(a).to(dev)
@@ -210,8 +212,13 @@ def main():
     loss = torch.empty((B,), device=dev)
     out = torch.empty((N,), device=dev)
 
+    one_call_bwd_ok = K * (12 * H + 4 * n_in) + 40 * H + 2048 <= 160 * 1024
+    if args.path == "windows" and args.input_grads:
+        print("--input-grads is not timed on the windows path", file=sys.stderr)
+        sys.exit(2)
     if args.path is None:
-        args.path = "fused" if (n_in <= 128 and H <= 128 and K <= 64) else "separate"
+        args.path = "fused" if (n_in <= 128 and H <= 128 and K <= 64) else \
+            "separate" if one_call_bwd_ok else "windows"
 
     def step_separate(ev=None):
         if ev is not None:
@@ -266,6 +273,23 @@ def main():
         if ev is not None:
             ev[3].record()
 
+    delta_carry = torch.empty((B, H), device=dev)
+
+    def step_windows(ev=None):
+        # forward, then the backward as windows of --window steps (dL/dh carried in place)
+        if ev is not None:
+            ev[0].record()
+        C.cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, h_seq=h_seq, cell=cell)
+        if ev is not None:
+            ev[1].record()
+        C.cfc_backward_windows(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, args.window, scratch=scratch, loss=loss,
+                               grad_h0=delta_carry, cell=cell)
+        if ev is not None:
+            ev[2].record()
+        C.reduce_axis0(scratch, out=out)
+        if ev is not None:
+            ev[3].record()
+
     def step_fused_accumulate(ev=None):
         # the pages' clear-then-accumulate form: explicit zero fill, then += gradient
         if ev is not None:
@@ -281,8 +305,8 @@ def main():
         """W warm-up steps, then K steps bracketed by a sync on both sides, with
         HIP events around every launch on the stream the launches use."""
         step = {"fused": step_fused, "separate": step_separate, "accumulate": step_fused_accumulate,
-                "fused_ig": step_fused_ig, "separate_ig": step_separate_ig}[path]
-        nev = {"fused": 3, "separate": 4, "accumulate": 2, "fused_ig": 3, "separate_ig": 4}[path]
+                "fused_ig": step_fused_ig, "separate_ig": step_separate_ig, "windows": step_windows}[path]
+        nev = {"fused": 3, "separate": 4, "accumulate": 2, "fused_ig": 3, "separate_ig": 4, "windows": 4}[path]
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
@@ -298,7 +322,7 @@ def main():
         per = lambda a, c: sum(e[a].elapsed_time(e[c]) for e in evs) / args.steps
         if path in ("fused", "fused_ig"):
             km = {"cfc_fb_kernel": per(0, 1), "reduce_axis0_kernel": per(1, 2)}
-        elif path in ("separate", "separate_ig"):
+        elif path in ("separate", "separate_ig", "windows"):
             km = {"cfc_fwd_kernel": per(0, 1), "cfc_bwd_kernel": per(1, 2), "reduce_axis0_kernel": per(2, 3)}
         else:
             km = {}
@@ -307,6 +331,8 @@ def main():
         return ms, km, {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9)}
 
     other = "separate" if args.path == "fused" else "fused"
+    if args.path == "windows":
+        args.main_only = True   # the other one-call paths refuse this K
     if not args.main_only:
         ms_other, k_other, _ = timed(other)
         ms_acc, _, pct_acc = timed("accumulate")

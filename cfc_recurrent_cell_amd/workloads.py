@@ -64,6 +64,11 @@ TRAIN = CfcConfig("train_B256_K64_H128", B=256, K=64, n_in=128, n_hid=128, dt=0.
 LARGE = CfcConfig("large_B8192_K8_H256", B=8192, K=8, n_in=256, n_hid=256, dt=1.0, seed=4,
                   h0_var=0.1)
 
+# A sequence four times the training length, beyond the one-call backward's
+# on-chip bound at this width (76 steps): run in windows.
+LONG = CfcConfig("long_B256_K256_H128", B=256, K=256, n_in=128, n_hid=128, dt=0.5, seed=5,
+                 x_feature_scale=True)
+
 # The tau-decay cell: the shape and dt of the pages' B=1 backward test (n_in=8,
 # n_hid=16, dt=0.02, tau ~ U[0.05, 2]) over a few rows and steps, and the
 # training-scale shape with the same dt and tau range.
@@ -72,7 +77,7 @@ TAU_TINY = CfcConfig("tau_tiny_B4_K8_n8_H16", B=4, K=8, n_in=8, n_hid=16, dt=0.0
 TAU_TRAIN = CfcConfig("tau_train_B256_K64_H128", B=256, K=64, n_in=128, n_hid=128, dt=0.02, seed=21,
                       x_feature_scale=True, cell="tau_decay")
 
-CFC_CONFIGS = {c.name: c for c in (TINY, SMOKE, TRAIN, LARGE, TAU_TINY, TAU_TRAIN)}
+CFC_CONFIGS = {c.name: c for c in (TINY, SMOKE, TRAIN, LARGE, LONG, TAU_TINY, TAU_TRAIN)}
 
 
 def scratch_row_len(n_in: int, n_hid: int) -> int:
