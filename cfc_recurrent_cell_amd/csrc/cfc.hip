@@ -275,21 +275,68 @@ __device__ __forceinline__ double dpp_move(double v) {
 }
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141;
 
-// p[r] is this lane's partial sum for output 4*ib + r; the 8 lanes jb = 0..7
-// (lane bits 0..2) of a group hold partials over disjoint column blocks.
-// Returns the full sum of output 4*ib + 2*(jb>>2) + ((jb>>1)&1) in both lanes
-// jb and jb^1.  Stage 1 pairs jb with 7-jb (half-mirror), stage 2 with jb^2,
-// stage 3 with jb^1; each stage halves the values a lane carries.  Fixed
-// order, so the result is deterministic.
-__device__ __forceinline__ double reduce_scatter8(const double p[4], int jb) {
-    const bool hi = jb & 4, b1 = jb & 2;
-    const double send0 = hi ? p[0] : p[2], send1 = hi ? p[1] : p[3];
-    const double keep0 = hi ? p[2] : p[0], keep1 = hi ? p[3] : p[1];
-    const double q0 = keep0 + dpp_move<kDppHalfMirror>(send0);
-    const double q1 = keep1 + dpp_move<kDppHalfMirror>(send1);
-    const double send = b1 ? q0 : q1, keep = b1 ? q1 : q0;
-    const double r = keep + dpp_move<kDppXor2>(send);
-    return r + dpp_move<kDppXor1>(r);
+constexpr int kDppRor8 = 0x128;  // row_ror:8: lane i of each 16-lane row reads lane i ^ 8
+
+// Serial-chain layout of the one-row kernels.  The 16 lanes of a DPP row
+// (jb = lane bits 0..3) share the row block ib = 4*wave + lane/16, i.e. units
+// 8ib .. 8ib+7, and lane jb takes the column block 8jb .. 8jb+7 of the step's
+// 128 x 128 matrix-vector product, so a lane reads 8 state values (64 bytes)
+// per step.  reduce_scatter16 leaves unit o = 8ib + 4 b3 + 2 b2 + b1 (b_n =
+// bit n of jb) in lanes jb and jb^1; the odd one evaluates the gate and the
+// even one tanh.
+struct ChainLane {
+    int jb, ib, o;
+    bool gate;
+};
+__device__ __forceinline__ ChainLane chain_lane(int wave, int lane) {
+    const int jb = lane & 15, ib = wave * 4 + (lane >> 4);
+    return ChainLane{jb, ib, 8 * ib + ((jb & 8) ? 4 : 0) + ((jb & 4) ? 2 : 0) + ((jb & 2) ? 1 : 0), (jb & 1) != 0};
+}
+
+// p[r] is this lane's partial sum for unit 8ib + r over its 8 columns; the 16
+// lanes of the row hold partials over disjoint column blocks.  Returns the
+// full sum of unit 8ib + 4 b3 + 2 b2 + b1 in lanes jb and jb^1.  Stage 1 pairs
+// jb with jb^8 (row_ror:8), stage 2 with 7 - jb inside each half-row
+// (row_half_mirror, jb ^ 7), stage 3 with jb^2, stage 4 with jb^1; each of the
+// first three halves the values a lane carries.  Fixed order: deterministic.
+__device__ __forceinline__ double reduce_scatter16(const double p[8], int jb) {
+    const bool b3 = jb & 8, b2 = jb & 4, b1 = jb & 2;
+    double q[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const double send = b3 ? p[m] : p[4 + m], keep = b3 ? p[4 + m] : p[m];
+        q[m] = keep + dpp_move<kDppRor8>(send);
+    }
+    double r[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const double send = b2 ? q[m] : q[2 + m], keep = b2 ? q[2 + m] : q[m];
+        r[m] = keep + dpp_move<kDppHalfMirror>(send);
+    }
+    const double send = b1 ? r[0] : r[1], keep = b1 ? r[1] : r[0];
+    const double t = keep + dpp_move<kDppXor2>(send);
+    return t + dpp_move<kDppXor1>(t);
+}
+
+// The lane's 8 state values v[8jb .. 8jb+7] from LDS (four 16-byte reads).
+__device__ __forceinline__ void chain_read(double (&vj)[8], const double* v, int jb) {
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) {
+        const double2 v2 = *reinterpret_cast<const double2*>(v + 8 * jb + c);
+        vj[c] = v2.x;
+        vj[c + 1] = v2.y;
+    }
+}
+
+// 64 FMAs into 8 independent sums (w[r][c] multiplies vj[c] into unit
+// 8ib + r), then the reduce-scatter: the full product for the lane's unit.
+__device__ __forceinline__ double chain_product(const double (&w)[8][8], const double (&vj)[8], int jb) {
+    double p[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) p[r] = fma(w[r][c], vj[c], p[r]);
+    return reduce_scatter16(p, jb);
 }
 
 // e^x for |x| <= 700: x = n ln2 + r with the two-constant (Cody-Waite) split
@@ -447,6 +494,31 @@ __device__ __forceinline__ void load_span_f64(double (&dst)[COUNT], const float*
     }
 }
 
+// The chain's weights: the forward's W_rec slice w[r][c] = W_rec[8ib + r][8jb + c],
+// or (transposed) the backward's w[r][c] = W_rec[8jb + c][8ib + r]; zero
+// outside the H x H matrix.
+__device__ __forceinline__ void load_chain_weights(double (&w)[8][8], const float* __restrict__ w_rec, int H,
+                                                   const ChainLane& cl, bool transposed) {
+    if (!transposed) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int row = 8 * cl.ib + r;
+            const int valid = row < H ? min(max(H - 8 * cl.jb, 0), 8) : 0;
+            load_span_f64<8>(w[r], w_rec + (long long)min(row, H - 1) * H + min(8 * cl.jb, H - 1), valid);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int row = 8 * cl.jb + c;
+            double w8[8];
+            const int valid = row < H ? min(max(H - 8 * cl.ib, 0), 8) : 0;
+            load_span_f64<8>(w8, w_rec + (long long)min(row, H - 1) * H + min(8 * cl.ib, H - 1), valid);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) w[r][c] = w8[r];
+        }
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
@@ -460,10 +532,9 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const long long b = blockIdx.x;
-    const int jb = lane & 7;
-    const int ib = wave * 8 + (lane >> 3);
-    const int o = 4 * ib + ((jb & 4) ? 2 : 0) + ((jb & 2) ? 1 : 0);
-    const bool gate_lane = jb & 1;
+    const ChainLane cl = chain_lane(wave, lane);
+    const int jb = cl.jb, o = cl.o;
+    const bool gate_lane = cl.gate;
 
     // Weight operand of the input projection, kept in registers.  The
     // contraction index of chunk jc in k-slot s = lane/16 is j = 32*s + jc, so a
@@ -477,14 +548,9 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
         const int valid = row < H ? min(max(n_in - 32 * slot, 0), NP / 4) : 0;
         load_span_f64<NP / 4>(wb[q], w_in + (long long)min(row, H - 1) * n_in + min(32 * slot, n_in - 1), valid);
     }
-    // W_rec slice for the recurrence: wr[r][c] = W_rec[4ib + r][16jb + c]
-    double wr[4][16];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = 4 * ib + r;
-        const int valid = row < H ? min(max(H - 16 * jb, 0), 16) : 0;
-        load_span_f64<16>(wr[r], w_rec + (long long)min(row, H - 1) * H + min(16 * jb, H - 1), valid);
-    }
+    // W_rec slice for the recurrence
+    double wr[8][8];
+    load_chain_weights(wr, w_rec, H, cl, false);
     for (int u = t; u < HP; u += kThreads) hb[u] = u < H ? (double)h0[b * H + u] : 0.0;
     const UnitGate ug = unit_gate(cell, o < H ? (double)w_tau[o] : 0.0, dt, o < H);
     double hprev = o < H ? (double)h0[b * H + o] : 0.0;
@@ -528,26 +594,9 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
         // ---- serial recurrence through the window
         for (int kk = 0; kk < kw; ++kk) {
             const double u = U[kk * HP + o];
-            const double* hv = hb + cur * HP + 16 * jb;
-            double hj[16];
-#pragma unroll
-            for (int c = 0; c < 16; c += 2) {
-                const double2 v2 = *reinterpret_cast<const double2*>(hv + c);
-                hj[c] = v2.x;
-                hj[c + 1] = v2.y;
-            }
-            double pe[4] = {0.0, 0.0, 0.0, 0.0}, po[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-            for (int c = 0; c < 16; c += 2)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    pe[r] = fma(wr[r][c], hj[c], pe[r]);
-                    po[r] = fma(wr[r][c + 1], hj[c + 1], po[r]);
-                }
-            double p[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = pe[r] + po[r];
-            const double a = u + reduce_scatter8(p, jb);
+            double hj[8];
+            chain_read(hj, hb + cur * HP, jb);
+            const double a = u + chain_product(wr, hj, jb);
             double g, c;
             cell_gates(a, gl, g, c);
             const double hn = fma(g, hprev - c, c);  // g*h + (1-g)*c
@@ -585,17 +634,9 @@ __device__ __forceinline__ void small_reverse_and_grads(
     bool gate_lane) {
     constexpr int HP = kSmall, NP = kSmall, ZW = kSmallZW, ZS = kSmallZS;
     constexpr int KP = kSmallBwdMaxK;
-    // ---- W_rec^T slice into registers: wt[r][c] = W_rec[16jb + c][4ib + r]
-    double wt[4][16];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        const int row = 16 * jb + c;
-        double w4[4];
-        const int valid = row < H ? min(max(H - 4 * ib, 0), 4) : 0;
-        load_span_f64<4>(w4, w_rec + (long long)min(row, H - 1) * H + min(4 * ib, H - 1), valid);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) wt[r][c] = w4[r];
-    }
+    // ---- W_rec^T slice into registers
+    double wt[8][8];
+    load_chain_weights(wt, w_rec, H, ChainLane{jb, ib, o, gate_lane}, true);
 
     // ---- loss seed
     {
@@ -607,45 +648,41 @@ __device__ __forceinline__ void small_reverse_and_grads(
     __syncthreads();
     if (wave == 0 && lane == 0 && loss_b) *loss_b = (float)(((red[0] + red[1]) + red[2]) + red[3]);
 
-    // ---- serial reverse chain
+    // ---- serial reverse chain.  Per step only delta carries a dependency:
+    // dz = delta P, dL/da = delta Q, the dw_tau term = delta R, with g, P, Q,
+    // R functions of a_k and h_k alone; they are computed one step ahead,
+    // after the barrier, while the step's LDS reads and products are in
+    // flight.  a_k-1 is still in AD when they are read (it is overwritten by
+    // dL/da_k-1 one step later, by the same lane pair).
     double gb = 0.0, gwt = 0.0;
-    double a_next = AD[(K - 1) * HP + o];
-    double h_next = (double)zs[(K - 1) * ZS + NP + o];
-    for (int k = K - 1; k >= 0; --k) {
-        const double a = a_next, hk = h_next;
-        if (k > 0) {
-            a_next = AD[(k - 1) * HP + o];
-            h_next = (double)zs[(k - 1) * ZS + NP + o];
-        }
-        double g, c;
+    auto step_consts = [&](int k, double& g, double& Q, double& R) {
+        const double a = AD[k * HP + o];
+        const double hk = (double)zs[k * ZS + NP + o];
+        double c;
         cell_gates(a, gl, g, c);
-        const double dz = delta * (hk - c) * g * fma(-ug.vmul, g, 1.0);
-        const double da = delta * (1.0 - g) * (1.0 - c * c) - dz * ug.rho;
+        const double P = (hk - c) * g * fma(-ug.vmul, g, 1.0);
+        Q = (1.0 - g) * (1.0 - c * c) - P * ug.rho;
+        R = P * fma(-a, ug.alpha, ug.beta);
+    };
+    double g, Q, R;
+    step_consts(K - 1, g, Q, R);
+    for (int k = K - 1; k >= 0; --k) {
+        const double da = delta * Q;
         gb += da;
-        gwt += dz * fma(-a, ug.alpha, ug.beta);
+        gwt += delta * R;
         if (!gate_lane) AD[k * HP + o] = da;
         __syncthreads();
         if (k == 0 && !gh0_row) break;
-        const double* dak = AD + k * HP + 16 * jb;
-        double dj[16];
-#pragma unroll
-        for (int cc = 0; cc < 16; cc += 2) {
-            const double2 v2 = *reinterpret_cast<const double2*>(dak + cc);
-            dj[cc] = v2.x;
-            dj[cc + 1] = v2.y;
-        }
-        double pe[4] = {0.0, 0.0, 0.0, 0.0}, po[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-        for (int cc = 0; cc < 16; cc += 2)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pe[r] = fma(wt[r][cc], dj[cc], pe[r]);
-                po[r] = fma(wt[r][cc + 1], dj[cc + 1], po[r]);
-            }
-        double p[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = pe[r] + po[r];
-        delta = fma(delta, g, reduce_scatter8(p, jb));
+        double dj[8];
+        chain_read(dj, AD + k * HP, jb);
+        // next step's constants (unused after k = 0), in the same block as
+        // the products so that their latency overlaps them
+        double gn, Qn, Rn;
+        step_consts(k > 0 ? k - 1 : 0, gn, Qn, Rn);
+        delta = fma(delta, g, chain_product(wt, dj, jb));
+        g = gn;
+        Q = Qn;
+        R = Rn;
     }
     if (gh0_row && !gate_lane && o < H) gh0_row[o] = (float)delta;  // dL/dh_0
 
@@ -794,10 +831,9 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     float* gst = zs + KP * ZS + wave * 16 * kSmallGS;  // this wave's [16][kSmallGS] tile buffer
     const long long b = blockIdx.x;
     const long long N = (long long)H * (n_in + H + 2);
-    const int jb = lane & 7;
-    const int ib = wave * 8 + (lane >> 3);
-    const int o = 4 * ib + ((jb & 4) ? 2 : 0) + ((jb & 2) ? 1 : 0);
-    const bool gate_lane = jb & 1;
+    const ChainLane cl = chain_lane(wave, lane);
+    const int jb = cl.jb, ib = cl.ib, o = cl.o;
+    const bool gate_lane = cl.gate;
 
     // Weight operand of the recomputation, in registers.  Chunk jc of k-slot
     // s = lane/16 contracts index j = 64*s + jc of [x | h_prev], so a lane holds
@@ -893,10 +929,9 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     float* gst = zs + KP * ZS + wave * 16 * kSmallGS;
     const long long b = blockIdx.x;
     const long long N = (long long)H * (n_in + H + 2);
-    const int jb = lane & 7;
-    const int ib = wave * 8 + (lane >> 3);
-    const int o = 4 * ib + ((jb & 4) ? 2 : 0) + ((jb & 2) ? 1 : 0);
-    const bool gate_lane = jb & 1;
+    const ChainLane cl = chain_lane(wave, lane);
+    const int jb = cl.jb, ib = cl.ib, o = cl.o;
+    const bool gate_lane = cl.gate;
     const int slot = lane >> 4;
 
     // ---- stage x (rows >= K zero), h0 as row 0 of the h_prev half (rows >= K
@@ -948,39 +983,17 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
 
     // ---- forward chain (as in cfc_fwd_small_kernel); a_k replaces the
     // projection in AD, h_k goes to h_seq and to the h_prev half of row k+1
-    double wr[4][16];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = 4 * ib + r;
-        const int valid = row < H ? min(max(H - 16 * jb, 0), 16) : 0;
-        load_span_f64<16>(wr[r], w_rec + (long long)min(row, H - 1) * H + min(16 * jb, H - 1), valid);
-    }
+    double wr[8][8];
+    load_chain_weights(wr, w_rec, H, cl, false);
     double hprev = o < H ? (double)h0[b * H + o] : 0.0;
     const GateLane gl = gate_lane_consts(gate_lane, ug);
     __syncthreads();
     int cur = 0;
     for (int k = 0; k < K; ++k) {
         const double u = AD[k * HP + o];
-        const double* hv = hb + cur * HP + 16 * jb;
-        double hj[16];
-#pragma unroll
-        for (int c = 0; c < 16; c += 2) {
-            const double2 v2 = *reinterpret_cast<const double2*>(hv + c);
-            hj[c] = v2.x;
-            hj[c + 1] = v2.y;
-        }
-        double pe[4] = {0.0, 0.0, 0.0, 0.0}, po[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-        for (int c = 0; c < 16; c += 2)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pe[r] = fma(wr[r][c], hj[c], pe[r]);
-                po[r] = fma(wr[r][c + 1], hj[c + 1], po[r]);
-            }
-        double p[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = pe[r] + po[r];
-        const double a = u + reduce_scatter8(p, jb);
+        double hj[8];
+        chain_read(hj, hb + cur * HP, jb);
+        const double a = u + chain_product(wr, hj, jb);
         double g, c;
         cell_gates(a, gl, g, c);
         const double hn = fma(g, hprev - c, c);
