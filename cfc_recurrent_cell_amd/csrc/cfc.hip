@@ -282,40 +282,40 @@ constexpr int kDppRor8 = 0x128;  // row_ror:8: lane i of each 16-lane row reads 
 // (jb = lane bits 0..3) share the row block ib = 4*wave + lane/16, i.e. units
 // 8ib .. 8ib+7, and lane jb takes the column block 8jb .. 8jb+7 of the step's
 // 128 x 128 matrix-vector product, so a lane reads 8 state values (64 bytes)
-// per step.  reduce_scatter16 leaves unit o = 8ib + 4 b3 + 2 b2 + b1 (b_n =
-// bit n of jb) in lanes jb and jb^1; the odd one evaluates the gate and the
-// even one tanh.
+// per step.  Slot s of a lane's 8 partial sums belongs to unit 8ib + (s ^ x)
+// with x = 4 b3 + 2 b2 + (b1 ^ b2) (b_n = bit n of jb): the order is fixed per
+// lane when its weights are loaded, so that every stage of reduce_scatter16
+// keeps the low half of the lane's values and sends the high half, with no
+// per-lane selects.  It leaves unit o = 8ib + x in lanes jb and jb^1; the odd
+// one evaluates the gate and the even one tanh.
 struct ChainLane {
     int jb, ib, o;
     bool gate;
 };
+__device__ __forceinline__ int chain_unit_xor(int jb) {
+    return (jb & 8 ? 4 : 0) + (jb & 4 ? 2 : 0) + (((jb >> 1) ^ (jb >> 2)) & 1);
+}
 __device__ __forceinline__ ChainLane chain_lane(int wave, int lane) {
     const int jb = lane & 15, ib = wave * 4 + (lane >> 4);
-    return ChainLane{jb, ib, 8 * ib + ((jb & 8) ? 4 : 0) + ((jb & 4) ? 2 : 0) + ((jb & 2) ? 1 : 0), (jb & 1) != 0};
+    return ChainLane{jb, ib, 8 * ib + chain_unit_xor(jb), (jb & 1) != 0};
 }
 
-// p[r] is this lane's partial sum for unit 8ib + r over its 8 columns; the 16
-// lanes of the row hold partials over disjoint column blocks.  Returns the
-// full sum of unit 8ib + 4 b3 + 2 b2 + b1 in lanes jb and jb^1.  Stage 1 pairs
-// jb with jb^8 (row_ror:8), stage 2 with 7 - jb inside each half-row
-// (row_half_mirror, jb ^ 7), stage 3 with jb^2, stage 4 with jb^1; each of the
-// first three halves the values a lane carries.  Fixed order: deterministic.
-__device__ __forceinline__ double reduce_scatter16(const double p[8], int jb) {
-    const bool b3 = jb & 8, b2 = jb & 4, b1 = jb & 2;
+// p[s] is this lane's partial sum for unit 8ib + (s ^ x) over its 8 columns;
+// the 16 lanes of the row hold partials over disjoint column blocks.  Returns
+// the full sum of unit 8ib + x in lanes jb and jb^1.  Stage 1 pairs jb with
+// jb^8 (row_ror:8), stage 2 with jb^7 inside each half-row (row_half_mirror),
+// stage 3 with jb^2, stage 4 with jb^1.  A partner's x differs from the lane's
+// by 4, 2 + 1 and 1 in the first three stages, so slot m + half of the
+// partner holds the unit of the lane's slot m: each stage adds the partner's
+// upper half onto the lane's lower half.  Fixed order: deterministic.
+__device__ __forceinline__ double reduce_scatter16(const double p[8]) {
     double q[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const double send = b3 ? p[m] : p[4 + m], keep = b3 ? p[4 + m] : p[m];
-        q[m] = keep + dpp_move<kDppRor8>(send);
-    }
+    for (int m = 0; m < 4; ++m) q[m] = p[m] + dpp_move<kDppRor8>(p[4 + m]);
     double r[2];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const double send = b2 ? q[m] : q[2 + m], keep = b2 ? q[2 + m] : q[m];
-        r[m] = keep + dpp_move<kDppHalfMirror>(send);
-    }
-    const double send = b1 ? r[0] : r[1], keep = b1 ? r[1] : r[0];
-    const double t = keep + dpp_move<kDppXor2>(send);
+    for (int m = 0; m < 2; ++m) r[m] = q[m] + dpp_move<kDppHalfMirror>(q[2 + m]);
+    const double t = r[0] + dpp_move<kDppXor2>(r[1]);
     return t + dpp_move<kDppXor1>(t);
 }
 
@@ -329,15 +329,16 @@ __device__ __forceinline__ void chain_read(double (&vj)[8], const double* v, int
     }
 }
 
-// 64 FMAs into 8 independent sums (w[r][c] multiplies vj[c] into unit
-// 8ib + r), then the reduce-scatter: the full product for the lane's unit.
-__device__ __forceinline__ double chain_product(const double (&w)[8][8], const double (&vj)[8], int jb) {
+// 64 FMAs into 8 independent sums (w[s][c] multiplies vj[c] into slot s,
+// unit 8ib + (s ^ x)), then the reduce-scatter: the full product for the
+// lane's unit.
+__device__ __forceinline__ double chain_product(const double (&w)[8][8], const double (&vj)[8]) {
     double p[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
         for (int r = 0; r < 8; ++r) p[r] = fma(w[r][c], vj[c], p[r]);
-    return reduce_scatter16(p, jb);
+    return reduce_scatter16(p);
 }
 
 // e^x for |x| <= 700: x = n ln2 + r with the two-constant (Cody-Waite) split
@@ -518,6 +519,23 @@ __device__ __forceinline__ void load_chain_weights(double (&w)[8][8], const floa
             for (int r = 0; r < 8; ++r) w[r][c] = w8[r];
         }
     }
+    // slot s takes unit s ^ x: swap rows s and s ^ 4, s ^ 2, s ^ 1 where x has
+    // that bit (once per kernel, off the chains)
+    const int x = chain_unit_xor(cl.jb);
+#pragma unroll
+    for (int bit = 4; bit >= 1; bit >>= 1) {
+        const bool sw = (x & bit) != 0;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if (r & bit) continue;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const double lo = w[r][c], hi = w[r | bit][c];
+                w[r][c] = sw ? hi : lo;
+                w[r | bit][c] = sw ? lo : hi;
+            }
+        }
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
@@ -597,7 +615,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
             const double u = U[kk * HP + o];
             double hj[8];
             chain_read(hj, hb + cur * HP, jb);
-            const double a = u + chain_product(wr, hj, jb);
+            const double a = u + chain_product(wr, hj);
             double g, c;
             cell_gates(a, gl, g, c);
             const double hn = fma(g, hprev - c, c);  // g*h + (1-g)*c
@@ -680,7 +698,7 @@ __device__ __forceinline__ void small_reverse_and_grads(
         // the products so that their latency overlaps them
         double gn, Qn, Rn;
         step_consts(k > 0 ? k - 1 : 0, gn, Qn, Rn);
-        delta = fma(delta, g, chain_product(wt, dj, jb));
+        delta = fma(delta, g, chain_product(wt, dj));
         g = gn;
         Q = Qn;
         R = Rn;
@@ -994,7 +1012,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
         const double u = AD[k * HP + o];
         double hj[8];
         chain_read(hj, hb + cur * HP, jb);
-        const double a = u + chain_product(wr, hj, jb);
+        const double a = u + chain_product(wr, hj);
         double g, c;
         cell_gates(a, gl, g, c);
         const double hn = fma(g, hprev - c, c);
