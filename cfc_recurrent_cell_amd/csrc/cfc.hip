@@ -620,10 +620,11 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
             cell_gates(a, gl, g, c);
             const double hn = fma(g, hprev - c, c);  // g*h + (1-g)*c
             hprev = hn;
-            if (!gate_lane) {
-                hb[(cur ^ 1) * HP + o] = hn;
-                if (o < H) h_seq[(b * K + k0 + kk) * (long long)H + o] = (float)hn;
-            }
+            // both lanes of the unit's pair hold the same bits (the last
+            // reduce stage adds the same two values, and g, c are exchanged),
+            // so both store: no branch in the loop
+            hb[(cur ^ 1) * HP + o] = hn;
+            if (o < H) h_seq[(b * K + k0 + kk) * (long long)H + o] = (float)hn;
             cur ^= 1;
             __syncthreads();
         }
@@ -1017,12 +1018,11 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
         cell_gates(a, gl, g, c);
         const double hn = fma(g, hprev - c, c);
         hprev = hn;
-        if (!gate_lane) {
-            AD[k * HP + o] = a;
-            hb[(cur ^ 1) * HP + o] = hn;
-            if (k + 1 < K) zs[(k + 1) * ZS + NP + o] = (float)hn;
-            if (o < H) h_seq[(b * K + k) * (long long)H + o] = (float)hn;
-        }
+        // both lanes of the pair hold the same bits: both store, no branch
+        AD[k * HP + o] = a;
+        hb[(cur ^ 1) * HP + o] = hn;
+        if (k + 1 < K) zs[(k + 1) * ZS + NP + o] = (float)hn;
+        if (o < H) h_seq[(b * K + k) * (long long)H + o] = (float)hn;
         cur ^= 1;
         __syncthreads();
     }
