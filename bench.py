@@ -406,7 +406,9 @@ def main():
             "path": other, "value": B * K / (ms_other * 1e-3), "ms_per_step": ms_other, "kernels_ms": k_other},
         "reduce_axis0": {"GB_per_s": red_gbps, "frac_hbm": red_gbps / PEAK_HBM_GBPS,
                          "bytes": work["reduce_bytes"],
-                         "note": "scratch of this step (33.8 MB) may be served partly from the MALL"},
+                         "note": "HIP events around the launch inside the step (an empty launch measures about "
+                                 "6 us this way); the step's scratch (%.1f MB) was just written, so part of it may "
+                                 "be served from the MALL" % (work["reduce_bytes"] / 1e6)},
         "kernel_source_sha256_16": source_hash(),
     }
     if args.reduce_sweep:
