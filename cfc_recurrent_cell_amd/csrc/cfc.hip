@@ -1184,12 +1184,16 @@ __device__ __forceinline__ void large_preact(dbl4 acc[4], const float* __restric
     for (int tb = 0; tb < 4; ++tb) acc[tb] += acc_odd[tb];
 }
 
-template <bool FULL>
+// PARK (one-call entry, overwrite mode): a_k of row b is also written, as
+// float64, to a_park + b * N (floats [0, 2 K H) of the row's scratch, which the
+// backward overwrites only after reading them back), so the backward needs no
+// recomputation.  a_park + b * N must be 8-byte aligned.
+template <bool FULL, bool PARK>
 __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, double dt, int B, int K, int n_in,
-    int H, float* __restrict__ h_seq, int cell) {
+    int H, float* __restrict__ h_seq, int cell, float* __restrict__ a_park, long long N) {
     extern __shared__ __align__(16) unsigned char smem[];
     float* zx = reinterpret_cast<float*>(smem);                        // [256][16] x_k
     double* zh = reinterpret_cast<double*>(smem + 4 * kLarge * kLR);   // [256][16] h_k
@@ -1235,6 +1239,10 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
             for (int v = 0; v < 4; ++v) {
                 const int i = lunit(wave, tb, s + 4 * v);
                 const double a = acc[tb][v] + bias_v[tb][v];
+                if constexpr (PARK) {
+                    if (r0 + r < B && i < H)
+                        reinterpret_cast<double*>(a_park + (r0 + r) * N)[(long long)k * H + i] = a;
+                }
                 const double g = cell == CFC_CELL_TAU_DECAY ? spdt_v[tb][v] : inv_one_plus_exp(spdt_v[tb][v] * a);
                 const double c = fma(-2.0, inv_one_plus_exp(2.0 * a), 1.0);
                 double* hp = zh + zidx(i, r);
@@ -1257,7 +1265,10 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
     }
 }
 
-template <bool FULL, bool TAU>
+// PARKED (one-call entry, after cfc_fwd_large_kernel<FULL, true>): a_k is read
+// back from the head of the row's scratch instead of being recomputed, so x_k
+// is not staged; the window is then the whole sequence.
+template <bool FULL, bool TAU, bool PARKED>
 __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
@@ -1328,20 +1339,32 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     // inputs of step k (x_k and h_k-1 of the 16 rows), fetched one step ahead
     float xr[kLR], hr[kLR];
     auto fetch_step = [&](int k) {
-        fetch_t(xr, x + (k0 + k) * n_in, Kf * n_in, r0, B, n_in, t);
+        if constexpr (!PARKED) fetch_t(xr, x + (k0 + k) * n_in, Kf * n_in, r0, B, n_in, t);
         if (k0 + k == 0) fetch_t(hr, h0, H, r0, B, H, t);
         else fetch_t(hr, h_seq + (k0 + k - 1) * H, Kf * H, r0, B, H, t);
     };
     fetch_step(K - 1);
     for (int k = K - 1; k >= 0; --k) {
+        dbl4 acc[4];  // a_k - b (recomputed), or a_k itself (parked)
+        if constexpr (PARKED) {
+            const double* ap = reinterpret_cast<const double*>(scratch + b_own * N) + (k0 + k) * (long long)H;
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int i = lunit(wave, tb, s + 4 * v);
+                    acc[tb][v] = row_ok && i < H ? ap[i] : 0.0;
+                }
+        }
         __syncthreads();  // previous step is done with zx, zh, dab
-        store_t(zx, xr, t);
+        if constexpr (!PARKED) store_t(zx, xr, t);
         store_t(zh, hr, t);
         __syncthreads();
-        dbl4 acc[4];
+        if constexpr (!PARKED) {
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
-        large_preact<FULL>(acc, w_in, w_rec, n_in, H, zx, zh, wave, lane);
+            for (int tb = 0; tb < 4; ++tb) acc[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
+            large_preact<FULL>(acc, w_in, w_rec, n_in, H, zx, zh, wave, lane);
+        }
         double gk[4][4];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
@@ -1349,7 +1372,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                 for (int v = 0; v < 4; ++v) {
                     const int i = lunit(wave, tb, s + 4 * v);
                     const double spdt = uspdt[i];
-                    const double a = acc[tb][v] + ubias[i];
+                    const double a = PARKED ? acc[tb][v] : acc[tb][v] + ubias[i];
                     const double c = fma(-2.0, inv_one_plus_exp(2.0 * a), 1.0);
                     const double hp = zh[zidx(i, r)];
                     const double d = delta[tb][v];
@@ -1726,14 +1749,22 @@ void set_kernel_attributes() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fb_small_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<false>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<false, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<true>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<true, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-        for (const void* f : {reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, false>),
-                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false>),
-                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, true>),
-                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true>)})
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<false, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<true, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        for (const void* f : {reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, false, false>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false, false>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, true, false>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, false>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, false, true>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false, true>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, true, true>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, true>)})
             (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     });
 }
@@ -1794,14 +1825,10 @@ extern "C" int cfc_forward(const cfc_params_t* params, const float* x, const flo
         return launch_status();
     }
     const long long groups = ((long long)B + kLR - 1) / kLR;
-    if (large_full(params))
-        hipLaunchKernelGGL(cfc_fwd_large_kernel<true>, dim3((unsigned)groups), dim3(kThreads), large_fwd_lds_bytes(),
-                           stream, params->w_in, params->w_rec, params->b, params->w_tau, x, h0, (double)dt, B,
-                           K, n_in, H, h_seq, params->cell);
-    else
-        hipLaunchKernelGGL(cfc_fwd_large_kernel<false>, dim3((unsigned)groups), dim3(kThreads), large_fwd_lds_bytes(),
-                           stream, params->w_in, params->w_rec, params->b, params->w_tau, x, h0, (double)dt, B,
-                           K, n_in, H, h_seq, params->cell);
+    auto kern = large_full(params) ? cfc_fwd_large_kernel<true, false> : cfc_fwd_large_kernel<false, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kThreads), large_fwd_lds_bytes(), stream, params->w_in,
+                       params->w_rec, params->b, params->w_tau, x, h0, (double)dt, B, K, n_in, H, h_seq, params->cell,
+                       nullptr, 0LL);
     return launch_status();
 }
 
@@ -1855,8 +1882,9 @@ int backward_window(const cfc_params_t* params, const float* x, const float* h0,
     if (large) {
         const long long groups = ((long long)B + kLR - 1) / kLR;
         const bool tau = params->cell == CFC_CELL_TAU_DECAY;
-        auto kern = large_full(params) ? (tau ? &cfc_bwd_large_kernel<true, true> : &cfc_bwd_large_kernel<true, false>)
-                                       : (tau ? &cfc_bwd_large_kernel<false, true> : &cfc_bwd_large_kernel<false, false>);
+        auto kern = large_full(params)
+                        ? (tau ? &cfc_bwd_large_kernel<true, true, false> : &cfc_bwd_large_kernel<true, false, false>)
+                        : (tau ? &cfc_bwd_large_kernel<false, true, false> : &cfc_bwd_large_kernel<false, false, false>);
         hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kThreads), lds, stream, params->w_in, params->w_rec,
                            params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, win, n_in, H, scratch, loss,
                            grad_x);
@@ -1922,6 +1950,29 @@ extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, 
     const bool small_bwd = n_in <= kSmall && H <= kSmall && K <= kSmallBwdMaxK;
     const size_t lds = small_bwd ? small_bwd_lds_bytes() : large ? large_bwd_lds_bytes() : bwd_lds_bytes(K, n_in, H);
     if (lds > kLdsBytes) return CFC_ERR_UNSUPPORTED;
+    // 16-row kernels in overwrite mode: the forward parks a_k (float64) in the
+    // head of each scratch row and the backward reads it back instead of
+    // recomputing it (needs 8-byte-aligned rows; the head [0, 2KH) and the
+    // backward's parked dL/da in the tail [N - 2KH, N) are disjoint because
+    // 4K <= n_in + H + 2 at these widths and K)
+    if (large && N % 2 == 0 && (reinterpret_cast<uintptr_t>(scratch) & 7) == 0 && 4LL * K * H <= N) {
+        set_kernel_attributes();
+        const long long groups = ((long long)B + kLR - 1) / kLR;
+        const bool full = large_full(params), tau = params->cell == CFC_CELL_TAU_DECAY;
+        auto fwd = full ? cfc_fwd_large_kernel<true, true> : cfc_fwd_large_kernel<false, true>;
+        hipLaunchKernelGGL(fwd, dim3((unsigned)groups), dim3(kThreads), large_fwd_lds_bytes(), stream, params->w_in,
+                           params->w_rec, params->b, params->w_tau, x, h0, (double)dt, B, K, n_in, H, h_seq,
+                           params->cell, scratch, N);
+        rc = launch_status();
+        if (rc) return rc;
+        auto bwd = full ? (tau ? &cfc_bwd_large_kernel<true, true, true> : &cfc_bwd_large_kernel<true, false, true>)
+                        : (tau ? &cfc_bwd_large_kernel<false, true, true> : &cfc_bwd_large_kernel<false, false, true>);
+        const BwdWindow win{K, 0, K, nullptr, grad_h0};
+        hipLaunchKernelGGL(bwd, dim3((unsigned)groups), dim3(kThreads), large_bwd_lds_bytes(), stream, params->w_in,
+                           params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, win, n_in, H,
+                           scratch, loss, grad_x);
+        return launch_status();
+    }
     rc = cfc_forward(params, x, h0, dt, B, K, h_seq, stream);
     if (rc) return rc;
     return cfc_backward(params, x, h0, h_seq, y, dt, B, K, scratch, loss, grad_x, grad_h0, flags, stream);

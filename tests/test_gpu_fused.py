@@ -156,3 +156,43 @@ def test_fused_refusal_enqueues_nothing():
     assert e.value.code == C.CFC_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert torch.isnan(h_seq).all()
+
+
+WIDE_PARKED = [
+    # (B, K, n_in, H, dt, seed, cell): the one-call entry's 16-row path, where
+    # the forward parks a_k in the head of each scratch row and the backward
+    # reads it back (overwrite mode, even N)
+    (37, 7, 200, 256, 0.8, 53, "gated"),     # masked widths, ragged last group
+    (17, 20, 256, 256, 0.6, 54, "gated"),    # the 16-row backward's K limit, one row in the last group
+    (20, 9, 256, 200, 0.1, 55, "tau_decay"),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_PARKED, ids=lambda c: "B{}_K{}_n{}_H{}_{}".format(c[0], c[1], c[2], c[3], c[6]))
+def test_fused_wide_parked_preactivations(case):
+    """Every scratch element is overwritten (NaN poison gone, oracle parity),
+    the input gradients match, and rows run alone equal their batched rows."""
+    import torch
+    import cfc_recurrent_cell_amd as C
+    B, K, n_in, H, dt, seed, cell = case
+    inp = W.make_random_cfc_inputs(B, K, n_in, H, dt, seed, cell=cell)
+    assert W.scratch_row_len(n_in, H) % 2 == 0
+    say(f"[fused] parked a_k: B={B} K={K} n_in={n_in} H={H} {cell}")
+    d = to_dev(inp)
+    args = (d["w_in"], d["w_rec"], d["b"], d["w_tau"], d["x"], d["h0"], d["y"], d["dt"])
+    scratch = torch.full((B, W.scratch_row_len(n_in, H)), float("nan"), device="cuda")
+    h, s, l, gx, gh = C.cfc_forward_backward(*args, scratch=scratch, input_grads=True, cell=cell)
+    out = C.reduce_axis0(s)
+    h, s, l, gx, gh, out = [host(t) for t in (h, s, l, gx, gh, out)]
+    assert np.isfinite(s).all()
+    ref = O.cfc_step(inp, threads=oracle_threads(), input_grads=True)
+    for got, name in ((h, "h_seq"), (s, "scratch"), (l, "loss"), (out, "out"), (gx, "grad_x"), (gh, "grad_h0")):
+        assert_close(got, ref[name], f"parked {name}")
+    for r in (0, B - 1):
+        one = W.CfcInputs(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x[r:r + 1], inp.h0[r:r + 1],
+                          inp.y[r:r + 1], inp.dt, cell)
+        d1 = to_dev(one)
+        h1, s1, l1 = [host(t) for t in C.cfc_forward_backward(d1["w_in"], d1["w_rec"], d1["b"], d1["w_tau"], d1["x"],
+                                                               d1["h0"], d1["y"], d1["dt"], cell=cell)]
+        assert np.array_equal(h1[0].view(np.uint32), h[r].view(np.uint32))
+        assert np.array_equal(s1[0].view(np.uint32), s[r].view(np.uint32))
