@@ -4,8 +4,10 @@ One step = forward + backward (overwrite mode, so the scratch clear is part of
 the step) + reduce_axis0 over one batch of the training-scale workload (B=256,
 K=64, n_in=n_hid=128, dt=0.5), inputs resident in HBM.  By default the
 forward and backward are one cfc_forward_backward call (one kernel at this
-shape); --path separate times cfc_forward + cfc_backward instead.  Both paths
-are timed in every run; the other one is reported in "other_path".
+shape; at widths above 128 with K <= 20 two launches that pass the
+pre-activations through the scratch); --path separate times cfc_forward +
+cfc_backward instead.  Both paths are timed in every run; the other one is
+reported in "other_path".
 
 Prints ONE JSON line.  `value` is batch-steps/s = B*K / seconds per step.
 The roofline object describes the step's dominant kernel, timed with HIP
@@ -217,7 +219,10 @@ def main():
         print("--input-grads is not timed on the windows path", file=sys.stderr)
         sys.exit(2)
     if args.path is None:
-        args.path = "fused" if (n_in <= 128 and H <= 128 and K <= 64) else \
+        # the one-call entry where it is one kernel, or the two 16-row
+        # launches that skip the recomputation; otherwise separate calls
+        wide_parked = (n_in > 128 or H > 128) and K <= 20 and (H * (n_in + H + 2)) % 2 == 0
+        args.path = "fused" if (n_in <= 128 and H <= 128 and K <= 64) or wide_parked else \
             "separate" if one_call_bwd_ok else "windows"
 
     def step_separate(ev=None):

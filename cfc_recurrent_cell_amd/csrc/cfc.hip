@@ -1518,26 +1518,46 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
         if (rr + 1 < kLR && b + 1 < B) fetch_row(b + 1);
         float* grow = scratch + b * N;
         float* grec = grow + (long long)H * n_in;
-        // the wave's 64 units x 512 columns, in 16 x 64 blocks: 4 column tiles
-        // per block, transposed through LDS into float4 row stores
-        for (int ub = 0; ub < 4; ++ub) {
-            const int ib = 4 * wave + ub;
-            for (int jg = 0; jg < 2 * kLarge / 64; ++jg) {
-                dbl4 acc[4];
+        // the wave's 64 units x 512 columns: per 64-column group, the four
+        // 16-unit tiles together (16 accumulators, so each operand fetched
+        // from LDS feeds four MFMAs and a group runs 16 KP/4 of them), then
+        // each 16 x 64 tile transposed through LDS into float4 row stores.
+        // The dL/da operands of the wave's tiles are read once per row.
+        constexpr int KCM = kLargeBwdMaxK / 4;
+        const int KC = KP / 4;
+        double av[KCM][4];
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) acc[jj] = dbl4{0.0, 0.0, 0.0, 0.0};
-                for (int kc = 0; kc < KP / 4; ++kc) {
+        for (int kc = 0; kc < KCM; ++kc)
+#pragma unroll
+            for (int ub = 0; ub < 4; ++ub)
+                av[kc][ub] = kc < KC ? dak[(4 * kc + s) * kLarge + (4 * wave + ub) * 16 + (lane & 15)] : 0.0;
+        for (int jg = 0; jg < 2 * kLarge / 64; ++jg) {
+            dbl4 acc4[4][4];
+#pragma unroll
+            for (int ub = 0; ub < 4; ++ub)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) acc4[ub][jj] = dbl4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int kc = 0; kc < KCM; ++kc) {
+                if (kc < KC) {
                     const int kk = 4 * kc + s;
-                    const double a = dak[kk * kLarge + ib * 16 + (lane & 15)];
+                    double z[4];
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        acc[jj] = mfma_f64(a, (double)zk[kk * 2 * kLarge + (4 * jg + jj) * 16 + (lane & 15)], acc[jj]);
+                    for (int jj = 0; jj < 4; ++jj) z[jj] = (double)zk[kk * 2 * kLarge + (4 * jg + jj) * 16 + (lane & 15)];
+#pragma unroll
+                    for (int ub = 0; ub < 4; ++ub)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) acc4[ub][jj] = mfma_f64(av[kc][ub], z[jj], acc4[ub][jj]);
                 }
+            }
+#pragma unroll
+            for (int ub = 0; ub < 4; ++ub) {
+                const int ib = 4 * wave + ub;
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
-                        gst[(s + 4 * v) * kLargeGS + jj * 16 + (lane & 15)] = (float)acc[jj][v];
+                        gst[(s + 4 * v) * kLargeGS + jj * 16 + (lane & 15)] = (float)acc4[ub][jj][v];
                 const int c4 = 4 * (lane & 15);
                 const int jc0 = jg * 64 + c4;
                 const bool in_part = jc0 < kLarge;
