@@ -1597,7 +1597,71 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
 #pragma unroll
             for (int ub = 0; ub < 4; ++ub)
                 av[kc][ub] = kc < KC ? dak[(4 * kc + s) * kLarge + (4 * wave + ub) * 16 + (lane & 15)] : 0.0;
-        for (int jg = 0; jg < 2 * kLarge / 64; ++jg) {
+        if constexpr (FULL && PARKED) {
+            // 256 x 256 with aligned rows: no masking, and the work runs as
+            // (column group, pair of 16-unit tiles) steps whose two tiles are
+            // stored (held in float32 registers) under the first chunk's
+            // products of the next step
+            const int c4 = 4 * (lane & 15);
+            float pend[2][4][4];
+            auto store_tiles = [&](int jgp, int uhp) {
+#pragma unroll
+                for (int u2 = 0; u2 < 2; ++u2) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            gst[(s + 4 * v) * kLargeGS + jj * 16 + (lane & 15)] = pend[u2][jj][v];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int rr2 = s + 4 * m;
+                        const float4 val = *reinterpret_cast<const float4*>(gst + rr2 * kLargeGS + c4);
+                        const int i = (4 * wave + 2 * uhp + u2) * 16 + rr2;
+                        const int jc0 = jgp * 64 + c4;
+                        float* dst = jc0 < kLarge ? grow + (long long)i * kLarge + jc0
+                                                  : grec + (long long)i * kLarge + (jc0 - kLarge);
+                        *reinterpret_cast<float4*>(dst) = val;
+                    }
+                }
+            };
+            for (int jg = 0; jg < 2 * kLarge / 64; ++jg) {
+#pragma unroll
+                for (int uh = 0; uh < 2; ++uh) {
+                    dbl4 acc2[2][4];
+#pragma unroll
+                    for (int u2 = 0; u2 < 2; ++u2)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) acc2[u2][jj] = dbl4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+                    for (int kc = 0; kc < KCM; ++kc) {
+                        if (kc == 0 || kc < KC) {
+                            const int kk = 4 * kc + s;
+                            double z[4];
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj)
+                                z[jj] = (double)zk[kk * 2 * kLarge + (4 * jg + jj) * 16 + (lane & 15)];
+#pragma unroll
+                            for (int u2 = 0; u2 < 2; ++u2)
+#pragma unroll
+                                for (int jj = 0; jj < 4; ++jj)
+                                    acc2[u2][jj] = mfma_f64(av[kc][2 * uh + u2], z[jj], acc2[u2][jj]);
+                            if (kc == 0) {
+                                if (uh == 1) store_tiles(jg, 0);
+                                else if (jg > 0) store_tiles(jg - 1, 1);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int u2 = 0; u2 < 2; ++u2)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) pend[u2][jj][v] = (float)acc2[u2][jj][v];
+                }
+            }
+            store_tiles(2 * kLarge / 64 - 1, 1);
+        }
+        for (int jg = 0; jg < (FULL && PARKED ? 0 : 2 * kLarge / 64); ++jg) {
             dbl4 acc4[4][4];
 #pragma unroll
             for (int ub = 0; ub < 4; ++ub)
