@@ -422,6 +422,10 @@ constexpr int kSmallBwdMaxK = 64;    // backward: whole K-loop on chip
 constexpr int kSmallXS = kSmall + 2;             // padded LDS row stride (floats)
 constexpr int kSmallZW = 2 * kSmall;             // [x | h_prev] width
 constexpr int kSmallZS = kSmallZW + 2;
+// Row stride (doubles) of the one-row kernels' a / dL/da array: 4 doubles of
+// padding put the 16 rows that one matrix-core operand read touches in
+// different LDS banks (with 128 doubles per row they all fell in one).
+constexpr int kSmallAS = kSmall + 4;
 
 __host__ __device__ constexpr size_t small_fwd_lds_bytes() {
     return (size_t)8 * kSmallFwdKW * kSmall + (size_t)8 * 2 * kSmall +
@@ -431,7 +435,7 @@ __host__ __device__ constexpr size_t small_fwd_lds_bytes() {
 // contractions run without row guards.
 constexpr int kSmallGS = 64 + 4;  // row stride (floats) of a wave's gradient-tile buffer
 __host__ __device__ constexpr size_t small_bwd_lds_bytes() {
-    return (size_t)8 * kSmallBwdMaxK * kSmall + 8 * 8 +
+    return (size_t)8 * kSmallBwdMaxK * kSmallAS + 8 * 8 +
            (size_t)4 * kSmallBwdMaxK * kSmallZS + (size_t)4 * 4 * 16 * kSmallGS;
 }
 
@@ -652,7 +656,7 @@ __device__ __forceinline__ void small_reverse_and_grads(
     float* gst, float* __restrict__ row, float* __restrict__ loss_b, float* __restrict__ gx_row,
     float* __restrict__ gh0_row, int accumulate, int lane, int wave, int jb, int ib, int o,
     bool gate_lane) {
-    constexpr int HP = kSmall, NP = kSmall, ZW = kSmallZW, ZS = kSmallZS;
+    constexpr int HP = kSmall, NP = kSmall, ZW = kSmallZW, ZS = kSmallZS, AS = kSmallAS;
     constexpr int KP = kSmallBwdMaxK;
     // ---- W_rec^T slice into registers
     double wt[8][8];
@@ -676,7 +680,7 @@ __device__ __forceinline__ void small_reverse_and_grads(
     // dL/da_k-1 one step later, by the same lane pair).
     double gb = 0.0, gwt = 0.0;
     auto step_consts = [&](int k, double& g, double& Q, double& R) {
-        const double a = AD[k * HP + o];
+        const double a = AD[k * AS + o];
         const double hk = (double)zs[k * ZS + NP + o];
         double c;
         cell_gates(a, gl, g, c);
@@ -690,11 +694,11 @@ __device__ __forceinline__ void small_reverse_and_grads(
         const double da = delta * Q;
         gb += da;
         gwt += delta * R;
-        if (!gate_lane) AD[k * HP + o] = da;
+        if (!gate_lane) AD[k * AS + o] = da;
         __syncthreads();
         if (k == 0 && !gh0_row) break;
         double dj[8];
-        chain_read(dj, AD + k * HP, jb);
+        chain_read(dj, AD + k * AS, jb);
         // next step's constants (unused after k = 0), in the same block as
         // the products so that their latency overlaps them
         double gn, Qn, Rn;
@@ -711,7 +715,7 @@ __device__ __forceinline__ void small_reverse_and_grads(
     {
         const int ib0 = 2 * wave;
         constexpr int KC = KP / 4;
-        const double* ada = AD + (lane >> 4) * HP + ib0 * 16 + (lane & 15);
+        const double* ada = AD + (lane >> 4) * AS + ib0 * 16 + (lane & 15);
         const float* zb = zs + (lane >> 4) * ZS + (lane & 15);
         // Overwrite mode at exactly 128 x 128 with 16-byte-aligned rows: no
         // masking, and each group's tiles are stored while the next group's
@@ -754,7 +758,7 @@ __device__ __forceinline__ void small_reverse_and_grads(
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) {
                     const int kn = kc + 1 < KC ? kc + 1 : kc;
-                    const double na0 = ada[4 * kn * HP], na1 = ada[4 * kn * HP + 16];
+                    const double na0 = ada[4 * kn * AS], na1 = ada[4 * kn * AS + 16];
                     double nbz[4];
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) nbz[jj] = (double)zb[4 * kn * ZS + (jg * 4 + jj) * 16];
@@ -792,7 +796,7 @@ __device__ __forceinline__ void small_reverse_and_grads(
             for (int jj = 0; jj < 4; ++jj) bz[jj] = (double)zb[(jg * 4 + jj) * 16];
             for (int kc = 0; kc < KC; ++kc) {
                 const int kn = kc + 1 < KC ? kc + 1 : kc;
-                const double na0 = ada[4 * kn * HP], na1 = ada[4 * kn * HP + 16];
+                const double na0 = ada[4 * kn * AS], na1 = ada[4 * kn * AS + 16];
                 double nbz[4];
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) nbz[jj] = (double)zb[4 * kn * ZS + (jg * 4 + jj) * 16];
@@ -883,7 +887,7 @@ __device__ __forceinline__ void small_reverse_and_grads(
                 const int i = 4 * c + q;
                 const double w = (i < H && j < n_in) ? (double)w_in[(long long)i * n_in + j] : 0.0;
 #pragma unroll
-                for (int kt = 0; kt < KP / 16; ++kt) acc[kt] = mfma_f64(AD[(kt * 16 + m) * HP + i], w, acc[kt]);
+                for (int kt = 0; kt < KP / 16; ++kt) acc[kt] = mfma_f64(AD[(kt * 16 + m) * AS + i], w, acc[kt]);
             }
             if (j < n_in) {
 #pragma unroll
@@ -909,8 +913,9 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     const long long Kf = win.K, k0 = win.k0;
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int KP = kSmallBwdMaxK;
-    double* AD = reinterpret_cast<double*>(smem);  // [KP][HP]: a, then dL/da
-    double* red = AD + KP * HP;                    // [8]
+    constexpr int AS = kSmallAS;
+    double* AD = reinterpret_cast<double*>(smem);  // [KP][AS]: a, then dL/da
+    double* red = AD + KP * AS;                    // [8]
     float* zs = reinterpret_cast<float*>(red + 8);  // [KP][ZS] = [x_k | h_k]
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -972,7 +977,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int kk = kb * 16 + (lane >> 4) + 4 * v;
-                double* arow = AD + kk * HP + (2 * wave) * 16 + (lane & 15);
+                double* arow = AD + kk * AS + (2 * wave) * 16 + (lane & 15);
                 arow[0] = kk < K ? acc[kb][0][v] + bias_q0 : 0.0;
                 arow[16] = kk < K ? acc[kb][1][v] + bias_q1 : 0.0;
             }
@@ -1006,8 +1011,9 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     int cell) {
     constexpr int HP = kSmall, NP = kSmall, ZS = kSmallZS, KP = kSmallBwdMaxK;
     extern __shared__ __align__(16) unsigned char smem[];
-    double* AD = reinterpret_cast<double*>(smem);  // [KP][HP]: W_in x_k + b, then a_k, then dL/da_k
-    double* red = AD + KP * HP;                    // [8]
+    constexpr int AS = kSmallAS;
+    double* AD = reinterpret_cast<double*>(smem);  // [KP][AS]: W_in x_k + b, then a_k, then dL/da_k
+    double* red = AD + KP * AS;                    // [8]
     double* hb = red + 8;                          // [2][HP] h_k exchange
     float* zs = reinterpret_cast<float*>(hb + 2 * HP);  // [KP][ZS] = [x_k | h_k-1]
 
@@ -1061,7 +1067,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int kk = kb * 16 + (lane >> 4) + 4 * v;
-                double* urow = AD + kk * HP + (2 * wave) * 16 + (lane & 15);
+                double* urow = AD + kk * AS + (2 * wave) * 16 + (lane & 15);
                 urow[0] = kk < K ? acc[kb][0][v] + bias_q0 : 0.0;
                 urow[16] = kk < K ? acc[kb][1][v] + bias_q1 : 0.0;
             }
@@ -1076,7 +1082,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     __syncthreads();
     int cur = 0;
     for (int k = 0; k < K; ++k) {
-        const double u = AD[k * HP + o];
+        const double u = AD[k * AS + o];
         double hj[8];
         chain_read(hj, hb + cur * HP, jb);
         const double a = u + chain_product(wr, hj);
@@ -1085,7 +1091,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
         const double hn = fma(g, hprev - c, c);
         hprev = hn;
         // both lanes of the pair hold the same bits: both store, no branch
-        AD[k * HP + o] = a;
+        AD[k * AS + o] = a;
         hb[(cur ^ 1) * HP + o] = hn;
         if (k + 1 < K) zs[(k + 1) * ZS + NP + o] = (float)hn;
         if (o < H) h_seq[(b * K + k) * (long long)H + o] = (float)hn;
