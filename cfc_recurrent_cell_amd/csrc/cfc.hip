@@ -876,16 +876,28 @@ __device__ __forceinline__ void small_reverse_and_grads(
     // B = W_in[i][16jt + lane%16] from L2)
     if (gx_row) {
         const int m = lane & 15, q = lane >> 4;
+        // the wave's whole W_in operand (both column tiles, 64 floats per
+        // lane) is loaded first, so its latency is exposed once
+        float wv[2][HP / 4];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = (2 * wave + jj) * 16 + m;
+#pragma unroll
+            for (int c = 0; c < HP / 4; ++c) {
+                const int i = 4 * c + q;
+                wv[jj][c] = (i < H && j < n_in) ? w_in[(long long)i * n_in + j] : 0.f;
+            }
+        }
 #pragma unroll 1
         for (int jj = 0; jj < 2; ++jj) {
             const int j = (2 * wave + jj) * 16 + m;
             dbl4 acc[KP / 16];
 #pragma unroll
             for (int kt = 0; kt < KP / 16; ++kt) acc[kt] = dbl4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 8
+#pragma unroll
             for (int c = 0; c < HP / 4; ++c) {
                 const int i = 4 * c + q;
-                const double w = (i < H && j < n_in) ? (double)w_in[(long long)i * n_in + j] : 0.0;
+                const double w = (double)(jj == 0 ? wv[0][c] : wv[1][c]);
 #pragma unroll
                 for (int kt = 0; kt < KP / 16; ++kt) acc[kt] = mfma_f64(AD[(kt * 16 + m) * AS + i], w, acc[kt]);
             }
@@ -1090,9 +1102,12 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
         cell_gates(a, gl, g, c);
         const double hn = fma(g, hprev - c, c);
         hprev = hn;
-        // both lanes of the pair hold the same bits: both store, no branch
-        AD[k * AS + o] = a;
+        // both lanes of the pair hold the same bits: both store, no branch.
+        // The state the next step reads goes first; the scheduling barrier
+        // keeps the other stores' conversions from being hoisted above it.
         hb[(cur ^ 1) * HP + o] = hn;
+        __builtin_amdgcn_sched_barrier(0);
+        AD[k * AS + o] = a;
         if (k + 1 < K) zs[(k + 1) * ZS + NP + o] = (float)hn;
         if (o < H) h_seq[(b * K + k) * (long long)H + o] = (float)hn;
         cur ^= 1;
