@@ -26,6 +26,7 @@
 #include <cmath>
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "cfc.h"
 
@@ -92,9 +93,10 @@ __host__ __device__ inline size_t bwd_lds_bytes(int K, int n_in, int H) {
            (size_t)4 * K * H;
 }
 
+// Accumulate mode adds this call's gradient, rounded to float32, to the stored
+// value in float32 (a float32 += into the scratch), in every kernel.
 __device__ __forceinline__ void store_grad(float* p, double v, int accumulate) {
-    if (accumulate) v += (double)*p;
-    *p = (float)v;
+    *p = accumulate ? (float)v + *p : (float)v;
 }
 
 __global__ __launch_bounds__(kThreads) void cfc_bwd_kernel(
@@ -636,8 +638,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
 }
 
 __device__ __forceinline__ void store_grad_f(float* p, double v, int accumulate) {
-    if (accumulate) v += (double)*p;
-    *p = (float)v;
+    *p = accumulate ? (float)v + *p : (float)v;
 }
 
 // Second half of a row's backward pass, shared by cfc_bwd_small_kernel and
@@ -717,71 +718,88 @@ __device__ __forceinline__ void small_reverse_and_grads(
         constexpr int KC = KP / 4;
         const double* ada = AD + (lane >> 4) * AS + ib0 * 16 + (lane & 15);
         const float* zb = zs + (lane >> 4) * ZS + (lane & 15);
-        // Overwrite mode at exactly 128 x 128 with 16-byte-aligned rows: no
+        // Exactly 128 x 128 with 16-byte-aligned rows (either mode): no
         // masking, and each group's tiles are stored while the next group's
         // products run (the groups' stores otherwise wait for their products)
-        const bool interleave = !accumulate && n_in == NP && H == HP &&
-                                (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+        const bool interleave = n_in == NP && H == HP && (reinterpret_cast<uintptr_t>(row) & 15) == 0;
         if (interleave) {
             const int c4 = 4 * (lane & 15);
             // the previous group's tiles (float32, MFMA layout) and one step
             // of their store: kc 0..3 / 8..11 write tile q's columns jj = kc % 4
             // into the wave's LDS buffer, kc 4..7 / 12..15 read back row
             // block m = kc % 4 transposed and store it (float4, 256 bytes per
-            // 16 lanes)
-            float pend[2][4][4];
-            auto store_step = [&](int jgp, int kc) {
-                const int q = kc >> 3, st = kc & 7;
-                if (st < 4) {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        gst[((lane >> 4) + 4 * v) * kSmallGS + st * 16 + (lane & 15)] = pend[q][st][v];
-                } else {
-                    const int r = (lane >> 4) + 4 * (st - 4);
-                    const float4 val = *reinterpret_cast<const float4*>(gst + r * kSmallGS + c4);
-                    const int i = (ib0 + q) * 16 + r;
+            // 16 lanes).  Accumulate mode loads the old values of row block m
+            // four chunks ahead (at kc m / 8 + m) and adds the float32 tile to
+            // them in float32, as a float32 += into the scratch would.
+            // one instance of the loop per mode, so neither carries a branch
+            auto run = [&](auto acc_mode) {
+                constexpr bool ACC = decltype(acc_mode)::value;
+                float pend[2][4][4];
+                float4 old4[4];
+                auto dst_of = [&](int jgp, int q, int m) -> float* {
+                    const int i = (ib0 + q) * 16 + (lane >> 4) + 4 * m;
                     const int jc0 = jgp * 64 + c4;
-                    float* dst = jc0 < NP ? row + (long long)i * NP + jc0 : rrec + (long long)i * HP + (jc0 - NP);
-                    *reinterpret_cast<float4*>(dst) = val;
-                }
-            };
-            for (int jg = 0; jg < ZW / 64; ++jg) {
-                dbl4 acc[2][4];
+                    return jc0 < NP ? row + (long long)i * NP + jc0 : rrec + (long long)i * HP + (jc0 - NP);
+                };
+                auto store_step = [&](int jgp, int kc) {
+                    const int q = kc >> 3, st = kc & 7;
+                    if (st < 4) {
+                        if constexpr (ACC) old4[st] = *reinterpret_cast<const float4*>(dst_of(jgp, q, st));
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) acc[q][jj] = dbl4{0.0, 0.0, 0.0, 0.0};
-                double a0 = ada[0], a1 = ada[16];
-                double bz[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) bz[jj] = (double)zb[(jg * 4 + jj) * 16];
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    const int kn = kc + 1 < KC ? kc + 1 : kc;
-                    const double na0 = ada[4 * kn * AS], na1 = ada[4 * kn * AS + 16];
-                    double nbz[4];
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) nbz[jj] = (double)zb[4 * kn * ZS + (jg * 4 + jj) * 16];
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        acc[0][jj] = mfma_f64(a0, bz[jj], acc[0][jj]);
-                        acc[1][jj] = mfma_f64(a1, bz[jj], acc[1][jj]);
+                        for (int v = 0; v < 4; ++v)
+                            gst[((lane >> 4) + 4 * v) * kSmallGS + st * 16 + (lane & 15)] = pend[q][st][v];
+                    } else {
+                        const int m = st - 4, r = (lane >> 4) + 4 * m;
+                        float4 val = *reinterpret_cast<const float4*>(gst + r * kSmallGS + c4);
+                        if constexpr (ACC) {
+                            const float4 o = old4[m];
+                            val = make_float4(val.x + o.x, val.y + o.y, val.z + o.z, val.w + o.w);
+                        }
+                        *reinterpret_cast<float4*>(dst_of(jgp, q, m)) = val;
                     }
-                    if (jg > 0) store_step(jg - 1, kc);
-                    a0 = na0;
-                    a1 = na1;
+                };
+                for (int jg = 0; jg < ZW / 64; ++jg) {
+                    dbl4 acc[2][4];
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) bz[jj] = nbz[jj];
+                    for (int q = 0; q < 2; ++q)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) acc[q][jj] = dbl4{0.0, 0.0, 0.0, 0.0};
+                    double a0 = ada[0], a1 = ada[16];
+                    double bz[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) bz[jj] = (double)zb[(jg * 4 + jj) * 16];
+#pragma unroll
+                    for (int kc = 0; kc < KC; ++kc) {
+                        const int kn = kc + 1 < KC ? kc + 1 : kc;
+                        const double na0 = ada[4 * kn * AS], na1 = ada[4 * kn * AS + 16];
+                        double nbz[4];
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) nbz[jj] = (double)zb[4 * kn * ZS + (jg * 4 + jj) * 16];
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            acc[0][jj] = mfma_f64(a0, bz[jj], acc[0][jj]);
+                            acc[1][jj] = mfma_f64(a1, bz[jj], acc[1][jj]);
+                        }
+                        if (jg > 0) store_step(jg - 1, kc);
+                        a0 = na0;
+                        a1 = na1;
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) bz[jj] = nbz[jj];
+                    }
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) pend[q][jj][v] = (float)acc[q][jj][v];
                 }
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) pend[q][jj][v] = (float)acc[q][jj][v];
-            }
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) store_step(ZW / 64 - 1, kc);
+                for (int kc = 0; kc < KC; ++kc) store_step(ZW / 64 - 1, kc);
+            };
+            if (accumulate)
+                run(std::integral_constant<bool, true>{});
+            else
+                run(std::integral_constant<bool, false>{});
         }
         for (int jg = 0; jg < (interleave ? 0 : ZW / 64); ++jg) {
             dbl4 acc[2][4];

@@ -130,8 +130,8 @@ int cfc_forward(const cfc_params_t *params, const float *x, const float *h0, flo
  *            row b = dL_b / d(W_in, W_rec, b, w_tau) in the row layout above.
  *            flags = CFC_OVERWRITE: each row is written once with this call's
  *            gradient (equivalent to the pages' memset + K accumulating calls).
- *            flags = CFC_ACCUMULATE: each row is read and this call's gradient
- *            added (float64 add, one float32 rounding).
+ *            flags = CFC_ACCUMULATE: each row is read and this call's gradient,
+ *            rounded to float32, is added to it in float32 (scratch += g).
  *   loss     [B] OUTPUT or NULL: L_b per row
  *   grad_x   [B, K, n_in] OUTPUT or NULL: dL/dx_k = W_in^T dL/da_k for every
  *            step (overwritten whatever the flags)

@@ -196,3 +196,36 @@ def test_fused_wide_parked_preactivations(case):
                                                                d1["h0"], d1["y"], d1["dt"], cell=cell)]
         assert np.array_equal(h1[0].view(np.uint32), h[r].view(np.uint32))
         assert np.array_equal(s1[0].view(np.uint32), s[r].view(np.uint32))
+
+
+@pytest.mark.parametrize("entry", ["fused", "separate"])
+def test_accumulate_at_full_width_adds_float32(entry):
+    """At 128 x 128 the weight gradients are stored from float32 tiles: in
+    accumulate mode every scratch element becomes the float32 sum of its old
+    value and the overwrite-mode value (bitwise), and onto zeros accumulate
+    equals overwrite."""
+    import torch
+    import cfc_recurrent_cell_amd as C
+    inp = W.make_random_cfc_inputs(3, 64, 128, 128, 0.5, 56)
+    d = to_dev(inp)
+    say(f"[fused] accumulate at 128x128, {entry}")
+    args = (d["w_in"], d["w_rec"], d["b"], d["w_tau"], d["x"], d["h0"])
+
+    def run(scratch, accumulate):
+        if entry == "fused":
+            C.cfc_forward_backward(*args, d["y"], d["dt"], scratch=scratch, accumulate=accumulate)
+        else:
+            h = C.cfc_forward(*args, d["dt"])
+            C.cfc_backward(*args, h, d["y"], d["dt"], scratch=scratch, accumulate=accumulate)
+        return scratch
+
+    N = W.scratch_row_len(128, 128)
+    over = host(run(torch.full((3, N), float("nan"), device="cuda"), False)).copy()
+    zero = host(run(torch.zeros((3, N), device="cuda"), True))
+    assert np.array_equal(zero.view(np.uint32), over.view(np.uint32))
+    base = W.make_random_matrix(3, N, seed=57)
+    acc = host(run(torch.from_numpy(base.copy()).cuda(), True))
+    want = base.astype(np.float32) + over.astype(np.float32)
+    assert np.array_equal(acc.view(np.uint32), want.view(np.uint32))
+    ref = O.cfc_step(inp, threads=oracle_threads())
+    assert_close(over, ref["scratch"], "overwrite scratch at 128x128")
