@@ -1853,9 +1853,9 @@ __global__ __launch_bounds__(kThreads) void reduce_axis0_kernel(const float* __r
 // owns column t % N and starts at row t / N of the chunk, stepping RP = T / N
 // rows, 8 rows' loads in flight, accumulating in float64.  The RP sums of each
 // column are then combined by a fixed pairwise tree through LDS, and thread
-// j < N writes the chunk's sum of column j.  Phase 1 reads the float32 input
-// and writes float64 partials [P][N]; phase 2 is the same kernel over the
-// partials as one chunk, writing float32.
+// j < N writes the chunk's sum of column j.  This is phase 1: it reads the
+// float32 input and writes float64 partials [P][N]; reduce_partials_kernel is
+// phase 2.
 template <typename TIn, typename TOut>
 __global__ __launch_bounds__(kThreads) void reduce_rows_narrow_kernel(const TIn* __restrict__ in, long long B,
                                                                       int N, long long R,
@@ -1889,6 +1889,39 @@ __global__ __launch_bounds__(kThreads) void reduce_rows_narrow_kernel(const TIn*
         __syncthreads();
     }
     if (t < N) out[(long long)blockIdx.x * N + t] = (TOut)red[t];
+}
+
+// Second phase of the split reduce: the P float64 partial rows [P][N] summed
+// per column.  A workgroup owns 8 consecutive columns and has 32 row slots:
+// thread t reads column 8g + t % 8 in rows t / 8, t / 8 + 32, ... (8 loads in
+// flight), then the 32 slot sums of each column are combined by a fixed
+// pairwise tree through LDS.  The order depends only on (P, N).
+constexpr int kPartCols = 8, kPartSlots = kThreads / kPartCols;
+__global__ __launch_bounds__(kThreads) void reduce_partials_kernel(const double* __restrict__ part, long long P,
+                                                                   int N, float* __restrict__ out) {
+    __shared__ double red[kPartSlots][kPartCols + 1];
+    const int t = threadIdx.x, c = t % kPartCols, slot = t / kPartCols;
+    const int col = blockIdx.x * kPartCols + c;
+    double acc = 0.0;
+    if (col < N) {
+        const double* p = part + col;
+        long long r = slot;
+        for (; r + 7LL * kPartSlots < P; r += 8LL * kPartSlots) {
+            double q[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) q[u] = p[(r + (long long)u * kPartSlots) * N];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += q[u];
+        }
+        for (; r < P; r += kPartSlots) acc += p[r * N];
+    }
+    red[slot][c] = acc;
+    __syncthreads();
+    for (int w = 1; w < kPartSlots; w *= 2) {
+        if (slot % (2 * w) == 0 && slot + w < kPartSlots) red[slot][c] += red[slot + w][c];
+        __syncthreads();
+    }
+    if (slot == 0 && col < N) out[col] = (float)red[0][c];
 }
 
 // ---------------------------------------------------------- host helpers
@@ -2169,10 +2202,10 @@ extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, 
 
 // Chunking of the split reduce; it depends only on (B, N), so the summation
 // order -- and the result -- is the same on every device.  At most 1024
-// chunks and 64 K partials (512 KB) for the one-workgroup second phase; each
-// chunk is at least 8 passes of RP rows.
+// chunks and 256 K partials (2 MB of workspace); each chunk is at least 8
+// passes of RP rows.
 constexpr long long kSplitMaxChunks = 1024;
-constexpr long long kSplitMaxPartials = 65536;
+constexpr long long kSplitMaxPartials = 262144;
 struct SplitPlan {
     long long R, P;
 };
@@ -2207,8 +2240,8 @@ extern "C" int reduce_axis0_split(const float* per_batch, long long B, long long
     double* part = static_cast<double*>(workspace);
     hipLaunchKernelGGL((reduce_rows_narrow_kernel<float, double>), dim3((unsigned)sp.P), dim3(kThreads), 0, stream,
                        per_batch, B, (int)N, sp.R, part);
-    hipLaunchKernelGGL((reduce_rows_narrow_kernel<double, float>), dim3(1), dim3(kThreads), 0, stream,
-                       (const double*)part, sp.P, (int)N, sp.P, out);
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)((N + kPartCols - 1) / kPartCols)), dim3(kThreads), 0,
+                       stream, (const double*)part, sp.P, (int)N, out);
     return launch_status();
 }
 

@@ -186,7 +186,7 @@ def test_reduce_validation(lib):
 
 def test_split_reduce_workspace_sizes(lib):
     """Chunking depends only on (B, N): 256 // N rows per pass, at least 8
-    passes per chunk, at most 1024 chunks and 64 K partials."""
+    passes per chunk, at most 1024 chunks and 256 K partials."""
     ws = lib.reduce_axis0_split_workspace
     # N = 3: 85 rows per pass, chunks of max(ceil(524288/1024), 680) = 680 rows -> 772 chunks
     assert ws(524288, 3) == 772 * 3 * 8
@@ -195,9 +195,12 @@ def test_split_reduce_workspace_sizes(lib):
     assert ws(100000, 0) == 0
     assert ws(-1, 3) == -1 and ws(3, -1) == -1
     assert ws(2**40, 2**40) == -1            # B*N*4 overflows
-    # N = 256: one row per pass, 8-row chunks, 256 chunks at most (64 K partials):
-    # 20000 rows -> chunks of ceil(20000/256) = 79 rows -> 254 chunks
-    assert ws(20000, 256) == 254 * 256 * 8
+    # N = 256: one row per pass, at least 8-row chunks, 1024 chunks at most
+    # (256 K partials): 20000 rows -> chunks of ceil(20000/1024) = 20 rows -> 1000 chunks
+    assert ws(20000, 256) == 1000 * 256 * 8
+    # N = 200: one row per pass, 1024 chunks at most (1310 by the partials cap):
+    # 300000 rows -> chunks of ceil(300000/1024) = 293 rows -> 1024 chunks
+    assert ws(300000, 200) == 1024 * 200 * 8
     assert ws(2048, 256) == 256 * 256 * 8
     assert ws(16, 256) == 2 * 256 * 8
 
