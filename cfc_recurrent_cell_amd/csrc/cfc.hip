@@ -280,6 +280,23 @@ constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141;
 
 constexpr int kDppRor8 = 0x128;  // row_ror:8: lane i of each 16-lane row reads lane i ^ 8
 
+// Sum of v over the 64 lanes of the wave, in every lane: within each 16-lane
+// row by DPP (xor 1, xor 2, half-mirror, ror 8), then the four row sums read
+// out by lane.  A fixed order, and no LDS round trips.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v += dpp_move<kDppXor1>(v);
+    v += dpp_move<kDppXor2>(v);
+    v += dpp_move<kDppHalfMirror>(v);
+    v += dpp_move<kDppRor8>(v);
+    auto lane_value = [](double x, int l) {
+        const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+        const unsigned lo = __builtin_amdgcn_readlane((int)(unsigned)u, l);
+        const unsigned hi = __builtin_amdgcn_readlane((int)(unsigned)(u >> 32), l);
+        return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+    };
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
 // Serial-chain layout of the one-row kernels.  The 16 lanes of a DPP row
 // (jb = lane bits 0..3) share the row block ib = 4*wave + lane/16, i.e. units
 // 8ib .. 8ib+7, and lane jb takes the column block 8jb .. 8jb+7 of the step's
@@ -507,7 +524,52 @@ __device__ __forceinline__ void load_span_f64(double (&dst)[COUNT], const float*
 // outside the H x H matrix.
 __device__ __forceinline__ void load_chain_weights(double (&w)[8][8], const float* __restrict__ w_rec, int H,
                                                    const ChainLane& cl, bool transposed) {
-    if (!transposed) {
+    if ((H & 3) == 0 && (reinterpret_cast<uintptr_t>(w_rec) & 15) == 0) {
+        // every float4 chunk of a lane's span is wholly inside or outside its
+        // row (the same for all lanes): the 16 loads go out together from
+        // in-range addresses, then out-of-range elements are zeroed, so one
+        // load latency is exposed instead of one per row.  The slot order
+        // (slot s holds unit s ^ x) comes from the addresses where it can:
+        // the forward's slots are rows (row r0 + (s ^ x) is loaded into slot
+        // s); the backward's are columns of the span, so bit 2 of x picks
+        // the float4 half and bits 1, 0 swap within it (float32 selects).
+        const int x = chain_unit_xor(cl.jb);
+        const int r0 = transposed ? 8 * cl.jb : 8 * cl.ib, c0 = transposed ? 8 * cl.ib : 8 * cl.jb;
+        float4 raw[8][2];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int row = transposed ? r0 + r : r0 + (r ^ x);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int half = transposed ? m ^ ((x >> 2) & 1) : m;
+                raw[r][m] = *reinterpret_cast<const float4*>(w_rec + (long long)min(row, H - 1) * H +
+                                                             min(c0 + 4 * half, H - 4));
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                float4 v4 = raw[r][m];
+                if (transposed) {
+                    if (x & 1) v4 = make_float4(v4.y, v4.x, v4.w, v4.z);
+                    if (x & 2) v4 = make_float4(v4.z, v4.w, v4.x, v4.y);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int sc = 4 * m + e;  // slot (transposed) or column (forward)
+                    const float v = e == 0 ? v4.x : e == 1 ? v4.y : e == 2 ? v4.z : v4.w;
+                    if (transposed) {
+                        const bool ok = r0 + r < H && c0 + (sc ^ x) < H;
+                        w[sc][r] = ok ? (double)v : 0.0;
+                    } else {
+                        const bool ok = r0 + (r ^ x) < H && c0 + sc < H;
+                        w[r][sc] = ok ? (double)v : 0.0;
+                    }
+                }
+            }
+        return;
+    } else if (!transposed) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int row = 8 * cl.ib + r;
@@ -665,8 +727,7 @@ __device__ __forceinline__ void small_reverse_and_grads(
 
     // ---- loss seed
     {
-        double l = gate_lane ? 0.0 : 0.5 * delta * delta;
-        for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+        const double l = wave_sum_f64(gate_lane ? 0.0 : 0.5 * delta * delta);
         if (lane == 0) red[wave] = l;
     }
     const GateLane gl = gate_lane_consts(gate_lane, ug);
