@@ -10,10 +10,13 @@ cfc_backward instead.  Both paths are timed in every run; the other one is
 reported in "other_path".
 
 Prints ONE JSON line.  `value` is batch-steps/s = B*K / seconds per step.
-The roofline object describes the step's dominant kernel, timed with HIP
-events recorded around each launch on the stream the kernel runs on, inside
-the timed region.  The cpu_baseline object times the float64 oracle on the
-host (one thread) on a bounded sample of the same workload.
+Each path is run twice: a breakdown pass with HIP events around every launch
+("kernels_ms"), then the timed pass that gives `value`, with events only
+around the step's dominant kernel (each event record costs the stream about
+2-3 us).  The roofline object describes that kernel, with its average
+duration from the events of the timed pass, recorded on the stream the
+kernel runs on.  The cpu_baseline object times the float64 oracle on the
+host on a bounded sample of the same workload (all cores, and one thread).
 """
 from __future__ import annotations
 
@@ -225,124 +228,100 @@ def main():
         args.path = "fused" if (n_in <= 128 and H <= 128 and K <= 64) or wide_parked else \
             "separate" if one_call_bwd_ok else "windows"
 
-    def step_separate(ev=None):
-        if ev is not None:
-            ev[0].record()
-        C.cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, h_seq=h_seq, cell=cell)
-        if ev is not None:
-            ev[1].record()
-        C.cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, scratch=scratch, loss=loss, cell=cell)
-        if ev is not None:
-            ev[2].record()
-        C.reduce_axis0(scratch, out=out)
-        if ev is not None:
-            ev[3].record()
-
-    def step_fused(ev=None):
-        if ev is not None:
-            ev[0].record()
-        C.cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt, h_seq=h_seq, scratch=scratch, loss=loss,
-                               cell=cell)
-        if ev is not None:
-            ev[1].record()
-        C.reduce_axis0(scratch, out=out)
-        if ev is not None:
-            ev[2].record()
-
     grad_x = torch.empty((B, K, n_in), device=dev)
     grad_h0 = torch.empty((B, H), device=dev)
-
-    def step_fused_ig(ev=None):
-        # the one-call path with the input gradients (dL/dx, dL/dh_0) requested too
-        if ev is not None:
-            ev[0].record()
-        C.cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt, h_seq=h_seq, scratch=scratch, loss=loss,
-                               grad_x=grad_x, grad_h0=grad_h0, cell=cell)
-        if ev is not None:
-            ev[1].record()
-        C.reduce_axis0(scratch, out=out)
-        if ev is not None:
-            ev[2].record()
-
-    def step_separate_ig(ev=None):
-        if ev is not None:
-            ev[0].record()
-        C.cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, h_seq=h_seq, cell=cell)
-        if ev is not None:
-            ev[1].record()
-        C.cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, scratch=scratch, loss=loss,
-                       grad_x=grad_x, grad_h0=grad_h0, cell=cell)
-        if ev is not None:
-            ev[2].record()
-        C.reduce_axis0(scratch, out=out)
-        if ev is not None:
-            ev[3].record()
-
     delta_carry = torch.empty((B, H), device=dev)
 
-    def step_windows(ev=None):
-        # forward, then the backward as windows of --window steps (dL/dh carried in place)
-        if ev is not None:
-            ev[0].record()
+    def fwd():
         C.cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, h_seq=h_seq, cell=cell)
-        if ev is not None:
-            ev[1].record()
+
+    def bwd(ig=False):
+        C.cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, scratch=scratch, loss=loss,
+                       grad_x=grad_x if ig else None, grad_h0=grad_h0 if ig else None, cell=cell)
+
+    def fb(ig=False, accumulate=False):
+        C.cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt, h_seq=h_seq, scratch=scratch, loss=loss,
+                               grad_x=grad_x if ig else None, grad_h0=grad_h0 if ig else None,
+                               accumulate=accumulate, cell=cell)
+
+    def windows():
+        # the backward as windows of --window steps (dL/dh carried in place)
         C.cfc_backward_windows(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt, args.window, scratch=scratch, loss=loss,
                                grad_h0=delta_carry, cell=cell)
-        if ev is not None:
-            ev[2].record()
-        C.reduce_axis0(scratch, out=out)
-        if ev is not None:
-            ev[3].record()
 
-    def step_fused_accumulate(ev=None):
+    def red():
+        C.reduce_axis0(scratch, out=out)
+
+    # each step is a list of (kernel name, launch); the names key kernels_ms
+    # and the roofline's kernel
+    STEPS = {
+        "fused": [("cfc_fb_kernel", fb), ("reduce_axis0_kernel", red)],
+        "fused_ig": [("cfc_fb_kernel", lambda: fb(ig=True)), ("reduce_axis0_kernel", red)],
+        "separate": [("cfc_fwd_kernel", fwd), ("cfc_bwd_kernel", bwd), ("reduce_axis0_kernel", red)],
+        "separate_ig": [("cfc_fwd_kernel", fwd), ("cfc_bwd_kernel", lambda: bwd(ig=True)),
+                        ("reduce_axis0_kernel", red)],
+        "windows": [("cfc_fwd_kernel", fwd), ("cfc_bwd_kernel", windows), ("reduce_axis0_kernel", red)],
         # the pages' clear-then-accumulate form: explicit zero fill, then += gradient
-        if ev is not None:
-            ev[0].record()
-        scratch.zero_()
-        C.cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt, h_seq=h_seq, scratch=scratch, loss=loss,
-                               accumulate=True, cell=cell)
-        C.reduce_axis0(scratch, out=out)
-        if ev is not None:
-            ev[1].record()
+        "accumulate": [("zero_fill", scratch.zero_), ("cfc_fb_kernel", lambda: fb(accumulate=True)),
+                       ("reduce_axis0_kernel", red)],
+    }
 
-    def timed(path):
-        """W warm-up steps, then K steps bracketed by a sync on both sides, with
-        HIP events around every launch on the stream the launches use."""
-        step = {"fused": step_fused, "separate": step_separate, "accumulate": step_fused_accumulate,
-                "fused_ig": step_fused_ig, "separate_ig": step_separate_ig, "windows": step_windows}[path]
-        nev = {"fused": 3, "separate": 4, "accumulate": 2, "fused_ig": 3, "separate_ig": 4, "windows": 4}[path]
+    def run_pass(path, bracket):
+        """W warm-up steps, then K steps bracketed by a sync on both sides.
+        bracket=None records a HIP event around every launch (the per-kernel
+        breakdown); bracket=name records only the pair around that kernel's
+        launch.  An event record costs the stream about 2-3 us, so the pass
+        that gives the step time records just the one pair it needs."""
+        launches = STEPS[path]
         for _ in range(args.warmup):
-            step()
+            for _, f in launches:
+                f()
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+        names = [n for n, _ in launches if bracket is None or n == bracket]
+        evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+               for _ in range(args.steps)]
         t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t_start.record()
         for i in range(args.steps):
-            step(evs[i])
+            for n, f in launches:
+                e = evs[i].get(n)
+                if e is not None:
+                    e[0].record()
+                f()
+                if e is not None:
+                    e[1].record()
         t_end.record()
         torch.cuda.synchronize()
         ms = t_start.elapsed_time(t_end) / args.steps
-        per = lambda a, c: sum(e[a].elapsed_time(e[c]) for e in evs) / args.steps
-        if path in ("fused", "fused_ig"):
-            km = {"cfc_fb_kernel": per(0, 1), "reduce_axis0_kernel": per(1, 2)}
-        elif path in ("separate", "separate_ig", "windows"):
-            km = {"cfc_fwd_kernel": per(0, 1), "cfc_bwd_kernel": per(1, 2), "reduce_axis0_kernel": per(2, 3)}
-        else:
-            km = {}
-        steps_ms = sorted(e[0].elapsed_time(e[nev - 1]) for e in evs)
+        km = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in evs) / args.steps for n in names}
+        # per-step times: from one step's first event to the next step's
+        first = names[0]
+        marks = [e[first][0] for e in evs]
+        steps_ms = sorted([marks[i].elapsed_time(marks[i + 1]) for i in range(len(marks) - 1)] +
+                          [marks[-1].elapsed_time(t_end)])
         q = lambda f: steps_ms[min(len(steps_ms) - 1, int(f * len(steps_ms)))]
         return ms, km, {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9)}
+
+    def timed(path):
+        """A breakdown pass (events around every launch), then the timed pass:
+        events only around the step's dominant kernel, whose average duration
+        there is the roofline's.  Returns (ms per step of the timed pass, the
+        breakdown's kernel ms, the dominant kernel, its ms in the timed pass,
+        step-time percentiles of the timed pass)."""
+        _, k_all, _ = run_pass(path, None)
+        dom = max((n for n in k_all if n != "zero_fill"), key=k_all.get)
+        ms, k_dom, pct = run_pass(path, dom)
+        return ms, k_all, dom, k_dom[dom], pct
 
     other = "separate" if args.path == "fused" else "fused"
     if args.path == "windows":
         args.main_only = True   # the other one-call paths refuse this K
     if not args.main_only:
-        ms_other, k_other, _ = timed(other)
-        ms_acc, _, pct_acc = timed("accumulate")
-        ms_ig, k_ig, pct_ig = timed(args.path + "_ig")
-    ms_per_step, k_ms, pct = timed(args.path + ("_ig" if args.input_grads else ""))
+        ms_other, k_other, _, _, _ = timed(other)
+        ms_acc, _, _, _, pct_acc = timed("accumulate")
+        ms_ig, k_ig, _, _, pct_ig = timed(args.path + "_ig")
+    ms_per_step, k_ms, dom, dom_ms, pct = timed(args.path + ("_ig" if args.input_grads else ""))
     work = algorithmic_work(B, K, n_in, H)
     flops = {"cfc_fwd_kernel": work["fwd_flops"], "cfc_bwd_kernel": work["bwd_flops"],
              "cfc_fb_kernel": work["fb_flops"], "reduce_axis0_kernel": 0}
@@ -352,19 +331,19 @@ def main():
         for kname in ("cfc_bwd_kernel", "cfc_fb_kernel"):
             flops[kname] += B * K * 2 * H * n_in + B * 2 * H * H
             nbytes[kname] += 4 * (B * K * n_in + B * H)
-    dom = max(k_ms, key=k_ms.get)
     # the bound is the roofline the kernel's algorithmic intensity falls under:
     # below the f64 ridge (78.6 TFLOP/s / 8 TB/s = 9.8 FLOP/B) it is HBM
     ridge = PEAK_F64_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
     if flops[dom] / nbytes[dom] < ridge:
-        ach = nbytes[dom] / (k_ms[dom] * 1e-3) / 1e9
+        ach = nbytes[dom] / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": ach / PEAK_HBM_GBPS}
     else:
-        ach = flops[dom] / (k_ms[dom] * 1e-3) / 1e12
+        ach = flops[dom] / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "alu", "achieved": ach, "peak": PEAK_F64_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_F64_TFLOPS}
     roof["kernel"] = dom
+    roof["kernel_ms"] = dom_ms
     roof["algorithmic_flops_per_launch"] = flops[dom]
     roof["algorithmic_bytes_per_launch"] = nbytes[dom]
     roof["traffic"] = measured_traffic(cfg.name + ("_input_grads" if args.input_grads else ""), dom)
@@ -411,9 +390,9 @@ def main():
             "path": other, "value": B * K / (ms_other * 1e-3), "ms_per_step": ms_other, "kernels_ms": k_other},
         "reduce_axis0": {"GB_per_s": red_gbps, "frac_hbm": red_gbps / PEAK_HBM_GBPS,
                          "bytes": work["reduce_bytes"],
-                         "note": "HIP events around the launch inside the step (an empty launch measures about "
-                                 "6 us this way); the step's scratch (%.1f MB) was just written, so part of it may "
-                                 "be served from the MALL" % (work["reduce_bytes"] / 1e6)},
+                         "note": "HIP events around the launch inside the step, breakdown pass (an empty launch "
+                                 "measures about 6 us this way); the step's scratch (%.1f MB) was just written, so "
+                                 "part of it may be served from the MALL" % (work["reduce_bytes"] / 1e6)},
         "kernel_source_sha256_16": source_hash(),
     }
     if args.reduce_sweep:
