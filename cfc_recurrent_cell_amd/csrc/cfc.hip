@@ -360,37 +360,37 @@ __device__ __forceinline__ double chain_product(const double (&w)[8][8], const d
     return reduce_scatter16(p);
 }
 
-// e^x for |x| <= 700: x = n ln2 + r with the two-constant (Cody-Waite) split
-// of ln2, |r| <= ln2/2, e^r by its degree-13 Taylor polynomial (truncation
-// below 5e-18 relative) evaluated with Estrin's scheme for a short dependency
-// chain, then scaled by 2^n.
+// e^x for |x| <= 700: x = n ln2 + r with n = rint(x log2e) and r by one FMA
+// with ln2 rounded to double (the reduction error |n| 2.3e-17 is below
+// 1.5e-15 relative for |x| < 40 and below 2.4e-14 at |x| = 700), |r| <= ln2/2,
+// e^r by its degree-12 Taylor polynomial (truncation below 2e-16 relative)
+// evaluated with Estrin's scheme for a short dependency chain, then scaled by
+// 2^n.
 __device__ __forceinline__ double exp_f64(double x) {
     constexpr double kLog2e = 1.4426950408889634074;
-    constexpr double kLn2Hi = 6.93147180369123816490e-01;
-    constexpr double kLn2Lo = 1.90821492927058770002e-10;
+    constexpr double kLn2 = 0.69314718055994530942;
     const double n = __builtin_rint(x * kLog2e);
-    double r = fma(-n, kLn2Hi, x);
-    r = fma(-n, kLn2Lo, r);
+    const double r = fma(-n, kLn2, x);
     constexpr double c2 = 1.0 / 2, c3 = 1.0 / 6, c4 = 1.0 / 24, c5 = 1.0 / 120, c6 = 1.0 / 720,
                      c7 = 1.0 / 5040, c8 = 1.0 / 40320, c9 = 1.0 / 362880, c10 = 1.0 / 3628800,
-                     c11 = 1.0 / 39916800, c12 = 1.0 / 479001600, c13 = 1.0 / 6227020800.0;
+                     c11 = 1.0 / 39916800, c12 = 1.0 / 479001600;
     const double r2 = r * r, r4 = r2 * r2, r8 = r4 * r4;
     const double q0 = 1.0 + r, q1 = fma(c3, r, c2), q2 = fma(c5, r, c4), q3 = fma(c7, r, c6);
-    const double q4 = fma(c9, r, c8), q5 = fma(c11, r, c10), q6 = fma(c13, r, c12);
+    const double q4 = fma(c9, r, c8), q5 = fma(c11, r, c10);
     const double s0 = fma(q1, r2, q0), s1 = fma(q3, r2, q2), s2 = fma(q5, r2, q4);
-    const double t0 = fma(s1, r4, s0), t1 = fma(q6, r4, s2);
+    const double t0 = fma(s1, r4, s0), t1 = fma(c12, r4, s2);
     return ldexp(fma(t1, r8, t0), (int)n);
 }
 
 // 1 / (1 + e^z) for any finite z: |z| is clamped to 700 (beyond it the result
-// is 0 or 1 to double precision); reciprocal by v_rcp_f64 and two Newton steps.
+// is 0 or 1 to double precision).  The reciprocal is v_rcp_f64 (24 correct
+// bits, measured over a full binade) and one Newton step: about 2e-15
+// relative.
 __device__ __forceinline__ double inv_one_plus_exp(double z) {
     z = fmin(fmax(z, -700.0), 700.0);
     const double d = 1.0 + exp_f64(z);
-    double y = __builtin_amdgcn_rcp(d);
-    double e = fma(-d, y, 1.0);
-    y = fma(y, e, y);
-    e = fma(-d, y, 1.0);
+    const double y = __builtin_amdgcn_rcp(d);
+    const double e = fma(-d, y, 1.0);
     return fma(y, e, y);
 }
 
