@@ -1093,6 +1093,12 @@ __host__ __device__ constexpr size_t small_fb_lds_bytes() {
     return small_bwd_lds_bytes() + (size_t)8 * 2 * kSmall;
 }
 
+// WHOLE: K = 64, n_in = n_hid = 128, W_in and x 16-byte aligned (the host
+// checks); the staging then runs with no guards and fetches the projection's
+// weights while x is staged.  A separate instance, so that no code path joins
+// the generic one (where the wait for the staging's loads would be merged
+// conservatively into a wait for all of them).
+template <bool WHOLE>
 __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
@@ -1101,6 +1107,14 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     float* __restrict__ loss, float* __restrict__ grad_x, float* __restrict__ grad_h0, int accumulate,
     int cell) {
     constexpr int HP = kSmall, NP = kSmall, ZS = kSmallZS, KP = kSmallBwdMaxK;
+    // the shared reverse pass gets the sizes as passed; the instance's own
+    // phases take them as constants
+    const int K_arg = K, n_in_arg = n_in, H_arg = H;
+    if constexpr (WHOLE) {
+        K = KP;
+        n_in = NP;
+        H = HP;
+    }
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int AS = kSmallAS;
     double* AD = reinterpret_cast<double*>(smem);  // [KP][AS]: W_in x_k + b, then a_k, then dL/da_k
@@ -1119,24 +1133,85 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
 
     // ---- stage x (rows >= K zero), h0 as row 0 of the h_prev half (rows >= K
     // zero; rows 1..K-1 are written by the chain), per-unit constants
-    stage_rows(zs, ZS, x + b * K * (long long)n_in, n_in, K, n_in, KP, NP, t);
-    stage_rows(zs + NP, ZS, h0 + b * H, H, 1, H, 1, HP, t);
-    stage_rows(zs + K * ZS + NP, ZS, h0, H, 0, H, KP - K, HP, t);
-    for (int u = t; u < HP; u += kThreads) hb[u] = u < H ? (double)h0[b * H + u] : 0.0;
-    const UnitGate ug = unit_gate(cell, o < H ? (double)w_tau[o] : 0.0, dt, o < H);
-    const double bias_q0 = (2 * wave) * 16 + (lane & 15) < H ? (double)bias[(2 * wave) * 16 + (lane & 15)] : 0.0;
-    const double bias_q1 = (2 * wave + 1) * 16 + (lane & 15) < H ? (double)bias[(2 * wave + 1) * 16 + (lane & 15)] : 0.0;
+    // In the WHOLE instance the projection's weight operand (below) is fetched
+    // while x is staged: x's loads go first, then the small per-unit ones,
+    // then W_in's, then x's LDS writes, which wait for x's loads only.
+    const float* xb = x + b * K * (long long)n_in;
+    f32x4 wpre[2][NP / 16];
+    // the per-unit inputs, as floats: w_tau and h_0 of unit o, the bias of
+    // the projection's two output columns
+    float wtau_o, h0_o, bias0, bias1;
+    const int bcol0 = (2 * wave) * 16 + (lane & 15), bcol1 = bcol0 + 16;
+    if constexpr (WHOLE) {
+        // every load is unconditional (all indices are in range here), and
+        // all go out before W_in's 16 float4 (vmcnt retires in order)
+        static_assert(KP * (NP / 4) == 8 * kThreads, "one pass of 8 float4 per thread");
+        f32x4 xv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) xv[u] = reinterpret_cast<const f32x4*>(xb)[t + u * kThreads];
+        const float h0_t = h0[b * H + (t & (HP - 1))];
+        wtau_o = w_tau[o];
+        h0_o = h0[b * H + o];
+        bias0 = bias[bcol0];
+        bias1 = bias[bcol1];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const f32x4* src = reinterpret_cast<const f32x4*>(w_in + ((2 * wave + q) * 16 + (lane & 15)) * NP + 32 * slot);
+#pragma unroll
+            for (int m = 0; m < NP / 16; ++m) wpre[q][m] = src[m];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = t + u * kThreads, r = e / (NP / 4), c4 = e % (NP / 4);
+            float2* d = reinterpret_cast<float2*>(zs + r * ZS + 4 * c4);
+            d[0] = make_float2(xv[u][0], xv[u][1]);
+            d[1] = make_float2(xv[u][2], xv[u][3]);
+        }
+        // h_0 into row 0's h_prev half and the h exchange (threads t and
+        // t + 128 write the same value)
+        zs[NP + (t & (HP - 1))] = h0_t;
+        hb[t & (HP - 1)] = (double)h0_t;
+    } else {
+        (void)wpre;
+        stage_rows(zs, ZS, xb, n_in, K, n_in, KP, NP, t);
+        stage_rows(zs + NP, ZS, h0 + b * H, H, 1, H, 1, HP, t);
+        stage_rows(zs + K * ZS + NP, ZS, h0, H, 0, H, KP - K, HP, t);
+        for (int u = t; u < HP; u += kThreads) hb[u] = u < H ? (double)h0[b * H + u] : 0.0;
+        wtau_o = o < H ? w_tau[o] : 0.f;
+        h0_o = o < H ? h0[b * H + o] : 0.f;
+        bias0 = bcol0 < H ? bias[bcol0] : 0.f;
+        bias1 = bcol1 < H ? bias[bcol1] : 0.f;
+    }
+    const UnitGate ug = unit_gate(cell, (double)wtau_o, dt, WHOLE || o < H);  // o < 128 = H in WHOLE
+    const double bias_q0 = bias0, bias_q1 = bias1;
     __syncthreads();
 
     // ---- input projection of all K steps on the matrix cores: chunk jc of
     // k-slot s contracts j = 32*s + jc, a contiguous span of a W_in row
     {
         double wb[2][NP / 4];
+        if constexpr (WHOLE) {
+            // the empty asm takes the loaded registers here, after the
+            // barrier, so the wait for them and their widening are not hoisted
+            // above the staging's later loads
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int row = (2 * wave + q) * 16 + (lane & 15);
-            const int valid = row < H ? min(max(n_in - 32 * slot, 0), NP / 4) : 0;
-            load_span_f64<NP / 4>(wb[q], w_in + (long long)min(row, H - 1) * n_in + min(32 * slot, n_in - 1), valid);
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int m = 0; m < NP / 16; ++m) {
+                    asm volatile("" : "+v"(wpre[q][m]));
+                    wb[q][4 * m] = wpre[q][m][0];
+                    wb[q][4 * m + 1] = wpre[q][m][1];
+                    wb[q][4 * m + 2] = wpre[q][m][2];
+                    wb[q][4 * m + 3] = wpre[q][m][3];
+                }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int row = (2 * wave + q) * 16 + (lane & 15);
+                const int valid = row < H ? min(max(n_in - 32 * slot, 0), NP / 4) : 0;
+                load_span_f64<NP / 4>(wb[q], w_in + (long long)min(row, H - 1) * n_in + min(32 * slot, n_in - 1),
+                                      valid);
+            }
         }
         dbl4 acc[KP / 16][2];
 #pragma unroll
@@ -1168,7 +1243,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     // projection in AD, h_k goes to h_seq and to the h_prev half of row k+1
     double wr[8][8];
     load_chain_weights(wr, w_rec, H, cl, false);
-    double hprev = o < H ? (double)h0[b * H + o] : 0.0;
+    double hprev = h0_o;
     const GateLane gl = gate_lane_consts(gate_lane, ug);
     __syncthreads();
     int cur = 0;
@@ -1195,7 +1270,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
 
     // ---- backward from the float32 h_K, as the separate backward sees it
     const double delta = o < H ? (double)(float)hprev - (double)y[b * H + o] : 0.0;
-    small_reverse_and_grads(w_in, w_rec, K, n_in, H, delta, AD, ug, red, zs, gst, scratch + b * N,
+    small_reverse_and_grads(w_in, w_rec, K_arg, n_in_arg, H_arg, delta, AD, ug, red, zs, gst, scratch + b * N,
                             loss ? loss + b : nullptr, grad_x ? grad_x + b * K * (long long)n_in : nullptr,
                             grad_h0 ? grad_h0 + b * H : nullptr, accumulate, lane, wave, jb, ib, o, gate_lane);
 }
@@ -2030,7 +2105,9 @@ void set_kernel_attributes() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_small_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fb_small_kernel),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fb_small_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fb_small_kernel<true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<false, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
@@ -2221,7 +2298,11 @@ extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, 
     if (!outputs_disjoint(outs, 5, ins, 7)) return CFC_ERR_OVERLAP;
     if (n_in <= kSmall && H <= kSmall && K <= kSmallBwdMaxK) {
         set_kernel_attributes();
-        hipLaunchKernelGGL(cfc_fb_small_kernel, dim3(B), dim3(kThreads), small_fb_lds_bytes(), stream,
+        const bool whole = K == kSmallBwdMaxK && n_in == kSmall && H == kSmall &&
+                           (reinterpret_cast<uintptr_t>(params->w_in) & 15) == 0 &&
+                           (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+        auto* kern = whole ? &cfc_fb_small_kernel<true> : &cfc_fb_small_kernel<false>;
+        hipLaunchKernelGGL(kern, dim3(B), dim3(kThreads), small_fb_lds_bytes(), stream,
                            params->w_in, params->w_rec, params->b, params->w_tau, x, h0, y, (double)dt, K,
                            n_in, H, h_seq, scratch, loss, grad_x, grad_h0, flags == CFC_ACCUMULATE ? 1 : 0,
                            params->cell);
