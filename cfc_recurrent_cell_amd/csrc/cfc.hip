@@ -519,55 +519,69 @@ __device__ __forceinline__ void load_span_f64(double (&dst)[COUNT], const float*
     }
 }
 
+// The fast path of load_chain_weights (H % 4 == 0, W_rec 16-byte aligned)
+// in two parts, so that the 16 loads can go out early and the widening come
+// later.  Every float4 chunk of a lane's span is wholly inside or outside its
+// row (the same for all lanes): the loads go out together from in-range
+// addresses and out-of-range elements are zeroed afterwards.  The slot order
+// (slot s holds unit s ^ x) comes from the addresses where it can: the
+// forward's slots are rows (row r0 + (s ^ x) is loaded into slot s); the
+// backward's are columns of the span, so bit 2 of x picks the float4 half and
+// bits 1, 0 swap within it (float32 swaps).
+__device__ __forceinline__ bool chain_weights_vec(const float* w_rec, int H) {
+    return (H & 3) == 0 && (reinterpret_cast<uintptr_t>(w_rec) & 15) == 0;
+}
+__device__ __forceinline__ void chain_weights_fetch(f32x4 (&raw)[8][2], const float* __restrict__ w_rec, int H,
+                                                    const ChainLane& cl, bool transposed) {
+    const int x = chain_unit_xor(cl.jb);
+    const int r0 = transposed ? 8 * cl.jb : 8 * cl.ib, c0 = transposed ? 8 * cl.ib : 8 * cl.jb;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int row = transposed ? r0 + r : r0 + (r ^ x);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int half = transposed ? m ^ ((x >> 2) & 1) : m;
+            raw[r][m] = *reinterpret_cast<const f32x4*>(w_rec + (long long)min(row, H - 1) * H +
+                                                        min(c0 + 4 * half, H - 4));
+        }
+    }
+}
+__device__ __forceinline__ void chain_weights_widen(double (&w)[8][8], const f32x4 (&raw)[8][2], int H,
+                                                    const ChainLane& cl, bool transposed) {
+    const int x = chain_unit_xor(cl.jb);
+    const int r0 = transposed ? 8 * cl.jb : 8 * cl.ib, c0 = transposed ? 8 * cl.ib : 8 * cl.jb;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            f32x4 v4 = raw[r][m];
+            if (transposed) {
+                if (x & 1) v4 = v4.yxwz;
+                if (x & 2) v4 = v4.zwxy;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int sc = 4 * m + e;  // slot (transposed) or column (forward)
+                if (transposed) {
+                    const bool ok = r0 + r < H && c0 + (sc ^ x) < H;
+                    w[sc][r] = ok ? (double)v4[e] : 0.0;
+                } else {
+                    const bool ok = r0 + (r ^ x) < H && c0 + sc < H;
+                    w[r][sc] = ok ? (double)v4[e] : 0.0;
+                }
+            }
+        }
+}
+
 // The chain's weights: the forward's W_rec slice w[r][c] = W_rec[8ib + r][8jb + c],
 // or (transposed) the backward's w[r][c] = W_rec[8jb + c][8ib + r]; zero
 // outside the H x H matrix.
 __device__ __forceinline__ void load_chain_weights(double (&w)[8][8], const float* __restrict__ w_rec, int H,
                                                    const ChainLane& cl, bool transposed) {
-    if ((H & 3) == 0 && (reinterpret_cast<uintptr_t>(w_rec) & 15) == 0) {
-        // every float4 chunk of a lane's span is wholly inside or outside its
-        // row (the same for all lanes): the 16 loads go out together from
-        // in-range addresses, then out-of-range elements are zeroed, so one
-        // load latency is exposed instead of one per row.  The slot order
-        // (slot s holds unit s ^ x) comes from the addresses where it can:
-        // the forward's slots are rows (row r0 + (s ^ x) is loaded into slot
-        // s); the backward's are columns of the span, so bit 2 of x picks
-        // the float4 half and bits 1, 0 swap within it (float32 selects).
-        const int x = chain_unit_xor(cl.jb);
-        const int r0 = transposed ? 8 * cl.jb : 8 * cl.ib, c0 = transposed ? 8 * cl.ib : 8 * cl.jb;
-        float4 raw[8][2];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int row = transposed ? r0 + r : r0 + (r ^ x);
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int half = transposed ? m ^ ((x >> 2) & 1) : m;
-                raw[r][m] = *reinterpret_cast<const float4*>(w_rec + (long long)min(row, H - 1) * H +
-                                                             min(c0 + 4 * half, H - 4));
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                float4 v4 = raw[r][m];
-                if (transposed) {
-                    if (x & 1) v4 = make_float4(v4.y, v4.x, v4.w, v4.z);
-                    if (x & 2) v4 = make_float4(v4.z, v4.w, v4.x, v4.y);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int sc = 4 * m + e;  // slot (transposed) or column (forward)
-                    const float v = e == 0 ? v4.x : e == 1 ? v4.y : e == 2 ? v4.z : v4.w;
-                    if (transposed) {
-                        const bool ok = r0 + r < H && c0 + (sc ^ x) < H;
-                        w[sc][r] = ok ? (double)v : 0.0;
-                    } else {
-                        const bool ok = r0 + (r ^ x) < H && c0 + sc < H;
-                        w[r][sc] = ok ? (double)v : 0.0;
-                    }
-                }
-            }
+    if (chain_weights_vec(w_rec, H)) {
+        f32x4 raw[8][2];
+        chain_weights_fetch(raw, w_rec, H, cl, transposed);
+        chain_weights_widen(w, raw, H, cl, transposed);
         return;
     } else if (!transposed) {
 #pragma unroll
@@ -1138,9 +1152,10 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     // then W_in's, then x's LDS writes, which wait for x's loads only.
     const float* xb = x + b * K * (long long)n_in;
     f32x4 wpre[2][NP / 16];
-    // the per-unit inputs, as floats: w_tau and h_0 of unit o, the bias of
-    // the projection's two output columns
-    float wtau_o, h0_o, bias0, bias1;
+    // the per-unit inputs, as floats: w_tau, h_0 and y of unit o, the bias
+    // of the projection's two output columns
+    float wtau_o, h0_o, y_o, bias0, bias1;
+    f32x4 wr_raw[8][2];  // WHOLE: the forward chain's W_rec slice, fetched under the projection
     const int bcol0 = (2 * wave) * 16 + (lane & 15), bcol1 = bcol0 + 16;
     if constexpr (WHOLE) {
         // every load is unconditional (all indices are in range here), and
@@ -1179,6 +1194,8 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
         for (int u = t; u < HP; u += kThreads) hb[u] = u < H ? (double)h0[b * H + u] : 0.0;
         wtau_o = o < H ? w_tau[o] : 0.f;
         h0_o = o < H ? h0[b * H + o] : 0.f;
+        y_o = o < H ? y[b * H + o] : 0.f;
+        (void)wr_raw;
         bias0 = bcol0 < H ? bias[bcol0] : 0.f;
         bias1 = bcol1 < H ? bias[bcol1] : 0.f;
     }
@@ -1204,6 +1221,10 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
                     wb[q][4 * m + 2] = wpre[q][m][2];
                     wb[q][4 * m + 3] = wpre[q][m][3];
                 }
+            // the forward chain's weights and the loss target stream in
+            // under the products
+            chain_weights_fetch(wr_raw, w_rec, HP, cl, false);
+            y_o = y[b * H + o];
         } else {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -1242,7 +1263,16 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     // ---- forward chain (as in cfc_fwd_small_kernel); a_k replaces the
     // projection in AD, h_k goes to h_seq and to the h_prev half of row k+1
     double wr[8][8];
-    load_chain_weights(wr, w_rec, H, cl, false);
+    if constexpr (WHOLE) {
+        // as with W_in: the wait and the widening stay here
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) asm volatile("" : "+v"(wr_raw[r][m]));
+        chain_weights_widen(wr, wr_raw, H, cl, false);
+    } else {
+        load_chain_weights(wr, w_rec, H, cl, false);
+    }
     double hprev = h0_o;
     const GateLane gl = gate_lane_consts(gate_lane, ug);
     __syncthreads();
@@ -1269,7 +1299,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     }
 
     // ---- backward from the float32 h_K, as the separate backward sees it
-    const double delta = o < H ? (double)(float)hprev - (double)y[b * H + o] : 0.0;
+    const double delta = o < H ? (double)(float)hprev - (double)y_o : 0.0;
     small_reverse_and_grads(w_in, w_rec, K_arg, n_in_arg, H_arg, delta, AD, ug, red, zs, gst, scratch + b * N,
                             loss ? loss + b : nullptr, grad_x ? grad_x + b * K * (long long)n_in : nullptr,
                             grad_h0 ? grad_h0 + b * H : nullptr, accumulate, lane, wave, jb, ib, o, gate_lane);
