@@ -1539,7 +1539,12 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
 // PARKED (one-call entry, after cfc_fwd_large_kernel<FULL, true>): a_k is read
 // back from the head of the row's scratch instead of being recomputed, so x_k
 // is not staged; the window is then the whole sequence.
-template <bool FULL, bool TAU, bool PARKED>
+// STAGE 0 runs both phases.  The parked path runs them as two launches, so
+// that each gets the compiler's register allocation to itself: STAGE 1 runs
+// phase 1 and leaves each row's dL/dw_tau sums (float64) in the head of its
+// scratch row, where the a_k it has consumed were; STAGE 2 runs phase 2 and
+// reads them back before the row's dW_in overwrites them.
+template <bool FULL, bool TAU, bool PARKED, int STAGE = 0>
 __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
@@ -1569,6 +1574,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     // every element there is rewritten afterwards.
     const long long tmp_off = N - 2LL * K * H;
 
+    if constexpr (STAGE != 2) {
     for (int u = t; u < kLarge; u += kThreads) {
         const bool ok = u < H;
         const double w = ok ? (double)w_tau[u] : 0.0;
@@ -1615,8 +1621,10 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
         else fetch_t(hr, h_seq + (k0 + k - 1) * H, Kf * H, r0, B, H, t);
     };
     fetch_step(K - 1);
-    for (int k = K - 1; k >= 0; --k) {
-        dbl4 acc[4];  // a_k - b (recomputed), or a_k itself (parked)
+    // PARKED: a_k of the step to come, fetched during the current step's
+    // products (after their weight loads, which in-order waits then skip)
+    dbl4 apre[4];
+    auto fetch_a = [&](int k) {
         if constexpr (PARKED) {
             const double* ap = reinterpret_cast<const double*>(scratch + b_own * N) + (k0 + k) * (long long)H;
 #pragma unroll
@@ -1624,8 +1632,87 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int i = lunit(wave, tb, s + 4 * v);
-                    acc[tb][v] = row_ok && i < H ? ap[i] : 0.0;
+                    apre[tb][v] = row_ok && i < H ? ap[i] : 0.0;
                 }
+        }
+    };
+    fetch_a(K - 1);
+    const int jw = 64 * wave + 4 * (lane & 15);
+    // accp += M^T dL/da_k for a weight matrix M (rows: the H units, row
+    // stride ld, width columns): chunk ic of k-slot s contracts unit
+    // i = 64*s + ic; the four tiles' operands M[i][lunit(wave, 0..3, lane%16)]
+    // are one float4.  The float4 operands are double-buffered PF chunks
+    // ahead, so their L2 latency hides under the previous chunks' products
+    // (PF = 4 where the registers allow it, else 2); the next step's inputs
+    // are fetched after the last of them if asked.
+    constexpr int PF = FULL ? 4 : 2;
+    auto dab_product = [&](const float* __restrict__ wm, int ld, int width, dbl4 (&accp)[4], bool fetch_next,
+                           int k) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) accp[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
+        auto wld = [&](int ic) -> float4 {
+            const int i = 64 * s + ic;
+            if constexpr (FULL) return *reinterpret_cast<const float4*>(wm + (long long)i * kLarge + jw);
+            else return load4_masked(wm + (long long)min(i, H - 1) * ld, jw, width, i < H);
+        };
+        auto chunks1 = [&](const float4 (&w4)[1], int icb) {
+            const double bz = dab[zidx(64 * s + icb, r)];
+            accp[0] = mfma_f64((double)w4[0].x, bz, accp[0]);
+            accp[1] = mfma_f64((double)w4[0].y, bz, accp[1]);
+            accp[2] = mfma_f64((double)w4[0].z, bz, accp[2]);
+            accp[3] = mfma_f64((double)w4[0].w, bz, accp[3]);
+        };
+        auto chunks = [&](const float4 (&w4)[PF], int icb) {
+#pragma unroll
+            for (int u = 0; u < PF; ++u) {
+                const double bz = dab[zidx(64 * s + icb + u, r)];
+                accp[0] = mfma_f64((double)w4[u].x, bz, accp[0]);
+                accp[1] = mfma_f64((double)w4[u].y, bz, accp[1]);
+                accp[2] = mfma_f64((double)w4[u].z, bz, accp[2]);
+                accp[3] = mfma_f64((double)w4[u].w, bz, accp[3]);
+            }
+        };
+        if constexpr (!PARKED) {
+            // the recomputing kernels have no registers to spare: plain
+            // loop, the next step's inputs first
+            if (fetch_next) {
+                fetch_step(k - 1);
+                fetch_a(k - 1);
+            }
+#pragma unroll 4
+            for (int ic = 0; ic < 64; ++ic) {
+                const float4 w1[1] = {wld(ic)};
+                chunks1(w1, ic);
+            }
+            return;
+        }
+        float4 wa[PF], wb[PF];
+#pragma unroll
+        for (int u = 0; u < PF; ++u) wa[u] = wld(u);
+#pragma unroll 1
+        for (int ic0 = 0; ic0 < 64 - 2 * PF; ic0 += 2 * PF) {
+#pragma unroll
+            for (int u = 0; u < PF; ++u) wb[u] = wld(ic0 + PF + u);
+            chunks(wa, ic0);
+#pragma unroll
+            for (int u = 0; u < PF; ++u) wa[u] = wld(ic0 + 2 * PF + u);
+            chunks(wb, ic0 + PF);
+        }
+        // the last block, with the next step's fetch after its weight loads
+#pragma unroll
+        for (int u = 0; u < PF; ++u) wb[u] = wld(64 - PF + u);
+        chunks(wa, 64 - 2 * PF);
+        if (fetch_next) {
+            fetch_step(k - 1);
+            fetch_a(k - 1);
+        }
+        chunks(wb, 64 - PF);
+    };
+    for (int k = K - 1; k >= 0; --k) {
+        dbl4 acc[4];  // a_k - b (recomputed), or a_k itself (parked)
+        if constexpr (PARKED) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) acc[tb] = apre[tb];
         }
         __syncthreads();  // previous step is done with zx, zh, dab
         if constexpr (!PARKED) store_t(zx, xr, t);
@@ -1663,7 +1750,35 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                     dab[zidx(i, r)] = da;
                 }
         __syncthreads();  // dab of step k complete
+        if (k > 0 || grad_h0) {
+            // delta_k = delta_k+1 * g + W_rec^T dL/da
+            dbl4 acc2[4];
+            dab_product(w_rec, H, H, acc2, k > 0 && !grad_x, k);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    delta[tb][v] = fma(delta[tb][v], gk[tb][v], acc2[tb][v]);
+        }
+        if (grad_x) {
+            // dL/dx_k = W_in^T dL/da, the same product with W_in's rows; the
+            // lane's elements are column lunit(wave, tb, s + 4v) of row r
+            dbl4 acc3[4];
+            dab_product(w_in, n_in, n_in, acc3, k > 0, k);
+            if (row_ok) {
+                float* gx = grad_x + (b_own * Kf + k0 + k) * n_in;
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int j = lunit(wave, tb, s + 4 * v);
+                        if (j < n_in) gx[j] = (float)acc3[tb][v];
+                    }
+            }
+        }
         // park dL/da_k of the 16 rows in their scratch tails, row-contiguous
+        // (after the products, so that their weight loads' waits do not
+        // cover these stores)
 #pragma unroll 4
         for (int m = 0; m < kLR; ++m) {
             const int e = t + kThreads * m;
@@ -1676,62 +1791,6 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                 q[1] = (unsigned)(u >> 32);
             }
         }
-        if (k > 0) fetch_step(k - 1);
-        const int jw = 64 * wave + 4 * (lane & 15);
-        if (k > 0 || grad_h0) {
-            // delta_k = delta_k+1 * g + W_rec^T dL/da: chunk ic of k-slot s
-            // contracts unit i = 64*s + ic; the four tiles' operands
-            // W_rec[i][lunit(wave, 0..3, lane%16)] are one float4
-            dbl4 acc2[4];
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc2[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-            for (int ic = 0; ic < 64; ++ic) {
-                const int i = 64 * s + ic;
-                const double bz = dab[zidx(i, r)];
-                float4 w4;
-                if constexpr (FULL) w4 = *reinterpret_cast<const float4*>(w_rec + (long long)i * kLarge + jw);
-                else w4 = load4_masked(w_rec + (long long)min(i, H - 1) * H, jw, H, i < H);
-                acc2[0] = mfma_f64((double)w4.x, bz, acc2[0]);
-                acc2[1] = mfma_f64((double)w4.y, bz, acc2[1]);
-                acc2[2] = mfma_f64((double)w4.z, bz, acc2[2]);
-                acc2[3] = mfma_f64((double)w4.w, bz, acc2[3]);
-            }
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    delta[tb][v] = fma(delta[tb][v], gk[tb][v], acc2[tb][v]);
-        }
-        if (grad_x) {
-            // dL/dx_k = W_in^T dL/da, the same product with W_in's rows; the
-            // lane's elements are column lunit(wave, tb, s + 4v) of row r
-            dbl4 acc3[4];
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc3[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-            for (int ic = 0; ic < 64; ++ic) {
-                const int i = 64 * s + ic;
-                const double bz = dab[zidx(i, r)];
-                float4 w4;
-                if constexpr (FULL) w4 = *reinterpret_cast<const float4*>(w_in + (long long)i * kLarge + jw);
-                else w4 = load4_masked(w_in + (long long)min(i, H - 1) * n_in, jw, n_in, i < H);
-                acc3[0] = mfma_f64((double)w4.x, bz, acc3[0]);
-                acc3[1] = mfma_f64((double)w4.y, bz, acc3[1]);
-                acc3[2] = mfma_f64((double)w4.z, bz, acc3[2]);
-                acc3[3] = mfma_f64((double)w4.w, bz, acc3[3]);
-            }
-            if (row_ok) {
-                float* gx = grad_x + (b_own * Kf + k0 + k) * n_in;
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int j = lunit(wave, tb, s + 4 * v);
-                        if (j < n_in) gx[j] = (float)acc3[tb][v];
-                    }
-            }
-        }
     }
     if (grad_h0 && row_ok) {  // after the window's first step, delta is dL/dh_k0
 #pragma unroll
@@ -1742,6 +1801,17 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                 if (j < H) grad_h0[b_own * H + j] = (float)delta[tb][v];
             }
     }
+    if constexpr (STAGE == 1) {
+        // the rows' dL/dw_tau sums to the heads of their scratch rows
+        __syncthreads();
+        for (int e = t; e < kLR * kLarge; e += kThreads) {
+            const int rr = e / kLarge, u = e % kLarge;
+            const long long b = r0 + rr;
+            if (b < B && u < H) reinterpret_cast<double*>(scratch + b * N)[u] = gwt[zidx(u, rr)];
+        }
+        return;
+    }
+    }  // STAGE != 2
 
     // ---- per row: G = DA^T [X | H_prev] over the K steps, then db and dw_tau
     __syncthreads();
@@ -1754,7 +1824,9 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     // holds dL/da_kk[t] (from the parked tail), x_kk[t] and h_kk-1[t]
     double pd[kLargeBwdMaxK];
     float px[kLargeBwdMaxK], ph[kLargeBwdMaxK];
+    double pg = 0.0;  // STAGE 2: dL/dw_tau of unit t, from the row's head
     auto fetch_row = [&](long long b) {
+        if constexpr (STAGE == 2) pg = t < H ? reinterpret_cast<const double*>(scratch + b * N)[t] : 0.0;
         const unsigned* tq = reinterpret_cast<const unsigned*>(scratch + b * N + tmp_off);
 #pragma unroll
         for (int kk = 0; kk < kLargeBwdMaxK; ++kk) {
@@ -1777,6 +1849,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     for (int rr = 0; rr < kLR; ++rr) {
         const long long b = r0 + rr;
         if (b >= B) break;
+        const double gw_t = pg;
 #pragma unroll
         for (int kk = 0; kk < kLargeBwdMaxK; ++kk) {
             if (kk < KP) {
@@ -1924,7 +1997,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
             double gb = 0.0;
             for (int kk = K - 1; kk >= 0; --kk) gb += dak[kk * kLarge + t];
             grec[(long long)H * H + t] = (float)gb;
-            grec[(long long)H * H + H + t] = (float)gwt[zidx(t, rr)];
+            grec[(long long)H * H + H + t] = STAGE == 2 ? (float)gw_t : (float)gwt[zidx(t, rr)];
         }
         __syncthreads();  // LDS reused by the next row
     }
@@ -2151,10 +2224,14 @@ void set_kernel_attributes() {
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false, false>),
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, true, false>),
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, false>),
-                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, false, true>),
-                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false, true>),
-                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, true, true>),
-                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, true>)})
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, false, true, 1>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false, true, 1>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, true, true, 1>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, true, 1>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, false, true, 2>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false, true, 2>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, true, true, 2>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, true, 2>)})
             (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     });
 }
@@ -2359,12 +2436,15 @@ extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, 
                            params->cell, scratch, N);
         rc = launch_status();
         if (rc) return rc;
-        auto bwd = full ? (tau ? &cfc_bwd_large_kernel<true, true, true> : &cfc_bwd_large_kernel<true, false, true>)
-                        : (tau ? &cfc_bwd_large_kernel<false, true, true> : &cfc_bwd_large_kernel<false, false, true>);
+        auto bwd1 = full ? (tau ? &cfc_bwd_large_kernel<true, true, true, 1> : &cfc_bwd_large_kernel<true, false, true, 1>)
+                         : (tau ? &cfc_bwd_large_kernel<false, true, true, 1> : &cfc_bwd_large_kernel<false, false, true, 1>);
+        auto bwd2 = full ? (tau ? &cfc_bwd_large_kernel<true, true, true, 2> : &cfc_bwd_large_kernel<true, false, true, 2>)
+                         : (tau ? &cfc_bwd_large_kernel<false, true, true, 2> : &cfc_bwd_large_kernel<false, false, true, 2>);
         const BwdWindow win{K, 0, K, nullptr, grad_h0};
-        hipLaunchKernelGGL(bwd, dim3((unsigned)groups), dim3(kThreads), large_bwd_lds_bytes(), stream, params->w_in,
-                           params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, win, n_in, H,
-                           scratch, loss, grad_x);
+        for (auto* bwd : {bwd1, bwd2})
+            hipLaunchKernelGGL(bwd, dim3((unsigned)groups), dim3(kThreads), large_bwd_lds_bytes(), stream, params->w_in,
+                               params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, win, n_in, H,
+                               scratch, loss, grad_x);
         return launch_status();
     }
     rc = cfc_forward(params, x, h0, dt, B, K, h_seq, stream);
