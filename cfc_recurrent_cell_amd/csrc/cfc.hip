@@ -1490,7 +1490,13 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
     __syncthreads();
 
     for (int k = 0; k < K; ++k) {
-        // next step's inputs, loaded now and written to LDS after this step
+        dbl4 acc[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
+        large_preact<FULL>(acc, w_in, w_rec, n_in, H, zx, zh, wave, lane);
+        // next step's inputs, loaded after the product's weight loads (so
+        // that their in-order waits do not cover these) and written to LDS
+        // after the elementwise phase
         float xn[kLR];
 #pragma unroll
         for (int m = 0; m < kLR; ++m) {
@@ -1499,10 +1505,6 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
             const long long b = r0 + rr;
             xn[m] = (k + 1 < K && b < B && j < n_in) ? x[(b * K + k + 1) * (long long)n_in + j] : 0.f;
         }
-        dbl4 acc[4];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
-        large_preact<FULL>(acc, w_in, w_rec, n_in, H, zx, zh, wave, lane);
         __syncthreads();  // every wave is done reading zx / zh of step k
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
