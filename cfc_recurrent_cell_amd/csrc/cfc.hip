@@ -1007,6 +1007,13 @@ __device__ __forceinline__ void small_reverse_and_grads(
     }
 }
 
+// WHOLE: a 64-step window, n_in = n_hid = 128, and x, h0, h_seq, W_in, W_rec
+// 16-byte aligned (the host checks): the staging then runs unconditionally
+// and fetches the recomputation's weights while [x | h_prev] is staged (x and
+// h first, then the per-unit inputs, then the weights: vmcnt retires in
+// order), widening them after the barrier.  A separate instance, so that no
+// path joins the generic one.
+template <bool WHOLE>
 __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
@@ -1037,28 +1044,90 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     // wb[q][jc] = [W_in | W_rec][(2*wave + q)*16 + lane%16][64*s + jc]
     const int slot = lane >> 4;
     double wb[2][ZW / 4];
+    auto load_weights = [&]() {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int row = (2 * wave + q) * 16 + (lane & 15);
-        const int rowc = min(row, H - 1);
-        const bool in_part = slot < 2;
-        const int c0 = in_part ? 64 * slot : 64 * (slot - 2);
-        const int width = in_part ? n_in : H;
-        const int valid = row < H ? min(max(width - c0, 0), ZW / 4) : 0;
-        const float* src = in_part ? w_in + (long long)rowc * n_in + min(c0, n_in - 1)
-                                   : w_rec + (long long)rowc * H + min(c0, H - 1);
-        load_span_f64<ZW / 4>(wb[q], src, valid);
+        for (int q = 0; q < 2; ++q) {
+            const int row = (2 * wave + q) * 16 + (lane & 15);
+            const int rowc = min(row, H - 1);
+            const bool in_part = slot < 2;
+            const int c0 = in_part ? 64 * slot : 64 * (slot - 2);
+            const int width = in_part ? n_in : H;
+            const int valid = row < H ? min(max(width - c0, 0), ZW / 4) : 0;
+            const float* src = in_part ? w_in + (long long)rowc * n_in + min(c0, n_in - 1)
+                                       : w_rec + (long long)rowc * H + min(c0, H - 1);
+            load_span_f64<ZW / 4>(wb[q], src, valid);
+        }
+    };
+    float wtau_o, bias0, bias1;
+    const int bcol0 = (2 * wave) * 16 + (lane & 15), bcol1 = bcol0 + 16;
+    f32x4 wpre[2][ZW / 16];
+    if constexpr (WHOLE) {
+        // ---- stage [x_k | h_k]: KP rows of ZW / 4 float4, x in the first
+        // NP / 4 of them (8 per thread), h in the rest (8 per thread; row 0 is
+        // h_k0-1, from h0 when the window starts the sequence)
+        static_assert(KP * (NP / 4) == 8 * kThreads && KP * (HP / 4) == 8 * kThreads, "one pass per half");
+        const f32x4* xb = reinterpret_cast<const f32x4*>(x + (b * Kf + k0) * NP);
+        const float* h_first = k0 == 0 ? h0 + b * HP : h_seq + (b * Kf + k0 - 1) * HP;
+        const float* h_rest = h_seq + (b * Kf + k0) * HP;  // row r >= 1 is h_rest[r - 1]
+        f32x4 xv[8], hv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = t + u * kThreads;
+            xv[u] = xb[e];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = t + u * kThreads, r = e / (HP / 4), c4 = e % (HP / 4);
+            const float* src = r == 0 ? h_first : h_rest + (r - 1) * HP;
+            hv[u] = reinterpret_cast<const f32x4*>(src)[c4];
+        }
+        wtau_o = w_tau[o];
+        bias0 = bias[bcol0];
+        bias1 = bias[bcol1];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int row = (2 * wave + q) * 16 + (lane & 15);
+            const float* src = slot < 2 ? w_in + row * NP + 64 * slot : w_rec + row * HP + 64 * (slot - 2);
+#pragma unroll
+            for (int m = 0; m < ZW / 16; ++m) wpre[q][m] = reinterpret_cast<const f32x4*>(src)[m];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = t + u * kThreads, r = e / (NP / 4), c4 = e % (NP / 4);
+            float2* dx = reinterpret_cast<float2*>(zs + r * ZS + 4 * c4);
+            dx[0] = make_float2(xv[u][0], xv[u][1]);
+            dx[1] = make_float2(xv[u][2], xv[u][3]);
+            float2* dh = reinterpret_cast<float2*>(zs + r * ZS + NP + 4 * c4);
+            dh[0] = make_float2(hv[u][0], hv[u][1]);
+            dh[1] = make_float2(hv[u][2], hv[u][3]);
+        }
+    } else {
+        (void)wpre;
+        load_weights();
+        // ---- stage [x_k | h_k] for every step of the window (h_0 = h0, h_k = h_seq[k-1])
+        stage_rows(zs, ZS, x + (b * Kf + k0) * n_in, n_in, K, n_in, KP, NP, t);
+        stage_rows(zs + NP, ZS, k0 == 0 ? h0 + b * H : h_seq + (b * Kf + k0 - 1) * H, H, 1, H, 1, HP, t);
+        if (K > 1) stage_rows(zs + ZS + NP, ZS, h_seq + (b * Kf + k0) * H, H, K - 1, H, KP - 1, HP, t);
+        else stage_rows(zs + ZS + NP, ZS, h_seq, H, 0, H, KP - 1, HP, t);
+        wtau_o = o < H ? w_tau[o] : 0.f;
+        bias0 = bcol0 < H ? bias[bcol0] : 0.f;
+        bias1 = bcol1 < H ? bias[bcol1] : 0.f;
     }
-
-    // ---- stage [x_k | h_k] for every step of the window (h_0 = h0, h_k = h_seq[k-1])
-    stage_rows(zs, ZS, x + (b * Kf + k0) * n_in, n_in, K, n_in, KP, NP, t);
-    stage_rows(zs + NP, ZS, k0 == 0 ? h0 + b * H : h_seq + (b * Kf + k0 - 1) * H, H, 1, H, 1, HP, t);
-    if (K > 1) stage_rows(zs + ZS + NP, ZS, h_seq + (b * Kf + k0) * H, H, K - 1, H, KP - 1, HP, t);
-    else stage_rows(zs + ZS + NP, ZS, h_seq, H, 0, H, KP - 1, HP, t);
-    const UnitGate ug = unit_gate(cell, o < H ? (double)w_tau[o] : 0.0, dt, o < H);
-    const double bias_q0 = (2 * wave) * 16 + (lane & 15) < H ? (double)bias[(2 * wave) * 16 + (lane & 15)] : 0.0;
-    const double bias_q1 = (2 * wave + 1) * 16 + (lane & 15) < H ? (double)bias[(2 * wave + 1) * 16 + (lane & 15)] : 0.0;
+    const UnitGate ug = unit_gate(cell, (double)wtau_o, dt, WHOLE || o < H);  // o < 128 = H in WHOLE
+    const double bias_q0 = bias0, bias_q1 = bias1;
     __syncthreads();
+    if constexpr (WHOLE) {
+        // the empty asm takes the loaded registers here, after the barrier,
+        // so the wait for them and their widening are not hoisted above it
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int m = 0; m < ZW / 16; ++m) {
+                asm volatile("" : "+v"(wpre[q][m]));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) wb[q][4 * m + e] = wpre[q][m][e];
+            }
+    }
 
     // ---- recompute every step's pre-activation on the matrix cores
     {
@@ -2208,7 +2277,9 @@ void set_kernel_attributes() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_small_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_small_kernel),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_small_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_small_kernel<true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fb_small_kernel<false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
@@ -2343,7 +2414,11 @@ int backward_window(const cfc_params_t* params, const float* x, const float* h0,
     const BwdWindow win{K, k_begin, Kw, delta_in, delta_out};
     set_kernel_attributes();
     if (small) {
-        hipLaunchKernelGGL(cfc_bwd_small_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
+        auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+        const bool whole = Kw == kSmallBwdMaxK && n_in == kSmall && H == kSmall && al16(x) && al16(h0) &&
+                           al16(h_seq) && al16(params->w_in) && al16(params->w_rec);
+        auto kern = whole ? &cfc_bwd_small_kernel<true> : &cfc_bwd_small_kernel<false>;
+        hipLaunchKernelGGL(kern, dim3(B), dim3(kThreads), lds, stream, params->w_in,
                            params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, win, n_in, H,
                            scratch, loss, grad_x, flags == CFC_ACCUMULATE ? 1 : 0, params->cell);
         return launch_status();

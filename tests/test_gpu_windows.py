@@ -124,3 +124,34 @@ def test_seeded_window_must_end_at_K():
         C.cfc_backward_window(d["w_in"], d["w_rec"], d["b"], d["w_tau"], d["x"], d["h0"], h, d["dt"], 0, 4, s,
                               y=d["y"])
     assert e.value.code == C.CFC_ERR_DIM
+
+
+@pytest.mark.parametrize("K", [64, 128], ids=["one_window", "two_windows"])
+def test_whole_shape_backward_instance_matches_generic(K):
+    """64-step windows at 128 x 128 with 16-byte-aligned inputs run an instance
+    whose staging fetches the recomputation's weights while [x | h_prev] is
+    staged; x one float off alignment runs the generic one.  Same arithmetic:
+    scratch, loss, grad_x and dL/dh_0 bitwise equal (the second window's first
+    h_prev row comes from h_seq, the first's from h0)."""
+    import torch
+    import cfc_recurrent_cell_amd as C
+    B, n = 3, 128
+    inp = W.make_random_cfc_inputs(B, K, n, n, 0.5, 96)
+    d = to_dev(inp)
+    h = _forward(d)
+    buf = torch.empty(B * K * n + 1, device="cuda")
+    x_off = buf[1:].view(B, K, n)
+    x_off.copy_(d["x"])
+    assert d["x"].data_ptr() % 16 == 0 and x_off.data_ptr() % 16 == 4
+    say(f"[windows] whole-shape backward instance vs generic, K={K}")
+    outs = []
+    for xx in (d["x"], x_off):
+        gx = torch.empty((B, K, n), device="cuda")
+        s, l, gx, gh = C.cfc_backward_windows(d["w_in"], d["w_rec"], d["b"], d["w_tau"], xx, d["h0"], h, d["y"],
+                                              d["dt"], 64, grad_x=gx)
+        outs.append([host(t) for t in (s, l, gx, gh)])
+    for name, a, b_ in zip(("scratch", "loss", "grad_x", "grad_h0"), *outs):
+        assert np.array_equal(a.view(np.uint32), b_.view(np.uint32)), f"K={K}: {name} differs between instances"
+    ref = O.cfc_step(inp, threads=oracle_threads())
+    assert_close(outs[0][0], ref["scratch"], f"K={K} scratch")
+    assert_close(outs[0][1], ref["loss"], f"K={K} loss")
