@@ -193,9 +193,13 @@ int cfc_backward_window(const cfc_params_t *params, const float *x, const float 
  * reverse pass then uses the unrounded pre-activations (the separate backward
  * recomputes them from float32 h); every other input of the backward
  * (h_K - y, h_k-1 in the gradients) is the float32 value written to h_seq.
- * Other shapes run cfc_forward and cfc_backward as two launches on `stream`,
- * after checking the backward's limits, so nothing is enqueued when either
- * direction would be refused.
+ * Wider shapes with K <= 20 in overwrite mode (N even, scratch 8-byte
+ * aligned) run three launches on `stream`: a forward that also parks its
+ * float64 pre-activations in the head of each scratch row, then a backward in
+ * two stages (the reverse pass, then the weight gradients) that reads them back
+ * instead of recomputing them.  Other shapes run cfc_forward and cfc_backward
+ * as two launches on `stream`.  In both cases the backward's limits are checked
+ * first, so nothing is enqueued when either direction would be refused.
  * Returns a CFC_* status; the same argument rules as the two calls, and no
  * output (h_seq, scratch, loss, grad_x, grad_h0) may overlap another. */
 int cfc_forward_backward(const cfc_params_t *params, const float *x, const float *h0,
