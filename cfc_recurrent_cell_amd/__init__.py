@@ -19,7 +19,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["cfc_forward", "cfc_backward", "cfc_backward_window", "cfc_backward_windows",
-           "cfc_forward_backward", "reduce_axis0",
+           "cfc_backward_workspace", "cfc_forward_backward", "reduce_axis0",
            "reduce_axis0_split_workspace", "cfc_scratch_row_len", "CfcError", "load_library"]
 
 
@@ -90,14 +90,35 @@ def _input_grad_buffers(x, p, grad_x, grad_h0, input_grads):
     return grad_x, grad_h0
 
 
+def _workspace_arg(workspace):
+    if workspace is None:
+        return None, 0
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the GPU")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def cfc_backward_workspace(B: int, Kw: int, n_in: int, n_hid: int, accumulate: bool = True) -> int:
+    """Bytes of workspace cfc_backward_window_ws needs for a window of Kw
+    steps (0: the window's kernel uses none)."""
+    n = int(load_library().cfc_backward_workspace(B, Kw, n_in, n_hid,
+                                                   CFC_ACCUMULATE if accumulate else CFC_OVERWRITE))
+    if n < 0:
+        raise ValueError(f"invalid backward size B={B} Kw={Kw} n_in={n_in} n_hid={n_hid}")
+    return n
+
+
 def cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, scratch=None,
                  loss=None, accumulate: bool = False, want_loss: bool = True,
                  input_grads: bool = False, grad_x=None, grad_h0=None,
-                 stream=None, cell: str = "gated") -> Tuple[object, ...]:
+                 stream=None, cell: str = "gated", workspace=None) -> Tuple[object, ...]:
     """(scratch [B, N], loss [B] or None): per-row parameter gradients of
     L_b = 1/2 |h_K - y_b|^2 (see include/cfc.h for the row layout).  With
     ``input_grads`` (or explicit ``grad_x`` / ``grad_h0`` buffers) it returns
-    (scratch, loss, grad_x [B, K, n_in], grad_h0 [B, H]) instead."""
+    (scratch, loss, grad_x [B, K, n_in], grad_h0 [B, H]) instead.  A device
+    ``workspace`` (cfc_backward_workspace bytes) goes to cfc_backward_window_ws
+    over all K steps: accumulate mode at widths above 128 then runs the
+    16-row kernel."""
     import torch
     lib = load_library()
     p = _params(w_in, w_rec, b, w_tau, cell)
@@ -118,10 +139,17 @@ def cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, scratch=None
     grad_x, grad_h0 = _input_grad_buffers(x, p, grad_x, grad_h0, input_grads)
     flags = CFC_ACCUMULATE if accumulate else CFC_OVERWRITE
     ptr = lambda t: t.data_ptr() if t is not None else None
-    _check("cfc_backward", lib.cfc_backward(
-        ctypes.byref(p), x.data_ptr(), h0.data_ptr(), h_seq.data_ptr(), y.data_ptr(), float(dt),
-        B, K, scratch.data_ptr(), ptr(loss), ptr(grad_x), ptr(grad_h0), flags,
-        _stream(x.device, stream)))
+    if workspace is not None:
+        ws_ptr, ws_bytes = _workspace_arg(workspace)
+        _check("cfc_backward_window_ws", lib.cfc_backward_window_ws(
+            ctypes.byref(p), x.data_ptr(), h0.data_ptr(), h_seq.data_ptr(), y.data_ptr(), None, float(dt),
+            B, K, 0, K, scratch.data_ptr(), ptr(loss), ptr(grad_x), ptr(grad_h0), flags, ws_ptr, ws_bytes,
+            _stream(x.device, stream)))
+    else:
+        _check("cfc_backward", lib.cfc_backward(
+            ctypes.byref(p), x.data_ptr(), h0.data_ptr(), h_seq.data_ptr(), y.data_ptr(), float(dt),
+            B, K, scratch.data_ptr(), ptr(loss), ptr(grad_x), ptr(grad_h0), flags,
+            _stream(x.device, stream)))
     if want_inputs:
         return scratch, loss, grad_x, grad_h0
     return scratch, loss
@@ -129,12 +157,13 @@ def cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, scratch=None
 
 def cfc_backward_window(w_in, w_rec, b, w_tau, x, h0, h_seq, dt: float, k_begin: int, k_end: int, scratch,
                         y=None, delta_in=None, delta_out=None, loss=None, grad_x=None,
-                        accumulate: bool = False, stream=None, cell: str = "gated"):
+                        accumulate: bool = False, stream=None, cell: str = "gated", workspace=None):
     """Backward over steps [k_begin, k_end) of the forward that produced
     h_seq (see include/cfc.h): dL/dh_k_end comes in as ``delta_in`` (or, when
     None, from the loss seed h_K - y), dL/dh_k_begin goes out in ``delta_out``
     (may be ``delta_in`` itself), the window's parameter gradient goes into
-    ``scratch`` (overwritten, or added with ``accumulate``).  Returns
+    ``scratch`` (overwritten, or added with ``accumulate``).  With a device
+    ``workspace`` it calls cfc_backward_window_ws.  Returns
     (scratch, loss, grad_x, delta_out)."""
     lib = load_library()
     p = _params(w_in, w_rec, b, w_tau, cell)
@@ -151,25 +180,39 @@ def cfc_backward_window(w_in, w_rec, b, w_tau, x, h0, h_seq, dt: float, k_begin:
             _dev_f32(t, name, shape)
     ptr = lambda t: t.data_ptr() if t is not None else None
     flags = CFC_ACCUMULATE if accumulate else CFC_OVERWRITE
-    _check("cfc_backward_window", lib.cfc_backward_window(
-        ctypes.byref(p), x.data_ptr(), h0.data_ptr(), h_seq.data_ptr(), ptr(y), ptr(delta_in), float(dt), B, K,
-        int(k_begin), int(k_end), scratch.data_ptr(), ptr(loss), ptr(grad_x), ptr(delta_out), flags,
-        _stream(x.device, stream)))
+    if workspace is not None:
+        ws_ptr, ws_bytes = _workspace_arg(workspace)
+        _check("cfc_backward_window_ws", lib.cfc_backward_window_ws(
+            ctypes.byref(p), x.data_ptr(), h0.data_ptr(), h_seq.data_ptr(), ptr(y), ptr(delta_in), float(dt), B,
+            K, int(k_begin), int(k_end), scratch.data_ptr(), ptr(loss), ptr(grad_x), ptr(delta_out), flags, ws_ptr,
+            ws_bytes, _stream(x.device, stream)))
+    else:
+        _check("cfc_backward_window", lib.cfc_backward_window(
+            ctypes.byref(p), x.data_ptr(), h0.data_ptr(), h_seq.data_ptr(), ptr(y), ptr(delta_in), float(dt), B,
+            K, int(k_begin), int(k_end), scratch.data_ptr(), ptr(loss), ptr(grad_x), ptr(delta_out), flags,
+            _stream(x.device, stream)))
     return scratch, loss, grad_x, delta_out
 
 
 def cfc_backward_windows(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, window: int, scratch=None,
-                         loss=None, grad_x=None, grad_h0=None, stream=None, cell: str = "gated"):
+                         loss=None, grad_x=None, grad_h0=None, stream=None, cell: str = "gated",
+                         workspace=None):
     """The whole backward as windows of ``window`` steps, from the last to the
     first: the last window is seeded from y and overwrites the scratch, each
     earlier one takes the carried dL/dh and accumulates.  For K beyond the
-    one-call backward's on-chip limit.  Returns (scratch, loss, grad_x,
-    grad_h0) with grad_h0 = dL/dh_0 (allocated here if not given)."""
+    one-call backward's on-chip limit.  The accumulating windows get a device
+    workspace (allocated here unless given; none where their kernel needs
+    none).  Returns (scratch, loss, grad_x, grad_h0) with grad_h0 = dL/dh_0
+    (allocated here if not given)."""
     import torch
     B, K, _ = x.shape
     if window < 1:
         raise ValueError("window must be >= 1")
     H = w_rec.shape[0]
+    if workspace is None and K > window:
+        need = cfc_backward_workspace(B, window, w_in.shape[1], H, accumulate=True)
+        if need > 0:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
     if scratch is None:
         scratch = torch.empty((B, cfc_scratch_row_len(w_in.shape[1], H)), dtype=torch.float32, device=x.device)
     if loss is None:
@@ -182,7 +225,7 @@ def cfc_backward_windows(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, wind
         cfc_backward_window(w_in, w_rec, b, w_tau, x, h0, h_seq, dt, k_begin, k_end, scratch,
                             y=y if seeded else None, delta_in=None if seeded else delta, delta_out=delta,
                             loss=loss if seeded else None, grad_x=grad_x, accumulate=not seeded, stream=stream,
-                            cell=cell)
+                            cell=cell, workspace=workspace)
         k_end = k_begin
     return scratch, loss, grad_x, delta
 

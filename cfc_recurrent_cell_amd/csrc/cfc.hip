@@ -1615,13 +1615,18 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
 // phase 1 and leaves each row's dL/dw_tau sums (float64) in the head of its
 // scratch row, where the a_k it has consumed were; STAGE 2 runs phase 2 and
 // reads them back before the row's dW_in overwrites them.
-template <bool FULL, bool TAU, bool PARKED, int STAGE = 0>
+// ACC (accumulate mode, STAGE 0, not PARKED): the scratch rows are read and
+// the gradient, rounded to float32, is added in float32; dL/da is parked in
+// the caller's workspace `ws` (2 K H 32-bit words per row) instead of the
+// scratch tail, whose old values are still needed.
+template <bool FULL, bool TAU, bool PARKED, int STAGE = 0, bool ACC = false>
 __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
     const float* __restrict__ y, double dt, int B, BwdWindow win, int n_in, int H, float* __restrict__ scratch,
-    float* __restrict__ loss, float* __restrict__ grad_x) {
+    float* __restrict__ loss, float* __restrict__ grad_x, unsigned* __restrict__ ws) {
+    static_assert(!ACC || (!PARKED && STAGE == 0), "accumulate mode recomputes a_k and runs both phases");
     constexpr int cell = TAU ? CFC_CELL_TAU_DECAY : CFC_CELL_GATED;
     const int K = win.Kw;  // steps of this launch; indices below are relative to win.k0
     const long long Kf = win.K, k0 = win.k0;
@@ -1642,8 +1647,12 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const bool row_ok = b_own < B;
     // dL/da of every step is parked in the tail of its row's scratch (as two
     // 32-bit halves per double) until the row's weight gradients are formed;
-    // every element there is rewritten afterwards.
+    // every element there is rewritten afterwards.  ACC parks it in ws.
     const long long tmp_off = N - 2LL * K * H;
+    auto park_row = [&](long long b) -> unsigned* {
+        if constexpr (ACC) return ws + b * (2LL * K * H);
+        else return reinterpret_cast<unsigned*>(scratch + b * N + tmp_off);
+    };
 
     if constexpr (STAGE != 2) {
     for (int u = t; u < kLarge; u += kThreads) {
@@ -1857,7 +1866,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
             const long long b = r0 + rr;
             if (b < B && i < H) {
                 const unsigned long long u = __builtin_bit_cast(unsigned long long, dab[zidx(i, rr)]);
-                unsigned* q = reinterpret_cast<unsigned*>(scratch + b * N + tmp_off) + 2 * ((long long)k * H + i);
+                unsigned* q = park_row(b) + 2 * ((long long)k * H + i);
                 q[0] = (unsigned)u;
                 q[1] = (unsigned)(u >> 32);
             }
@@ -1898,7 +1907,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     double pg = 0.0;  // STAGE 2: dL/dw_tau of unit t, from the row's head
     auto fetch_row = [&](long long b) {
         if constexpr (STAGE == 2) pg = t < H ? reinterpret_cast<const double*>(scratch + b * N)[t] : 0.0;
-        const unsigned* tq = reinterpret_cast<const unsigned*>(scratch + b * N + tmp_off);
+        const unsigned* tq = park_row(b);
 #pragma unroll
         for (int kk = 0; kk < kLargeBwdMaxK; ++kk) {
             double dv = 0.0;
@@ -2016,6 +2025,29 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
             for (int ub = 0; ub < 4; ++ub)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) acc4[ub][jj] = dbl4{0.0, 0.0, 0.0, 0.0};
+            // ACC: the old float4 values of one 16-unit tile's stores: tile 0's
+            // are loaded before the products (their latency hides under
+            // them), tile ub + 1's as soon as tile ub is stored (unaligned or
+            // partial spans are read at the store instead)
+            float4 old[4];
+            auto load_old = [&](int ub) {
+                if constexpr (ACC) {
+                    const int jc0 = jg * 64 + 4 * (lane & 15);
+                    const bool in_part = jc0 < kLarge;
+                    const int col = in_part ? jc0 : jc0 - kLarge;
+                    const int width = in_part ? n_in : H;
+                    const float* base = in_part ? grow : grec;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int i = (4 * wave + ub) * 16 + s + 4 * m;
+                        const float* src = base + (long long)i * width + col;
+                        const bool fast =
+                            i < H && col + 4 <= width && (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+                        old[m] = fast ? *reinterpret_cast<const float4*>(src) : float4{0.f, 0.f, 0.f, 0.f};
+                    }
+                }
+            };
+            load_old(0);
 #pragma unroll
             for (int kc = 0; kc < KCM; ++kc) {
                 if (kc < KC) {
@@ -2051,7 +2083,18 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                     if (i < H) {
                         float* dst = base + (long long)i * width + col;
                         if (col + 4 <= width && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-                            *reinterpret_cast<float4*>(dst) = val;
+                            if constexpr (ACC) {
+                                const float4 o = old[m];
+                                *reinterpret_cast<float4*>(dst) =
+                                    float4{o.x + val.x, o.y + val.y, o.z + val.z, o.w + val.w};
+                            } else {
+                                *reinterpret_cast<float4*>(dst) = val;
+                            }
+                        } else if constexpr (ACC) {
+                            const float v4[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+                            for (int c = 0; c < 4; ++c)
+                                if (col + c < width) dst[c] += v4[c];
                         } else {
                             if (col < width) dst[0] = val.x;
                             if (col + 1 < width) dst[1] = val.y;
@@ -2060,6 +2103,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                         }
                     }
                 }
+                if (ub < 3) load_old(ub + 1);
             }
         }
         // db: the row's parked dL/da summed over k, last step first (the order
@@ -2067,8 +2111,13 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
         if (t < H) {
             double gb = 0.0;
             for (int kk = K - 1; kk >= 0; --kk) gb += dak[kk * kLarge + t];
-            grec[(long long)H * H + t] = (float)gb;
-            grec[(long long)H * H + H + t] = STAGE == 2 ? (float)gw_t : (float)gwt[zidx(t, rr)];
+            if constexpr (ACC) {
+                grec[(long long)H * H + t] += (float)gb;
+                grec[(long long)H * H + H + t] += (float)gwt[zidx(t, rr)];
+            } else {
+                grec[(long long)H * H + t] = (float)gb;
+                grec[(long long)H * H + H + t] = STAGE == 2 ? (float)gw_t : (float)gwt[zidx(t, rr)];
+            }
         }
         __syncthreads();  // LDS reused by the next row
     }
@@ -2304,7 +2353,11 @@ void set_kernel_attributes() {
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, false, true, 2>),
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false, true, 2>),
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, true, true, 2>),
-                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, true, 2>)})
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, true, 2>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, false, false, 0, true>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false, false, 0, true>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, true, false, 0, true>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, false, 0, true>)})
             (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     });
 }
@@ -2372,12 +2425,24 @@ extern "C" int cfc_forward(const cfc_params_t* params, const float* x, const flo
     return launch_status();
 }
 
+extern "C" long long cfc_backward_workspace(int B, int Kw, int n_in, int n_hid, int flags) {
+    if (B < 1 || Kw < 1 || n_in < 1 || n_hid < 1) return -1;
+    if (flags != CFC_OVERWRITE && flags != CFC_ACCUMULATE) return -1;
+    if (cfc_scratch_row_len(n_in, n_hid) < 0) return -1;
+    const bool wide = n_in > kSmall || n_hid > kSmall;
+    if (!wide || Kw > kLargeBwdMaxK || flags != CFC_ACCUMULATE) return 0;
+    long long n;  // dL/da of every row-step in float64
+    if (!mul_ok(8LL * B * Kw, n_hid, &n)) return -1;
+    return n;
+}
+
 namespace {
 // Validation and dispatch shared by cfc_backward (one window covering all K
-// steps, seeded from y) and cfc_backward_window.
+// steps, seeded from y), cfc_backward_window and cfc_backward_window_ws.
 int backward_window(const cfc_params_t* params, const float* x, const float* h0, const float* h_seq,
                     const float* y, const float* delta_in, float dt, int B, int K, int k_begin, int k_end,
-                    float* scratch, float* loss, float* grad_x, float* delta_out, int flags, hipStream_t stream) {
+                    float* scratch, float* loss, float* grad_x, float* delta_out, int flags, void* workspace,
+                    long long workspace_bytes, hipStream_t stream) {
     int rc = check_params(params);
     if (rc) return rc;
     if (!x || !h0 || !h_seq || !scratch) return CFC_ERR_NULL;
@@ -2394,21 +2459,30 @@ int backward_window(const cfc_params_t* params, const float* x, const float* h0,
     if (N < 0 || !mul_ok((long long)B * K, n_in, &nx) || !mul_ok((long long)B * K, H, &ns) ||
         !mul_ok((long long)B, N, &nsc))
         return CFC_ERR_DIM;
+    // accumulate mode in the 16-row kernel parks dL/da in the workspace
+    const long long ws_need = cfc_backward_workspace(B, Kw, n_in, H, flags);
+    if (ws_need < 0) return CFC_ERR_DIM;
+    if (workspace && ws_need > 0 &&
+        (workspace_bytes < ws_need || (reinterpret_cast<uintptr_t>(workspace) & 7) != 0))
+        return CFC_ERR_DIM;
+    const bool ws_used = workspace && ws_need > 0;
     const bool small = n_in <= kSmall && H <= kSmall && Kw <= kSmallBwdMaxK;
     const bool large = !small && (n_in > kSmall || H > kSmall) && Kw <= kLargeBwdMaxK &&
-                       flags == CFC_OVERWRITE;
+                       (flags == CFC_OVERWRITE || ws_used);
     const size_t lds = small ? small_bwd_lds_bytes() : large ? large_bwd_lds_bytes() : bwd_lds_bytes(Kw, n_in, H);
     if (lds > kLdsBytes) return CFC_ERR_UNSUPPORTED;
     const long long BH = (long long)B * H;
     const Range outs[] = {span(scratch, nsc), span(loss, loss ? B : 0), span(grad_x, grad_x ? nx : 0),
-                          span(delta_out, delta_out && delta_out != delta_in ? BH : 0)};
+                          span(delta_out, delta_out && delta_out != delta_in ? BH : 0),
+                          Range{reinterpret_cast<uintptr_t>(workspace),
+                                reinterpret_cast<uintptr_t>(workspace) + (ws_used ? (uintptr_t)ws_need : 0)}};
     const Range ins[] = {span(x, nx), span(h0, BH), span(h_seq, ns), span(y, y && !delta_in ? BH : 0),
                          span(delta_in, delta_in ? BH : 0), span(params->w_in, (long long)H * n_in),
                          span(params->w_rec, (long long)H * H), span(params->b, H), span(params->w_tau, H)};
-    if (!outputs_disjoint(outs, 4, ins, 9)) return CFC_ERR_OVERLAP;
+    if (!outputs_disjoint(outs, 5, ins, 9)) return CFC_ERR_OVERLAP;
     if (delta_out && delta_out == delta_in) {  // in place: still disjoint from the other outputs
         const Range d = span(delta_out, BH);
-        for (int o = 0; o < 3; ++o)
+        for (int o : {0, 1, 2, 4})
             if (overlap(d, outs[o])) return CFC_ERR_OVERLAP;
     }
     const BwdWindow win{K, k_begin, Kw, delta_in, delta_out};
@@ -2425,13 +2499,17 @@ int backward_window(const cfc_params_t* params, const float* x, const float* h0,
     }
     if (large) {
         const long long groups = ((long long)B + kLR - 1) / kLR;
-        const bool tau = params->cell == CFC_CELL_TAU_DECAY;
-        auto kern = large_full(params)
-                        ? (tau ? &cfc_bwd_large_kernel<true, true, false> : &cfc_bwd_large_kernel<true, false, false>)
-                        : (tau ? &cfc_bwd_large_kernel<false, true, false> : &cfc_bwd_large_kernel<false, false, false>);
+        const bool tau = params->cell == CFC_CELL_TAU_DECAY, full = large_full(params);
+        auto kern = full ? (tau ? &cfc_bwd_large_kernel<true, true, false> : &cfc_bwd_large_kernel<true, false, false>)
+                         : (tau ? &cfc_bwd_large_kernel<false, true, false> : &cfc_bwd_large_kernel<false, false, false>);
+        if (flags == CFC_ACCUMULATE)
+            kern = full ? (tau ? &cfc_bwd_large_kernel<true, true, false, 0, true>
+                               : &cfc_bwd_large_kernel<true, false, false, 0, true>)
+                        : (tau ? &cfc_bwd_large_kernel<false, true, false, 0, true>
+                               : &cfc_bwd_large_kernel<false, false, false, 0, true>);
         hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kThreads), lds, stream, params->w_in, params->w_rec,
                            params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, win, n_in, H, scratch, loss,
-                           grad_x);
+                           grad_x, ws_used ? static_cast<unsigned*>(workspace) : nullptr);
         return launch_status();
     }
     hipLaunchKernelGGL(cfc_bwd_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
@@ -2447,7 +2525,7 @@ extern "C" int cfc_backward(const cfc_params_t* params, const float* x, const fl
                             hipStream_t stream) {
     if (!y) return CFC_ERR_NULL;
     return backward_window(params, x, h0, h_seq, y, nullptr, dt, B, K, 0, K, scratch, loss, grad_x, grad_h0,
-                           flags, stream);
+                           flags, nullptr, 0, stream);
 }
 
 extern "C" int cfc_backward_window(const cfc_params_t* params, const float* x, const float* h0,
@@ -2455,7 +2533,16 @@ extern "C" int cfc_backward_window(const cfc_params_t* params, const float* x, c
                                    int B, int K, int k_begin, int k_end, float* scratch, float* loss,
                                    float* grad_x, float* delta_out, int flags, hipStream_t stream) {
     return backward_window(params, x, h0, h_seq, y, delta_in, dt, B, K, k_begin, k_end, scratch, loss, grad_x,
-                           delta_out, flags, stream);
+                           delta_out, flags, nullptr, 0, stream);
+}
+
+extern "C" int cfc_backward_window_ws(const cfc_params_t* params, const float* x, const float* h0,
+                                      const float* h_seq, const float* y, const float* delta_in, float dt,
+                                      int B, int K, int k_begin, int k_end, float* scratch, float* loss,
+                                      float* grad_x, float* delta_out, int flags, void* workspace,
+                                      long long workspace_bytes, hipStream_t stream) {
+    return backward_window(params, x, h0, h_seq, y, delta_in, dt, B, K, k_begin, k_end, scratch, loss, grad_x,
+                           delta_out, flags, workspace, workspace_bytes, stream);
 }
 
 extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, const float* h0,
@@ -2521,7 +2608,7 @@ extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, 
         for (auto* bwd : {bwd1, bwd2})
             hipLaunchKernelGGL(bwd, dim3((unsigned)groups), dim3(kThreads), large_bwd_lds_bytes(), stream, params->w_in,
                                params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, win, n_in, H,
-                               scratch, loss, grad_x);
+                               scratch, loss, grad_x, nullptr);
         return launch_status();
     }
     rc = cfc_forward(params, x, h0, dt, B, K, h_seq, stream);

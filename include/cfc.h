@@ -173,14 +173,50 @@ int cfc_backward(const cfc_params_t *params, const float *x, const float *h0,
  *   delta_out [B, n_hid] or NULL: dL/dh_k_begin -- the next window's
  *             delta_in, or dL/dh_0 for k_begin = 0.  It may be the same buffer
  *             as delta_in (every element is read before it is written).
- * Windows of at most 64 steps at n_in, n_hid <= 128 (20 at wider shapes,
- * overwrite mode) run the specialised kernels.
+ * Windows of at most 64 steps at n_in, n_hid <= 128 (20 at wider shapes, in
+ * overwrite mode, or in accumulate mode through cfc_backward_window_ws) run
+ * the specialised kernels.
  * Returns a CFC_* status: CFC_ERR_DIM for a bad window, a missing seed or a
  * loss without one; CFC_ERR_UNSUPPORTED if the window exceeds the LDS bound. */
 int cfc_backward_window(const cfc_params_t *params, const float *x, const float *h0,
                         const float *h_seq, const float *y, const float *delta_in, float dt,
                         int B, int K, int k_begin, int k_end, float *scratch, float *loss,
                         float *grad_x, float *delta_out, int flags, hipStream_t stream);
+
+/* Bytes of device workspace that cfc_backward_window_ws needs for a window of
+ * Kw steps: 8 * B * Kw * n_hid (dL/da of every row-step, float64) where the
+ * window runs the 16-row backward in accumulate mode (n_in or n_hid above
+ * 128, Kw <= 20, flags = CFC_ACCUMULATE); 0 where no kernel uses one.
+ * Returns -1 for a non-positive size, unknown flags or overflow. */
+long long cfc_backward_workspace(int B, int Kw, int n_in, int n_hid, int flags);
+
+/* cfc_backward_window with a caller-owned device workspace.  The pages' form
+ * of the backward adds each call's gradient into the scratch ("K-loop
+ * Parallelization Implementation Plan", Task 5: scratch zeroed once, the K
+ * calls accumulate); at widths above 128 the 16-row backward keeps dL/da of
+ * the window's steps in its rows' scratch tails until the weight gradients are
+ * formed, which accumulate mode cannot do, since the old values there are
+ * still needed.  With a workspace it parks dL/da there instead, so
+ * accumulating windows of at most 20 steps at these widths run the 16-row
+ * kernel rather than the general one-row-per-workgroup backward.
+ *   arguments 1-16  as for cfc_backward_window
+ *   workspace        device memory, 8-byte aligned, or NULL (then the call is
+ *                    cfc_backward_window); contents on entry are ignored and
+ *                    on return unspecified; it must not overlap any other
+ *                    argument while it is in use (CFC_ERR_OVERLAP)
+ *   workspace_bytes  its size; below cfc_backward_workspace(B, k_end -
+ *                    k_begin, n_in, n_hid, flags), or a misaligned workspace,
+ *                    is CFC_ERR_DIM when the window would use it
+ * Outputs are the same as cfc_backward_window's for the same arguments up to
+ * the summation order of the kernel that runs (the 16-row kernel's overwrite
+ * and accumulate modes compute the same float32 gradient, bitwise).  The
+ * workspace is ignored where the window does not use it (overwrite mode, or
+ * n_in, n_hid <= 128, or more than 20 steps at the wider shapes). */
+int cfc_backward_window_ws(const cfc_params_t *params, const float *x, const float *h0,
+                           const float *h_seq, const float *y, const float *delta_in, float dt,
+                           int B, int K, int k_begin, int k_end, float *scratch, float *loss,
+                           float *grad_x, float *delta_out, int flags, void *workspace,
+                           long long workspace_bytes, hipStream_t stream);
 
 /* cfc_forward followed by cfc_backward on the same inputs, in one call
  * ("K-loop Parallelization Implementation Plan", Tasks 2 and 3 back to back):

@@ -28,7 +28,8 @@ def test_exports_every_declared_symbol(lib):
     names = _lib.declared_symbols()
     assert set(names) == {"cfc_scratch_row_len", "cfc_forward", "cfc_backward", "cfc_backward_window",
                           "cfc_forward_backward", "reduce_axis0", "reduce_axis0_split",
-                          "reduce_axis0_split_workspace", "cfc_status_string"}
+                          "reduce_axis0_split_workspace", "cfc_status_string", "cfc_backward_workspace",
+                          "cfc_backward_window_ws"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -164,6 +165,48 @@ def test_backward_window_validation(lib):
     # the window's own LDS bound: 64 steps of 128/128 fit, 77 do not
     big = _params(n_in=128, n_hid=128)
     assert _win(lib, big, 0, 77, K=200, y=None, delta_in=D1) == C.CFC_ERR_UNSUPPORTED
+
+
+def test_backward_workspace_sizes(lib):
+    """8 B Kw n_hid bytes (dL/da of every row-step in float64) where the
+    16-row backward runs in accumulate mode, 0 elsewhere."""
+    ws = lib.cfc_backward_workspace
+    assert ws(8192, 8, 256, 256, C.CFC_ACCUMULATE) == 8 * 8192 * 8 * 256
+    assert ws(3, 20, 129, 7, C.CFC_ACCUMULATE) == 8 * 3 * 20 * 7       # n_in alone above 128
+    assert ws(3, 20, 7, 129, C.CFC_ACCUMULATE) == 8 * 3 * 20 * 129
+    assert ws(3, 21, 256, 256, C.CFC_ACCUMULATE) == 0                  # beyond 20 steps: general kernel
+    assert ws(3, 8, 256, 256, C.CFC_OVERWRITE) == 0                    # overwrite parks in the scratch
+    assert ws(3, 64, 128, 128, C.CFC_ACCUMULATE) == 0                  # one-row kernels keep dL/da on chip
+    assert ws(0, 8, 256, 256, C.CFC_ACCUMULATE) == -1
+    assert ws(3, 0, 256, 256, C.CFC_ACCUMULATE) == -1
+    assert ws(3, 8, 0, 256, C.CFC_ACCUMULATE) == -1
+    assert ws(3, 8, 256, 256, 7) == -1
+    assert ws(2**31 - 1, 20, 256, 2**31 - 1, C.CFC_ACCUMULATE) == -1   # overflow
+
+
+def _win_ws(lib, p, ws, ws_bytes, k_begin=0, k_end=6, K=6, flags=C.CFC_ACCUMULATE, scratch=FAKE + 0x900000):
+    return lib.cfc_backward_window_ws(ctypes.byref(p), FAKE + 0x400000, FAKE + 0x500000, FAKE + 0x600000,
+                                      FAKE + 0x700000, None, 1.0, 2, K, k_begin, k_end, scratch, None, None, None,
+                                      flags, ws, ws_bytes, None)
+
+
+def test_backward_window_ws_validation(lib):
+    """The workspace is checked where the window would use it: size, 8-byte
+    alignment, overlap with every other argument.  Every call here fails
+    validation, so none launches anything."""
+    p = _params(n_in=256, n_hid=256)                     # scratch [2, 131584] at FAKE + 0x900000 (1 MB)
+    need = 8 * 2 * 6 * 256
+    WS = FAKE + 0x1000000
+    assert _win_ws(lib, p, WS, need - 1) == C.CFC_ERR_DIM            # too small
+    assert _win_ws(lib, p, WS + 4, need) == C.CFC_ERR_DIM            # misaligned
+    assert _win_ws(lib, p, FAKE + 0x900000 + 64, need) == C.CFC_ERR_OVERLAP   # over the scratch
+    assert _win_ws(lib, p, FAKE + 0x400000, need) == C.CFC_ERR_OVERLAP        # over x
+    assert _win_ws(lib, p, FAKE + 0x100000, need) == C.CFC_ERR_OVERLAP        # over W_in
+    # the cfc_backward_window checks still come first
+    assert _win_ws(lib, p, WS, need, k_begin=0, k_end=4) == C.CFC_ERR_DIM      # seeded, not ending at K
+    assert _win_ws(lib, p, WS, need, flags=9) == C.CFC_ERR_DIM
+    # a window of 7 steps needs more than a 6-step workspace
+    assert _win_ws(lib, p, WS, need, K=7, k_end=7) == C.CFC_ERR_DIM
 
 
 def test_backward_lds_limit_matches_header(lib):

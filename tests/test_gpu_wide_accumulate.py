@@ -1,0 +1,125 @@
+"""GPU parity of accumulate mode at widths above 128 with a caller workspace
+(cfc_backward_window_ws): the 16-row backward parks dL/da in the workspace
+instead of the scratch tail and adds its float32 gradient into the scratch.
+Checked bitwise against the same kernel's overwrite mode, against the float64
+oracle, and against the general backward that accumulate mode runs without a
+workspace.
+"""
+import numpy as np
+import pytest
+
+from parity_util import assert_close, host, oracle_threads, say, to_dev
+from oracle import oracle as O
+from cfc_recurrent_cell_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests selected but torch sees no GPU")
+    import cfc_recurrent_cell_amd as C
+    C.load_library()
+    return torch.device("cuda:0")
+
+
+CASES = [
+    # (B, K, n_in, H, dt, seed, cell, note)
+    (20, 8, 256, 256, 1.0, 131, "gated", "unmasked 256 x 256, two row groups (16 + 4)"),
+    (19, 20, 200, 140, 0.7, 132, "gated", "masked widths, K at the 16-row bound"),
+    (17, 5, 256, 256, 0.05, 133, "tau_decay", "tau-decay cell, unmasked"),
+    (3, 11, 130, 96, 0.8, 134, "tau_decay", "one partial row group, n_in alone above 128"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_K{}_n{}_H{}_{}".format(*c[:4], c[6]))
+def test_wide_accumulate_with_workspace(case):
+    """Onto zeros, accumulate equals overwrite bitwise; onto random values it
+    is their float32 sum with the overwrite gradient, bitwise; loss, grad_x and
+    grad_h0 are the overwrite call's; the workspace's contents on entry do not
+    matter; and the result is within tolerance of the oracle and of the
+    general backward's accumulate mode."""
+    import torch
+    import cfc_recurrent_cell_amd as C
+    B, K, n_in, H, dt, seed, cell, note = case
+    say(f"[wide accumulate] B={B} K={K} {n_in}/{H} {cell}: {note}")
+    inp = W.make_random_cfc_inputs(B, K, n_in, H, dt, seed, cell=cell)
+    d = to_dev(inp)
+    args = (d["w_in"], d["w_rec"], d["b"], d["w_tau"], d["x"], d["h0"])
+    h = C.cfc_forward(*args, d["dt"], cell=cell)
+    N = W.scratch_row_len(n_in, H)
+    need = C.cfc_backward_workspace(B, K, n_in, H, accumulate=True)
+    assert need == 8 * B * K * H
+    ws = torch.full((need // 4,), float("nan"), device="cuda")   # float32 NaN words: contents ignored
+
+    def run(scratch, accumulate, workspace):
+        gx = torch.full((B, K, n_in), float("nan"), device="cuda")
+        gh = torch.full((B, H), float("nan"), device="cuda")
+        loss = torch.full((B,), float("nan"), device="cuda")
+        C.cfc_backward(*args, h, d["y"], d["dt"], scratch=scratch, loss=loss, grad_x=gx, grad_h0=gh,
+                       accumulate=accumulate, cell=cell, workspace=workspace)
+        return [host(t).copy() for t in (scratch, loss, gx, gh)]
+
+    over = run(torch.full((B, N), float("nan"), device="cuda"), False, None)
+    zero = run(torch.zeros((B, N), device="cuda"), True, ws)
+    for a, b, name in zip(zero, over, ("scratch", "loss", "grad_x", "grad_h0")):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"accumulate onto zeros: {name}"
+    base = W.make_random_matrix(B, N, seed=seed + 1000)
+    acc = run(torch.from_numpy(base.copy()).cuda(), True, ws)
+    want = base.astype(np.float32) + over[0]
+    assert np.array_equal(acc[0].view(np.uint32), want.view(np.uint32))
+    for a, b, name in zip(acc[1:], over[1:], ("loss", "grad_x", "grad_h0")):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"accumulate onto values: {name}"
+    ref = O.cfc_step(inp, threads=oracle_threads(), input_grads=True)
+    assert_close(over[0], ref["scratch"], "overwrite scratch")
+    assert_close(acc[0] - base.astype(np.float32), ref["scratch"], "accumulated gradient")
+    assert_close(acc[2], ref["grad_x"], "grad_x")
+    assert_close(acc[3], ref["grad_h0"], "grad_h0")
+    # the general backward (no workspace) accumulates the same gradient in
+    # another summation order
+    gen = run(torch.from_numpy(base.copy()).cuda(), True, None)
+    assert_close(gen[0], acc[0], "general backward's accumulate mode")
+
+
+def test_workspace_reuse_over_calls_and_shapes():
+    """One workspace serves consecutive calls of different sizes (a larger
+    call, then a smaller one), each checked against a fresh overwrite."""
+    import torch
+    import cfc_recurrent_cell_amd as C
+    say("[wide accumulate] one workspace, two calls of different sizes")
+    big = C.cfc_backward_workspace(18, 9, 256, 256, accumulate=True)
+    ws = torch.empty((big,), dtype=torch.uint8, device="cuda")
+    for B, K, seed in ((18, 9, 141), (5, 4, 142)):
+        inp = W.make_random_cfc_inputs(B, K, 256, 256, 0.9, seed)
+        d = to_dev(inp)
+        args = (d["w_in"], d["w_rec"], d["b"], d["w_tau"], d["x"], d["h0"])
+        h = C.cfc_forward(*args, d["dt"])
+        N = W.scratch_row_len(256, 256)
+        over, _ = C.cfc_backward(*args, h, d["y"], d["dt"], scratch=torch.empty((B, N), device="cuda"))
+        base = W.make_random_matrix(B, N, seed=seed + 7)
+        acc, _ = C.cfc_backward(*args, h, d["y"], d["dt"], scratch=torch.from_numpy(base.copy()).cuda(),
+                                accumulate=True, workspace=ws)
+        want = base.astype(np.float32) + host(over)
+        assert np.array_equal(host(acc).view(np.uint32), want.view(np.uint32))
+
+
+def test_too_small_workspace_is_refused_before_launch():
+    import torch
+    import cfc_recurrent_cell_amd as C
+    say("[wide accumulate] refusal of a short workspace")
+    B, K = 4, 3
+    inp = W.make_random_cfc_inputs(B, K, 256, 256, 1.0, 151)
+    d = to_dev(inp)
+    args = (d["w_in"], d["w_rec"], d["b"], d["w_tau"], d["x"], d["h0"])
+    h = C.cfc_forward(*args, d["dt"])
+    N = W.scratch_row_len(256, 256)
+    base = W.make_random_matrix(B, N, seed=152)
+    scratch = torch.from_numpy(base.copy()).cuda()
+    need = C.cfc_backward_workspace(B, K, 256, 256, accumulate=True)
+    ws = torch.empty((need - 8,), dtype=torch.uint8, device="cuda")
+    with pytest.raises(C.CfcError):
+        C.cfc_backward(*args, h, d["y"], d["dt"], scratch=scratch, accumulate=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(scratch).view(np.uint32), base.view(np.uint32))   # nothing was enqueued

@@ -33,7 +33,8 @@ CASES = [
     (3, 150, 128, 128, 0.5, 91, 64, "gated", "K = 150 > 76 at 128/128: one-row kernels per window"),
     (2, 90, 20, 100, 0.4, 92, 70, "gated", "70-step windows: the general backward"),
     (2, 61, 40, 56, 0.6, 93, 16, "tau_decay", "tau-decay cell, ragged last window"),
-    (3, 45, 256, 256, 1.0, 94, 20, "gated", "K = 45 > 37 at 256/256: 16-row kernel, then accumulating"),
+    (3, 45, 256, 256, 1.0, 94, 20, "gated", "K = 45 > 37 at 256/256: 16-row kernel, accumulating windows "
+                                            "parked in a workspace"),
     (2, 7, 12, 20, 0.9, 95, 1, "gated", "one step per window, as the pages' K launches"),
 ]
 
