@@ -4,16 +4,21 @@
 //   cfc_fwd_small_kernel / cfc_bwd_small_kernel   n_in, n_hid <= 128: one
 //       workgroup per batch row runs the whole (reverse) K-loop; dense
 //       contractions on the f64 matrix cores, the serial chain on the vector
-//       units with W_rec held in registers.
+//       units with W_rec held in registers.  cfc_fb_small_kernel runs both
+//       directions in one launch, keeping the forward's a_k on chip.
 //   cfc_fwd_large_kernel / cfc_bwd_large_kernel   n_in or n_hid in (128, 256]:
 //       a workgroup owns 16 batch rows, so every step is a matrix-core product.
 //   cfc_bwd_kernel    general backward (any n_in, n_hid <= 256, and the
-//       accumulate mode at the larger sizes): one workgroup per row, matvecs on
-//       the vector units with the weights read from L2.
+//       accumulate mode at the larger sizes when the caller gives no
+//       workspace): one workgroup per row, matvecs on the vector units with
+//       the weights read from L2.
 //   Every backward keeps dL/da for all steps on chip (or parked in its own
-//   scratch row) and forms the weight gradients as contractions over k, so
-//   each scratch element is written once (no per-step read-modify-write).
-//   reduce_axis0_kernel  column-tiled sum over the leading axis.
+//   scratch row, or in the caller's workspace) and forms the weight gradients
+//   as contractions over k, so each scratch element is written once (no
+//   per-step read-modify-write).
+//   reduce_axis0_kernel  column-tiled sum over the leading axis;
+//   reduce_rows_narrow_kernel + reduce_partials_kernel  the two-phase sum for
+//       narrow rows over a long leading axis.
 //
 // The block-per-batch layout and the single-writer scratch come from the
 // "K-loop Parallelization Implementation Plan" (foxhunt, 2026-05-17), Tasks 2
