@@ -248,7 +248,7 @@ def main():
     def fb(ig=False, accumulate=False):
         C.cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt, h_seq=h_seq, scratch=scratch, loss=loss,
                                grad_x=grad_x if ig else None, grad_h0=grad_h0 if ig else None,
-                               accumulate=accumulate, cell=cell)
+                               accumulate=accumulate, cell=cell, workspace=acc_ws if accumulate else None)
 
     def windows():
         # the backward as windows of --window steps (dL/dh carried in place)
@@ -269,13 +269,11 @@ def main():
         "windows": [("cfc_fwd_kernel", fwd), ("cfc_bwd_kernel", windows), ("reduce_axis0_kernel", red)],
         # the pages' clear-then-accumulate form: explicit zero fill, then += gradient
         "accumulate": [("zero_fill", scratch.zero_), ("cfc_fb_kernel", lambda: fb(accumulate=True)),
-                       ("reduce_axis0_kernel", red)] if acc_ws is None else
-                      [("zero_fill", scratch.zero_), ("cfc_fwd_kernel", fwd),
-                       ("cfc_bwd_kernel", lambda: bwd(accumulate=True)), ("reduce_axis0_kernel", red)],
+                       ("reduce_axis0_kernel", red)],
     }
     acc_step = ("scratch zero fill + cfc_forward_backward(CFC_ACCUMULATE) + reduce_axis0" if acc_ws is None else
-                "scratch zero fill + cfc_forward + cfc_backward_window_ws(CFC_ACCUMULATE, %d-byte workspace) + "
-                "reduce_axis0" % acc_ws_bytes)
+                "scratch zero fill + cfc_forward_backward_ws(CFC_ACCUMULATE, %d-byte workspace) + reduce_axis0"
+                % acc_ws_bytes)
 
     def run_pass(path, bracket):
         """W warm-up steps, then K steps bracketed by a sync on both sides.

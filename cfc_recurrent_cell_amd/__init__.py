@@ -233,10 +233,13 @@ def cfc_backward_windows(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, wind
 def cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt: float, h_seq=None, scratch=None,
                          loss=None, accumulate: bool = False, want_loss: bool = True,
                          input_grads: bool = False, grad_x=None, grad_h0=None,
-                         stream=None, cell: str = "gated") -> Tuple[object, ...]:
+                         stream=None, cell: str = "gated", workspace=None) -> Tuple[object, ...]:
     """(h_seq [B, K, H], scratch [B, N], loss [B] or None): the forward and the
     backward of the same inputs in one library call (see include/cfc.h).  With
-    ``input_grads`` (or explicit buffers) grad_x and grad_h0 are appended."""
+    ``input_grads`` (or explicit buffers) grad_x and grad_h0 are appended.  A
+    device ``workspace`` (cfc_backward_workspace bytes) goes to
+    cfc_forward_backward_ws: accumulate mode at widths above 128 then runs the
+    16-row backward."""
     import torch
     lib = load_library()
     p = _params(w_in, w_rec, b, w_tau, cell)
@@ -259,10 +262,17 @@ def cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt: float, h_seq=None,
     grad_x, grad_h0 = _input_grad_buffers(x, p, grad_x, grad_h0, input_grads)
     flags = CFC_ACCUMULATE if accumulate else CFC_OVERWRITE
     ptr = lambda t: t.data_ptr() if t is not None else None
-    _check("cfc_forward_backward", lib.cfc_forward_backward(
-        ctypes.byref(p), x.data_ptr(), h0.data_ptr(), y.data_ptr(), float(dt), B, K,
-        h_seq.data_ptr(), scratch.data_ptr(), ptr(loss), ptr(grad_x), ptr(grad_h0), flags,
-        _stream(x.device, stream)))
+    if workspace is not None:
+        ws_ptr, ws_bytes = _workspace_arg(workspace)
+        _check("cfc_forward_backward_ws", lib.cfc_forward_backward_ws(
+            ctypes.byref(p), x.data_ptr(), h0.data_ptr(), y.data_ptr(), float(dt), B, K,
+            h_seq.data_ptr(), scratch.data_ptr(), ptr(loss), ptr(grad_x), ptr(grad_h0), flags, ws_ptr, ws_bytes,
+            _stream(x.device, stream)))
+    else:
+        _check("cfc_forward_backward", lib.cfc_forward_backward(
+            ctypes.byref(p), x.data_ptr(), h0.data_ptr(), y.data_ptr(), float(dt), B, K,
+            h_seq.data_ptr(), scratch.data_ptr(), ptr(loss), ptr(grad_x), ptr(grad_h0), flags,
+            _stream(x.device, stream)))
     if want_inputs:
         return h_seq, scratch, loss, grad_x, grad_h0
     return h_seq, scratch, loss

@@ -72,6 +72,9 @@ def load_library(path: str = LIB_PATH):
     lib.cfc_forward_backward.restype = i
     lib.cfc_forward_backward.argtypes = [ctypes.POINTER(CfcParams), vp, vp, vp, f, i, i, vp, vp, vp, vp, vp,
                                          i, vp]
+    lib.cfc_forward_backward_ws.restype = i
+    lib.cfc_forward_backward_ws.argtypes = [ctypes.POINTER(CfcParams), vp, vp, vp, f, i, i, vp, vp, vp, vp, vp,
+                                            i, vp, ll, vp]
     lib.reduce_axis0.restype = i
     lib.reduce_axis0.argtypes = [vp, ll, ll, vp, vp]
     lib.reduce_axis0_split_workspace.restype = ll

@@ -2558,10 +2558,10 @@ extern "C" int cfc_backward_window_ws(const cfc_params_t* params, const float* x
                            delta_out, flags, workspace, workspace_bytes, stream);
 }
 
-extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, const float* h0,
-                                    const float* y, float dt, int B, int K, float* h_seq, float* scratch,
-                                    float* loss, float* grad_x, float* grad_h0, int flags,
-                                    hipStream_t stream) {
+namespace {
+int forward_backward(const cfc_params_t* params, const float* x, const float* h0, const float* y, float dt, int B,
+                     int K, float* h_seq, float* scratch, float* loss, float* grad_x, float* grad_h0, int flags,
+                     void* workspace, long long workspace_bytes, hipStream_t stream) {
     int rc = check_params(params);
     if (rc) return rc;
     if (!x || !h0 || !y || !h_seq || !scratch) return CFC_ERR_NULL;
@@ -2593,8 +2593,17 @@ extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, 
         return launch_status();
     }
     // other shapes: the two directions as separate launches on the same stream;
-    // the backward's shape limits are checked before anything is launched
-    const bool large = (n_in > kSmall || H > kSmall) && K <= kLargeBwdMaxK && flags == CFC_OVERWRITE;
+    // the backward's shape limits and workspace are checked before anything is
+    // launched
+    const long long ws_need = cfc_backward_workspace(B, K, n_in, H, flags);
+    if (ws_need < 0) return CFC_ERR_DIM;
+    const bool ws_used = workspace && ws_need > 0;
+    if (ws_used) {
+        if (workspace_bytes < ws_need || (reinterpret_cast<uintptr_t>(workspace) & 7) != 0) return CFC_ERR_DIM;
+        const Range w{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + (uintptr_t)ws_need};
+        if (!outputs_disjoint(&w, 1, outs, 5) || !outputs_disjoint(&w, 1, ins, 7)) return CFC_ERR_OVERLAP;
+    }
+    const bool large = (n_in > kSmall || H > kSmall) && K <= kLargeBwdMaxK && (flags == CFC_OVERWRITE || ws_used);
     const bool small_bwd = n_in <= kSmall && H <= kSmall && K <= kSmallBwdMaxK;
     const size_t lds = small_bwd ? small_bwd_lds_bytes() : large ? large_bwd_lds_bytes() : bwd_lds_bytes(K, n_in, H);
     if (lds > kLdsBytes) return CFC_ERR_UNSUPPORTED;
@@ -2603,7 +2612,8 @@ extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, 
     // recomputing it (needs 8-byte-aligned rows; the head [0, 2KH) and the
     // backward's parked dL/da in the tail [N - 2KH, N) are disjoint because
     // 4K <= n_in + H + 2 at these widths and K)
-    if (large && N % 2 == 0 && (reinterpret_cast<uintptr_t>(scratch) & 7) == 0 && 4LL * K * H <= N) {
+    if (large && flags == CFC_OVERWRITE && N % 2 == 0 && (reinterpret_cast<uintptr_t>(scratch) & 7) == 0 &&
+        4LL * K * H <= N) {
         set_kernel_attributes();
         const long long groups = ((long long)B + kLR - 1) / kLR;
         const bool full = large_full(params), tau = params->cell == CFC_CELL_TAU_DECAY;
@@ -2626,7 +2636,25 @@ extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, 
     }
     rc = cfc_forward(params, x, h0, dt, B, K, h_seq, stream);
     if (rc) return rc;
-    return cfc_backward(params, x, h0, h_seq, y, dt, B, K, scratch, loss, grad_x, grad_h0, flags, stream);
+    return backward_window(params, x, h0, h_seq, y, nullptr, dt, B, K, 0, K, scratch, loss, grad_x, grad_h0, flags,
+                           workspace, workspace_bytes, stream);
+}
+}  // namespace
+
+extern "C" int cfc_forward_backward(const cfc_params_t* params, const float* x, const float* h0,
+                                    const float* y, float dt, int B, int K, float* h_seq, float* scratch,
+                                    float* loss, float* grad_x, float* grad_h0, int flags,
+                                    hipStream_t stream) {
+    return forward_backward(params, x, h0, y, dt, B, K, h_seq, scratch, loss, grad_x, grad_h0, flags, nullptr, 0,
+                            stream);
+}
+
+extern "C" int cfc_forward_backward_ws(const cfc_params_t* params, const float* x, const float* h0,
+                                       const float* y, float dt, int B, int K, float* h_seq, float* scratch,
+                                       float* loss, float* grad_x, float* grad_h0, int flags, void* workspace,
+                                       long long workspace_bytes, hipStream_t stream) {
+    return forward_backward(params, x, h0, y, dt, B, K, h_seq, scratch, loss, grad_x, grad_h0, flags, workspace,
+                            workspace_bytes, stream);
 }
 
 // Chunking of the split reduce; it depends only on (B, N), so the summation

@@ -243,6 +243,24 @@ int cfc_forward_backward(const cfc_params_t *params, const float *x, const float
                          float *loss, float *grad_x, float *grad_h0, int flags,
                          hipStream_t stream);
 
+/* cfc_forward_backward with a caller-owned device workspace, for accumulate
+ * mode at widths above 128 (the pages' scratch += of "K-loop Parallelization
+ * Implementation Plan", Task 5): with K <= 20 the backward then runs the
+ * 16-row kernel, parking dL/da in the workspace, as cfc_backward_window_ws
+ * does; otherwise the call is cfc_forward_backward and the workspace is
+ * ignored.
+ *   arguments 1-13   as for cfc_forward_backward
+ *   workspace        device memory, 8-byte aligned, or NULL; contents on entry
+ *                    ignored, on return unspecified
+ *   workspace_bytes  at least cfc_backward_workspace(B, K, n_in, n_hid, flags)
+ *                    where it is used (else CFC_ERR_DIM); a workspace that
+ *                    overlaps another argument is CFC_ERR_OVERLAP.  Both are
+ *                    checked before the forward is enqueued. */
+int cfc_forward_backward_ws(const cfc_params_t *params, const float *x, const float *h0,
+                            const float *y, float dt, int B, int K, float *h_seq, float *scratch,
+                            float *loss, float *grad_x, float *grad_h0, int flags,
+                            void *workspace, long long workspace_bytes, hipStream_t stream);
+
 /* Column sum ("K-loop Parallelization Implementation Plan", Task 1):
  *   out[j] = sum_{b < B} per_batch[b, j]   for j < N, OVERWRITING out.
  * Float64 accumulation in a fixed order (no atomics), one float32 rounding.

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"cfc_scratch_row_len", "cfc_forward", "cfc_backward", "cfc_backward_window",
                           "cfc_forward_backward", "reduce_axis0", "reduce_axis0_split",
                           "reduce_axis0_split_workspace", "cfc_status_string", "cfc_backward_workspace",
-                          "cfc_backward_window_ws"}
+                          "cfc_backward_window_ws", "cfc_forward_backward_ws"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -207,6 +207,25 @@ def test_backward_window_ws_validation(lib):
     assert _win_ws(lib, p, WS, need, flags=9) == C.CFC_ERR_DIM
     # a window of 7 steps needs more than a 6-step workspace
     assert _win_ws(lib, p, WS, need, K=7, k_end=7) == C.CFC_ERR_DIM
+
+
+def test_forward_backward_ws_validation(lib):
+    """The one-call entry checks the workspace before it enqueues the
+    forward: size, alignment, overlap (with h_seq too)."""
+    p = _params(n_in=256, n_hid=256)
+    need = 8 * 2 * 6 * 256
+    WS = FAKE + 0x1000000
+
+    def fbw(ws, nbytes, flags=C.CFC_ACCUMULATE):
+        return lib.cfc_forward_backward_ws(ctypes.byref(p), FAKE + 0x400000, FAKE + 0x500000, FAKE + 0x700000,
+                                           1.0, 2, 6, FAKE + 0x600000, FAKE + 0x900000, None, None, None, flags,
+                                           ws, nbytes, None)
+    assert fbw(WS, need - 1) == C.CFC_ERR_DIM
+    assert fbw(WS + 4, need) == C.CFC_ERR_DIM
+    assert fbw(FAKE + 0x600000, need) == C.CFC_ERR_OVERLAP     # over h_seq
+    assert fbw(FAKE + 0x900000, need) == C.CFC_ERR_OVERLAP     # over the scratch
+    assert fbw(FAKE + 0x200000, need) == C.CFC_ERR_OVERLAP     # over b
+    assert fbw(WS, need, flags=3) == C.CFC_ERR_DIM
 
 
 def test_backward_lds_limit_matches_header(lib):

@@ -83,6 +83,33 @@ def test_wide_accumulate_with_workspace(case):
     assert_close(gen[0], acc[0], "general backward's accumulate mode")
 
 
+@pytest.mark.parametrize("cell", ["gated", "tau_decay"])
+def test_one_call_entry_with_workspace(cell):
+    """cfc_forward_backward_ws in accumulate mode: the forward's h_seq and the
+    backward's outputs bitwise equal to cfc_forward then the workspace
+    backward, and onto random values the float32 sum with the one-call
+    overwrite gradient (the parked path) within the backward's tolerance."""
+    import torch
+    import cfc_recurrent_cell_amd as C
+    B, K, n = 21, 8, 256
+    say(f"[wide accumulate] one-call entry with a workspace, {cell}")
+    inp = W.make_random_cfc_inputs(B, K, n, n, 0.3 if cell == "tau_decay" else 1.0, 161, cell=cell)
+    d = to_dev(inp)
+    args = (d["w_in"], d["w_rec"], d["b"], d["w_tau"], d["x"], d["h0"])
+    N = W.scratch_row_len(n, n)
+    ws = torch.empty((C.cfc_backward_workspace(B, K, n, n),), dtype=torch.uint8, device="cuda")
+    base = W.make_random_matrix(B, N, seed=162)
+    h1, s1, l1 = C.cfc_forward_backward(*args, d["y"], d["dt"], scratch=torch.from_numpy(base.copy()).cuda(),
+                                        accumulate=True, cell=cell, workspace=ws)
+    h2 = C.cfc_forward(*args, d["dt"], cell=cell)
+    s2, l2 = C.cfc_backward(*args, h2, d["y"], d["dt"], scratch=torch.from_numpy(base.copy()).cuda(),
+                            accumulate=True, cell=cell, workspace=ws)
+    for a, b_, name in ((h1, h2, "h_seq"), (s1, s2, "scratch"), (l1, l2, "loss")):
+        assert np.array_equal(host(a).view(np.uint32), host(b_).view(np.uint32)), name
+    _, over, _ = C.cfc_forward_backward(*args, d["y"], d["dt"], cell=cell)
+    assert_close(host(s1) - base, host(over), "accumulated one-call gradient")
+
+
 def test_workspace_reuse_over_calls_and_shapes():
     """One workspace serves consecutive calls of different sizes (a larger
     call, then a smaller one), each checked against a fresh overwrite."""
