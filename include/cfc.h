@@ -9,7 +9,11 @@
  *   reduce_axis0  scratch [B,N]                    -> out [N]
  *
  * cfc_forward_backward does the first two in one call (one launch where the
- * shape allows it).
+ * shape allows it).  cfc_backward_window runs the backward over a window of
+ * steps; cfc_forward_backward_ws and cfc_backward_window_ws take a caller
+ * workspace that lets accumulate mode at widths above 128 run the fast
+ * 16-row backward; reduce_axis0_split is the reducer for narrow rows over a
+ * long leading axis.
  *
  * The structure -- one independent chain per batch row, a per-batch gradient
  * scratch in which each row has a single writer and no atomics, and a
