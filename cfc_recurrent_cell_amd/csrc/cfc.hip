@@ -2087,6 +2087,35 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                 const int col = in_part ? jc0 : jc0 - kLarge;
                 const int width = in_part ? n_in : H;
                 float* base = in_part ? grow : grec;
+                if constexpr (ACC) {
+                    // the tile's sums first, then the next tile's old values
+                    // (issued ahead of this tile's stores, so that their wait
+                    // does not include the stores' completion), then the stores
+                    f32x4 sum[4];
+                    float4 tile[4];  // the bare tile, for unaligned or partial spans
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        tile[m] = *reinterpret_cast<const float4*>(gst + (s + 4 * m) * kLargeGS + c4);
+                        sum[m] = f32x4{old[m].x + tile[m].x, old[m].y + tile[m].y, old[m].z + tile[m].z,
+                                       old[m].w + tile[m].w};
+                    }
+                    if (ub < 3) load_old(ub + 1);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int i = ib * 16 + s + 4 * m;
+                        if (i < H) {
+                            float* dst = base + (long long)i * width + col;
+                            if (col + 4 <= width && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                                __builtin_nontemporal_store(sum[m], reinterpret_cast<f32x4*>(dst));
+                            } else {
+                                const float v4[4] = {tile[m].x, tile[m].y, tile[m].z, tile[m].w};
+#pragma unroll
+                                for (int c = 0; c < 4; ++c)
+                                    if (col + c < width) dst[c] += v4[c];
+                            }
+                        }
+                    }
+                } else {
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int rr2 = s + 4 * m;
@@ -2095,19 +2124,8 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                     if (i < H) {
                         float* dst = base + (long long)i * width + col;
                         if (col + 4 <= width && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-                            if constexpr (ACC) {
-                                const float4 o = old[m];
-                                __builtin_nontemporal_store(f32x4{o.x + val.x, o.y + val.y, o.z + val.z, o.w + val.w},
-                                                            reinterpret_cast<f32x4*>(dst));
-                            } else {
-                                __builtin_nontemporal_store(f32x4{val.x, val.y, val.z, val.w},
-                                                            reinterpret_cast<f32x4*>(dst));
-                            }
-                        } else if constexpr (ACC) {
-                            const float v4[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-                            for (int c = 0; c < 4; ++c)
-                                if (col + c < width) dst[c] += v4[c];
+                            __builtin_nontemporal_store(f32x4{val.x, val.y, val.z, val.w},
+                                                        reinterpret_cast<f32x4*>(dst));
                         } else {
                             if (col < width) dst[0] = val.x;
                             if (col + 1 < width) dst[1] = val.y;
@@ -2116,7 +2134,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                         }
                     }
                 }
-                if (ub < 3) load_old(ub + 1);
+                }
             }
         }
         // db: the row's parked dL/da summed over k, last step first (the order
