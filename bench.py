@@ -12,10 +12,10 @@ reported in "other_path".
 Prints ONE JSON line.  `value` is batch-steps/s = B*K / seconds per step.
 Each path is run twice: a breakdown pass with HIP events around every launch
 ("kernels_ms"), then the timed pass that gives `value`, with events only
-around the step's dominant kernel (each event record costs the stream about
-2-3 us).  The roofline object describes that kernel, with its average
-duration from the events of the timed pass, recorded on the stream the
-kernel runs on.  The cpu_baseline object times the float64 oracle on the
+around the step's dominant kernel and only on every --event-stride-th step
+(each event record costs the stream about 2.5 us).  The roofline object
+describes that kernel, with its average duration from the events of the
+timed pass, recorded on the stream the kernel runs on.  The cpu_baseline object times the float64 oracle on the
 host on a bounded sample of the same workload (all cores, and one thread).
 """
 from __future__ import annotations
@@ -158,6 +158,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-stride", type=int, default=10,
+                    help="timed pass: HIP events around the dominant kernel on every Nth step")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (to scale PMC byte counters)")
@@ -277,24 +279,31 @@ def main():
 
     def run_pass(path, bracket):
         """W warm-up steps, then K steps bracketed by a sync on both sides.
-        bracket=None records a HIP event around every launch (the per-kernel
-        breakdown); bracket=name records only the pair around that kernel's
-        launch.  An event record costs the stream about 2-3 us, so the pass
-        that gives the step time records just the one pair it needs."""
+        bracket=None records a HIP event pair around every launch of every
+        step (the per-kernel breakdown).  bracket=name records only the pair
+        around that kernel's launch, and only on the last step of every
+        --event-stride steps (not the first step, which follows the idle
+        sync): each event record costs the stream about 2.5 us, which on a
+        0.1 ms step would be counted as step time.  The kernel's average
+        duration is taken over the steps that carry the pair; the step-time
+        percentiles over the windows between the marks, per step."""
         launches = STEPS[path]
         for _ in range(args.warmup):
             for _, f in launches:
                 f()
         torch.cuda.synchronize()
         names = [n for n, _ in launches if bracket is None or n == bracket]
-        evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
-               for _ in range(args.steps)]
+        stride = 1 if bracket is None else max(1, args.event_stride)
+        marked = [i for i in range(args.steps) if i % stride == stride - 1] or [args.steps - 1]
+        evs = {i: {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+               for i in marked}
         t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t_start.record()
         for i in range(args.steps):
+            step_evs = evs.get(i, {})
             for n, f in launches:
-                e = evs[i].get(n)
+                e = step_evs.get(n)
                 if e is not None:
                     e[0].record()
                 f()
@@ -303,12 +312,15 @@ def main():
         t_end.record()
         torch.cuda.synchronize()
         ms = t_start.elapsed_time(t_end) / args.steps
-        km = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in evs) / args.steps for n in names}
-        # per-step times: from one step's first event to the next step's
+        km = {n: sum(evs[i][n][0].elapsed_time(evs[i][n][1]) for i in marked) / len(marked) for n in names}
+        # per-step times: windows from the start to the first marked step's
+        # first event, between marked steps, and from the last to the end,
+        # each divided by the steps it holds
         first = names[0]
-        marks = [e[first][0] for e in evs]
-        steps_ms = sorted([marks[i].elapsed_time(marks[i + 1]) for i in range(len(marks) - 1)] +
-                          [marks[-1].elapsed_time(t_end)])
+        bounds = [t_start] + [evs[i][first][0] for i in marked] + [t_end]
+        idx = [0] + marked + [args.steps]
+        steps_ms = sorted(bounds[j].elapsed_time(bounds[j + 1]) / (idx[j + 1] - idx[j])
+                          for j in range(len(bounds) - 1) if idx[j + 1] > idx[j])
         q = lambda f: steps_ms[min(len(steps_ms) - 1, int(f * len(steps_ms)))]
         return ms, km, {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9)}
 
@@ -385,6 +397,7 @@ def main():
         "input_grads": args.input_grads,
         "fused_call_is_one_kernel": n_in <= 128 and H <= 128 and K <= 64,
         "step_ms_percentiles": pct,
+        "timed_pass_event_stride": args.event_stride,
         "step_floors": floors,
         "kernels_ms": k_ms,
         "with_input_grads": None if args.main_only else {
