@@ -98,6 +98,17 @@ def _workspace_arg(workspace):
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
+def _accumulate_workspace(x, p, K, accumulate, workspace):
+    """The workspace accumulate mode needs at widths above 128 (K <= 20), allocated here when the
+    caller passed none: without it that mode runs the general one-row-per-workgroup backward,
+    about 8x slower at B=8192, K=8, 256/256."""
+    import torch
+    if workspace is not None or not accumulate:
+        return workspace
+    need = cfc_backward_workspace(x.shape[0], K, p.n_in, p.n_hid, accumulate=True)
+    return torch.empty((need,), dtype=torch.uint8, device=x.device) if need > 0 else None
+
+
 def cfc_backward_workspace(B: int, Kw: int, n_in: int, n_hid: int, accumulate: bool = True) -> int:
     """Bytes of workspace cfc_backward_window_ws needs for a window of Kw
     steps (0: the window's kernel uses none)."""
@@ -115,10 +126,10 @@ def cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, scratch=None
     """(scratch [B, N], loss [B] or None): per-row parameter gradients of
     L_b = 1/2 |h_K - y_b|^2 (see include/cfc.h for the row layout).  With
     ``input_grads`` (or explicit ``grad_x`` / ``grad_h0`` buffers) it returns
-    (scratch, loss, grad_x [B, K, n_in], grad_h0 [B, H]) instead.  A device
-    ``workspace`` (cfc_backward_workspace bytes) goes to cfc_backward_window_ws
-    over all K steps: accumulate mode at widths above 128 then runs the
-    16-row kernel."""
+    (scratch, loss, grad_x [B, K, n_in], grad_h0 [B, H]) instead.  Accumulate
+    mode at widths above 128 with K <= 20 runs the 16-row kernel through
+    cfc_backward_window_ws with a device ``workspace`` of
+    cfc_backward_workspace bytes, allocated here unless given."""
     import torch
     lib = load_library()
     p = _params(w_in, w_rec, b, w_tau, cell)
@@ -139,6 +150,7 @@ def cfc_backward(w_in, w_rec, b, w_tau, x, h0, h_seq, y, dt: float, scratch=None
     grad_x, grad_h0 = _input_grad_buffers(x, p, grad_x, grad_h0, input_grads)
     flags = CFC_ACCUMULATE if accumulate else CFC_OVERWRITE
     ptr = lambda t: t.data_ptr() if t is not None else None
+    workspace = _accumulate_workspace(x, p, K, accumulate, workspace)
     if workspace is not None:
         ws_ptr, ws_bytes = _workspace_arg(workspace)
         _check("cfc_backward_window_ws", lib.cfc_backward_window_ws(
@@ -236,10 +248,10 @@ def cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt: float, h_seq=None,
                          stream=None, cell: str = "gated", workspace=None) -> Tuple[object, ...]:
     """(h_seq [B, K, H], scratch [B, N], loss [B] or None): the forward and the
     backward of the same inputs in one library call (see include/cfc.h).  With
-    ``input_grads`` (or explicit buffers) grad_x and grad_h0 are appended.  A
-    device ``workspace`` (cfc_backward_workspace bytes) goes to
-    cfc_forward_backward_ws: accumulate mode at widths above 128 then runs the
-    16-row backward."""
+    ``input_grads`` (or explicit buffers) grad_x and grad_h0 are appended.
+    Accumulate mode at widths above 128 with K <= 20 runs the 16-row backward
+    through cfc_forward_backward_ws with a device ``workspace`` of
+    cfc_backward_workspace bytes, allocated here unless given."""
     import torch
     lib = load_library()
     p = _params(w_in, w_rec, b, w_tau, cell)
@@ -262,6 +274,7 @@ def cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt: float, h_seq=None,
     grad_x, grad_h0 = _input_grad_buffers(x, p, grad_x, grad_h0, input_grads)
     flags = CFC_ACCUMULATE if accumulate else CFC_OVERWRITE
     ptr = lambda t: t.data_ptr() if t is not None else None
+    workspace = _accumulate_workspace(x, p, K, accumulate, workspace)
     if workspace is not None:
         ws_ptr, ws_bytes = _workspace_arg(workspace)
         _check("cfc_forward_backward_ws", lib.cfc_forward_backward_ws(

@@ -252,11 +252,11 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_kernel(
 //    + b (backward) and the weight gradients DA^T [X | H_prev] (backward) --
 //    run on the f64 matrix cores (v_mfma_f64_16x16x4f64); the weight operand
 //    of the first two is held in registers for the whole contraction;
-//  * the serial chain keeps its 128x128 slice of W_rec (or W_rec^T) in
-//    registers: thread (ib, jb) holds rows 4ib..4ib+3, columns 16jb..16jb+15,
-//    reads 16 values of the state from LDS, and the 8 threads of a row block
+//  * the serial chain keeps W_rec (or W_rec^T) in registers, an 8x8 slice per
+//    lane: lane (ib, jb) holds rows 8ib..8ib+7, columns 8jb..8jb+7, reads 8
+//    values of the state from LDS per step, and the 16 lanes of a row block
 //    combine with a DPP reduce-scatter so that lanes jb and jb^1 both end with
-//    the total of one output unit;
+//    the total of one output unit (ChainLane below);
 //  * those two lanes share the transcendental work: one evaluates
 //    exp(2a) -> tanh(a) = 1 - 2/(1+exp(2a)), the other exp(sp a dt) -> the gate
 //    1/(1+exp(sp a dt)), and they swap results.
@@ -371,11 +371,9 @@ __device__ __forceinline__ double chain_product(const double (&w)[8][8], const d
 // e^r by its degree-12 Taylor polynomial (truncation below 2e-16 relative)
 // evaluated with Estrin's scheme for a short dependency chain, then scaled by
 // 2^n.
-__device__ __forceinline__ double exp_f64(double x) {
-    constexpr double kLog2e = 1.4426950408889634074;
-    constexpr double kLn2 = 0.69314718055994530942;
-    const double n = __builtin_rint(x * kLog2e);
-    const double r = fma(-n, kLn2, x);
+constexpr double kLog2e = 1.4426950408889634074;
+constexpr double kLn2 = 0.69314718055994530942;
+__device__ __forceinline__ double exp_poly_scaled(double r, int n) {
     constexpr double c2 = 1.0 / 2, c3 = 1.0 / 6, c4 = 1.0 / 24, c5 = 1.0 / 120, c6 = 1.0 / 720,
                      c7 = 1.0 / 5040, c8 = 1.0 / 40320, c9 = 1.0 / 362880, c10 = 1.0 / 3628800,
                      c11 = 1.0 / 39916800, c12 = 1.0 / 479001600;
@@ -384,19 +382,46 @@ __device__ __forceinline__ double exp_f64(double x) {
     const double q4 = fma(c9, r, c8), q5 = fma(c11, r, c10);
     const double s0 = fma(q1, r2, q0), s1 = fma(q3, r2, q2), s2 = fma(q5, r2, q4);
     const double t0 = fma(s1, r4, s0), t1 = fma(c12, r4, s2);
-    return ldexp(fma(t1, r8, t0), (int)n);
+    return ldexp(fma(t1, r8, t0), n);
+}
+__device__ __forceinline__ double exp_f64(double x) {
+    const double n = __builtin_rint(x * kLog2e);
+    return exp_poly_scaled(fma(-n, kLn2, x), (int)n);
 }
 
-// 1 / (1 + e^z) for any finite z: |z| is clamped to 700 (beyond it the result
-// is 0 or 1 to double precision).  The reciprocal is v_rcp_f64 (24 correct
-// bits, measured over a full binade) and one Newton step: about 2e-15
-// relative.
+// 1 / (1 + e^z) for finite z: |z| is clamped to 700 (beyond it the result is
+// 0 or 1 to double precision).  The reciprocal is v_rcp_f64 (24 correct bits,
+// measured over a full binade) and one Newton step: about 2e-15 relative.
+// The clamp maps a NaN z to a finite value, so this form serves rows whose
+// inputs are all finite (then every pre-activation is finite: |a| stays below
+// 1e80 for float32 inputs); inv_one_plus_exp_exact serves the others.
 __device__ __forceinline__ double inv_one_plus_exp(double z) {
     z = fmin(fmax(z, -700.0), 700.0);
     const double d = 1.0 + exp_f64(z);
     const double y = __builtin_amdgcn_rcp(d);
     const double e = fma(-d, y, 1.0);
     return fma(y, e, y);
+}
+
+// 1 / (1 + e^(m a)) for any a, with m_log2e = m log2e: NaN in, NaN out.
+// z = m a and t = fma(m_log2e, a, 1.5 * 2^52) are formed side by side; adding
+// 1.5 * 2^52 rounds z log2e to the nearest integer n, which then sits in the
+// low bits of t's significand (exact for |z log2e| < 2^51), so n = t - 1.5 * 2^52
+// and the integer exponent are read off t with no float-to-int conversion.
+// Where |z| > 700 the result is 0 or 1 to double precision and is selected
+// after the evaluation (whose value is then unspecified); a NaN z fails that
+// comparison and comes out as NaN.
+constexpr double kExpShift = 6755399441055744.0;  // 1.5 * 2^52
+__device__ __forceinline__ double inv_one_plus_exp_exact(double m, double m_log2e, double a) {
+    const double z = m * a;
+    const double t = fma(m_log2e, a, kExpShift);
+    const double n = t - kExpShift;
+    const int ni = (int)(unsigned)__builtin_bit_cast(unsigned long long, t);
+    const double d = 1.0 + exp_poly_scaled(fma(-n, kLn2, z), ni);
+    const double y = __builtin_amdgcn_rcp(d);
+    const double e = fma(-d, y, 1.0);
+    const double v = fma(y, e, y);
+    return fabs(z) > 700.0 ? (z > 0.0 ? 0.0 : 1.0) : v;
 }
 
 // The gate of one unit for both cells, as constants of one set of formulas
@@ -439,6 +464,53 @@ __device__ __forceinline__ void cell_gates(double a, const GateLane& L, double& 
     g = L.gate ? val : other;
     c = L.gate ? other : val;
 }
+// The same for a row whose inputs are not all finite: NaN propagates as in the
+// definition (zl = L.zmul * log2e, hoisted by the caller).
+__device__ __forceinline__ void cell_gates_exact(double a, const GateLane& L, double zl, double& g, double& c) {
+    const double r = inv_one_plus_exp_exact(L.zmul, zl, a);
+    const double val = fma(r, L.vmul, L.vadd);
+    const double other = dpp_move<kDppXor1>(val);
+    g = L.gate ? val : other;
+    c = L.gate ? other : val;
+}
+
+// s_waitcnt lgkmcnt(0): wait for every outstanding LDS and scalar-memory
+// access.  Placed at the top of a chain loop, where the previous step's barrier
+// has already drained the LDS queue, it costs nothing; it tells the compiler's
+// wait insertion that no scalar load issued before the loop is still in
+// flight.  Scalar loads return out of order, so without it the loop's first
+// LDS wait (its state read) becomes a wait for all of the step's LDS reads in
+// every iteration (measured: the forward chain about 80 cycles per step slower).
+__device__ __forceinline__ void lds_and_scalar_drained() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <bool EXACT>
+__device__ __forceinline__ void cell_gates_t(double a, const GateLane& L, double zl, double& g, double& c) {
+    if constexpr (EXACT)
+        cell_gates_exact(a, L, zl, g, c);
+    else
+        cell_gates(a, L, g, c);
+}
+
+// Rows whose chains consume a non-finite value (a NaN or infinity in x, h_0,
+// h_seq, the weights, the bias or w_tau reaches the projection, the chain
+// weights, the initial state or the gate constants) run the chain loops with
+// cell_gates_exact; all others run the shorter cell_gates.  Each thread tests
+// what it loaded or computed, and the workgroup ORs the tests through one LDS
+// word, so the choice is uniform across the workgroup.
+__device__ __forceinline__ bool not_finite(double v) { return !__builtin_isfinite(v); }
+__device__ __forceinline__ bool any_not_finite(const UnitGate& u) {
+    return not_finite(u.zmul) || not_finite(u.vmul) || not_finite(u.vadd) || not_finite(u.rho) ||
+           not_finite(u.alpha) || not_finite(u.beta);
+}
+template <int R, int C>
+__device__ __forceinline__ bool any_not_finite(const double (&w)[R][C]) {
+    bool bad = false;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < C; ++c) bad |= not_finite(w[r][c]);
+    return bad;
+}
 
 constexpr int kSmall = 128;          // padded n_in and n_hid of the small kernels
 constexpr int kSmallFwdKW = 64;      // forward steps per window
@@ -452,7 +524,7 @@ constexpr int kSmallZS = kSmallZW + 2;
 constexpr int kSmallAS = kSmall + 4;
 
 __host__ __device__ constexpr size_t small_fwd_lds_bytes() {
-    return (size_t)8 * kSmallFwdKW * kSmall + (size_t)8 * 2 * kSmall +
+    return (size_t)8 * kSmallFwdKW * kSmall + (size_t)8 * 2 * kSmall + 16 +
            (size_t)4 * kSmallFwdKW * kSmallXS;
 }
 // The backward always stages kSmallBwdMaxK rows (rows >= K are zero), so its
@@ -634,13 +706,15 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
     extern __shared__ __align__(16) unsigned char smem[];
     double* U = reinterpret_cast<double*>(smem);  // [KW][HP]
     double* hb = U + KW * HP;                     // [2][HP]
-    float* xs = reinterpret_cast<float*>(hb + 2 * HP);  // [KW][XS]
+    int* nonfinite = reinterpret_cast<int*>(hb + 2 * HP);  // the row's flag (16 bytes reserved)
+    float* xs = reinterpret_cast<float*>(hb + 2 * HP + 2);  // [KW][XS]
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const long long b = blockIdx.x;
     const ChainLane cl = chain_lane(wave, lane);
     const int jb = cl.jb, o = cl.o;
     const bool gate_lane = cl.gate;
+    if (t == 0) *nonfinite = 0;  // read only after the first window's barriers
 
     // Weight operand of the input projection, kept in registers.  The
     // contraction index of chunk jc in k-slot s = lane/16 is j = 32*s + jc, so a
@@ -662,6 +736,9 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
     double hprev = o < H ? (double)h0[b * H + o] : 0.0;
     const double bias_q0 = (2 * wave) * 16 + (lane & 15) < H ? (double)bias[(2 * wave) * 16 + (lane & 15)] : 0.0;
     const double bias_q1 = (2 * wave + 1) * 16 + (lane & 15) < H ? (double)bias[(2 * wave + 1) * 16 + (lane & 15)] : 0.0;
+    // the flag is sticky: once a window has a non-finite input, later windows
+    // carry the NaN in their state
+    bool bad = any_not_finite(wr) || any_not_finite(ug) || not_finite(hprev);
 
     int cur = 0;
     for (int k0 = 0; k0 < K; k0 += KW) {
@@ -691,30 +768,42 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     double* urow = U + (kb * 16 + (lane >> 4) + 4 * v) * HP + (2 * wave) * 16 + (lane & 15);
-                    urow[0] = acc[kb][0][v] + bias_q0;
-                    urow[16] = acc[kb][1][v] + bias_q1;
+                    const double u0 = acc[kb][0][v] + bias_q0, u1 = acc[kb][1][v] + bias_q1;
+                    urow[0] = u0;
+                    urow[16] = u1;
+                    bad |= not_finite(u0) || not_finite(u1);
                 }
         }
         const GateLane gl = gate_lane_consts(gate_lane, ug);
+        if (bad) *nonfinite = 1;
         __syncthreads();
         // ---- serial recurrence through the window
-        for (int kk = 0; kk < kw; ++kk) {
-            const double u = U[kk * HP + o];
-            double hj[8];
-            chain_read(hj, hb + cur * HP, jb);
-            const double a = u + chain_product(wr, hj);
-            double g, c;
-            cell_gates(a, gl, g, c);
-            const double hn = fma(g, hprev - c, c);  // g*h + (1-g)*c
-            hprev = hn;
-            // both lanes of the unit's pair hold the same bits (the last
-            // reduce stage adds the same two values, and g, c are exchanged),
-            // so both store: no branch in the loop
-            hb[(cur ^ 1) * HP + o] = hn;
-            if (o < H) h_seq[(b * K + k0 + kk) * (long long)H + o] = (float)hn;
-            cur ^= 1;
-            __syncthreads();
-        }
+        auto chain = [&](auto exact) {
+            constexpr bool EXACT = decltype(exact)::value;
+            const double zl = gl.zmul * kLog2e;
+            for (int kk = 0; kk < kw; ++kk) {
+                lds_and_scalar_drained();
+                const double u = U[kk * HP + o];
+                double hj[8];
+                chain_read(hj, hb + cur * HP, jb);
+                const double a = u + chain_product(wr, hj);
+                double g, c;
+                cell_gates_t<EXACT>(a, gl, zl, g, c);
+                const double hn = fma(g, hprev - c, c);  // g*h + (1-g)*c
+                hprev = hn;
+                // both lanes of the unit's pair hold the same bits (the last
+                // reduce stage adds the same two values, and g, c are exchanged),
+                // so both store: no branch in the loop
+                hb[(cur ^ 1) * HP + o] = hn;
+                if (o < H) h_seq[(b * K + k0 + kk) * (long long)H + o] = (float)hn;
+                cur ^= 1;
+                __syncthreads();
+            }
+        };
+        if (*nonfinite)
+            chain(std::true_type{});
+        else
+            chain(std::false_type{});
     }
 }
 
@@ -731,18 +820,22 @@ __device__ __forceinline__ void store_grad_f(float* p, double v, int accumulate)
 // cores and writes the row [dW_in | dW_rec | db | dw_tau].  Optionally also
 // the input gradients of the row: gh0_row [H] = dL/dh_0 (the chain runs its
 // W_rec^T step once more, at k = 0) and gx_row [K][n_in] = DA W_in (a third
-// product on the matrix cores).
+// product on the matrix cores).  red[4] holds the row's non-finite flag as an
+// int (zeroed before an earlier barrier); `bad` is this thread's own test of
+// what the pre-activations in AD were formed from.
 __device__ __forceinline__ void small_reverse_and_grads(
     const float* __restrict__ w_in, const float* __restrict__ w_rec, int K, int n_in, int H,
     double delta, double* AD, const UnitGate& ug, double* red, const float* zs,
     float* gst, float* __restrict__ row, float* __restrict__ loss_b, float* __restrict__ gx_row,
     float* __restrict__ gh0_row, int accumulate, int lane, int wave, int jb, int ib, int o,
-    bool gate_lane) {
+    bool gate_lane, bool bad) {
     constexpr int HP = kSmall, NP = kSmall, ZW = kSmallZW, ZS = kSmallZS, AS = kSmallAS;
     constexpr int KP = kSmallBwdMaxK;
+    int* nonfinite = reinterpret_cast<int*>(red + 4);
     // ---- W_rec^T slice into registers
     double wt[8][8];
     load_chain_weights(wt, w_rec, H, ChainLane{jb, ib, o, gate_lane}, true);
+    if (bad || any_not_finite(wt) || any_not_finite(ug)) *nonfinite = 1;
 
     // ---- loss seed
     {
@@ -760,35 +853,43 @@ __device__ __forceinline__ void small_reverse_and_grads(
     // flight.  a_k-1 is still in AD when they are read (it is overwritten by
     // dL/da_k-1 one step later, by the same lane pair).
     double gb = 0.0, gwt = 0.0;
-    auto step_consts = [&](int k, double& g, double& Q, double& R) {
-        const double a = AD[k * AS + o];
-        const double hk = (double)zs[k * ZS + NP + o];
-        double c;
-        cell_gates(a, gl, g, c);
-        const double P = (hk - c) * g * fma(-ug.vmul, g, 1.0);
-        Q = (1.0 - g) * (1.0 - c * c) - P * ug.rho;
-        R = P * fma(-a, ug.alpha, ug.beta);
+    auto reverse_chain = [&](auto exact) {
+        constexpr bool EXACT = decltype(exact)::value;
+        const double zl = gl.zmul * kLog2e;
+        auto step_consts = [&](int k, double& g, double& Q, double& R) {
+            const double a = AD[k * AS + o];
+            const double hk = (double)zs[k * ZS + NP + o];
+            double c;
+            cell_gates_t<EXACT>(a, gl, zl, g, c);
+            const double P = (hk - c) * g * fma(-ug.vmul, g, 1.0);
+            Q = (1.0 - g) * (1.0 - c * c) - P * ug.rho;
+            R = P * fma(-a, ug.alpha, ug.beta);
+        };
+        double g, Q, R;
+        step_consts(K - 1, g, Q, R);
+        for (int k = K - 1; k >= 0; --k) {
+            const double da = delta * Q;
+            gb += da;
+            gwt += delta * R;
+            if (!gate_lane) AD[k * AS + o] = da;
+            __syncthreads();
+            if (k == 0 && !gh0_row) break;
+            double dj[8];
+            chain_read(dj, AD + k * AS, jb);
+            // next step's constants (unused after k = 0), in the same block as
+            // the products so that their latency overlaps them
+            double gn, Qn, Rn;
+            step_consts(k > 0 ? k - 1 : 0, gn, Qn, Rn);
+            delta = fma(delta, g, chain_product(wt, dj));
+            g = gn;
+            Q = Qn;
+            R = Rn;
+        }
     };
-    double g, Q, R;
-    step_consts(K - 1, g, Q, R);
-    for (int k = K - 1; k >= 0; --k) {
-        const double da = delta * Q;
-        gb += da;
-        gwt += delta * R;
-        if (!gate_lane) AD[k * AS + o] = da;
-        __syncthreads();
-        if (k == 0 && !gh0_row) break;
-        double dj[8];
-        chain_read(dj, AD + k * AS, jb);
-        // next step's constants (unused after k = 0), in the same block as
-        // the products so that their latency overlaps them
-        double gn, Qn, Rn;
-        step_consts(k > 0 ? k - 1 : 0, gn, Qn, Rn);
-        delta = fma(delta, g, chain_product(wt, dj));
-        g = gn;
-        Q = Qn;
-        R = Rn;
-    }
+    if (*nonfinite)
+        reverse_chain(std::true_type{});
+    else
+        reverse_chain(std::false_type{});
     if (gh0_row && !gate_lane && o < H) gh0_row[o] = (float)delta;  // dL/dh_0
 
     // ---- weight gradients on the matrix cores: G = DA^T [X | H_prev]
@@ -1042,6 +1143,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     const ChainLane cl = chain_lane(wave, lane);
     const int jb = cl.jb, ib = cl.ib, o = cl.o;
     const bool gate_lane = cl.gate;
+    if (t == 0) reinterpret_cast<int*>(red + 4)[0] = 0;  // the row's non-finite flag
 
     // Weight operand of the recomputation, in registers.  Chunk jc of k-slot
     // s = lane/16 contracts index j = 64*s + jc of [x | h_prev], so a lane holds
@@ -1135,6 +1237,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     }
 
     // ---- recompute every step's pre-activation on the matrix cores
+    bool bad = false;
     {
         dbl4 acc[4][2];
 #pragma unroll
@@ -1157,8 +1260,11 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
             for (int v = 0; v < 4; ++v) {
                 const int kk = kb * 16 + (lane >> 4) + 4 * v;
                 double* arow = AD + kk * AS + (2 * wave) * 16 + (lane & 15);
-                arow[0] = kk < K ? acc[kb][0][v] + bias_q0 : 0.0;
-                arow[16] = kk < K ? acc[kb][1][v] + bias_q1 : 0.0;
+                const double a0 = kk < K ? acc[kb][0][v] + bias_q0 : 0.0;
+                const double a1 = kk < K ? acc[kb][1][v] + bias_q1 : 0.0;
+                arow[0] = a0;
+                arow[16] = a1;
+                bad |= not_finite(a0) || not_finite(a1);
             }
         }
     }
@@ -1170,7 +1276,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
                             loss && !win.delta_in ? loss + b : nullptr,
                             grad_x ? grad_x + (b * Kf + k0) * n_in : nullptr,
                             win.delta_out ? win.delta_out + b * H : nullptr, accumulate, lane, wave, jb, ib, o,
-                            gate_lane);
+                            gate_lane, bad);
 }
 
 // Forward and backward of one row in one workgroup (n_in, n_hid <= 128,
@@ -1218,6 +1324,8 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     const int jb = cl.jb, ib = cl.ib, o = cl.o;
     const bool gate_lane = cl.gate;
     const int slot = lane >> 4;
+    int* nonfinite = reinterpret_cast<int*>(red + 4);
+    if (t == 0) *nonfinite = 0;
 
     // ---- stage x (rows >= K zero), h0 as row 0 of the h_prev half (rows >= K
     // zero; rows 1..K-1 are written by the chain), per-unit constants
@@ -1279,6 +1387,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
 
     // ---- input projection of all K steps on the matrix cores: chunk jc of
     // k-slot s contracts j = 32*s + jc, a contiguous span of a W_in row
+    bool bad = false;
     {
         double wb[2][NP / 4];
         if constexpr (WHOLE) {
@@ -1329,8 +1438,11 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
             for (int v = 0; v < 4; ++v) {
                 const int kk = kb * 16 + (lane >> 4) + 4 * v;
                 double* urow = AD + kk * AS + (2 * wave) * 16 + (lane & 15);
-                urow[0] = kk < K ? acc[kb][0][v] + bias_q0 : 0.0;
-                urow[16] = kk < K ? acc[kb][1][v] + bias_q1 : 0.0;
+                const double u0 = kk < K ? acc[kb][0][v] + bias_q0 : 0.0;
+                const double u1 = kk < K ? acc[kb][1][v] + bias_q1 : 0.0;
+                urow[0] = u0;
+                urow[16] = u1;
+                bad |= not_finite(u0) || not_finite(u1);
             }
     }
 
@@ -1349,34 +1461,45 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     }
     double hprev = h0_o;
     const GateLane gl = gate_lane_consts(gate_lane, ug);
+    if (bad || any_not_finite(wr) || any_not_finite(ug) || not_finite(hprev)) *nonfinite = 1;
     __syncthreads();
-    int cur = 0;
-    for (int k = 0; k < K; ++k) {
-        const double u = AD[k * AS + o];
-        double hj[8];
-        chain_read(hj, hb + cur * HP, jb);
-        const double a = u + chain_product(wr, hj);
-        double g, c;
-        cell_gates(a, gl, g, c);
-        const double hn = fma(g, hprev - c, c);
-        hprev = hn;
-        // both lanes of the pair hold the same bits: both store, no branch.
-        // The state the next step reads goes first; the scheduling barrier
-        // keeps the other stores' conversions from being hoisted above it.
-        hb[(cur ^ 1) * HP + o] = hn;
-        __builtin_amdgcn_sched_barrier(0);
-        AD[k * AS + o] = a;
-        if (k + 1 < K) zs[(k + 1) * ZS + NP + o] = (float)hn;
-        if (o < H) h_seq[(b * K + k) * (long long)H + o] = (float)hn;
-        cur ^= 1;
-        __syncthreads();
-    }
+    auto forward_chain = [&](auto exact) {
+        constexpr bool EXACT = decltype(exact)::value;
+        const double zl = gl.zmul * kLog2e;
+        int cur = 0;
+        for (int k = 0; k < K; ++k) {
+            lds_and_scalar_drained();
+            const double u = AD[k * AS + o];
+            double hj[8];
+            chain_read(hj, hb + cur * HP, jb);
+            const double a = u + chain_product(wr, hj);
+            double g, c;
+            cell_gates_t<EXACT>(a, gl, zl, g, c);
+            const double hn = fma(g, hprev - c, c);
+            hprev = hn;
+            // both lanes of the pair hold the same bits: both store, no branch.
+            // The state the next step reads goes first; the scheduling barrier
+            // keeps the other stores' conversions from being hoisted above it.
+            hb[(cur ^ 1) * HP + o] = hn;
+            __builtin_amdgcn_sched_barrier(0);
+            AD[k * AS + o] = a;
+            if (k + 1 < K) zs[(k + 1) * ZS + NP + o] = (float)hn;
+            if (o < H) h_seq[(b * K + k) * (long long)H + o] = (float)hn;
+            cur ^= 1;
+            __syncthreads();
+        }
+    };
+    if (*nonfinite)
+        forward_chain(std::true_type{});
+    else
+        forward_chain(std::false_type{});
 
     // ---- backward from the float32 h_K, as the separate backward sees it
     const double delta = o < H ? (double)(float)hprev - (double)y_o : 0.0;
     small_reverse_and_grads(w_in, w_rec, K_arg, n_in_arg, H_arg, delta, AD, ug, red, zs, gst, scratch + b * N,
                             loss ? loss + b : nullptr, grad_x ? grad_x + b * K * (long long)n_in : nullptr,
-                            grad_h0 ? grad_h0 + b * H : nullptr, accumulate, lane, wave, jb, ib, o, gate_lane);
+                            grad_h0 ? grad_h0 + b * H : nullptr, accumulate, lane, wave, jb, ib, o, gate_lane,
+                            false);
 }
 
 // =====================================================================
@@ -1590,8 +1713,10 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
                     if (r0 + r < B && i < H)
                         reinterpret_cast<double*>(a_park + (r0 + r) * N)[(long long)k * H + i] = a;
                 }
-                const double g = cell == CFC_CELL_TAU_DECAY ? spdt_v[tb][v] : inv_one_plus_exp(spdt_v[tb][v] * a);
-                const double c = fma(-2.0, inv_one_plus_exp(2.0 * a), 1.0);
+                const double g = cell == CFC_CELL_TAU_DECAY
+                                     ? spdt_v[tb][v]
+                                     : inv_one_plus_exp_exact(spdt_v[tb][v], spdt_v[tb][v] * kLog2e, a);
+                const double c = fma(-2.0, inv_one_plus_exp_exact(2.0, 2.0 * kLog2e, a), 1.0);
                 double* hp = zh + zidx(i, r);
                 *hp = fma(g, *hp - c, c);  // g*h + (1-g)*c
             }
@@ -1816,7 +1941,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                     const int i = lunit(wave, tb, s + 4 * v);
                     const double spdt = uspdt[i];
                     const double a = PARKED ? acc[tb][v] : acc[tb][v] + ubias[i];
-                    const double c = fma(-2.0, inv_one_plus_exp(2.0 * a), 1.0);
+                    const double c = fma(-2.0, inv_one_plus_exp_exact(2.0, 2.0 * kLog2e, a), 1.0);
                     const double hp = zh[zidx(i, r)];
                     const double d = delta[tb][v];
                     double g, da;
@@ -1826,7 +1951,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                         da = d * (1.0 - g) * (1.0 - c * c);
                         gwt[zidx(i, r)] += dg * g * usw[i];
                     } else {
-                        g = inv_one_plus_exp(spdt * a);
+                        g = inv_one_plus_exp_exact(spdt, spdt * kLog2e, a);
                         const double dz = d * (hp - c) * g * (1.0 - g);
                         da = d * (1.0 - g) * (1.0 - c * c) - dz * spdt;
                         gwt[zidx(i, r)] += dz * (-a * dt) * usw[i];
@@ -2600,9 +2725,10 @@ int forward_backward(const cfc_params_t* params, const float* x, const float* h0
     if (!outputs_disjoint(outs, 5, ins, 7)) return CFC_ERR_OVERLAP;
     if (n_in <= kSmall && H <= kSmall && K <= kSmallBwdMaxK) {
         set_kernel_attributes();
-        const bool whole = K == kSmallBwdMaxK && n_in == kSmall && H == kSmall &&
-                           (reinterpret_cast<uintptr_t>(params->w_in) & 15) == 0 &&
-                           (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+        // the whole-shape instance reads x, W_in and W_rec as float4 without checks
+        auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+        const bool whole = K == kSmallBwdMaxK && n_in == kSmall && H == kSmall && al16(params->w_in) &&
+                           al16(params->w_rec) && al16(x);
         auto* kern = whole ? &cfc_fb_small_kernel<true> : &cfc_fb_small_kernel<false>;
         hipLaunchKernelGGL(kern, dim3(B), dim3(kThreads), small_fb_lds_bytes(), stream,
                            params->w_in, params->w_rec, params->b, params->w_tau, x, h0, y, (double)dt, K,

@@ -136,6 +136,12 @@ int cfc_forward(const cfc_params_t *params, const float *x, const float *h0, flo
  *            gradient (equivalent to the pages' memset + K accumulating calls).
  *            flags = CFC_ACCUMULATE: each row is read and this call's gradient,
  *            rounded to float32, is added to it in float32 (scratch += g).
+ *            At n_in or n_hid above 128 this entry has no workspace, so
+ *            accumulate mode runs the general one-row-per-workgroup backward:
+ *            about 8x slower than the 16-row kernel that
+ *            cfc_backward_window_ws / cfc_forward_backward_ws run with a
+ *            workspace (36.9 against 4.5 ms per step at B = 8192, K = 8,
+ *            256/256).  The Python binding passes such a workspace itself.
  *   loss     [B] OUTPUT or NULL: L_b per row
  *   grad_x   [B, K, n_in] OUTPUT or NULL: dL/dx_k = W_in^T dL/da_k for every
  *            step (overwritten whatever the flags)

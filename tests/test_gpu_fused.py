@@ -233,11 +233,12 @@ def test_accumulate_at_full_width_adds_float32(entry):
 
 @pytest.mark.parametrize("cell", ["gated", "tau_decay"])
 def test_fused_whole_shape_instance_matches_generic(cell):
-    """At K = 64, n_in = H = 128 with 16-byte-aligned x and W_in the library
-    launches an instance whose staging fetches the projection's weights while
-    x is staged; with x one float off alignment it launches the generic one.
-    Same arithmetic: every output (with the input gradients) bitwise equal,
-    and the aligned one within tolerance of the oracle."""
+    """At K = 64, n_in = H = 128 with 16-byte-aligned x, W_in and W_rec the
+    library launches an instance whose staging fetches the projection's
+    weights while x is staged and reads W_rec as float4; with x, or W_rec, one
+    float off alignment it launches the generic one.  Same arithmetic: every
+    output (with the input gradients) bitwise equal, and the aligned one
+    within tolerance of the oracle."""
     import torch
     import cfc_recurrent_cell_amd as C
     B, K, n = 4, 64, 128
@@ -246,14 +247,19 @@ def test_fused_whole_shape_instance_matches_generic(cell):
     buf = torch.empty(B * K * n + 1, device="cuda")
     x_off = buf[1:].view(B, K, n)
     x_off.copy_(d["x"])
+    wbuf = torch.empty(n * n + 1, device="cuda")
+    w_rec_off = wbuf[1:].view(n, n)
+    w_rec_off.copy_(d["w_rec"])
     assert d["x"].data_ptr() % 16 == 0 and d["w_in"].data_ptr() % 16 == 0 and x_off.data_ptr() % 16 == 4
+    assert d["w_rec"].data_ptr() % 16 == 0 and w_rec_off.data_ptr() % 16 == 4
     say(f"[fused] whole-shape instance vs generic, {cell}")
     outs = []
-    for xx in (d["x"], x_off):
-        outs.append([host(t) for t in C.cfc_forward_backward(d["w_in"], d["w_rec"], d["b"], d["w_tau"], xx, d["h0"],
+    for xx, wr in ((d["x"], d["w_rec"]), (x_off, d["w_rec"]), (d["x"], w_rec_off)):
+        outs.append([host(t) for t in C.cfc_forward_backward(d["w_in"], wr, d["b"], d["w_tau"], xx, d["h0"],
                                                              d["y"], d["dt"], input_grads=True, cell=cell)])
-    for name, a, b_ in zip(("h_seq", "scratch", "loss", "grad_x", "grad_h0"), *outs):
-        assert np.array_equal(a.view(np.uint32), b_.view(np.uint32)), f"{cell}: {name} differs between instances"
+    for other, what in ((outs[1], "x off alignment"), (outs[2], "W_rec off alignment")):
+        for name, a, b_ in zip(("h_seq", "scratch", "loss", "grad_x", "grad_h0"), outs[0], other):
+            assert np.array_equal(a.view(np.uint32), b_.view(np.uint32)), f"{cell}, {what}: {name} differs"
     ref = O.cfc_step(inp, threads=oracle_threads())
     assert_close(outs[0][0], ref["h_seq"], cell + " h_seq")
     assert_close(outs[0][1], ref["scratch"], cell + " scratch")

@@ -92,44 +92,99 @@ def test_train_workload_ten_steps_bitwise():
 
 
 def test_large_workload_all_rows():
-    """B=8192, K=8, 256/256: every h_seq element, every one of the 8192 scratch
-    rows (compared block by block), the loss and the reduced gradient."""
+    """B=8192, K=8, 256/256 (a 4.31 GB scratch, row offsets past 2^32 bytes),
+    through each way the library runs this shape, against the same oracle rows:
+      separate    cfc_forward + cfc_backward (16-row forward, recomputing
+                  16-row backward);
+      one_call    cfc_forward_backward in overwrite mode onto a NaN-poisoned
+                  scratch (the forward parks a_k in the head of each scratch
+                  row, the backward's two stages read it back and park dL/da
+                  in the row's tail);
+      accumulate  cfc_forward_backward_ws accumulating onto a base that
+                  depends on row and column (dL/da parked in the workspace),
+                  compared as result - base.
+    Every h_seq element, every scratch row (block by block), the loss and the
+    reduced gradient; each path is then run again and must repeat bitwise."""
     import torch
+    import cfc_recurrent_cell_amd as C
     cfg = W.LARGE
     inp = W.make_cfc_inputs(cfg)
-    say(f"[parity] {cfg.name}: GPU step")
     d = to_dev(inp)
-    h_seq, scratch, loss, out = gpu_step(d)
+    B, K, H, n_in = cfg.B, cfg.K, cfg.n_hid, cfg.n_in
+    N = W.scratch_row_len(n_in, H)
+    args = (d["w_in"], d["w_rec"], d["b"], d["w_tau"], d["x"], d["h0"])
+    # base[b, j] = (b % 7 - 3) + (j % 5 - 2): small integers, exact in float32
+    rowval = (torch.arange(B, device="cuda") % 7 - 3).float()
+    colval = (torch.arange(N, device="cuda") % 5 - 2).float()
+    ws = torch.empty((C.cfc_backward_workspace(B, K, n_in, H),), dtype=torch.uint8, device="cuda")
+
+    def run(path):
+        scratch = torch.empty((B, N), device="cuda")
+        if path == "separate":
+            h_seq, scratch, loss, out = gpu_step(d, scratch=scratch)
+            return h_seq, scratch, loss, out
+        if path == "one_call":
+            scratch.fill_(float("nan"))
+            h_seq, scratch, loss = C.cfc_forward_backward(*args, d["y"], d["dt"], scratch=scratch)
+        else:
+            torch.add(rowval[:, None], colval[None, :], out=scratch)
+            h_seq, scratch, loss = C.cfc_forward_backward(*args, d["y"], d["dt"], scratch=scratch,
+                                                          accumulate=True, workspace=ws)
+        return h_seq, scratch, loss, C.reduce_axis0(scratch)
+
+    paths = ("separate", "one_call", "accumulate")
+    res = {}
+    for p in paths:
+        say(f"[parity] {cfg.name}: GPU step, {p}")
+        res[p] = run(p)
     torch.cuda.synchronize()
     threads = oracle_threads()
     say(f"[parity] {cfg.name}: oracle forward ({threads} threads)")
     ref_h = O.cfc_forward(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x, inp.h0, inp.dt, threads=threads)
-    assert_close(host(h_seq), ref_h, cfg.name + " h_seq")
-    _ulp_check(host(h_seq), ref_h, cfg.name)
-    N = W.scratch_row_len(cfg.n_in, cfg.n_hid)
+    for p in paths:
+        assert_close(host(res[p][0]), ref_h, f"{cfg.name} {p} h_seq")
+        _ulp_check(host(res[p][0]), ref_h, f"{cfg.name} {p}")
     ref_out = np.zeros(N)
-    own_out = np.zeros(N)
-    g_loss = host(loss)
+    own_out = {p: np.zeros(N) for p in paths}
+    losses = {p: host(res[p][2]) for p in paths}
     blk = 512
-    for r0 in range(0, cfg.B, blk):
-        r1 = min(cfg.B, r0 + blk)
+    for r0 in range(0, B, blk):
+        r1 = min(B, r0 + blk)
         s, l = O.cfc_backward(inp.w_in, inp.w_rec, inp.b, inp.w_tau, inp.x[r0:r1], inp.h0[r0:r1],
                               ref_h[r0:r1], inp.y[r0:r1], inp.dt, threads=threads)
-        g = scratch[r0:r1].cpu().numpy()
-        assert_close(g, s, f"{cfg.name} scratch rows {r0}..{r1}")
-        assert_close(g_loss[r0:r1], l, f"{cfg.name} loss rows {r0}..{r1}")
+        base = None
+        for p in paths:
+            g = res[p][1][r0:r1].cpu().numpy()
+            own_out[p] += O.reduce_axis0_f32(g)
+            if p == "accumulate":
+                base = (np.arange(r0, r1)[:, None] % 7 - 3) + (np.arange(N)[None, :] % 5 - 2)
+                g = g.astype(np.float64) - base
+            assert_close(g, s, f"{cfg.name} {p} scratch rows {r0}..{r1}")
+            assert_close(losses[p][r0:r1], l, f"{cfg.name} {p} loss rows {r0}..{r1}")
         for r in range(r1 - r0):
             ref_out += s[r]
-        own_out += O.reduce_axis0_f32(g)
-        say(f"[parity] {cfg.name}: rows {r0}..{r1} ok")
-    g_out = host(out)
-    assert_close(g_out, ref_out, cfg.name + " out")
-    diff = np.abs(g_out.astype(np.float64) - own_out)
-    assert np.all(diff <= np.spacing(np.abs(own_out.astype(np.float32))).astype(np.float64) * 1.0001)
-    # a second step is bitwise identical
-    h2, s2, l2, o2 = gpu_step(d)
-    assert torch.equal(h2, h_seq) and torch.equal(s2.view(torch.int32), scratch.view(torch.int32))
-    assert torch.equal(o2.view(torch.int32), out.view(torch.int32))
+        say(f"[parity] {cfg.name}: rows {r0}..{r1} ok on every path")
+    col_base = float(sum((b % 7) - 3 for b in range(B))) + (np.arange(N) % 5 - 2) * B
+    for p in paths:
+        g_out = host(res[p][3])
+        own = own_out[p]
+        diff = np.abs(g_out.astype(np.float64) - own)
+        assert np.all(diff <= np.spacing(np.abs(own.astype(np.float32))).astype(np.float64) * 1.0001), p
+        if p == "accumulate":
+            # the reduced base is an exact integer; the gradient part is checked
+            # against the oracle at float32 resolution of the combined sum
+            assert_close(g_out.astype(np.float64) - col_base, ref_out, f"{cfg.name} {p} out - base",
+                         atol=max(1e-5, float(np.spacing(np.float32(np.abs(col_base).max())))))
+        else:
+            assert_close(g_out, ref_out, f"{cfg.name} {p} out")
+    # a second run of each path is bitwise identical
+    for p in paths:
+        say(f"[parity] {cfg.name}: bitwise repeat, {p}")
+        again = run(p)
+        for a, b_, name in zip(again, res[p], ("h_seq", "scratch", "loss", "out")):
+            assert torch.equal(a.view(torch.int32), b_.view(torch.int32)), f"{p}: {name} differs on repeat"
+        del again
+        torch.cuda.synchronize()
 
 
 RAGGED = [
@@ -209,8 +264,9 @@ def test_permuted_rows():
 @pytest.mark.parametrize("dims", [(12, 20), (140, 160)], ids=["n12_H20", "n140_H160"])
 def test_scratch_clear_and_accumulate_modes(dims):
     """Overwrite mode ignores what the scratch held (NaN poison); accumulate mode
-    on a zeroed scratch equals overwrite to float32 rounding (bitwise when both
-    take the same kernel); a second accumulate adds."""
+    on a zeroed scratch equals overwrite bitwise (both modes run the same
+    kernel: at 140/160 the binding gives accumulate mode the workspace of the
+    16-row backward); a second accumulate adds."""
     import torch
     import cfc_recurrent_cell_amd as C
     n_in, H = dims
@@ -230,10 +286,7 @@ def test_scratch_clear_and_accumulate_modes(dims):
     h = C.cfc_forward(db["w_in"], db["w_rec"], db["b"], db["w_tau"], db["x"], db["h0"], db["dt"])
     C.cfc_backward(db["w_in"], db["w_rec"], db["b"], db["w_tau"], db["x"], db["h0"], h, db["y"],
                    db["dt"], scratch=z, accumulate=True)
-    if max(dims) <= 128:   # same kernel for both modes
-        assert torch.equal(z.view(torch.int32), fresh_b.view(torch.int32))
-    else:                  # accumulate mode takes the general kernel: same values to rounding
-        assert_close(host(z), host(fresh_b), "accumulate vs overwrite", rtol=1e-6, atol=1e-7)
+    assert torch.equal(z.view(torch.int32), fresh_b.view(torch.int32))
     C.cfc_backward(db["w_in"], db["w_rec"], db["b"], db["w_tau"], db["x"], db["h0"], h, db["y"],
                    db["dt"], scratch=z, accumulate=True)
     assert_close(host(z), 2.0 * host(fresh_b).astype(np.float64), "accumulate twice", rtol=1e-6, atol=1e-7)

@@ -54,12 +54,16 @@ def test_wide_accumulate_with_workspace(case):
     assert need == 8 * B * K * H
     ws = torch.full((need // 4,), float("nan"), device="cuda")   # float32 NaN words: contents ignored
 
-    def run(scratch, accumulate, workspace):
+    def run(scratch, accumulate, workspace, general=False):
         gx = torch.full((B, K, n_in), float("nan"), device="cuda")
         gh = torch.full((B, H), float("nan"), device="cuda")
         loss = torch.full((B,), float("nan"), device="cuda")
-        C.cfc_backward(*args, h, d["y"], d["dt"], scratch=scratch, loss=loss, grad_x=gx, grad_h0=gh,
-                       accumulate=accumulate, cell=cell, workspace=workspace)
+        if general:   # cfc_backward_window without a workspace: the general backward
+            C.cfc_backward_window(*args, h, d["dt"], 0, K, scratch, y=d["y"], delta_out=gh, loss=loss,
+                                  grad_x=gx, accumulate=accumulate, cell=cell)
+        else:
+            C.cfc_backward(*args, h, d["y"], d["dt"], scratch=scratch, loss=loss, grad_x=gx, grad_h0=gh,
+                           accumulate=accumulate, cell=cell, workspace=workspace)
         return [host(t).copy() for t in (scratch, loss, gx, gh)]
 
     over = run(torch.full((B, N), float("nan"), device="cuda"), False, None)
@@ -79,8 +83,13 @@ def test_wide_accumulate_with_workspace(case):
     assert_close(acc[3], ref["grad_h0"], "grad_h0")
     # the general backward (no workspace) accumulates the same gradient in
     # another summation order
-    gen = run(torch.from_numpy(base.copy()).cuda(), True, None)
+    gen = run(torch.from_numpy(base.copy()).cuda(), True, None, general=True)
     assert_close(gen[0], acc[0], "general backward's accumulate mode")
+    # the binding sizes the workspace itself when none is given: the 16-row
+    # kernel's bits, not the general backward's
+    auto = run(torch.from_numpy(base.copy()).cuda(), True, None)
+    for a, b, name in zip(auto, acc, ("scratch", "loss", "grad_x", "grad_h0")):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"binding's own workspace: {name}"
 
 
 @pytest.mark.parametrize("cell", ["gated", "tau_decay"])
@@ -108,6 +117,11 @@ def test_one_call_entry_with_workspace(cell):
         assert np.array_equal(host(a).view(np.uint32), host(b_).view(np.uint32)), name
     _, over, _ = C.cfc_forward_backward(*args, d["y"], d["dt"], cell=cell)
     assert_close(host(s1) - base, host(over), "accumulated one-call gradient")
+    # no workspace given: the binding allocates one, same bits
+    h3, s3, l3 = C.cfc_forward_backward(*args, d["y"], d["dt"], scratch=torch.from_numpy(base.copy()).cuda(),
+                                        accumulate=True, cell=cell)
+    for a, b_, name in ((h3, h1, "h_seq"), (s3, s1, "scratch"), (l3, l1, "loss")):
+        assert np.array_equal(host(a).view(np.uint32), host(b_).view(np.uint32)), "binding's workspace: " + name
 
 
 def test_workspace_reuse_over_calls_and_shapes():
