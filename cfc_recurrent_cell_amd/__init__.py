@@ -19,7 +19,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["cfc_forward", "cfc_backward", "cfc_backward_window", "cfc_backward_windows",
-           "cfc_backward_workspace", "cfc_forward_backward", "reduce_axis0",
+           "cfc_backward_workspace", "cfc_forward_backward", "reduce_axis0", "reduce_axis0_noalloc",
            "reduce_axis0_split_workspace", "cfc_scratch_row_len", "CfcError", "load_library"]
 
 
@@ -327,6 +327,25 @@ def reduce_axis0(per_batch, out=None, stream=None, leading_axes: int = 1, split:
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("reduce_axis0_split", lib.reduce_axis0_split(per_batch.data_ptr(), B, N, out.data_ptr(), ws_ptr,
                                                         ws_bytes, s))
+    return out
+
+
+def reduce_axis0_noalloc(per_batch, out, stream=None, leading_axes: int = 1):
+    """reduce_axis0_split_noalloc: the split column sum with its partials in
+    the library's static device array, for callers that cannot allocate
+    (graph capture, serving loops).  ``out`` must be given; neither the
+    binding nor the library allocates.  Calls that overlap on one GPU share
+    that array and must be serialised (one stream)."""
+    import math
+    lib = load_library()
+    if not 1 <= leading_axes <= per_batch.dim():
+        raise ValueError(f"leading_axes must be in [1, {per_batch.dim()}], got {leading_axes}")
+    _dev_f32(per_batch, "per_batch")
+    tail = tuple(per_batch.shape[leading_axes:])
+    B, N = math.prod(per_batch.shape[:leading_axes]), math.prod(tail)
+    _dev_f32(out, "out", tail)
+    _check("reduce_axis0_split_noalloc", lib.reduce_axis0_split_noalloc(per_batch.data_ptr(), B, N, out.data_ptr(),
+                                                                        _stream(per_batch.device, stream)))
     return out
 
 

@@ -2846,6 +2846,53 @@ extern "C" int reduce_axis0_split(const float* per_batch, long long B, long long
     return launch_status();
 }
 
+// The allocation-free variant's partials: one static array per GPU (each
+// device holds its own copy at its own address).  In host code `scratch` is
+// only a handle for hipGetSymbolAddress; kernels get the per-device address
+// resolved below.
+static_assert(CFC_SPLIT_STATIC_BYTES == kSplitMaxPartials * (long long)sizeof(double),
+              "the static array holds the largest split plan's partials");
+static __device__ __align__(256) double scratch[kSplitMaxPartials];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, resolved once per
+// device with that device current; nullptr on failure.
+void* static_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" int reduce_axis0_split_noalloc(const float* per_batch, long long B, long long N, float* out,
+                                          hipStream_t stream) {
+    const long long need = reduce_axis0_split_workspace(B, N);
+    if (need < 0) return CFC_ERR_DIM;
+    if (need == 0) return reduce_axis0(per_batch, B, N, out, stream);
+    if (!out || !per_batch) return CFC_ERR_NULL;
+    if (need > CFC_SPLIT_STATIC_BYTES) return CFC_ERR_UNSUPPORTED;
+    if (overlap(span(out, N), span(per_batch, B * N))) return CFC_ERR_OVERLAP;
+    void* ws = static_scratch();
+    if (!ws) return CFC_ERR_HIP;
+    const SplitPlan sp = split_plan(B, N);
+    double* part = static_cast<double*>(ws);
+    hipLaunchKernelGGL((reduce_rows_narrow_kernel<float, double>), dim3((unsigned)sp.P), dim3(kThreads), 0, stream,
+                       per_batch, B, (int)N, sp.R, part);
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)((N + kPartCols - 1) / kPartCols)), dim3(kThreads), 0,
+                       stream, (const double*)part, sp.P, (int)N, out);
+    return launch_status();
+}
+
 extern "C" int reduce_axis0(const float* per_batch, long long B, long long N, float* out,
                             hipStream_t stream) {
     if (B < 0 || N < 0) return CFC_ERR_DIM;

@@ -306,6 +306,30 @@ long long reduce_axis0_split_workspace(long long B, long long N);
 int reduce_axis0_split(const float *per_batch, long long B, long long N, float *out,
                        void *workspace, long long workspace_bytes, hipStream_t stream);
 
+/* Maximum bytes of partials reduce_axis0_split ever needs (256 K float64
+ * partials); reduce_axis0_split_noalloc keeps them in a static device array of
+ * this size. */
+#define CFC_SPLIT_STATIC_BYTES (2LL * 1024 * 1024)
+
+/* reduce_axis0_split for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and result (bitwise) as reduce_axis0_split, without the
+ * workspace: the float64 partials go to a static device array of
+ * CFC_SPLIT_STATIC_BYTES that the library holds on each GPU it runs on until
+ * the process ends.  Nothing is allocated, freed or copied to the host; phase 1
+ * writes every partial that phase 2 reads, so the array needs no clearing.
+ *   - The first call on a device resolves the array's address on that device
+ *     (hipGetSymbolAddress, with the device current); make that first call
+ *     outside a graph capture.  A failure there is CFC_ERR_HIP.
+ *   - Every call on one GPU uses the same array: calls that may overlap on one
+ *     GPU (concurrent streams, several host threads) race and must be
+ *     serialised by the caller, e.g. by issuing them on one stream.
+ *   - A shape whose partials would exceed the array is CFC_ERR_UNSUPPORTED
+ *     (the split plan never needs more, so this is a guard).
+ * Returns a CFC_* status, as reduce_axis0_split. */
+int reduce_axis0_split_noalloc(const float *per_batch, long long B, long long N, float *out,
+                               hipStream_t stream);
+
 /* Static text for a status code (never NULL). */
 const char *cfc_status_string(int code);
 

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"cfc_scratch_row_len", "cfc_forward", "cfc_backward", "cfc_backward_window",
                           "cfc_forward_backward", "reduce_axis0", "reduce_axis0_split",
                           "reduce_axis0_split_workspace", "cfc_status_string", "cfc_backward_workspace",
-                          "cfc_backward_window_ws", "cfc_forward_backward_ws"}
+                          "cfc_backward_window_ws", "cfc_forward_backward_ws", "reduce_axis0_split_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -277,6 +277,22 @@ def test_split_reduce_validation(lib):
     assert f(FAKE, 524288, 3, big, FAKE + 64, 18528, None) == C.CFC_ERR_OVERLAP    # over the input
     assert f(FAKE, 524288, 3, big, big + 8, 18528, None) == C.CFC_ERR_OVERLAP      # over out
     assert f(FAKE, -5, 3, big, None, 0, None) == C.CFC_ERR_DIM
+
+
+def test_split_reduce_noalloc_validation(lib):
+    """Argument errors of the allocation-free split reduce are reported before
+    the static array's address is resolved (no HIP call)."""
+    big = FAKE + 0x10000000
+    f = lib.reduce_axis0_split_noalloc
+    assert f(FAKE, 524288, 3, None, None) == C.CFC_ERR_NULL
+    assert f(None, 524288, 3, big, None) == C.CFC_ERR_NULL
+    assert f(FAKE, 524288, 3, FAKE + 64, None) == C.CFC_ERR_OVERLAP     # out over the input
+    assert f(FAKE, -5, 3, big, None) == C.CFC_ERR_DIM
+    assert f(FAKE, 2**40, 2**40, big, None) == C.CFC_ERR_DIM            # B*N*4 overflows
+    # the largest split plan fits the static array
+    worst = max(lib.reduce_axis0_split_workspace(B, N) for N in range(1, 257)
+                for B in (2**20, 2**26, 3 * 2**30 // N))
+    assert 0 < worst <= 2 * 1024 * 1024
 
 
 def test_reduce_binding_checks_leading_axes():
