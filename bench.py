@@ -114,6 +114,82 @@ def cpu_baseline(inp, budget_s=10.0):
             "host_cores_available": ncores}
 
 
+def profiled_kernel_us(profile, kernel, grid=None):
+    """Average duration (us) of `kernel` in the committed rocprofv3 kernel-trace
+    summary profiles/<profile>.txt, only if it was taken on the current kernel
+    source; `grid` selects the row of that grid size where the summary splits a
+    kernel by grid."""
+    try:
+        with open(os.path.join(PROFILES, profile + ".txt")) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    if not any(l.startswith("kernel source sha256[:16]: " + source_hash()) for l in lines):
+        return None
+    for l in lines:
+        parts = l.split()
+        if not parts or parts[0] != kernel:
+            continue
+        if grid is not None and not any(p == "grid=%d" % grid for p in parts):
+            continue
+        try:
+            return float(parts[parts.index("avg_us") + 1]) if "avg_us" in parts else float(parts[-4])
+        except (ValueError, IndexError):
+            return None
+    return None
+
+
+REDUCE_GRID = lambda N: ((N + 63) // 64) * 256   # reduce_axis0_kernel<4, 16>: one workgroup per 64 columns
+
+
+def reduce_standalone(torch, C, W, dev, reps=20):
+    """reduce_axis0 alone on the reduce workload [32, 40960] and on the
+    large-batch workload's scratch shape [8192, 131584] (4.31 GB), each launch
+    preceded by an overwrite of a 512 MiB buffer so that neither the L2 nor the
+    256 MB MALL holds its input: HBM-resident numbers.  Each launch is
+    bracketed by HIP events on the launch stream (which include the launch gap,
+    about 6 us); the rocprofv3 kernel duration of the same launches, from the
+    committed summary, is reported beside it."""
+    flush = torch.empty(128 * 1024 * 1024, device=dev)
+    out = []
+    large_N = W.scratch_row_len(W.LARGE.n_in, W.LARGE.n_hid)
+    for name, B, N in ((W.REDUCE.name, W.REDUCE.B, W.REDUCE.N),
+                       ("scratch_B8192_N131584", W.LARGE.B, large_N)):
+        a = torch.randn(B, N, device=dev)
+        o = torch.empty(N, device=dev)
+        stream = torch.cuda.current_stream(dev)
+        C.reduce_axis0(a, out=o)
+        times = []
+        for _ in range(reps):
+            flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            C.reduce_axis0(a, out=o)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        med = times[len(times) // 2]
+        nbytes = (B * N + N) * 4
+        gbps = nbytes / (med * 1e-3) / 1e9
+        rec = {"workload": name, "B": B, "N": N, "bytes": nbytes, "flushed": True,
+               "kernel_ms_events_median": med, "GB_per_s": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS,
+               "hbm_floor_us": nbytes / (PEAK_HBM_GBPS * 1e9) * 1e6}
+        us = profiled_kernel_us("kernels_reduce_axis0_standalone", "reduce_axis0_kernel<4,16>", REDUCE_GRID(N))
+        if us is not None:
+            rec["kernel_us_rocprof"] = us
+            rec["GB_per_s_rocprof"] = nbytes / (us * 1e-6) / 1e9
+            rec["frac_hbm_rocprof"] = rec["GB_per_s_rocprof"] / PEAK_HBM_GBPS
+        # a launch that cannot approach its HBM floor is bound by launch and
+        # memory latency, not by bandwidth
+        kernel_us = rec.get("kernel_us_rocprof", med * 1e3)
+        rec["bound"] = "hbm" if kernel_us < 4 * rec["hbm_floor_us"] else "launch and memory latency"
+        out.append(rec)
+        del a, o
+    del flush
+    return out
+
+
 def reduce_sweep(torch, C, W, dev, reps=20):
     """reduce_axis0 alone at several [B, N], timed with HIP events per launch,
     with a 512 MiB buffer overwritten between launches so that neither the L2
@@ -166,6 +242,8 @@ def main():
     ap.add_argument("--workload", default="train",
                     choices=["train", "smoke", "tiny", "large", "long", "tau_train", "tau_tiny"],
                     help="which seeded workload one step runs (the metric is quoted on 'train')")
+    ap.add_argument("--no-reduce", action="store_true",
+                    help="skip the standalone, cache-flushed reduce_axis0 measurement")
     ap.add_argument("--reduce-sweep", action="store_true",
                     help="also time reduce_axis0 alone, cache-flushed, over a range of sizes")
     ap.add_argument("--main-only", action="store_true",
@@ -368,6 +446,15 @@ def main():
     roof["algorithmic_flops_per_launch"] = flops[dom]
     roof["algorithmic_bytes_per_launch"] = nbytes[dom]
     roof["traffic"] = measured_traffic(cfg.name + ("_input_grads" if args.input_grads else ""), dom)
+    # the same kernel's average duration under rocprofv3 (committed summary of
+    # this workload's bench step, current kernel source only)
+    launched = {"cfc_fb_kernel": "cfc_fb_small_kernel<true>" if args.path == "fused" else None}.get(dom)
+    prof_name = "kernels_" + cfg.name + ("_input_grads" if args.input_grads else "")
+    prof_us = profiled_kernel_us(prof_name, launched) if launched else None
+    if prof_us is not None:
+        roof["kernel_ms_rocprof"] = prof_us * 1e-3
+        roof["frac_rocprof"] = (flops[dom] / (prof_us * 1e-6) / 1e12 / PEAK_F64_TFLOPS if roof["bound"] == "alu"
+                                else nbytes[dom] / (prof_us * 1e-6) / 1e9 / PEAK_HBM_GBPS)
     red_gbps = work["reduce_bytes"] / (k_ms["reduce_axis0_kernel"] * 1e-3) / 1e9
     # floors of the whole step: algorithmic bytes at 8 TB/s, algorithmic f64
     # flops at 78.6 TFLOP/s; frac = the larger floor / measured time
@@ -410,11 +497,12 @@ def main():
             "kernels_ms": k_acc, "step": acc_step},
         "other_path": None if args.main_only else {
             "path": other, "value": B * K / (ms_other * 1e-3), "ms_per_step": ms_other, "kernels_ms": k_other},
-        "reduce_axis0": {"GB_per_s": red_gbps, "frac_hbm": red_gbps / PEAK_HBM_GBPS,
-                         "bytes": work["reduce_bytes"],
-                         "note": "HIP events around the launch inside the step, breakdown pass (an empty launch "
-                                 "measures about 6 us this way); the step's scratch (%.1f MB) was just written, so "
-                                 "part of it may be served from the MALL" % (work["reduce_bytes"] / 1e6)},
+        "reduce_axis0": {
+            "standalone": None if args.no_reduce else reduce_standalone(torch, C, W, dev),
+            "in_step": {"GB_per_s": red_gbps, "frac_hbm": red_gbps / PEAK_HBM_GBPS, "bytes": work["reduce_bytes"],
+                        "note": "HIP events around the launch inside the step, breakdown pass (an empty launch "
+                                "measures about 6 us this way); the step's scratch (%.1f MB) was just written, so "
+                                "part of it may be served from the MALL" % (work["reduce_bytes"] / 1e6)}},
         "kernel_source_sha256_16": source_hash(),
     }
     if args.reduce_sweep:

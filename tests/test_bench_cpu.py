@@ -86,6 +86,27 @@ def test_traffic_is_used_only_for_the_current_source(tmp_path, monkeypatch):
     assert bench.measured_traffic("wl", "cfc_fb_kernel") is None
 
 
+def test_profiled_kernel_duration_only_for_the_current_source(tmp_path, monkeypatch):
+    """bench.py reads a kernel's rocprofv3 average from a committed trace
+    summary only when the summary names the current kernel source; rows of a
+    kernel split by grid size are selected by grid."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    rows = ("kernel                      calls     avg_us     min_us     max_us  share%\n"
+            "cfc_fb_small_kernel<true>       46      97.75      95.67     103.47   18.46\n"
+            "reduce_axis0_kernel<4,16> grid=163840    21       3.70       3.52       5.12    0.32\n"
+            "reduce_axis0_kernel<4,16> grid=526336    21     710.49     695.88     852.46   61.26\n")
+    (tmp_path / "kernels_x.txt").write_text("t\ncommand: rocprofv3 ...\nkernel source sha256[:16]: "
+                                            + bench.source_hash() + "\n\n" + rows)
+    assert bench.profiled_kernel_us("kernels_x", "cfc_fb_small_kernel<true>") == 97.75
+    assert bench.profiled_kernel_us("kernels_x", "reduce_axis0_kernel<4,16>", 526336) == 710.49
+    assert bench.profiled_kernel_us("kernels_x", "reduce_axis0_kernel<4,16>", 163840) == 3.70
+    assert bench.profiled_kernel_us("kernels_x", "reduce_axis0_kernel<4,16>", 1) is None
+    assert bench.REDUCE_GRID(40960) == 163840 and bench.REDUCE_GRID(131584) == 526336
+    (tmp_path / "kernels_y.txt").write_text("t\ncommand: rocprofv3\nkernel source sha256[:16]: 0123456789abcdef\n"
+                                            + rows)
+    assert bench.profiled_kernel_us("kernels_y", "cfc_fb_small_kernel<true>") is None
+
+
 def test_committed_profiles_name_their_source_and_command():
     """Every committed traffic summary carries the kernel-source hash it was
     taken on, and every summary the command that made it."""
