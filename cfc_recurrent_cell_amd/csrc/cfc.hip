@@ -302,67 +302,94 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
-// Serial-chain layout of the one-row kernels.  The 16 lanes of a DPP row
-// (jb = lane bits 0..3) share the row block ib = 4*wave + lane/16, i.e. units
-// 8ib .. 8ib+7, and lane jb takes the column block 8jb .. 8jb+7 of the step's
-// 128 x 128 matrix-vector product, so a lane reads 8 state values (64 bytes)
-// per step.  Slot s of a lane's 8 partial sums belongs to unit 8ib + (s ^ x)
-// with x = 4 b3 + 2 b2 + (b1 ^ b2) (b_n = bit n of jb): the order is fixed per
-// lane when its weights are loaded, so that every stage of reduce_scatter16
-// keeps the low half of the lane's values and sends the high half, with no
-// per-lane selects.  It leaves unit o = 8ib + x in lanes jb and jb^1; the odd
-// one evaluates the gate and the even one tanh.
+// Serial-chain layout of the one-row kernels.  Lane (wave w, row r = lane / 16,
+// l = lane % 16) owns unit o = 32w + 16 (r / 2) + l over the column half
+// hf = r % 2 (columns 64hf .. 64hf + 63 of the step's 128 x 128 product), so
+// rows 2p and 2p + 1 of a wave hold the same 16 units over the two halves.  A
+// lane keeps the 64 weights of its unit and half in registers and reads 4
+// values of the state (columns 64hf + 4l .. 64hf + 4l + 3) from LDS per step;
+// the 16 lanes of a row broadcast their state values to each other inside the
+// product (v_fmac_f64 with row_newbcast DPP: lane j's value multiplies every
+// lane's own weight), so the product needs no reduction inside the row.  The
+// two halves are added across the row pair with v_permlane16_swap, which leaves
+// the same sum, bitwise, in both lanes of the unit; the even-row lane then
+// evaluates tanh and the odd-row lane the gate.
 struct ChainLane {
-    int jb, ib, o;
+    int o, hf, l;
     bool gate;
 };
-__device__ __forceinline__ int chain_unit_xor(int jb) {
-    return (jb & 8 ? 4 : 0) + (jb & 4 ? 2 : 0) + (((jb >> 1) ^ (jb >> 2)) & 1);
-}
 __device__ __forceinline__ ChainLane chain_lane(int wave, int lane) {
-    const int jb = lane & 15, ib = wave * 4 + (lane >> 4);
-    return ChainLane{jb, ib, 8 * ib + chain_unit_xor(jb), (jb & 1) != 0};
+    const int r = lane >> 4, l = lane & 15;
+    return ChainLane{32 * wave + 16 * (r >> 1) + l, r & 1, l, (r & 1) != 0};
 }
 
-// p[s] is this lane's partial sum for unit 8ib + (s ^ x) over its 8 columns;
-// the 16 lanes of the row hold partials over disjoint column blocks.  Returns
-// the full sum of unit 8ib + x in lanes jb and jb^1.  Stage 1 pairs jb with
-// jb^8 (row_ror:8), stage 2 with jb^7 inside each half-row (row_half_mirror),
-// stage 3 with jb^2, stage 4 with jb^1.  A partner's x differs from the lane's
-// by 4, 2 + 1 and 1 in the first three stages, so slot m + half of the
-// partner holds the unit of the lane's slot m: each stage adds the partner's
-// upper half onto the lane's lower half.  Fixed order: deterministic.
-__device__ __forceinline__ double reduce_scatter16(const double p[8]) {
-    double q[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) q[m] = p[m] + dpp_move<kDppRor8>(p[4 + m]);
-    double r[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) r[m] = q[m] + dpp_move<kDppHalfMirror>(q[2 + m]);
-    const double t = r[0] + dpp_move<kDppXor2>(r[1]);
-    return t + dpp_move<kDppXor1>(t);
+// Both lanes of a row pair get the even row's v and the odd row's v (the two
+// 32-bit halves go through v_permlane16_swap, which exchanges a register's odd
+// rows with another's even rows).
+__device__ __forceinline__ void row_pair_values(double v, double& even, double& odd) {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    const auto lo = __builtin_amdgcn_permlane16_swap((unsigned)u, (unsigned)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((unsigned)(u >> 32), (unsigned)(u >> 32), false, false);
+    even = __builtin_bit_cast(double, ((unsigned long long)hi[0] << 32) | lo[0]);
+    odd = __builtin_bit_cast(double, ((unsigned long long)hi[1] << 32) | lo[1]);
 }
 
-// The lane's 8 state values v[8jb .. 8jb+7] from LDS (four 16-byte reads).
-__device__ __forceinline__ void chain_read(double (&vj)[8], const double* v, int jb) {
-#pragma unroll
-    for (int c = 0; c < 8; c += 2) {
-        const double2 v2 = *reinterpret_cast<const double2*>(v + 8 * jb + c);
-        vj[c] = v2.x;
-        vj[c + 1] = v2.y;
-    }
+// The lane's 4 state values of columns 64hf + 4l .. 64hf + 4l + 3 (two 16-byte
+// LDS reads; a row reads 512 contiguous bytes).
+__device__ __forceinline__ void chain_read(double (&s)[4], const double* v, const ChainLane& cl) {
+    const double2* p = reinterpret_cast<const double2*>(v + 64 * cl.hf + 4 * cl.l);
+    const double2 v0 = p[0], v1 = p[1];
+    s[0] = v0.x;
+    s[1] = v0.y;
+    s[2] = v1.x;
+    s[3] = v1.y;
 }
 
-// 64 FMAs into 8 independent sums (w[s][c] multiplies vj[c] into slot s,
-// unit 8ib + (s ^ x)), then the reduce-scatter: the full product for the
-// lane's unit.
-__device__ __forceinline__ double chain_product(const double (&w)[8][8], const double (&vj)[8]) {
-    double p[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) p[r] = fma(w[r][c], vj[c], p[r]);
-    return reduce_scatter16(p);
+// seed + sum over j < 16, m < 4 of w[j][m] * (lane j's s[m]) for this lane's
+// half of the unit, in a fixed order into two accumulators (both seeded with
+// `seed`): 64 v_fmac_f64 whose first operand is broadcast from lane j of the
+// row (row_newbcast:j).  Two asm statements, one per pair of state values, so
+// that the first can start when the first LDS read has returned.  Each begins
+// with two wait states, the distance a DPP source needs from a vector-ALU write
+// of it.
+#define CFC_FMAC_J(J, S, W)                                                                  \
+    "v_fmac_f64_dpp %[a0], %[" #S "a], %[" #W "0_" #J "] row_newbcast:" #J " row_mask:0xf bank_mask:0xf\n" \
+    "v_fmac_f64_dpp %[a1], %[" #S "b], %[" #W "1_" #J "] row_newbcast:" #J " row_mask:0xf bank_mask:0xf\n"
+#define CFC_FMAC_16(S, W)                                                                    \
+    CFC_FMAC_J(0, S, W) CFC_FMAC_J(1, S, W) CFC_FMAC_J(2, S, W) CFC_FMAC_J(3, S, W)           \
+    CFC_FMAC_J(4, S, W) CFC_FMAC_J(5, S, W) CFC_FMAC_J(6, S, W) CFC_FMAC_J(7, S, W)           \
+    CFC_FMAC_J(8, S, W) CFC_FMAC_J(9, S, W) CFC_FMAC_J(10, S, W) CFC_FMAC_J(11, S, W)         \
+    CFC_FMAC_J(12, S, W) CFC_FMAC_J(13, S, W) CFC_FMAC_J(14, S, W) CFC_FMAC_J(15, S, W)
+#define CFC_W_OPS(W, M0, M1)                                                                  \
+    [W##0_0] "v"(w[0][M0]), [W##1_0] "v"(w[0][M1]), [W##0_1] "v"(w[1][M0]), [W##1_1] "v"(w[1][M1]),         \
+    [W##0_2] "v"(w[2][M0]), [W##1_2] "v"(w[2][M1]), [W##0_3] "v"(w[3][M0]), [W##1_3] "v"(w[3][M1]),         \
+    [W##0_4] "v"(w[4][M0]), [W##1_4] "v"(w[4][M1]), [W##0_5] "v"(w[5][M0]), [W##1_5] "v"(w[5][M1]),         \
+    [W##0_6] "v"(w[6][M0]), [W##1_6] "v"(w[6][M1]), [W##0_7] "v"(w[7][M0]), [W##1_7] "v"(w[7][M1]),         \
+    [W##0_8] "v"(w[8][M0]), [W##1_8] "v"(w[8][M1]), [W##0_9] "v"(w[9][M0]), [W##1_9] "v"(w[9][M1]),         \
+    [W##0_10] "v"(w[10][M0]), [W##1_10] "v"(w[10][M1]), [W##0_11] "v"(w[11][M0]), [W##1_11] "v"(w[11][M1]), \
+    [W##0_12] "v"(w[12][M0]), [W##1_12] "v"(w[12][M1]), [W##0_13] "v"(w[13][M0]), [W##1_13] "v"(w[13][M1]), \
+    [W##0_14] "v"(w[14][M0]), [W##1_14] "v"(w[14][M1]), [W##0_15] "v"(w[15][M0]), [W##1_15] "v"(w[15][M1])
+__device__ __forceinline__ double chain_product(const double (&w)[16][4], const double (&s)[4], double seed) {
+    double a0 = seed, a1 = seed;
+    asm volatile("s_nop 1\n" CFC_FMAC_16(s0, w)
+                 : [a0] "+v"(a0), [a1] "+v"(a1)
+                 : [s0a] "v"(s[0]), [s0b] "v"(s[1]), CFC_W_OPS(w, 0, 1));
+    asm volatile("s_nop 1\n" CFC_FMAC_16(s1, x)
+                 : [a0] "+v"(a0), [a1] "+v"(a1)
+                 : [s1a] "v"(s[2]), [s1b] "v"(s[3]), CFC_W_OPS(x, 2, 3));
+    return a0 + a1;
+}
+#undef CFC_FMAC_J
+#undef CFC_FMAC_16
+#undef CFC_W_OPS
+
+// The unit's full sum in both lanes of the row pair: the two halves' partial
+// sums added in the order (even row) + (odd row), so both lanes hold the same
+// bits.
+__device__ __forceinline__ double chain_total(double half_sum) {
+    double even, odd;
+    row_pair_values(half_sum, even, odd);
+    return even + odd;
 }
 
 // e^x for |x| <= 700: x = n ln2 + r with n = rint(x log2e) and r by one FMA
@@ -455,23 +482,18 @@ __device__ __forceinline__ GateLane gate_lane_consts(bool gate_lane, const UnitG
     return GateLane{gate_lane ? u.zmul : 2.0, gate_lane ? u.vmul : -2.0, gate_lane ? u.vadd : 1.0, gate_lane};
 }
 
-// tanh(a) and the gate for the unit owned by a lane pair; each lane evaluates
-// one of the two and they swap.  Both lanes return both values.
+// tanh(a) and the gate for the unit owned by a lane pair: the even-row lane
+// evaluates tanh, the odd-row lane the gate, and the row-pair exchange gives
+// both lanes both values.
 __device__ __forceinline__ void cell_gates(double a, const GateLane& L, double& g, double& c) {
     const double r = inv_one_plus_exp(L.zmul * a);
-    const double val = fma(r, L.vmul, L.vadd);
-    const double other = dpp_move<kDppXor1>(val);
-    g = L.gate ? val : other;
-    c = L.gate ? other : val;
+    row_pair_values(fma(r, L.vmul, L.vadd), c, g);
 }
 // The same for a row whose inputs are not all finite: NaN propagates as in the
 // definition (zl = L.zmul * log2e, hoisted by the caller).
 __device__ __forceinline__ void cell_gates_exact(double a, const GateLane& L, double zl, double& g, double& c) {
     const double r = inv_one_plus_exp_exact(L.zmul, zl, a);
-    const double val = fma(r, L.vmul, L.vadd);
-    const double other = dpp_move<kDppXor1>(val);
-    g = L.gate ? val : other;
-    c = L.gate ? other : val;
+    row_pair_values(fma(r, L.vmul, L.vadd), c, g);
 }
 
 // s_waitcnt lgkmcnt(0): wait for every outstanding LDS and scalar-memory
@@ -596,105 +618,47 @@ __device__ __forceinline__ void load_span_f64(double (&dst)[COUNT], const float*
     }
 }
 
-// The fast path of load_chain_weights (H % 4 == 0, W_rec 16-byte aligned)
-// in two parts, so that the 16 loads can go out early and the widening come
-// later.  Every float4 chunk of a lane's span is wholly inside or outside its
-// row (the same for all lanes): the loads go out together from in-range
-// addresses and out-of-range elements are zeroed afterwards.  The slot order
-// (slot s holds unit s ^ x) comes from the addresses where it can: the
-// forward's slots are rows (row r0 + (s ^ x) is loaded into slot s); the
-// backward's are columns of the span, so bit 2 of x picks the float4 half and
-// bits 1, 0 swap within it (float32 swaps).
+// The chain's weights: w[j][m] = W_rec[o][64hf + 4j + m] for the forward, or
+// (transposed) W_rec[64hf + 4j + m][o] for the backward's W_rec^T; zero outside
+// the H x H matrix.  The forward's fast path (H % 4 == 0, W_rec 16-byte aligned)
+// is split into fetch (16 float4 loads of the unit's row, from in-range
+// addresses, issued together) and widen (masked conversion to double), so that
+// the loads can go out early and the widening come later.
 __device__ __forceinline__ bool chain_weights_vec(const float* w_rec, int H) {
     return (H & 3) == 0 && (reinterpret_cast<uintptr_t>(w_rec) & 15) == 0;
 }
-__device__ __forceinline__ void chain_weights_fetch(f32x4 (&raw)[8][2], const float* __restrict__ w_rec, int H,
-                                                    const ChainLane& cl, bool transposed) {
-    const int x = chain_unit_xor(cl.jb);
-    const int r0 = transposed ? 8 * cl.jb : 8 * cl.ib, c0 = transposed ? 8 * cl.ib : 8 * cl.jb;
+__device__ __forceinline__ void chain_weights_fetch(f32x4 (&raw)[16], const float* __restrict__ w_rec, int H,
+                                                    const ChainLane& cl) {
+    const float* row = w_rec + (long long)min(cl.o, H - 1) * H;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int row = transposed ? r0 + r : r0 + (r ^ x);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int half = transposed ? m ^ ((x >> 2) & 1) : m;
-            raw[r][m] = *reinterpret_cast<const f32x4*>(w_rec + (long long)min(row, H - 1) * H +
-                                                        min(c0 + 4 * half, H - 4));
-        }
-    }
+    for (int j = 0; j < 16; ++j)
+        raw[j] = *reinterpret_cast<const f32x4*>(row + min(64 * cl.hf + 4 * j, H - 4));
 }
-__device__ __forceinline__ void chain_weights_widen(double (&w)[8][8], const f32x4 (&raw)[8][2], int H,
-                                                    const ChainLane& cl, bool transposed) {
-    const int x = chain_unit_xor(cl.jb);
-    const int r0 = transposed ? 8 * cl.jb : 8 * cl.ib, c0 = transposed ? 8 * cl.ib : 8 * cl.jb;
+__device__ __forceinline__ void chain_weights_widen(double (&w)[16][4], const f32x4 (&raw)[16], int H,
+                                                    const ChainLane& cl) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
+    for (int j = 0; j < 16; ++j)
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            f32x4 v4 = raw[r][m];
-            if (transposed) {
-                if (x & 1) v4 = v4.yxwz;
-                if (x & 2) v4 = v4.zwxy;
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int sc = 4 * m + e;  // slot (transposed) or column (forward)
-                if (transposed) {
-                    const bool ok = r0 + r < H && c0 + (sc ^ x) < H;
-                    w[sc][r] = ok ? (double)v4[e] : 0.0;
-                } else {
-                    const bool ok = r0 + (r ^ x) < H && c0 + sc < H;
-                    w[r][sc] = ok ? (double)v4[e] : 0.0;
-                }
-            }
-        }
+        for (int m = 0; m < 4; ++m) w[j][m] = cl.o < H && 64 * cl.hf + 4 * j + m < H ? (double)raw[j][m] : 0.0;
 }
-
-// The chain's weights: the forward's W_rec slice w[r][c] = W_rec[8ib + r][8jb + c],
-// or (transposed) the backward's w[r][c] = W_rec[8jb + c][8ib + r]; zero
-// outside the H x H matrix.
-__device__ __forceinline__ void load_chain_weights(double (&w)[8][8], const float* __restrict__ w_rec, int H,
+__device__ __forceinline__ void load_chain_weights(double (&w)[16][4], const float* __restrict__ w_rec, int H,
                                                    const ChainLane& cl, bool transposed) {
-    if (chain_weights_vec(w_rec, H)) {
-        f32x4 raw[8][2];
-        chain_weights_fetch(raw, w_rec, H, cl, transposed);
-        chain_weights_widen(w, raw, H, cl, transposed);
+    if (!transposed && chain_weights_vec(w_rec, H)) {
+        f32x4 raw[16];
+        chain_weights_fetch(raw, w_rec, H, cl);
+        chain_weights_widen(w, raw, H, cl);
         return;
-    } else if (!transposed) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int row = 8 * cl.ib + r;
-            const int valid = row < H ? min(max(H - 8 * cl.jb, 0), 8) : 0;
-            load_span_f64<8>(w[r], w_rec + (long long)min(row, H - 1) * H + min(8 * cl.jb, H - 1), valid);
-        }
-    } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int row = 8 * cl.jb + c;
-            double w8[8];
-            const int valid = row < H ? min(max(H - 8 * cl.ib, 0), 8) : 0;
-            load_span_f64<8>(w8, w_rec + (long long)min(row, H - 1) * H + min(8 * cl.ib, H - 1), valid);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) w[r][c] = w8[r];
-        }
     }
-    // slot s takes unit s ^ x: swap rows s and s ^ 4, s ^ 2, s ^ 1 where x has
-    // that bit (once per kernel, off the chains)
-    const int x = chain_unit_xor(cl.jb);
+    const long long o = min(cl.o, H - 1);
 #pragma unroll
-    for (int bit = 4; bit >= 1; bit >>= 1) {
-        const bool sw = (x & bit) != 0;
+    for (int j = 0; j < 16; ++j)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            if (r & bit) continue;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const double lo = w[r][c], hi = w[r | bit][c];
-                w[r][c] = sw ? hi : lo;
-                w[r | bit][c] = sw ? lo : hi;
-            }
+        for (int m = 0; m < 4; ++m) {
+            const int col = 64 * cl.hf + 4 * j + m;
+            const long long c = min(col, H - 1);
+            const float v = transposed ? w_rec[c * H + o] : w_rec[o * H + c];
+            w[j][m] = cl.o < H && col < H ? (double)v : 0.0;
         }
-    }
 }
 
 __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
@@ -712,7 +676,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const long long b = blockIdx.x;
     const ChainLane cl = chain_lane(wave, lane);
-    const int jb = cl.jb, o = cl.o;
+    const int o = cl.o;
     const bool gate_lane = cl.gate;
     if (t == 0) *nonfinite = 0;  // read only after the first window's barriers
 
@@ -729,7 +693,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
         load_span_f64<NP / 4>(wb[q], w_in + (long long)min(row, H - 1) * n_in + min(32 * slot, n_in - 1), valid);
     }
     // W_rec slice for the recurrence
-    double wr[8][8];
+    double wr[16][4];
     load_chain_weights(wr, w_rec, H, cl, false);
     for (int u = t; u < HP; u += kThreads) hb[u] = u < H ? (double)h0[b * H + u] : 0.0;
     const UnitGate ug = unit_gate(cell, o < H ? (double)w_tau[o] : 0.0, dt, o < H);
@@ -768,9 +732,11 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     double* urow = U + (kb * 16 + (lane >> 4) + 4 * v) * HP + (2 * wave) * 16 + (lane & 15);
+                    // stored as a quarter: it seeds both accumulators of both
+                    // lanes of the unit's pair in the chain product
                     const double u0 = acc[kb][0][v] + bias_q0, u1 = acc[kb][1][v] + bias_q1;
-                    urow[0] = u0;
-                    urow[16] = u1;
+                    urow[0] = 0.25 * u0;
+                    urow[16] = 0.25 * u1;
                     bad |= not_finite(u0) || not_finite(u1);
                 }
         }
@@ -783,10 +749,10 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_small_kernel(
             const double zl = gl.zmul * kLog2e;
             for (int kk = 0; kk < kw; ++kk) {
                 lds_and_scalar_drained();
-                const double u = U[kk * HP + o];
-                double hj[8];
-                chain_read(hj, hb + cur * HP, jb);
-                const double a = u + chain_product(wr, hj);
+                const double u4 = U[kk * HP + o];
+                double hs[4];
+                chain_read(hs, hb + cur * HP, cl);
+                const double a = chain_total(chain_product(wr, hs, u4));
                 double g, c;
                 cell_gates_t<EXACT>(a, gl, zl, g, c);
                 const double hn = fma(g, hprev - c, c);  // g*h + (1-g)*c
@@ -827,14 +793,15 @@ __device__ __forceinline__ void small_reverse_and_grads(
     const float* __restrict__ w_in, const float* __restrict__ w_rec, int K, int n_in, int H,
     double delta, double* AD, const UnitGate& ug, double* red, const float* zs,
     float* gst, float* __restrict__ row, float* __restrict__ loss_b, float* __restrict__ gx_row,
-    float* __restrict__ gh0_row, int accumulate, int lane, int wave, int jb, int ib, int o,
-    bool gate_lane, bool bad) {
+    float* __restrict__ gh0_row, int accumulate, int lane, int wave, const ChainLane& cl, bool bad) {
     constexpr int HP = kSmall, NP = kSmall, ZW = kSmallZW, ZS = kSmallZS, AS = kSmallAS;
     constexpr int KP = kSmallBwdMaxK;
     int* nonfinite = reinterpret_cast<int*>(red + 4);
+    const int o = cl.o;
+    const bool gate_lane = cl.gate;
     // ---- W_rec^T slice into registers
-    double wt[8][8];
-    load_chain_weights(wt, w_rec, H, ChainLane{jb, ib, o, gate_lane}, true);
+    double wt[16][4];
+    load_chain_weights(wt, w_rec, H, cl, true);
     if (bad || any_not_finite(wt) || any_not_finite(ug)) *nonfinite = 1;
 
     // ---- loss seed
@@ -856,17 +823,20 @@ __device__ __forceinline__ void small_reverse_and_grads(
     auto reverse_chain = [&](auto exact) {
         constexpr bool EXACT = decltype(exact)::value;
         const double zl = gl.zmul * kLog2e;
-        auto step_consts = [&](int k, double& g, double& Q, double& R) {
+        // g4 = g / 4: delta g seeds both accumulators of both lanes of the
+        // unit's pair in the chain product as a quarter each
+        auto step_consts = [&](int k, double& g4, double& Q, double& R) {
             const double a = AD[k * AS + o];
             const double hk = (double)zs[k * ZS + NP + o];
-            double c;
+            double g, c;
             cell_gates_t<EXACT>(a, gl, zl, g, c);
             const double P = (hk - c) * g * fma(-ug.vmul, g, 1.0);
             Q = (1.0 - g) * (1.0 - c * c) - P * ug.rho;
             R = P * fma(-a, ug.alpha, ug.beta);
+            g4 = 0.25 * g;
         };
-        double g, Q, R;
-        step_consts(K - 1, g, Q, R);
+        double g4, Q, R;
+        step_consts(K - 1, g4, Q, R);
         for (int k = K - 1; k >= 0; --k) {
             const double da = delta * Q;
             gb += da;
@@ -874,14 +844,14 @@ __device__ __forceinline__ void small_reverse_and_grads(
             if (!gate_lane) AD[k * AS + o] = da;
             __syncthreads();
             if (k == 0 && !gh0_row) break;
-            double dj[8];
-            chain_read(dj, AD + k * AS, jb);
+            double ds[4];
+            chain_read(ds, AD + k * AS, cl);
             // next step's constants (unused after k = 0), in the same block as
             // the products so that their latency overlaps them
-            double gn, Qn, Rn;
-            step_consts(k > 0 ? k - 1 : 0, gn, Qn, Rn);
-            delta = fma(delta, g, chain_product(wt, dj));
-            g = gn;
+            double g4n, Qn, Rn;
+            step_consts(k > 0 ? k - 1 : 0, g4n, Qn, Rn);
+            delta = chain_total(chain_product(wt, ds, delta * g4));  // delta g + W_rec^T dL/da_k
+            g4 = g4n;
             Q = Qn;
             R = Rn;
         }
@@ -1141,8 +1111,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     const long long b = blockIdx.x;
     const long long N = (long long)H * (n_in + H + 2);
     const ChainLane cl = chain_lane(wave, lane);
-    const int jb = cl.jb, ib = cl.ib, o = cl.o;
-    const bool gate_lane = cl.gate;
+    const int o = cl.o;
     if (t == 0) reinterpret_cast<int*>(red + 4)[0] = 0;  // the row's non-finite flag
 
     // Weight operand of the recomputation, in registers.  Chunk jc of k-slot
@@ -1275,8 +1244,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_small_kernel(
     small_reverse_and_grads(w_in, w_rec, K, n_in, H, delta, AD, ug, red, zs, gst, scratch + b * N,
                             loss && !win.delta_in ? loss + b : nullptr,
                             grad_x ? grad_x + (b * Kf + k0) * n_in : nullptr,
-                            win.delta_out ? win.delta_out + b * H : nullptr, accumulate, lane, wave, jb, ib, o,
-                            gate_lane, bad);
+                            win.delta_out ? win.delta_out + b * H : nullptr, accumulate, lane, wave, cl, bad);
 }
 
 // Forward and backward of one row in one workgroup (n_in, n_hid <= 128,
@@ -1321,7 +1289,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     const long long b = blockIdx.x;
     const long long N = (long long)H * (n_in + H + 2);
     const ChainLane cl = chain_lane(wave, lane);
-    const int jb = cl.jb, ib = cl.ib, o = cl.o;
+    const int o = cl.o;
     const bool gate_lane = cl.gate;
     const int slot = lane >> 4;
     int* nonfinite = reinterpret_cast<int*>(red + 4);
@@ -1337,7 +1305,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     // the per-unit inputs, as floats: w_tau, h_0 and y of unit o, the bias
     // of the projection's two output columns
     float wtau_o, h0_o, y_o, bias0, bias1;
-    f32x4 wr_raw[8][2];  // WHOLE: the forward chain's W_rec slice, fetched under the projection
+    f32x4 wr_raw[16];    // WHOLE: the forward chain's W_rec slice, fetched under the projection
     const int bcol0 = (2 * wave) * 16 + (lane & 15), bcol1 = bcol0 + 16;
     if constexpr (WHOLE) {
         // every load is unconditional (all indices are in range here), and
@@ -1406,7 +1374,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
                 }
             // the forward chain's weights and the loss target stream in
             // under the products
-            chain_weights_fetch(wr_raw, w_rec, HP, cl, false);
+            chain_weights_fetch(wr_raw, w_rec, HP, cl);
             y_o = y[b * H + o];
         } else {
 #pragma unroll
@@ -1438,24 +1406,24 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
             for (int v = 0; v < 4; ++v) {
                 const int kk = kb * 16 + (lane >> 4) + 4 * v;
                 double* urow = AD + kk * AS + (2 * wave) * 16 + (lane & 15);
+                // stored as a quarter: it seeds both accumulators of both lanes
+                // of the unit's pair in the forward chain's product
                 const double u0 = kk < K ? acc[kb][0][v] + bias_q0 : 0.0;
                 const double u1 = kk < K ? acc[kb][1][v] + bias_q1 : 0.0;
-                urow[0] = u0;
-                urow[16] = u1;
+                urow[0] = 0.25 * u0;
+                urow[16] = 0.25 * u1;
                 bad |= not_finite(u0) || not_finite(u1);
             }
     }
 
     // ---- forward chain (as in cfc_fwd_small_kernel); a_k replaces the
     // projection in AD, h_k goes to h_seq and to the h_prev half of row k+1
-    double wr[8][8];
+    double wr[16][4];
     if constexpr (WHOLE) {
         // as with W_in: the wait and the widening stay here
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-            for (int m = 0; m < 2; ++m) asm volatile("" : "+v"(wr_raw[r][m]));
-        chain_weights_widen(wr, wr_raw, H, cl, false);
+        for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(wr_raw[j]));
+        chain_weights_widen(wr, wr_raw, H, cl);
     } else {
         load_chain_weights(wr, w_rec, H, cl, false);
     }
@@ -1469,10 +1437,10 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
         int cur = 0;
         for (int k = 0; k < K; ++k) {
             lds_and_scalar_drained();
-            const double u = AD[k * AS + o];
-            double hj[8];
-            chain_read(hj, hb + cur * HP, jb);
-            const double a = u + chain_product(wr, hj);
+            const double u4 = AD[k * AS + o];
+            double hs[4];
+            chain_read(hs, hb + cur * HP, cl);
+            const double a = chain_total(chain_product(wr, hs, u4));
             double g, c;
             cell_gates_t<EXACT>(a, gl, zl, g, c);
             const double hn = fma(g, hprev - c, c);
@@ -1498,8 +1466,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     const double delta = o < H ? (double)(float)hprev - (double)y_o : 0.0;
     small_reverse_and_grads(w_in, w_rec, K_arg, n_in_arg, H_arg, delta, AD, ug, red, zs, gst, scratch + b * N,
                             loss ? loss + b : nullptr, grad_x ? grad_x + b * K * (long long)n_in : nullptr,
-                            grad_h0 ? grad_h0 + b * H : nullptr, accumulate, lane, wave, jb, ib, o, gate_lane,
-                            false);
+                            grad_h0 ? grad_h0 + b * H : nullptr, accumulate, lane, wave, cl, false);
 }
 
 // =====================================================================
