@@ -405,8 +405,13 @@ __device__ __forceinline__ double exp_poly_scaled(double r, int n) {
                      c7 = 1.0 / 5040, c8 = 1.0 / 40320, c9 = 1.0 / 362880, c10 = 1.0 / 3628800,
                      c11 = 1.0 / 39916800, c12 = 1.0 / 479001600;
     const double r2 = r * r, r4 = r2 * r2, r8 = r4 * r4;
-    const double q0 = 1.0 + r, q1 = fma(c3, r, c2), q2 = fma(c5, r, c4), q3 = fma(c7, r, c6);
-    const double q4 = fma(c9, r, c8), q5 = fma(c11, r, c10);
+    auto fma3 = [](double a, double x, double c) {
+        double d;
+        asm("v_fma_f64 %0, %1, %2, %3" : "=v"(d) : "s"(a), "v"(x), "v"(c));
+        return d;
+    };
+    const double q0 = 1.0 + r, q1 = fma(c3, r, c2), q2 = fma3(c5, r, c4), q3 = fma3(c7, r, c6);
+    const double q4 = fma3(c9, r, c8), q5 = fma3(c11, r, c10);
     const double s0 = fma(q1, r2, q0), s1 = fma(q3, r2, q2), s2 = fma(q5, r2, q4);
     const double t0 = fma(s1, r4, s0), t1 = fma(c12, r4, s2);
     return ldexp(fma(t1, r8, t0), n);
