@@ -395,26 +395,29 @@ __device__ __forceinline__ double chain_total(double half_sum) {
 // e^x for |x| <= 700: x = n ln2 + r with n = rint(x log2e) and r by one FMA
 // with ln2 rounded to double (the reduction error |n| 2.3e-17 is below
 // 1.5e-15 relative for |x| < 40 and below 2.4e-14 at |x| = 700), |r| <= ln2/2,
-// e^r by its degree-12 Taylor polynomial (truncation below 2e-16 relative)
-// evaluated with Estrin's scheme for a short dependency chain, then scaled by
-// 2^n.
+// e^r by a degree-10 polynomial with constant term 1 whose other coefficients
+// minimise the largest relative error on [-ln2/2, ln2/2] (Remez exchange,
+// computed in 50-digit arithmetic and rounded to double: 2.4e-15 relative,
+// against 2.4e-13 for the degree-10 Taylor polynomial), evaluated with
+// Estrin's scheme for a short dependency chain, then scaled by 2^n.
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr double kLn2 = 0.69314718055994530942;
 __device__ __forceinline__ double exp_poly_scaled(double r, int n) {
-    constexpr double c2 = 1.0 / 2, c3 = 1.0 / 6, c4 = 1.0 / 24, c5 = 1.0 / 120, c6 = 1.0 / 720,
-                     c7 = 1.0 / 5040, c8 = 1.0 / 40320, c9 = 1.0 / 362880, c10 = 1.0 / 3628800,
-                     c11 = 1.0 / 39916800, c12 = 1.0 / 479001600;
+    constexpr double c1 = 1.0000000000000009, c2 = 0.49999999999997086, c3 = 0.16666666666632235,
+                     c4 = 0.04166666667007467, c5 = 0.008333333358760514, c6 = 0.0013888887798236404,
+                     c7 = 0.00019841203906994798, c8 = 2.4802862967019124e-05, c9 = 2.7626408481260957e-06,
+                     c10 = 2.7086871132720806e-07;
     const double r2 = r * r, r4 = r2 * r2, r8 = r4 * r4;
     auto fma3 = [](double a, double x, double c) {
         double d;
         asm("v_fma_f64 %0, %1, %2, %3" : "=v"(d) : "s"(a), "v"(x), "v"(c));
         return d;
     };
-    const double q0 = 1.0 + r, q1 = fma(c3, r, c2), q2 = fma3(c5, r, c4), q3 = fma3(c7, r, c6);
-    const double q4 = fma3(c9, r, c8), q5 = fma3(c11, r, c10);
-    const double s0 = fma(q1, r2, q0), s1 = fma(q3, r2, q2), s2 = fma(q5, r2, q4);
-    const double t0 = fma(s1, r4, s0), t1 = fma(c12, r4, s2);
-    return ldexp(fma(t1, r8, t0), n);
+    const double q0 = fma(c1, r, 1.0), q1 = fma3(c3, r, c2), q2 = fma3(c5, r, c4), q3 = fma3(c7, r, c6);
+    const double q4 = fma3(c9, r, c8);
+    const double s0 = fma(q1, r2, q0), s1 = fma(q3, r2, q2), s2 = fma(c10, r2, q4);
+    const double t0 = fma(s1, r4, s0);
+    return ldexp(fma(s2, r8, t0), n);
 }
 __device__ __forceinline__ double exp_f64(double x) {
     const double n = __builtin_rint(x * kLog2e);
@@ -646,9 +649,48 @@ __device__ __forceinline__ void chain_weights_widen(double (&w)[16][4], const f3
 #pragma unroll
         for (int m = 0; m < 4; ++m) w[j][m] = cl.o < H && 64 * cl.hf + 4 * j + m < H ? (double)raw[j][m] : 0.0;
 }
+// The backward's W_rec^T slice in the same two parts: raw[j][m] =
+// W_rec[64hf + 4j + m][o] from clamped (in-range) addresses, 64 loads that
+// are coalesced across the 16 lanes of a row (consecutive units), then the
+// masked widening.  At H = 128 (every index in range) a separate path takes
+// constant offsets from one base address and no masks: the general path
+// spends four address operations per load and three per widening.
+__device__ __forceinline__ void chain_weights_t_fetch(float (&raw)[16][4], const float* __restrict__ w_rec, int H,
+                                                      const ChainLane& cl) {
+    const long long o = min(cl.o, H - 1);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) raw[j][m] = w_rec[(long long)min(64 * cl.hf + 4 * j + m, H - 1) * H + o];
+}
+__device__ __forceinline__ void chain_weights_t_widen(double (&w)[16][4], const float (&raw)[16][4], int H,
+                                                      const ChainLane& cl) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) w[j][m] = cl.o < H && 64 * cl.hf + 4 * j + m < H ? (double)raw[j][m] : 0.0;
+}
 __device__ __forceinline__ void load_chain_weights(double (&w)[16][4], const float* __restrict__ w_rec, int H,
                                                    const ChainLane& cl, bool transposed) {
-    if (!transposed && chain_weights_vec(w_rec, H)) {
+    if (transposed) {
+        float raw[16][4];
+        if (H == kSmall) {
+            const float* p = w_rec + 64 * cl.hf * kSmall + cl.o;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) raw[j][m] = p[(4 * j + m) * kSmall];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) w[j][m] = raw[j][m];
+            return;
+        }
+        chain_weights_t_fetch(raw, w_rec, H, cl);
+        chain_weights_t_widen(w, raw, H, cl);
+        return;
+    }
+    if (chain_weights_vec(w_rec, H)) {
         f32x4 raw[16];
         chain_weights_fetch(raw, w_rec, H, cl);
         chain_weights_widen(w, raw, H, cl);
@@ -660,9 +702,7 @@ __device__ __forceinline__ void load_chain_weights(double (&w)[16][4], const flo
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int col = 64 * cl.hf + 4 * j + m;
-            const long long c = min(col, H - 1);
-            const float v = transposed ? w_rec[c * H + o] : w_rec[o * H + c];
-            w[j][m] = cl.o < H && col < H ? (double)v : 0.0;
+            w[j][m] = cl.o < H && col < H ? (double)w_rec[o * H + min(col, H - 1)] : 0.0;
         }
 }
 
@@ -804,10 +844,13 @@ __device__ __forceinline__ void small_reverse_and_grads(
     int* nonfinite = reinterpret_cast<int*>(red + 4);
     const int o = cl.o;
     const bool gate_lane = cl.gate;
-    // ---- W_rec^T slice into registers
+    // ---- W_rec^T slice into registers.  Its values need no finiteness test
+    // here: both callers' pre-activations contract all of W_rec, and a
+    // non-finite weight makes them non-finite (inf times 0 is NaN), which the
+    // callers have flagged.
     double wt[16][4];
     load_chain_weights(wt, w_rec, H, cl, true);
-    if (bad || any_not_finite(wt) || any_not_finite(ug)) *nonfinite = 1;
+    if (bad || any_not_finite(ug)) *nonfinite = 1;
 
     // ---- loss seed
     {
@@ -1364,21 +1407,10 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
     {
         double wb[2][NP / 4];
         if constexpr (WHOLE) {
-            // the empty asm takes the loaded registers here, after the
-            // barrier, so the wait for them and their widening are not hoisted
-            // above the staging's later loads
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-#pragma unroll
-                for (int m = 0; m < NP / 16; ++m) {
-                    asm volatile("" : "+v"(wpre[q][m]));
-                    wb[q][4 * m] = wpre[q][m][0];
-                    wb[q][4 * m + 1] = wpre[q][m][1];
-                    wb[q][4 * m + 2] = wpre[q][m][2];
-                    wb[q][4 * m + 3] = wpre[q][m][3];
-                }
             // the forward chain's weights and the loss target stream in
-            // under the products
+            // under the products; W_in's float4 are taken one chunk group
+            // at a time inside the product loop (below), so that the products
+            // start as the first of them arrive
             chain_weights_fetch(wr_raw, w_rec, HP, cl);
             y_o = y[b * H + o];
         } else {
@@ -1398,6 +1430,18 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
         const float* xa = zs + (lane & 15) * ZS + 32 * slot;
 #pragma unroll
         for (int jc = 0; jc < NP / 4; ++jc) {
+            if constexpr (WHOLE) {
+                if (jc % 4 == 0) {
+                    // the empty asm takes float4 jc / 4 of both rows here, so
+                    // the wait for it and its widening are not hoisted
+                    const int m = jc / 4;
+                    asm volatile("" : "+v"(wpre[0][m]), "+v"(wpre[1][m]));
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) wb[q][4 * m + e] = wpre[q][m][e];
+                }
+            }
 #pragma unroll
             for (int kb = 0; kb < KP / 16; ++kb) {
                 const double a = (double)xa[kb * 16 * ZS + jc];
