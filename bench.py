@@ -10,7 +10,9 @@ cfc_backward instead.  Both paths are timed in every run; the other one is
 reported in "other_path".
 
 Prints ONE JSON line.  `value` is batch-steps/s = B*K / seconds per step.
-Each path is run twice: a breakdown pass with HIP events around every launch
+Before any timed pass the measured step runs back to back, untimed, for
+--gpu-warmup-ms (default 300 ms), so that the GPU's clocks have left their
+idle state (recorded in "gpu_warmup").  Each path is run twice: a breakdown pass with HIP events around every launch
 ("kernels_ms"), then the timed pass that gives `value`, with events only
 around the step's dominant kernel and only on every --event-stride-th step
 (each event record costs the stream about 2.5 us).  The roofline object
@@ -234,6 +236,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gpu-warmup-ms", type=float, default=300.0,
+                    help="before any timed pass, run the measured step back to back for this long (untimed), "
+                         "so that the GPU's clocks have left their idle state")
     ap.add_argument("--event-stride", type=int, default=10,
                     help="timed pass: HIP events around the dominant kernel on every Nth step")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -413,6 +418,26 @@ def main():
         ms, k_dom, pct = run_pass(path, dom)
         return ms, k_all, dom, k_dom[dom], pct
 
+    def gpu_warmup(path):
+        """The step back to back for --gpu-warmup-ms, untimed.  After an idle
+        period the GPU's clocks take tens of milliseconds of load to settle:
+        measured on MI355X at the training-scale workload, 20-step passes
+        separated by 10 ms of idle ran at 102 us per step, back-to-back steps
+        at 96 us for the first 200 and 93 us from then on."""
+        launches = STEPS[path]
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            for _ in range(10):
+                for _, f in launches:
+                    f()
+            n += 10
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= args.gpu_warmup_ms:
+                return n
+
+    main_path = args.path + ("_ig" if args.input_grads else "")
+    warm_steps = gpu_warmup(main_path) if args.gpu_warmup_ms > 0 else 0
     other = "separate" if args.path == "fused" else "fused"
     if args.path == "windows":
         args.main_only = True   # the other one-call paths refuse this K
@@ -420,7 +445,7 @@ def main():
         ms_other, k_other, _, _, _ = timed(other)
         ms_acc, k_acc, _, _, pct_acc = timed("accumulate")
         ms_ig, k_ig, _, _, pct_ig = timed(args.path + "_ig")
-    ms_per_step, k_ms, dom, dom_ms, pct = timed(args.path + ("_ig" if args.input_grads else ""))
+    ms_per_step, k_ms, dom, dom_ms, pct = timed(main_path)
     work = algorithmic_work(B, K, n_in, H)
     flops = {"cfc_fwd_kernel": work["fwd_flops"], "cfc_bwd_kernel": work["bwd_flops"],
              "cfc_fb_kernel": work["fb_flops"], "reduce_axis0_kernel": 0}
@@ -485,6 +510,7 @@ def main():
         "fused_call_is_one_kernel": n_in <= 128 and H <= 128 and K <= 64,
         "step_ms_percentiles": pct,
         "timed_pass_event_stride": args.event_stride,
+        "gpu_warmup": {"ms": args.gpu_warmup_ms, "steps": warm_steps},
         "step_floors": floors,
         "kernels_ms": k_ms,
         "with_input_grads": None if args.main_only else {

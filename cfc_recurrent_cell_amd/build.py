@@ -21,6 +21,11 @@ HIPCC_FLAGS = [
     # loops start on 64-byte boundaries: the serial chains' loop bodies
     # measured up to 4 % slower when an unrelated edit shifted their start
     "-falign-loops=64",
+    # matrix-core results in architectural VGPRs: the weight-gradient tiles
+    # are converted to float32 straight from them instead of being copied out
+    # of accumulation registers first (the training-scale fused kernel then
+    # issues 680 fewer copies and ran 0.7 % faster on MI355X)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -919,7 +919,11 @@ __device__ __forceinline__ void small_reverse_and_grads(
         const float* zb = zs + (lane >> 4) * ZS + (lane & 15);
         // Exactly 128 x 128 with 16-byte-aligned rows (either mode): no
         // masking, and each group's tiles are stored while the next group's
-        // products run (the groups' stores otherwise wait for their products)
+        // products run (the groups' stores otherwise wait for their products).
+        // The float4 stores are non-temporal: the scratch is written once
+        // and read next by the reducer; measured on MI355X at B = 256, the
+        // fused kernel took 79.8 against 81.0 us and the reduce after it
+        // 10.5 against 11.6 us, against ordinary stores.
         const bool interleave = n_in == NP && H == HP && (reinterpret_cast<uintptr_t>(row) & 15) == 0;
         if (interleave) {
             const int c4 = 4 * (lane & 15);
@@ -954,7 +958,8 @@ __device__ __forceinline__ void small_reverse_and_grads(
                             const float4 o = old4[m];
                             val = make_float4(val.x + o.x, val.y + o.y, val.z + o.z, val.w + o.w);
                         }
-                        *reinterpret_cast<float4*>(dst_of(jgp, q, m)) = val;
+                        __builtin_nontemporal_store(f32x4{val.x, val.y, val.z, val.w},
+                                                    reinterpret_cast<f32x4*>(dst_of(jgp, q, m)));
                     }
                 };
                 for (int jg = 0; jg < ZW / 64; ++jg) {
