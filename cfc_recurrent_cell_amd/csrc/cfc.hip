@@ -1758,6 +1758,153 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
     }
 }
 
+// Thirty-two rows per workgroup, for exactly 256 x 256 with 16-byte-aligned
+// weights.  Each weight operand (a float4 load and its widening) then feeds
+// the products of two 16-row tiles, so the widenings per matrix-core product
+// halve against cfc_fwd_large_kernel; f64 matrix-core products and vector
+// instructions do not overlap on a SIMD (measured on MI355X: each vector
+// instruction between two products adds 13 cycles or more), so the widenings
+// set the product loop's pace.  [x_k ; h_k] of the 32 rows is staged as in
+// the 16-row kernel, in [256][32] arrays swizzled within each row of 32.
+// PARK as in cfc_fwd_large_kernel.
+constexpr int kLR2 = 32;  // batch rows per workgroup of the 32-row forward
+__device__ __forceinline__ int zidx2(int j, int r) { return j * kLR2 + (r ^ (j & 31)); }
+__host__ __device__ constexpr size_t large32_fwd_lds_bytes() {
+    return (size_t)4 * kLarge * kLR2 + (size_t)8 * kLarge * kLR2 + (size_t)8 * 2 * kLarge;
+}
+template <bool PARK>
+__global__ __launch_bounds__(kThreads) void cfc_fwd_large32_kernel(
+    const float* __restrict__ w_in, const float* __restrict__ w_rec, const float* __restrict__ bias,
+    const float* __restrict__ w_tau, const float* __restrict__ x, const float* __restrict__ h0, double dt, int B,
+    int K, float* __restrict__ h_seq, int cell, float* __restrict__ a_park, long long N) {
+    constexpr int H = kLarge, NI = kLarge;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* zx = reinterpret_cast<float*>(smem);                          // [256][32] x_k
+    double* zh = reinterpret_cast<double*>(smem + 4 * kLarge * kLR2);     // [256][32] h_k
+    double* ubias = reinterpret_cast<double*>(smem + 12 * kLarge * kLR2); // [256] b
+    double* uspdt = ubias + kLarge;  // [256] softplus(w_tau) dt (tau-decay: the decay)
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int s = lane >> 4, r = lane & 15;
+    const long long r0 = (long long)blockIdx.x * kLR2;
+    static_assert(kThreads == kLarge, "one thread per unit for the per-unit constants");
+    {
+        const double w = (double)w_tau[t];
+        ubias[t] = (double)bias[t];
+        if (cell == CFC_CELL_TAU_DECAY) {
+            double decay = 0.0, q;
+            tau_decay_consts(w, dt, decay, q);
+            uspdt[t] = decay;
+        } else {
+            uspdt[t] = softplus_f64(w) * dt;
+        }
+    }
+    // h_0 and x_0 of the 32 rows (rows >= B zero)
+#pragma unroll 4
+    for (int m = 0; m < kLR2; ++m) {
+        const int e = t + kThreads * m, rr = e >> 8, j = e & 255;
+        const long long b = r0 + rr;
+        zh[zidx2(j, rr)] = b < B ? (double)h0[b * H + j] : 0.0;
+        zx[zidx2(j, rr)] = b < B ? x[b * K * (long long)NI + j] : 0.f;
+    }
+    __syncthreads();
+
+    for (int k = 0; k < K; ++k) {
+        // D[i][r] = sum_j [W_in | W_rec][i][j] [x_k ; h_k][j][r] for the
+        // wave's four 16-unit tiles and both 16-row tiles; chunk (jq, cc) of
+        // half g and k-slot s contracts j = 256 g + 16 jq + 4 s + cc (the
+        // 16-row kernel's order), eight independent accumulators per chunk
+        dbl4 acc[4][2];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) acc[tb][rt] = dbl4{0.0, 0.0, 0.0, 0.0};
+        // both halves unrolled, so that the operand array of each is fixed
+        // at compile time (no per-read branch), and the swizzled operand
+        // offsets of the lane precomputed: chunk j = 32 jp + jr reads element
+        // 1024 jp + off[jr's parity][cc][rt], jr = 16 (jq & 1) + 4 s + cc
+        int off[2][4][2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) off[p][cc][rt] = zidx2(16 * p + 4 * s + cc, 16 * rt + r);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const float* wbase = g == 0 ? w_in : w_rec;
+            const float* wrow[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) wrow[tb] = wbase + lunit(wave, tb, r) * H;
+            float4 w4[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) w4[tb] = *reinterpret_cast<const float4*>(wrow[tb] + 4 * s);
+#pragma unroll 4
+            for (int jq = 0; jq < 16; ++jq) {
+                float4 nw4[4];
+                const int jn = jq + 1 < 16 ? jq + 1 : jq;  // the next chunk group's weights
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) nw4[tb] = *reinterpret_cast<const float4*>(wrow[tb] + 16 * jn + 4 * s);
+                const int base = 1024 * (jq >> 1), par = jq & 1;
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    double bz[2];
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+                        bz[rt] = g == 0 ? (double)zx[base + off[par][cc][rt]] : zh[base + off[par][cc][rt]];
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) {
+                        const double wa = (double)f4_get(w4[tb], cc);
+#pragma unroll
+                        for (int rt = 0; rt < 2; ++rt) acc[tb][rt] = mfma_f64(wa, bz[rt], acc[tb][rt]);
+                    }
+                }
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) w4[tb] = nw4[tb];
+            }
+        }
+        // next step's x, loaded after the product's weight loads and written
+        // to LDS after the elementwise phase
+        float xn[kLR2];
+#pragma unroll
+        for (int m = 0; m < kLR2; ++m) {
+            const int e = t + kThreads * m, rr = e >> 8, j = e & 255;
+            const long long b = r0 + rr;
+            xn[m] = (k + 1 < K && b < B) ? x[(b * K + k + 1) * (long long)NI + j] : 0.f;
+        }
+        __syncthreads();  // every wave is done reading zx / zh of step k
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int i = lunit(wave, tb, s + 4 * v), rr = 16 * rt + r;
+                    const double a = acc[tb][rt][v] + ubias[i];
+                    if constexpr (PARK) {
+                        if (r0 + rr < B) reinterpret_cast<double*>(a_park + (r0 + rr) * N)[(long long)k * H + i] = a;
+                    }
+                    const double sp = uspdt[i];
+                    const double gt = cell == CFC_CELL_TAU_DECAY ? sp : inv_one_plus_exp_exact(sp, sp * kLog2e, a);
+                    const double c = fma(-2.0, inv_one_plus_exp_exact(2.0, 2.0 * kLog2e, a), 1.0);
+                    double* hp = zh + zidx2(i, rr);
+                    *hp = fma(gt, *hp - c, c);  // g*h + (1-g)*c
+                }
+#pragma unroll
+        for (int m = 0; m < kLR2; ++m) {
+            const int e = t + kThreads * m;
+            zx[zidx2(e & 255, e >> 8)] = xn[m];
+        }
+        __syncthreads();
+        // h_k+1 of the 32 rows, row-contiguous stores
+#pragma unroll 4
+        for (int m = 0; m < kLR2; ++m) {
+            const int e = t + kThreads * m, rr = e >> 8, j = e & 255;
+            const long long b = r0 + rr;
+            if (b < B) h_seq[(b * K + k) * (long long)H + j] = (float)zh[zidx2(j, rr)];
+        }
+    }
+}
+
 // PARKED (one-call entry, after cfc_fwd_large_kernel<FULL, true>): a_k is read
 // back from the head of the row's scratch instead of being recomputed, so x_k
 // is not staged; the window is then the whole sequence.
@@ -2300,6 +2447,88 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     }
 }
 
+// Phase 2 of the parked backward at exactly 256 x 256 and K <= 8, on the
+// vector units: one workgroup per row.  The row's weight gradient is a sum of
+// K outer products, G[i][j] = sum_k dL/da_k[i] [x_k | h_k-1][j], so each
+// output element takes K multiply-adds; as K x 4 f64 FMAs per lane for four
+// adjacent columns of one unit row, with the lane's K x 4 operands of
+// [x | h_prev] held in registers and the unit's K values of dL/da read from
+// LDS as a broadcast, every wave instruction stores 1 KB of contiguous
+// gradient.  The matrix-core form of this product (cfc_bwd_large_kernel, the
+// other shapes) needs a transpose through LDS per 16 x 64 tile and converts
+// its accumulators tile by tile; at K = 8 that measured 0.90 ms for the
+// 4.3 GB scratch of B = 8192, of which 0.67 ms without its stores.
+// Inputs: dL/da parked in the tail of the row's scratch by phase 1 (two 32-bit
+// halves per double, [k][unit]) and the dL/dw_tau sums in its head (float64);
+// both are read before the barrier that precedes the first store.
+constexpr int kGradsMaxK = 8;
+__global__ __launch_bounds__(kThreads) void cfc_bwd_large_grads_kernel(
+    const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq, int K,
+    float* __restrict__ scratch, long long N) {
+    constexpr int H = kLarge, NI = kLarge;
+    __shared__ double das[kLarge][kGradsMaxK];  // dL/da of the row, unit-major
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const long long b = blockIdx.x;
+    float* row = scratch + b * N;
+    static_assert(kThreads == kLarge, "one thread per unit");
+    const unsigned* tq = reinterpret_cast<const unsigned*>(row + N - 2LL * K * H);
+    double gb = 0.0;
+    for (int kk = K - 1; kk >= 0; --kk) {  // db in the order of the per-step accumulation
+        const long long q = 2 * ((long long)kk * H + t);
+        const double dv = __builtin_bit_cast(double, ((unsigned long long)tq[q + 1] << 32) | tq[q]);
+        das[t][kk] = dv;
+        gb += dv;
+    }
+    for (int kk = K; kk < kGradsMaxK; ++kk) das[t][kk] = 0.0;
+    const double gw_t = reinterpret_cast<const double*>(row)[t];
+    // this lane's four columns of [x_k | h_k-1] for every step: waves 0 and
+    // 2 hold x (dW_in), waves 1 and 3 hold h_prev (dW_rec)
+    const int part = wave & 1, c = 4 * lane;
+    double z[kGradsMaxK][4];
+#pragma unroll
+    for (int k = 0; k < kGradsMaxK; ++k) {
+        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (k < K) {
+            const float* src = part == 0 ? x + (b * K + k) * NI + c
+                                         : (k == 0 ? h0 + b * H + c : h_seq + (b * K + k - 1) * H + c);
+            v = *reinterpret_cast<const f32x4*>(src);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) z[k][m] = v[m];
+    }
+    __syncthreads();  // every read of the row's head and tail precedes every store
+    float* base = part == 0 ? row : row + (long long)H * NI;
+    // unit rows i = wave / 2 + 2 u, two per iteration
+#pragma unroll 1
+    for (int u = 0; u < H / 2; u += 2) {
+        double acc[2][4];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int i = (wave >> 1) + 2 * (u + p);
+            const double* d = das[i];
+            double dk[kGradsMaxK];
+#pragma unroll
+            for (int k = 0; k < kGradsMaxK; ++k) dk[k] = d[k];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                double a = dk[0] * z[0][m];
+#pragma unroll
+                for (int k = 1; k < kGradsMaxK; ++k) a = fma(dk[k], z[k][m], a);
+                acc[p][m] = a;
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int i = (wave >> 1) + 2 * (u + p);
+            __builtin_nontemporal_store(f32x4{(float)acc[p][0], (float)acc[p][1], (float)acc[p][2], (float)acc[p][3]},
+                                        reinterpret_cast<f32x4*>(base + (long long)i * H + c));
+        }
+    }
+    // db and dw_tau of unit t
+    row[(long long)H * (NI + H) + t] = (float)gb;
+    row[(long long)H * (NI + H) + H + t] = (float)gw_t;
+}
+
 // -------------------------------------------------------- reduce_axis0
 // A workgroup (4 waves) owns a tile of TW = LPR * VEC consecutive columns.  A
 // row of the tile is read by LPR consecutive lanes (VEC floats each: 256 or
@@ -2513,11 +2742,11 @@ void set_kernel_attributes() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<false, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<true, true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<false, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<true, false>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large32_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large32_kernel<true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         for (const void* f : {reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, false, false>),
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false, false>),
@@ -2594,11 +2823,17 @@ extern "C" int cfc_forward(const cfc_params_t* params, const float* x, const flo
                            n_in, H, h_seq, params->cell);
         return launch_status();
     }
+    if (large_full(params)) {
+        const long long groups = ((long long)B + kLR2 - 1) / kLR2;
+        hipLaunchKernelGGL(cfc_fwd_large32_kernel<false>, dim3((unsigned)groups), dim3(kThreads),
+                           large32_fwd_lds_bytes(), stream, params->w_in, params->w_rec, params->b, params->w_tau, x,
+                           h0, (double)dt, B, K, h_seq, params->cell, nullptr, 0LL);
+        return launch_status();
+    }
     const long long groups = ((long long)B + kLR - 1) / kLR;
-    auto kern = large_full(params) ? cfc_fwd_large_kernel<true, false> : cfc_fwd_large_kernel<false, false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kThreads), large_fwd_lds_bytes(), stream, params->w_in,
-                       params->w_rec, params->b, params->w_tau, x, h0, (double)dt, B, K, n_in, H, h_seq, params->cell,
-                       nullptr, 0LL);
+    hipLaunchKernelGGL((cfc_fwd_large_kernel<false, false>), dim3((unsigned)groups), dim3(kThreads),
+                       large_fwd_lds_bytes(), stream, params->w_in, params->w_rec, params->b, params->w_tau, x, h0,
+                       (double)dt, B, K, n_in, H, h_seq, params->cell, nullptr, 0LL);
     return launch_status();
 }
 
@@ -2782,10 +3017,14 @@ int forward_backward(const cfc_params_t* params, const float* x, const float* h0
         set_kernel_attributes();
         const long long groups = ((long long)B + kLR - 1) / kLR;
         const bool full = large_full(params), tau = params->cell == CFC_CELL_TAU_DECAY;
-        auto fwd = full ? cfc_fwd_large_kernel<true, true> : cfc_fwd_large_kernel<false, true>;
-        hipLaunchKernelGGL(fwd, dim3((unsigned)groups), dim3(kThreads), large_fwd_lds_bytes(), stream, params->w_in,
-                           params->w_rec, params->b, params->w_tau, x, h0, (double)dt, B, K, n_in, H, h_seq,
-                           params->cell, scratch, N);
+        if (full)
+            hipLaunchKernelGGL(cfc_fwd_large32_kernel<true>, dim3((unsigned)(((long long)B + kLR2 - 1) / kLR2)),
+                               dim3(kThreads), large32_fwd_lds_bytes(), stream, params->w_in, params->w_rec, params->b,
+                               params->w_tau, x, h0, (double)dt, B, K, h_seq, params->cell, scratch, N);
+        else
+            hipLaunchKernelGGL((cfc_fwd_large_kernel<false, true>), dim3((unsigned)groups), dim3(kThreads),
+                               large_fwd_lds_bytes(), stream, params->w_in, params->w_rec, params->b, params->w_tau, x,
+                               h0, (double)dt, B, K, n_in, H, h_seq, params->cell, scratch, N);
         rc = launch_status();
         if (rc) return rc;
         auto bwd1 = full ? (tau ? &cfc_bwd_large_kernel<true, true, true, 1> : &cfc_bwd_large_kernel<true, false, true, 1>)
@@ -2793,10 +3032,20 @@ int forward_backward(const cfc_params_t* params, const float* x, const float* h0
         auto bwd2 = full ? (tau ? &cfc_bwd_large_kernel<true, true, true, 2> : &cfc_bwd_large_kernel<true, false, true, 2>)
                          : (tau ? &cfc_bwd_large_kernel<false, true, true, 2> : &cfc_bwd_large_kernel<false, false, true, 2>);
         const BwdWindow win{K, 0, K, nullptr, grad_h0};
-        for (auto* bwd : {bwd1, bwd2})
+        // phase 2 on the vector units where it applies (256 x 256, K <= 8,
+        // x, h0, h_seq and the scratch 16-byte aligned for its float4 accesses)
+        const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+        const bool vgrads = full && K <= kGradsMaxK && al16(x) && al16(h0) && al16(h_seq) && al16(scratch);
+        for (auto* bwd : {bwd1, bwd2}) {
+            if (vgrads && bwd == bwd2) {
+                hipLaunchKernelGGL(cfc_bwd_large_grads_kernel, dim3((unsigned)B), dim3(kThreads), 0, stream, x, h0,
+                                   h_seq, K, scratch, N);
+                break;
+            }
             hipLaunchKernelGGL(bwd, dim3((unsigned)groups), dim3(kThreads), large_bwd_lds_bytes(), stream, params->w_in,
                                params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, win, n_in, H,
                                scratch, loss, grad_x, nullptr);
+        }
         return launch_status();
     }
     rc = cfc_forward(params, x, h0, dt, B, K, h_seq, stream);

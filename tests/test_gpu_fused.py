@@ -165,6 +165,10 @@ WIDE_PARKED = [
     (37, 7, 200, 256, 0.8, 53, "gated"),     # masked widths, ragged last group
     (17, 20, 256, 256, 0.6, 54, "gated"),    # the 16-row backward's K limit, one row in the last group
     (20, 9, 256, 200, 0.1, 55, "tau_decay"),
+    # exactly 256 x 256 with K <= 8: the 32-row forward and phase 2 on the
+    # vector units (one workgroup per row)
+    (33, 8, 256, 256, 0.7, 56, "gated"),     # a ragged last 32-row group
+    (21, 3, 256, 256, 0.3, 57, "tau_decay"),
 ]
 
 
