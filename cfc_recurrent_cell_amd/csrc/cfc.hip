@@ -327,9 +327,15 @@ __device__ __forceinline__ ChainLane chain_lane(int wave, int lane) {
 // 32-bit halves go through v_permlane16_swap, which exchanges a register's odd
 // rows with another's even rows).
 __device__ __forceinline__ void row_pair_values(double v, double& even, double& odd) {
+    // the swap overwrites both of its operands: a second copy of v, made by
+    // one 64-bit move (the empty asm keeps it a distinct register), instead
+    // of a 32-bit move per half
+    double w = v;
+    asm volatile("" : "+v"(w));
     const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
-    const auto lo = __builtin_amdgcn_permlane16_swap((unsigned)u, (unsigned)u, false, false);
-    const auto hi = __builtin_amdgcn_permlane16_swap((unsigned)(u >> 32), (unsigned)(u >> 32), false, false);
+    const unsigned long long uw = __builtin_bit_cast(unsigned long long, w);
+    const auto lo = __builtin_amdgcn_permlane16_swap((unsigned)u, (unsigned)uw, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((unsigned)(u >> 32), (unsigned)(uw >> 32), false, false);
     even = __builtin_bit_cast(double, ((unsigned long long)hi[0] << 32) | lo[0]);
     odd = __builtin_bit_cast(double, ((unsigned long long)hi[1] << 32) | lo[1]);
 }
@@ -419,10 +425,12 @@ __device__ __forceinline__ double exp_poly_scaled(double r, int n) {
     const double t0 = fma(s1, r4, s0);
     return ldexp(fma(s2, r8, t0), n);
 }
-__device__ __forceinline__ double exp_f64(double x) {
-    const double n = __builtin_rint(x * kLog2e);
-    return exp_poly_scaled(fma(-n, kLn2, x), (int)n);
-}
+// The reduction of both forms below: adding 1.5 * 2^52 to x log2e (one FMA
+// from x) rounds it to the nearest integer n, which then sits in the low bits
+// of the sum's significand (exact for |x log2e| < 2^51), so n = t - 1.5 * 2^52
+// and the integer exponent are read off the sum with no rounding or
+// float-to-int instruction.
+constexpr double kExpShift = 6755399441055744.0;  // 1.5 * 2^52
 
 // 1 / (1 + e^z) for finite z: |z| is clamped to 700 (beyond it the result is
 // 0 or 1 to double precision).  The reciprocal is v_rcp_f64 (24 correct bits,
@@ -432,21 +440,20 @@ __device__ __forceinline__ double exp_f64(double x) {
 // 1e80 for float32 inputs); inv_one_plus_exp_exact serves the others.
 __device__ __forceinline__ double inv_one_plus_exp(double z) {
     z = fmin(fmax(z, -700.0), 700.0);
-    const double d = 1.0 + exp_f64(z);
+    const double t = fma(z, kLog2e, kExpShift);
+    const double n = t - kExpShift;
+    const int ni = (int)(unsigned)__builtin_bit_cast(unsigned long long, t);
+    const double d = 1.0 + exp_poly_scaled(fma(-n, kLn2, z), ni);
     const double y = __builtin_amdgcn_rcp(d);
     const double e = fma(-d, y, 1.0);
     return fma(y, e, y);
 }
 
 // 1 / (1 + e^(m a)) for any a, with m_log2e = m log2e: NaN in, NaN out.
-// z = m a and t = fma(m_log2e, a, 1.5 * 2^52) are formed side by side; adding
-// 1.5 * 2^52 rounds z log2e to the nearest integer n, which then sits in the
-// low bits of t's significand (exact for |z log2e| < 2^51), so n = t - 1.5 * 2^52
-// and the integer exponent are read off t with no float-to-int conversion.
+// z = m a and t = fma(m_log2e, a, 1.5 * 2^52) are formed side by side.
 // Where |z| > 700 the result is 0 or 1 to double precision and is selected
 // after the evaluation (whose value is then unspecified); a NaN z fails that
 // comparison and comes out as NaN.
-constexpr double kExpShift = 6755399441055744.0;  // 1.5 * 2^52
 __device__ __forceinline__ double inv_one_plus_exp_exact(double m, double m_log2e, double a) {
     const double z = m * a;
     const double t = fma(m_log2e, a, kExpShift);
