@@ -1879,23 +1879,43 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large32_kernel(
             xn[m] = (k + 1 < K && b < B) ? x[(b * K + k + 1) * (long long)NI + j] : 0.f;
         }
         __syncthreads();  // every wave is done reading zx / zh of step k
+        // a lane's four tiles hold units 4 m + tb (tb = 0..3) of a row: four
+        // consecutive doubles of its parked a_k, stored as two 16-byte
+        // halves, so the four k-slots of a row fill whole 128-byte lines
+        // (one 8-byte store per value wrote twice the bytes to HBM)
+        const bool park_vec = (reinterpret_cast<uintptr_t>(a_park) & 15) == 0;
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int v = 0; v < 4; ++v) {
+                const int rr = 16 * rt + r;
+                double av[4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int i = lunit(wave, tb, s + 4 * v), rr = 16 * rt + r;
-                    const double a = acc[tb][rt][v] + ubias[i];
-                    if constexpr (PARK) {
-                        if (r0 + rr < B) reinterpret_cast<double*>(a_park + (r0 + rr) * N)[(long long)k * H + i] = a;
+                for (int tb = 0; tb < 4; ++tb) av[tb] = acc[tb][rt][v] + ubias[lunit(wave, tb, s + 4 * v)];
+                if constexpr (PARK) {
+                    if (r0 + rr < B) {
+                        double* dst = reinterpret_cast<double*>(a_park + (r0 + rr) * N) + (long long)k * H +
+                                      lunit(wave, 0, s + 4 * v);
+                        if (park_vec) {
+                            reinterpret_cast<double2*>(dst)[0] = make_double2(av[0], av[1]);
+                            reinterpret_cast<double2*>(dst)[1] = make_double2(av[2], av[3]);
+                        } else {
+#pragma unroll
+                            for (int tb = 0; tb < 4; ++tb) dst[tb] = av[tb];
+                        }
                     }
+                }
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const int i = lunit(wave, tb, s + 4 * v);
+                    const double a = av[tb];
                     const double sp = uspdt[i];
                     const double gt = cell == CFC_CELL_TAU_DECAY ? sp : inv_one_plus_exp_exact(sp, sp * kLog2e, a);
                     const double c = fma(-2.0, inv_one_plus_exp_exact(2.0, 2.0 * kLog2e, a), 1.0);
                     double* hp = zh + zidx2(i, rr);
                     *hp = fma(gt, *hp - c, c);  // g*h + (1-g)*c
                 }
+            }
 #pragma unroll
         for (int m = 0; m < kLR2; ++m) {
             const int e = t + kThreads * m;
@@ -2012,6 +2032,23 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     auto fetch_a = [&](int k) {
         if constexpr (PARKED) {
             const double* ap = reinterpret_cast<const double*>(scratch + b_own * N) + (k0 + k) * (long long)H;
+            if (FULL && (reinterpret_cast<uintptr_t>(scratch) & 15) == 0) {
+                // units lunit(wave, 0..3, m) are four consecutive doubles
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    double2 lo = make_double2(0.0, 0.0), hi = make_double2(0.0, 0.0);
+                    if (row_ok) {
+                        const double2* q = reinterpret_cast<const double2*>(ap + lunit(wave, 0, s + 4 * v));
+                        lo = q[0];
+                        hi = q[1];
+                    }
+                    apre[0][v] = lo.x;
+                    apre[1][v] = lo.y;
+                    apre[2][v] = hi.x;
+                    apre[3][v] = hi.y;
+                }
+                return;
+            }
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
