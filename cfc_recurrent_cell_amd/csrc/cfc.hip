@@ -1765,6 +1765,39 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
     }
 }
 
+// The one-call path at exactly 256 x 256 reads its weights as float64 when
+// B >= 4: a short kernel widens [W_in ; W_rec] once per call into the middle
+// of scratch rows 0..3, which no other kernel of the call touches before the
+// weight-gradient phase rewrites those rows.  Quarter q (row q, floats
+// [off, off + 65536) with off = 2 K H, between the parked a_k in the head and
+// the parked dL/da in the tail) holds unit rows 128 (q & 1) .. 128 (q & 1) +
+// 127 of W_in (q < 2) or W_rec (q >= 2), row-major, in float64.  The
+// products then need no float32 -> float64 conversion per operand; vector
+// instructions stall the f64 matrix cores of their SIMD (measured on MI355X:
+// the forward 0.43 -> 0.41 ms and phase 1 0.30 -> 0.28 ms at B = 8192, K = 8).
+constexpr long long kWideElems = 2LL * kLarge * kLarge;
+__global__ __launch_bounds__(kThreads) void widen_weights_kernel(const float* __restrict__ w_in,
+                                                                 const float* __restrict__ w_rec,
+                                                                 float* __restrict__ wide, long long N) {
+    const int e = blockIdx.x * kThreads + threadIdx.x;  // grid: kWideElems / kThreads
+    const int g = e >> 16, u = (e >> 8) & 255, j = e & 255;
+    const float v = g == 0 ? w_in[e & 65535] : w_rec[e & 65535];
+    reinterpret_cast<double*>(wide + (long long)(2 * g + (u >> 7)) * N)[(u & 127) * kLarge + j] = (double)v;
+}
+// unit row u of W_in (g = 0) or W_rec (g = 1) in the widened copy
+__device__ __forceinline__ const double* wide_row(const float* wide, long long N, int g, int u) {
+    return reinterpret_cast<const double*>(wide + (long long)(2 * g + (u >> 7)) * N) + (u & 127) * kLarge;
+}
+// four consecutive weights of one unit row, as the products take them
+struct W4f {
+    float4 v;
+    __device__ double get(int cc) const { return (double)f4_get(v, cc); }
+};
+struct W4d {
+    double2 lo, hi;
+    __device__ double get(int cc) const { return cc == 0 ? lo.x : cc == 1 ? lo.y : cc == 2 ? hi.x : hi.y; }
+};
+
 // Thirty-two rows per workgroup, for exactly 256 x 256 with 16-byte-aligned
 // weights.  Each weight operand (a float4 load and its widening) then feeds
 // the products of two 16-row tiles, so the widenings per matrix-core product
@@ -1773,17 +1806,19 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
 // instruction between two products adds 13 cycles or more), so the widenings
 // set the product loop's pace.  [x_k ; h_k] of the 32 rows is staged as in
 // the 16-row kernel, in [256][32] arrays swizzled within each row of 32.
-// PARK as in cfc_fwd_large_kernel.
+// PARK as in cfc_fwd_large_kernel.  W64: the weights come from the widened
+// float64 copy `wide` (scratch row 0 + 2 K H floats, see widen_weights_kernel).
 constexpr int kLR2 = 32;  // batch rows per workgroup of the 32-row forward
 __device__ __forceinline__ int zidx2(int j, int r) { return j * kLR2 + (r ^ (j & 31)); }
 __host__ __device__ constexpr size_t large32_fwd_lds_bytes() {
     return (size_t)4 * kLarge * kLR2 + (size_t)8 * kLarge * kLR2 + (size_t)8 * 2 * kLarge;
 }
-template <bool PARK>
+template <bool PARK, bool W64>
 __global__ __launch_bounds__(kThreads) void cfc_fwd_large32_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec, const float* __restrict__ bias,
     const float* __restrict__ w_tau, const float* __restrict__ x, const float* __restrict__ h0, double dt, int B,
-    int K, float* __restrict__ h_seq, int cell, float* __restrict__ a_park, long long N) {
+    int K, float* __restrict__ h_seq, int cell, float* __restrict__ a_park, long long N,
+    const float* __restrict__ wide) {
     constexpr int H = kLarge, NI = kLarge;
     extern __shared__ __align__(16) unsigned char smem[];
     float* zx = reinterpret_cast<float*>(smem);                          // [256][32] x_k
@@ -1836,21 +1871,18 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large32_kernel(
             for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) off[p][cc][rt] = zidx2(16 * p + 4 * s + cc, 16 * rt + r);
+        // half g of the contraction; load(tb, jq) gives the four weights of
+        // chunk group jq for tile tb (float32 or the widened float64 copy)
+        auto half = [&](const int g, auto load) {
+            decltype(load(0, 0)) w4[4];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            const float* wbase = g == 0 ? w_in : w_rec;
-            const float* wrow[4];
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) wrow[tb] = wbase + lunit(wave, tb, r) * H;
-            float4 w4[4];
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) w4[tb] = *reinterpret_cast<const float4*>(wrow[tb] + 4 * s);
+            for (int tb = 0; tb < 4; ++tb) w4[tb] = load(tb, 0);
 #pragma unroll 4
             for (int jq = 0; jq < 16; ++jq) {
-                float4 nw4[4];
+                decltype(load(0, 0)) nw4[4];
                 const int jn = jq + 1 < 16 ? jq + 1 : jq;  // the next chunk group's weights
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb) nw4[tb] = *reinterpret_cast<const float4*>(wrow[tb] + 16 * jn + 4 * s);
+                for (int tb = 0; tb < 4; ++tb) nw4[tb] = load(tb, jn);
                 const int base = 1024 * (jq >> 1), par = jq & 1;
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) {
@@ -1860,13 +1892,33 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large32_kernel(
                         bz[rt] = g == 0 ? (double)zx[base + off[par][cc][rt]] : zh[base + off[par][cc][rt]];
 #pragma unroll
                     for (int tb = 0; tb < 4; ++tb) {
-                        const double wa = (double)f4_get(w4[tb], cc);
+                        const double wa = w4[tb].get(cc);
 #pragma unroll
                         for (int rt = 0; rt < 2; ++rt) acc[tb][rt] = mfma_f64(wa, bz[rt], acc[tb][rt]);
                     }
                 }
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) w4[tb] = nw4[tb];
+            }
+        };
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            if constexpr (W64) {
+                const double* wrow[4];
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) wrow[tb] = wide_row(wide, N, g, lunit(wave, tb, r));
+                half(g, [&](int tb, int jq) {
+                    const double2* q = reinterpret_cast<const double2*>(wrow[tb] + 16 * jq + 4 * s);
+                    return W4d{q[0], q[1]};
+                });
+            } else {
+                const float* wbase = g == 0 ? w_in : w_rec;
+                const float* wrow[4];
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) wrow[tb] = wbase + lunit(wave, tb, r) * H;
+                half(g, [&](int tb, int jq) {
+                    return W4f{*reinterpret_cast<const float4*>(wrow[tb] + 16 * jq + 4 * s)};
+                });
             }
         }
         // next step's x, loaded after the product's weight loads and written
@@ -1950,7 +2002,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
     const float* __restrict__ y, double dt, int B, BwdWindow win, int n_in, int H, float* __restrict__ scratch,
-    float* __restrict__ loss, float* __restrict__ grad_x, unsigned* __restrict__ ws) {
+    float* __restrict__ loss, float* __restrict__ grad_x, unsigned* __restrict__ ws, const float* __restrict__ wide) {
     static_assert(!ACC || (!PARKED && STAGE == 0), "accumulate mode recomputes a_k and runs both phases");
     constexpr int cell = TAU ? CFC_CELL_TAU_DECAY : CFC_CELL_GATED;
     const int K = win.Kw;  // steps of this launch; indices below are relative to win.k0
@@ -2066,12 +2118,54 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     // are one float4.  The float4 operands are double-buffered PF chunks
     // ahead, so their L2 latency hides under the previous chunks' products
     // (PF = 4 where the registers allow it, else 2); the next step's inputs
-    // are fetched after the last of them if asked.
+    // are fetched after the last of them if asked.  With `wide` (FULL phase 1
+    // of the parked path) the operands come from the widened float64 copy of
+    // M (g = 0: W_in, 1: W_rec) as two double2 loads, with no conversions.
     constexpr int PF = FULL ? 4 : 2;
-    auto dab_product = [&](const float* __restrict__ wm, int ld, int width, dbl4 (&accp)[4], bool fetch_next,
-                           int k) {
+    auto dab_product = [&](const float* __restrict__ wm, int g, int ld, int width, dbl4 (&accp)[4],
+                           bool fetch_next, int k) {
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) accp[tb] = dbl4{0.0, 0.0, 0.0, 0.0};
+        if constexpr (FULL && PARKED && STAGE == 1) {
+            if (wide) {
+                // chunk ic of k-slot s is unit row i = 64 s + ic: the lane's
+                // quarter of the copy is fixed (i >> 7 = s >> 1)
+                const double* wq = wide_row(wide, N, g, 64 * s) + jw;
+                auto wld64 = [&](int ic) -> W4d {
+                    const double2* q = reinterpret_cast<const double2*>(wq + ic * kLarge);
+                    return W4d{q[0], q[1]};
+                };
+                auto chunks64 = [&](const W4d (&w)[PF], int icb) {
+#pragma unroll
+                    for (int u = 0; u < PF; ++u) {
+                        const double bz = dab[zidx(64 * s + icb + u, r)];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) accp[q] = mfma_f64(w[u].get(q), bz, accp[q]);
+                    }
+                };
+                W4d va[PF], vb[PF];
+#pragma unroll
+                for (int u = 0; u < PF; ++u) va[u] = wld64(u);
+#pragma unroll 1
+                for (int ic0 = 0; ic0 < 64 - 2 * PF; ic0 += 2 * PF) {
+#pragma unroll
+                    for (int u = 0; u < PF; ++u) vb[u] = wld64(ic0 + PF + u);
+                    chunks64(va, ic0);
+#pragma unroll
+                    for (int u = 0; u < PF; ++u) va[u] = wld64(ic0 + 2 * PF + u);
+                    chunks64(vb, ic0 + PF);
+                }
+#pragma unroll
+                for (int u = 0; u < PF; ++u) vb[u] = wld64(64 - PF + u);
+                chunks64(va, 64 - 2 * PF);
+                if (fetch_next) {
+                    fetch_step(k - 1);
+                    fetch_a(k - 1);
+                }
+                chunks64(vb, 64 - PF);
+                return;
+            }
+        }
         auto wld = [&](int ic) -> float4 {
             const int i = 64 * s + ic;
             if constexpr (FULL) return *reinterpret_cast<const float4*>(wm + (long long)i * kLarge + jw);
@@ -2175,7 +2269,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
         if (k > 0 || grad_h0) {
             // delta_k = delta_k+1 * g + W_rec^T dL/da
             dbl4 acc2[4];
-            dab_product(w_rec, H, H, acc2, k > 0 && !grad_x, k);
+            dab_product(w_rec, 1, H, H, acc2, k > 0 && !grad_x, k);
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
@@ -2186,7 +2280,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
             // dL/dx_k = W_in^T dL/da, the same product with W_in's rows; the
             // lane's elements are column lunit(wave, tb, s + 4v) of row r
             dbl4 acc3[4];
-            dab_product(w_in, n_in, n_in, acc3, k > 0, k);
+            dab_product(w_in, 0, n_in, n_in, acc3, k > 0, k);
             if (row_ok) {
                 float* gx = grad_x + (b_own * Kf + k0 + k) * n_in;
 #pragma unroll
@@ -2788,10 +2882,10 @@ void set_kernel_attributes() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large_kernel<false, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large32_kernel<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_fwd_large32_kernel<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        for (const void* f : {reinterpret_cast<const void*>(&cfc_fwd_large32_kernel<false, false>),
+                              reinterpret_cast<const void*>(&cfc_fwd_large32_kernel<true, false>),
+                              reinterpret_cast<const void*>(&cfc_fwd_large32_kernel<true, true>)})
+            (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         for (const void* f : {reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, false, false>),
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false, false>),
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, true, false>),
@@ -2869,9 +2963,9 @@ extern "C" int cfc_forward(const cfc_params_t* params, const float* x, const flo
     }
     if (large_full(params)) {
         const long long groups = ((long long)B + kLR2 - 1) / kLR2;
-        hipLaunchKernelGGL(cfc_fwd_large32_kernel<false>, dim3((unsigned)groups), dim3(kThreads),
+        hipLaunchKernelGGL((cfc_fwd_large32_kernel<false, false>), dim3((unsigned)groups), dim3(kThreads),
                            large32_fwd_lds_bytes(), stream, params->w_in, params->w_rec, params->b, params->w_tau, x,
-                           h0, (double)dt, B, K, h_seq, params->cell, nullptr, 0LL);
+                           h0, (double)dt, B, K, h_seq, params->cell, nullptr, 0LL, nullptr);
         return launch_status();
     }
     const long long groups = ((long long)B + kLR - 1) / kLR;
@@ -2965,7 +3059,7 @@ int backward_window(const cfc_params_t* params, const float* x, const float* h0,
                                : &cfc_bwd_large_kernel<false, false, false, 0, true>);
         hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kThreads), lds, stream, params->w_in, params->w_rec,
                            params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, win, n_in, H, scratch, loss,
-                           grad_x, ws_used ? static_cast<unsigned*>(workspace) : nullptr);
+                           grad_x, ws_used ? static_cast<unsigned*>(workspace) : nullptr, nullptr);
         return launch_status();
     }
     hipLaunchKernelGGL(cfc_bwd_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
@@ -3061,11 +3155,22 @@ int forward_backward(const cfc_params_t* params, const float* x, const float* h0
         set_kernel_attributes();
         const long long groups = ((long long)B + kLR - 1) / kLR;
         const bool full = large_full(params), tau = params->cell == CFC_CELL_TAU_DECAY;
-        if (full)
-            hipLaunchKernelGGL(cfc_fwd_large32_kernel<true>, dim3((unsigned)(((long long)B + kLR2 - 1) / kLR2)),
+        const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+        // float64 weights for the 256 x 256 products, in the middle of
+        // scratch rows 0..3 (16-byte aligned for their double2 loads)
+        const bool use_wide = full && B >= 4 && al16(scratch) && N % 4 == 0 && 4LL * K * H + kWideElems / 2 <= N;
+        float* wide = use_wide ? scratch + 2LL * K * H : nullptr;
+        if (use_wide) {
+            hipLaunchKernelGGL(widen_weights_kernel, dim3((unsigned)(kWideElems / kThreads)), dim3(kThreads), 0,
+                               stream, params->w_in, params->w_rec, wide, N);
+            hipLaunchKernelGGL((cfc_fwd_large32_kernel<true, true>), dim3((unsigned)(((long long)B + kLR2 - 1) / kLR2)),
                                dim3(kThreads), large32_fwd_lds_bytes(), stream, params->w_in, params->w_rec, params->b,
-                               params->w_tau, x, h0, (double)dt, B, K, h_seq, params->cell, scratch, N);
-        else
+                               params->w_tau, x, h0, (double)dt, B, K, h_seq, params->cell, scratch, N, wide);
+        } else if (full) {
+            hipLaunchKernelGGL((cfc_fwd_large32_kernel<true, false>), dim3((unsigned)(((long long)B + kLR2 - 1) / kLR2)),
+                               dim3(kThreads), large32_fwd_lds_bytes(), stream, params->w_in, params->w_rec, params->b,
+                               params->w_tau, x, h0, (double)dt, B, K, h_seq, params->cell, scratch, N, nullptr);
+        } else
             hipLaunchKernelGGL((cfc_fwd_large_kernel<false, true>), dim3((unsigned)groups), dim3(kThreads),
                                large_fwd_lds_bytes(), stream, params->w_in, params->w_rec, params->b, params->w_tau, x,
                                h0, (double)dt, B, K, n_in, H, h_seq, params->cell, scratch, N);
@@ -3078,7 +3183,6 @@ int forward_backward(const cfc_params_t* params, const float* x, const float* h0
         const BwdWindow win{K, 0, K, nullptr, grad_h0};
         // phase 2 on the vector units where it applies (256 x 256, K <= 8,
         // x, h0, h_seq and the scratch 16-byte aligned for its float4 accesses)
-        const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
         const bool vgrads = full && K <= kGradsMaxK && al16(x) && al16(h0) && al16(h_seq) && al16(scratch);
         for (auto* bwd : {bwd1, bwd2}) {
             if (vgrads && bwd == bwd2) {
@@ -3088,7 +3192,7 @@ int forward_backward(const cfc_params_t* params, const float* x, const float* h0
             }
             hipLaunchKernelGGL(bwd, dim3((unsigned)groups), dim3(kThreads), large_bwd_lds_bytes(), stream, params->w_in,
                                params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, win, n_in, H,
-                               scratch, loss, grad_x, nullptr);
+                               scratch, loss, grad_x, nullptr, bwd == bwd1 ? wide : nullptr);
         }
         return launch_status();
     }

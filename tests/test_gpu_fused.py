@@ -169,6 +169,10 @@ WIDE_PARKED = [
     # vector units (one workgroup per row)
     (33, 8, 256, 256, 0.7, 56, "gated"),     # a ragged last 32-row group
     (21, 3, 256, 256, 0.3, 57, "tau_decay"),
+    # the float64 weight copy lives in scratch rows 0..3: B = 4 is the
+    # fewest rows that hold it, B = 3 reads the float32 weights
+    (4, 5, 256, 256, 0.5, 58, "gated"),
+    (3, 6, 256, 256, 0.5, 59, "tau_decay"),
 ]
 
 
