@@ -1769,8 +1769,8 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
 // B >= 4: a short kernel widens [W_in ; W_rec] once per call into the middle
 // of scratch rows 0..3, which no other kernel of the call touches before the
 // weight-gradient phase rewrites those rows.  Quarter q (row q, floats
-// [off, off + 65536) with off = 2 K H, between the parked a_k in the head and
-// the parked dL/da in the tail) holds unit rows 128 (q & 1) .. 128 (q & 1) +
+// [off, off + 65536) with off = 2 K H, between the parked values in the head
+// and the dL/dw_tau sums in the last 2 H floats) holds unit rows 128 (q & 1) .. 128 (q & 1) +
 // 127 of W_in (q < 2) or W_rec (q >= 2), row-major, in float64.  The
 // products then need no float32 -> float64 conversion per operand; vector
 // instructions stall the f64 matrix cores of their SIMD (measured on MI355X:
@@ -1989,9 +1989,10 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large32_kernel(
 // is not staged; the window is then the whole sequence.
 // STAGE 0 runs both phases.  The parked path runs them as two launches, so
 // that each gets the compiler's register allocation to itself: STAGE 1 runs
-// phase 1 and leaves each row's dL/dw_tau sums (float64) in the head of its
-// scratch row, where the a_k it has consumed were; STAGE 2 runs phase 2 and
-// reads them back before the row's dW_in overwrites them.
+// phase 1, parks each dL/da_k over the a_k it has consumed and leaves each
+// row's dL/dw_tau sums (float64) in the last 2 H floats of its scratch row;
+// STAGE 2 runs phase 2 and reads both back before the row's gradient
+// overwrites them.
 // ACC (accumulate mode, STAGE 0, not PARKED): the scratch rows are read and
 // the gradient, rounded to float32, is added in float32; dL/da is parked in
 // the caller's workspace `ws` (2 K H 32-bit words per row) instead of the
@@ -2022,10 +2023,14 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const long long N = (long long)H * (n_in + H + 2);
     const long long b_own = r0 + r;
     const bool row_ok = b_own < B;
-    // dL/da of every step is parked in the tail of its row's scratch (as two
-    // 32-bit halves per double) until the row's weight gradients are formed;
-    // every element there is rewritten afterwards.  ACC parks it in ws.
-    const long long tmp_off = N - 2LL * K * H;
+    // dL/da of every step is parked in its row's scratch (as two 32-bit halves
+    // per double) until the row's weight gradients are formed; every element
+    // there is rewritten afterwards.  PARKED: in the head, each dL/da_k over
+    // the a_k it was formed from (read one step earlier), so the call's parked
+    // values occupy one 2 K H-float region per row instead of two and fit the
+    // memory-side cache better; recomputing kernels: in the tail.  ACC parks
+    // it in ws.
+    const long long tmp_off = PARKED ? 0 : N - 2LL * K * H;
     auto park_row = [&](long long b) -> unsigned* {
         if constexpr (ACC) return ws + b * (2LL * K * H);
         else return reinterpret_cast<unsigned*>(scratch + b * N + tmp_off);
@@ -2292,7 +2297,8 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                     }
             }
         }
-        // park dL/da_k of the 16 rows in their scratch tails, row-contiguous
+        // park dL/da_k of the 16 rows (PARKED: over a_k, in the heads; else in
+        // the tails), row-contiguous
         // (after the products, so that their weight loads' waits do not
         // cover these stores)
 #pragma unroll 4
@@ -2323,7 +2329,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
         for (int e = t; e < kLR * kLarge; e += kThreads) {
             const int rr = e / kLarge, u = e % kLarge;
             const long long b = r0 + rr;
-            if (b < B && u < H) reinterpret_cast<double*>(scratch + b * N)[u] = gwt[zidx(u, rr)];
+            if (b < B && u < H) reinterpret_cast<double*>(scratch + b * N + N - 2LL * H)[u] = gwt[zidx(u, rr)];
         }
         return;
     }
@@ -2343,12 +2349,12 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     float* gst = reinterpret_cast<float*>(smem + large_bwd_lds_bytes() - (size_t)4 * 4 * 16 * kLargeGS) +
                  wave * 16 * kLargeGS;  // this wave's [16][kLargeGS] tile buffer
     // operands of one row, fetched into registers one row ahead: thread t
-    // holds dL/da_kk[t] (from the parked tail), x_kk[t] and h_kk-1[t]
+    // holds dL/da_kk[t] (parked by phase 1), x_kk[t] and h_kk-1[t]
     double pd[kLargeBwdMaxK];
     float px[kLargeBwdMaxK], ph[kLargeBwdMaxK];
-    double pg = 0.0;  // STAGE 2: dL/dw_tau of unit t, from the row's head
+    double pg = 0.0;  // STAGE 2: dL/dw_tau of unit t, from the row's last 2 H floats
     auto fetch_row = [&](long long b) {
-        if constexpr (STAGE == 2) pg = t < H ? reinterpret_cast<const double*>(scratch + b * N)[t] : 0.0;
+        if constexpr (STAGE == 2) pg = t < H ? reinterpret_cast<const double*>(scratch + b * N + N - 2LL * H)[t] : 0.0;
         const unsigned* tq = park_row(b);
 #pragma unroll
         for (int kk = 0; kk < kLargeBwdMaxK; ++kk) {
@@ -2596,9 +2602,9 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
 // other shapes) needs a transpose through LDS per 16 x 64 tile and converts
 // its accumulators tile by tile; at K = 8 that measured 0.90 ms for the
 // 4.3 GB scratch of B = 8192, of which 0.67 ms without its stores.
-// Inputs: dL/da parked in the tail of the row's scratch by phase 1 (two 32-bit
-// halves per double, [k][unit]) and the dL/dw_tau sums in its head (float64);
-// both are read before the barrier that precedes the first store.
+// Inputs: dL/da parked in the head of the row's scratch by phase 1 (two 32-bit
+// halves per double, [k][unit]) and the dL/dw_tau sums in its last 2 H floats
+// (float64); both are read before the barrier that precedes the first store.
 constexpr int kGradsMaxK = 8;
 __global__ __launch_bounds__(kThreads) void cfc_bwd_large_grads_kernel(
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq, int K,
@@ -2609,7 +2615,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_grads_kernel(
     const long long b = blockIdx.x;
     float* row = scratch + b * N;
     static_assert(kThreads == kLarge, "one thread per unit");
-    const unsigned* tq = reinterpret_cast<const unsigned*>(row + N - 2LL * K * H);
+    const unsigned* tq = reinterpret_cast<const unsigned*>(row);
     double gb = 0.0;
     for (int kk = K - 1; kk >= 0; --kk) {  // db in the order of the per-step accumulation
         const long long q = 2 * ((long long)kk * H + t);
@@ -2618,7 +2624,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_grads_kernel(
         gb += dv;
     }
     for (int kk = K; kk < kGradsMaxK; ++kk) das[t][kk] = 0.0;
-    const double gw_t = reinterpret_cast<const double*>(row)[t];
+    const double gw_t = reinterpret_cast<const double*>(row + N - 2LL * H)[t];
     // this lane's four columns of [x_k | h_k-1] for every step: waves 0 and
     // 2 hold x (dW_in), waves 1 and 3 hold h_prev (dW_rec)
     const int part = wave & 1, c = 4 * lane;
@@ -3146,10 +3152,10 @@ int forward_backward(const cfc_params_t* params, const float* x, const float* h0
     const size_t lds = small_bwd ? small_bwd_lds_bytes() : large ? large_bwd_lds_bytes() : bwd_lds_bytes(K, n_in, H);
     if (lds > kLdsBytes) return CFC_ERR_UNSUPPORTED;
     // 16-row kernels in overwrite mode: the forward parks a_k (float64) in the
-    // head of each scratch row and the backward reads it back instead of
-    // recomputing it (needs 8-byte-aligned rows; the head [0, 2KH) and the
-    // backward's parked dL/da in the tail [N - 2KH, N) are disjoint because
-    // 4K <= n_in + H + 2 at these widths and K)
+    // head [0, 2KH) of each scratch row and the backward reads it back instead
+    // of recomputing it, parking dL/da_k over a_k (needs 8-byte-aligned rows;
+    // the head and the dL/dw_tau sums in [N - 2H, N) are disjoint, and so is
+    // the widened weight copy between them, because 4KH <= N here)
     if (large && flags == CFC_OVERWRITE && N % 2 == 0 && (reinterpret_cast<uintptr_t>(scratch) & 7) == 0 &&
         4LL * K * H <= N) {
         set_kernel_attributes();
