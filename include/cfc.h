@@ -243,7 +243,11 @@ int cfc_backward_window_ws(const cfc_params_t *params, const float *x, const flo
  * aligned) run three launches on `stream`: a forward that also parks its
  * float64 pre-activations in the head of each scratch row, then a backward in
  * two stages (the reverse pass, then the weight gradients) that reads them back
- * instead of recomputing them.  Other shapes run cfc_forward and cfc_backward
+ * instead of recomputing them.  At exactly 256 x 256 with B >= 4 and a
+ * 16-byte-aligned scratch, a fourth, first launch copies the weights to
+ * float64 into scratch rows 0..3 for the forward and the reverse pass.  The
+ * scratch thus serves as the call's temporary storage; every element holds
+ * its gradient when the call's work completes.  Other shapes run cfc_forward and cfc_backward
  * as two launches on `stream`.  In both cases the backward's limits are checked
  * first, so nothing is enqueued when either direction would be refused.
  * Returns a CFC_* status; the same argument rules as the two calls, and no
