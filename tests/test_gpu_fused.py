@@ -272,3 +272,40 @@ def test_fused_whole_shape_instance_matches_generic(cell):
     assert_close(outs[0][0], ref["h_seq"], cell + " h_seq")
     assert_close(outs[0][1], ref["scratch"], cell + " scratch")
     assert_close(outs[0][2], ref["loss"], cell + " loss")
+
+
+@pytest.mark.parametrize("cell", ["gated", "tau_decay"])
+def test_fused_256_dispatch_variants(cell):
+    """At exactly 256 x 256, K <= 8 the one-call entry picks its kernels by
+    alignment: the float64 weight copy needs a 16-byte-aligned scratch, the
+    vector-unit weight-gradient phase also 16-byte-aligned x, h0 and h_seq.
+    With x one float off alignment (weight copy, matrix-core phase 2) and
+    with the scratch two floats off (float32 weights, matrix-core phase 2)
+    every output must be bitwise the same -- the widening is exact and the
+    phase-2 kernel is the same -- and each variant within tolerance of the
+    oracle, including the all-aligned one (weight copy, vector phase 2)."""
+    import torch
+    import cfc_recurrent_cell_amd as C
+    B, K, n = 37, 8, 256
+    inp = W.make_random_cfc_inputs(B, K, n, n, 0.7, 61, cell=cell)
+    d = to_dev(inp)
+    N = W.scratch_row_len(n, n)
+    xbuf = torch.empty(B * K * n + 1, device="cuda")
+    x_off = xbuf[1:].view(B, K, n)
+    x_off.copy_(d["x"])
+    sbuf = torch.full((B * N + 2,), float("nan"), device="cuda")
+    s_off = sbuf[2:].view(B, N)
+    assert x_off.data_ptr() % 16 == 4 and s_off.data_ptr() % 16 == 8 and d["x"].data_ptr() % 16 == 0
+    say(f"[fused] 256x256 dispatch variants, {cell}")
+    outs = {}
+    for name, xx, sc in (("aligned", d["x"], None), ("x_off", x_off, None), ("scratch_off", d["x"], s_off)):
+        h, s, l, gx, gh = C.cfc_forward_backward(d["w_in"], d["w_rec"], d["b"], d["w_tau"], xx, d["h0"], d["y"],
+                                                 d["dt"], scratch=sc, input_grads=True, cell=cell)
+        outs[name] = [host(t) for t in (h, s, l, gx, gh)]
+    for name, a, b_ in zip(("h_seq", "scratch", "loss", "grad_x", "grad_h0"), outs["x_off"], outs["scratch_off"]):
+        assert np.array_equal(a.view(np.uint32), b_.view(np.uint32)), f"{cell}: {name} differs"
+    ref = O.cfc_step(inp, threads=oracle_threads(), input_grads=True)
+    for variant, o in outs.items():
+        assert np.isfinite(o[1]).all(), variant
+        for got, name in zip(o, ("h_seq", "scratch", "loss", "grad_x", "grad_h0")):
+            assert_close(got, ref[name], f"{cell} {variant} {name}")
