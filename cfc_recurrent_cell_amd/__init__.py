@@ -20,8 +20,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = ["cfc_forward", "cfc_backward", "cfc_backward_window", "cfc_backward_windows",
            "cfc_backward_workspace", "cfc_forward_backward", "reduce_axis0", "reduce_axis0_noalloc",
-           "reduce_axis0_split_workspace", "reduce_axis0_banded_workspace", "cfc_scratch_row_len", "CfcError",
-           "load_library"]
+           "reduce_axis0_split_workspace", "cfc_scratch_row_len", "CfcError", "load_library"]
 
 
 def cfc_scratch_row_len(n_in: int, n_hid: int) -> int:
@@ -293,7 +292,7 @@ def cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt: float, h_seq=None,
 
 
 def reduce_axis0(per_batch, out=None, stream=None, leading_axes: int = 1, split: bool = False,
-                 workspace=None, banded: bool = False):
+                 workspace=None):
     """Column sums over the leading axis (overwrites ``out``).
 
     ``per_batch`` is contiguous float32 on the GPU.  Its first ``leading_axes``
@@ -303,8 +302,7 @@ def reduce_axis0(per_batch, out=None, stream=None, leading_axes: int = 1, split:
     (sizing N from the wrong axes reads past the buffer; here both come from
     the tensor's shape).  ``out`` gets shape per_batch.shape[leading_axes:].
     ``split=True`` uses reduce_axis0_split (narrow rows over a long leading
-    axis), ``banded=True`` reduce_axis0_banded (wide rows in row bands); their
-    workspace is allocated here unless given as a uint8 tensor."""
+    axis); its workspace is allocated here unless given as a uint8 tensor."""
     import math
     import torch
     lib = load_library()
@@ -317,20 +315,18 @@ def reduce_axis0(per_batch, out=None, stream=None, leading_axes: int = 1, split:
         out = torch.empty(tail, dtype=torch.float32, device=per_batch.device)
     _dev_f32(out, "out", tail)
     s = _stream(per_batch.device, stream)
-    if split and banded:
-        raise ValueError("split and banded are two different reducers; pick one")
-    if not split and not banded:
+    if not split:
         _check("reduce_axis0", lib.reduce_axis0(per_batch.data_ptr(), B, N, out.data_ptr(), s))
         return out
-    name = "reduce_axis0_banded" if banded else "reduce_axis0_split"
-    need = int(getattr(lib, name + "_workspace")(B, N))
+    need = int(lib.reduce_axis0_split_workspace(B, N))
     if need < 0:
         raise ValueError(f"invalid reduce size B={B} N={N}")
     if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=per_batch.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(name, getattr(lib, name)(per_batch.data_ptr(), B, N, out.data_ptr(), ws_ptr, ws_bytes, s))
+    _check("reduce_axis0_split", lib.reduce_axis0_split(per_batch.data_ptr(), B, N, out.data_ptr(), ws_ptr,
+                                                        ws_bytes, s))
     return out
 
 
@@ -356,8 +352,3 @@ def reduce_axis0_noalloc(per_batch, out, stream=None, leading_axes: int = 1):
 def reduce_axis0_split_workspace(B: int, N: int) -> int:
     """Bytes of workspace reduce_axis0_split needs for [B, N] (0: none)."""
     return int(load_library().reduce_axis0_split_workspace(B, N))
-
-
-def reduce_axis0_banded_workspace(B: int, N: int) -> int:
-    """Bytes of workspace reduce_axis0_banded needs for [B, N] (0: none)."""
-    return int(load_library().reduce_axis0_banded_workspace(B, N))

@@ -81,10 +81,6 @@ def load_library(path: str = LIB_PATH):
     lib.reduce_axis0_split_workspace.argtypes = [ll, ll]
     lib.reduce_axis0_split.restype = i
     lib.reduce_axis0_split.argtypes = [vp, ll, ll, vp, vp, ll, vp]
-    lib.reduce_axis0_banded_workspace.restype = ll
-    lib.reduce_axis0_banded_workspace.argtypes = [ll, ll]
-    lib.reduce_axis0_banded.restype = i
-    lib.reduce_axis0_banded.argtypes = [vp, ll, ll, vp, vp, ll, vp]
     lib.reduce_axis0_split_noalloc.restype = i
     lib.reduce_axis0_split_noalloc.argtypes = [vp, ll, ll, vp, vp]
     lib.cfc_status_string.restype = ctypes.c_char_p

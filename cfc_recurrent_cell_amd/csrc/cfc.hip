@@ -2753,51 +2753,6 @@ __global__ __launch_bounds__(kThreads) void reduce_axis0_kernel(const float* __r
     }
 }
 
-// Banded reduce for wide rows ("Custom Kernel Optimization Implementation
-// Plan", Tasks 4-5: batch-parallel partial sums, then a final reduce of the
-// partials, here for N >= 1024).  Workgroup q sums band p = q / chunks (rows
-// [p R, min(B, (p+1) R))) of column chunk q % chunks (1024 columns: one float4
-// per thread, 4 KB of each row) into float64 partials part[p][col], rows in
-// order, 8 loads in flight; reduce_partials_kernel then adds the P partials of
-// each column in a fixed order.  Consecutive workgroups read neighbouring 4 KB
-// pieces of the same rows, which reads faster than a 256-byte column tile down
-// all rows (measured on MI355X over a 4.3 GB input: 6.85 against 6.15 TB/s
-// with 512-row bands).  Needs N % 4 == 0 and a 16-byte-aligned input.
-constexpr long long kBandCols = 4 * kThreads;  // columns per workgroup
-__global__ __launch_bounds__(kThreads) void reduce_band_kernel(const float* __restrict__ in, long long B, long long N,
-                                                               long long R, long long chunks,
-                                                               double* __restrict__ part) {
-    const long long p = blockIdx.x / chunks, ch = blockIdx.x % chunks;
-    const long long col = ch * kBandCols + 4 * threadIdx.x;
-    if (col >= N) return;  // N % 4 == 0: the lane's four columns are all in range
-    const long long r0 = p * R, r1 = min(B, r0 + R);
-    const float* q = in + col;
-    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-    long long r = r0;
-    for (; r + 7 < r1; r += 8) {
-        f32x4 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(q + (r + u) * N));
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            a0 += (double)v[u].x;
-            a1 += (double)v[u].y;
-            a2 += (double)v[u].z;
-            a3 += (double)v[u].w;
-        }
-    }
-    for (; r < r1; ++r) {
-        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(q + r * N));
-        a0 += (double)v.x;
-        a1 += (double)v.y;
-        a2 += (double)v.z;
-        a3 += (double)v.w;
-    }
-    double2* dst = reinterpret_cast<double2*>(part + p * N + col);
-    dst[0] = make_double2(a0, a1);
-    dst[1] = make_double2(a2, a3);
-}
-
 // Split reduce for narrow rows (N <= 256) over a long leading axis ("Custom
 // Kernel Optimization Implementation Plan", Tasks 4-5: a batch-parallel first
 // phase of block partial sums, then a final reduce of the partials; here both
@@ -3312,53 +3267,6 @@ extern "C" int reduce_axis0_split(const float* per_batch, long long B, long long
                        per_batch, B, (int)N, sp.R, part);
     hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)((N + kPartCols - 1) / kPartCols)), dim3(kThreads), 0,
                        stream, (const double*)part, sp.P, (int)N, out);
-    return launch_status();
-}
-
-// Banding of reduce_axis0_banded; it depends only on (B, N), so the summation
-// order -- and the result -- is the same on every device.  About 2048
-// workgroups (P bands x ceil(N / 1024) chunks), bands of at least 64 rows;
-// P < 2 means the one-pass reduce_axis0.
-struct BandPlan {
-    long long R, P, chunks;
-};
-inline BandPlan band_plan(long long B, long long N) {
-    const long long chunks = (N + kBandCols - 1) / kBandCols;
-    long long P = std::min((B + 63) / 64, std::max(1LL, (2048 + chunks / 2) / chunks));
-    if (P < 1) P = 1;
-    const long long R = (B + P - 1) / P;
-    return BandPlan{R, R > 0 ? (B + R - 1) / R : 0, chunks};
-}
-
-extern "C" long long reduce_axis0_banded_workspace(long long B, long long N) {
-    if (B < 0 || N < 0) return -1;
-    long long n;
-    if (!mul_ok(B, N, &n)) return -1;
-    if (N < kBandCols || N % 4 != 0) return 0;
-    const BandPlan bp = band_plan(B, N);
-    long long bytes;
-    if (bp.P < 2 || !mul_ok(bp.P * (long long)sizeof(double), N, &bytes)) return 0;
-    return bytes;
-}
-
-extern "C" int reduce_axis0_banded(const float* per_batch, long long B, long long N, float* out, void* workspace,
-                                   long long workspace_bytes, hipStream_t stream) {
-    const long long need = reduce_axis0_banded_workspace(B, N);
-    if (need < 0) return CFC_ERR_DIM;
-    if (need == 0 || (reinterpret_cast<uintptr_t>(per_batch) & 15) != 0)
-        return reduce_axis0(per_batch, B, N, out, stream);
-    if (!out || !per_batch || !workspace) return CFC_ERR_NULL;
-    if (workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15) != 0) return CFC_ERR_DIM;
-    const Range ws{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + (uintptr_t)need};
-    const Range in = span(per_batch, B * N), o = span(out, N);
-    if (overlap(o, in) || overlap(ws, in) || overlap(ws, o)) return CFC_ERR_OVERLAP;
-    const BandPlan bp = band_plan(B, N);
-    if (bp.P * bp.chunks > INT_MAX || N > INT_MAX) return CFC_ERR_DIM;
-    double* part = static_cast<double*>(workspace);
-    hipLaunchKernelGGL(reduce_band_kernel, dim3((unsigned)(bp.P * bp.chunks)), dim3(kThreads), 0, stream, per_batch,
-                       B, N, bp.R, bp.chunks, part);
-    hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)((N + kPartCols - 1) / kPartCols)), dim3(kThreads), 0,
-                       stream, (const double*)part, bp.P, (int)N, out);
     return launch_status();
 }
 

@@ -310,33 +310,6 @@ long long reduce_axis0_split_workspace(long long B, long long N);
 int reduce_axis0_split(const float *per_batch, long long B, long long N, float *out,
                        void *workspace, long long workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace reduce_axis0_banded needs for a [B, N] input: 0 when it
- * runs the one-pass reduce_axis0 instead (N < 1024, N % 4 != 0, or too few
- * rows for two bands), -1 if B or N is negative or B*N*4 overflows. */
-long long reduce_axis0_banded_workspace(long long B, long long N);
-
-/* Column sum for wide rows in bands ("Custom Kernel Optimization
- * Implementation Plan", Tasks 4-5: batch-parallel partial sums, then a final
- * reduce of the partials): P bands of consecutive rows times ceil(N / 1024)
- * column chunks, about 2048 workgroups, each summing 4 KB of each of its
- * band's rows into float64 partials in `workspace`; a second kernel adds the
- * P partials of each column.  Both orders depend only on (B, N).  Reading
- * neighbouring 4 KB pieces of a band's rows is faster than reduce_axis0's
- * column tiles down all rows for large inputs (the large-batch scratch).
- *   per_batch, B, N, out   as for reduce_axis0 (out is overwritten)
- *   workspace  device memory of at least reduce_axis0_banded_workspace(B, N)
- *              bytes, 16-byte aligned, owned by the caller, not overlapping
- *              per_batch or out; contents on entry ignored, on return
- *              unspecified.  May be NULL when that size is 0.
- * A per_batch that is not 16-byte aligned, or a size of 0, runs reduce_axis0
- * (the workspace is then not touched).  The result is the float32 rounding of
- * a float64 sum, bitwise reproducible for a given (B, N); its grouping differs
- * from reduce_axis0's, so the two may differ in the last float32 bit.
- * Returns a CFC_* status: CFC_ERR_DIM also when the workspace is too small
- * or misaligned. */
-int reduce_axis0_banded(const float *per_batch, long long B, long long N, float *out,
-                        void *workspace, long long workspace_bytes, hipStream_t stream);
-
 /* Maximum bytes of partials reduce_axis0_split ever needs (256 K float64
  * partials); reduce_axis0_split_noalloc keeps them in a static device array of
  * this size. */

@@ -29,8 +29,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"cfc_scratch_row_len", "cfc_forward", "cfc_backward", "cfc_backward_window",
                           "cfc_forward_backward", "reduce_axis0", "reduce_axis0_split",
                           "reduce_axis0_split_workspace", "cfc_status_string", "cfc_backward_workspace",
-                          "cfc_backward_window_ws", "cfc_forward_backward_ws", "reduce_axis0_split_noalloc",
-                          "reduce_axis0_banded", "reduce_axis0_banded_workspace"}
+                          "cfc_backward_window_ws", "cfc_forward_backward_ws", "reduce_axis0_split_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -278,38 +277,6 @@ def test_split_reduce_validation(lib):
     assert f(FAKE, 524288, 3, big, FAKE + 64, 18528, None) == C.CFC_ERR_OVERLAP    # over the input
     assert f(FAKE, 524288, 3, big, big + 8, 18528, None) == C.CFC_ERR_OVERLAP      # over out
     assert f(FAKE, -5, 3, big, None, 0, None) == C.CFC_ERR_DIM
-
-
-def test_banded_reduce_workspace_sizes(lib):
-    """Banding depends only on (B, N): chunks of 1024 columns, P = min(ceil(B /
-    64), round(2048 / chunks)) bands of ceil(B / P) rows, P float64 partials
-    per column; 0 (one pass) below two bands, below 1024 columns or with N % 4
-    != 0."""
-    ws = lib.reduce_axis0_banded_workspace
-    assert ws(8192, 131584) == 16 * 131584 * 8   # 129 chunks -> 16 bands of 512 rows
-    assert ws(1000, 2000) == 16 * 2000 * 8       # 2 chunks -> 1024, capped by 16 bands of 63 rows
-    assert ws(129, 1028) == 3 * 1028 * 8         # 3 bands of 43 rows
-    assert ws(128, 1024) == 2 * 1024 * 8
-    assert ws(64, 4096) == 0                      # one band: the one-pass reduce runs
-    assert ws(32, 40960) == 0
-    assert ws(8192, 1023) == 0                    # narrower than one chunk
-    assert ws(8192, 2002) == 0                    # N % 4 != 0
-    assert ws(100000, 0) == 0
-    assert ws(-1, 4096) == -1 and ws(4096, -1) == -1
-    assert ws(2**40, 2**40) == -1                 # B*N*4 overflows
-
-
-def test_banded_reduce_validation(lib):
-    big = FAKE + 0x10000000
-    f = lib.reduce_axis0_banded
-    need = 16 * 2000 * 8
-    assert f(FAKE, 1000, 2000, big, None, 0, None) == C.CFC_ERR_NULL               # workspace needed
-    assert f(FAKE, 1000, 2000, None, big + 0x100000, need, None) == C.CFC_ERR_NULL
-    assert f(FAKE, 1000, 2000, big, big + 0x100000, need - 1, None) == C.CFC_ERR_DIM  # too small
-    assert f(FAKE, 1000, 2000, big, big + 0x100008, need, None) == C.CFC_ERR_DIM      # not 16-byte aligned
-    assert f(FAKE, 1000, 2000, big, FAKE + 64, need, None) == C.CFC_ERR_OVERLAP       # over the input
-    assert f(FAKE, 1000, 2000, big, big - 16, need, None) == C.CFC_ERR_OVERLAP        # over out
-    assert f(FAKE, -5, 2000, big, None, 0, None) == C.CFC_ERR_DIM
 
 
 def test_split_reduce_noalloc_validation(lib):

@@ -99,63 +99,3 @@ def test_merged_leading_axes(split):
     out3 = C.reduce_axis0(t, leading_axes=3, split=split)
     assert tuple(out3.shape) == (15,)
     assert np.array_equal(host(out3).astype(np.int64), a.astype(np.int64).sum(axis=(0, 1, 2)))
-
-
-# reduce_axis0_banded: wide rows in bands of consecutive rows (ragged last
-# band, ragged last 1024-column chunk, several bands per chunk)
-BANDED = [(1000, 2000), (129, 1028), (128, 1024), (8192, 4096), (2048, 33024)]
-
-
-@pytest.mark.parametrize("B,N", BANDED)
-def test_banded_reduce_integer_exact(B, N):
-    import torch
-    import cfc_recurrent_cell_amd as C
-    need = C.reduce_axis0_banded_workspace(B, N)
-    say(f"[banded reduce] integer B={B} N={N} workspace={need} bytes")
-    assert need > 0
-    a = W.make_random_matrix(B, N, seed=5 * B + N, integer=True)
-    t = torch.from_numpy(a).cuda()
-    out = torch.full((N,), float("nan"), device="cuda")
-    C.reduce_axis0(t, out=out, banded=True)
-    assert np.array_equal(host(out).astype(np.int64), a.astype(np.int64).sum(axis=0))
-
-
-@pytest.mark.parametrize("B,N", [(1000, 2000), (8192, 4096)])
-def test_banded_reduce_real_valued_and_deterministic(B, N):
-    import torch
-    import cfc_recurrent_cell_amd as C
-    say(f"[banded reduce] real B={B} N={N}")
-    a = W.make_random_matrix(B, N, seed=7 * B + N)
-    t = torch.from_numpy(a).cuda()
-    ws = torch.empty((C.reduce_axis0_banded_workspace(B, N),), dtype=torch.uint8, device="cuda")
-    first = host(C.reduce_axis0(t, banded=True, workspace=ws)).copy()
-    _within_one_ulp(first, a, f"banded B={B} N={N}")
-    ws.fill_(0xFF)   # NaN bytes: the workspace's contents on entry do not matter
-    again = host(C.reduce_axis0(t, banded=True, workspace=ws))
-    assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
-
-
-def test_banded_reduce_falls_back_to_one_pass():
-    """A shape with one band, and an input that is not 16-byte aligned, run
-    reduce_axis0: the same bits, and the workspace is not needed; a workspace
-    below the required size is refused."""
-    import torch
-    import cfc_recurrent_cell_amd as C
-    B, N = 64, 4096
-    assert C.reduce_axis0_banded_workspace(B, N) == 0
-    a = W.make_random_matrix(B, N, seed=13)
-    t = torch.from_numpy(a).cuda()
-    assert np.array_equal(host(C.reduce_axis0(t, banded=True)).view(np.uint32),
-                          host(C.reduce_axis0(t)).view(np.uint32))
-    B, N = 1000, 2000
-    a = W.make_random_matrix(B, N, seed=17)
-    buf = torch.empty(B * N + 1, device="cuda")
-    off = buf[1:].view(B, N)
-    off.copy_(torch.from_numpy(a).cuda())
-    assert off.data_ptr() % 16 == 4
-    assert np.array_equal(host(C.reduce_axis0(off, banded=True)).view(np.uint32),
-                          host(C.reduce_axis0(off)).view(np.uint32))
-    small = torch.empty((C.reduce_axis0_banded_workspace(B, N) - 16,), dtype=torch.uint8, device="cuda")
-    aligned = torch.from_numpy(a).cuda()
-    with pytest.raises(C.CfcError):
-        C.reduce_axis0(aligned, banded=True, workspace=small)
