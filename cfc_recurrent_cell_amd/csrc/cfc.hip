@@ -1554,6 +1554,11 @@ __global__ __launch_bounds__(kThreads) void cfc_fb_small_kernel(
 // weight operand of each product.
 // =====================================================================
 constexpr int kLarge = 256;  // padded n_in and n_hid
+// The fourth word of a gfx9 buffer descriptor for raw, untyped access
+// (32-bit data format, no swizzle): the weight operands of the wide kernels
+// are read through buffer descriptors, whose base sits in scalar registers,
+// so each load needs only a 32-bit lane offset and a scalar or immediate one.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 constexpr int kLR = 16;      // batch rows per workgroup
 constexpr int kLargeBwdMaxK = 20;
 
@@ -1657,9 +1662,21 @@ __device__ __forceinline__ void large_preact(dbl4 acc[4], const float* __restric
             rok[tb] = i < H;
             wrow[tb] = wbase + (long long)min(i, H - 1) * width;
         }
+        // FULL: buffer loads from the matrix's descriptor (scalar base), the
+        // lane's row and column in the vector offset, the chunk group's
+        // column in the scalar offset
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(wbase), (short)0, kLarge * kLarge * 4, kBufferRsrcWord3);
+        int voff[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) voff[tb] = lunit(wave, tb, lane & 15) * kLarge * 4;
         auto wload = [&](int tb, int col) -> float4 {
-            if constexpr (FULL) return *reinterpret_cast<const float4*>(wrow[tb] + col);
-            else return load4_masked(wrow[tb], col, width, rok[tb]);
+            if constexpr (FULL) {
+                const int cs = __builtin_amdgcn_readfirstlane(col - 4 * s);  // the chunk group's first column
+                return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[tb] + 16 * s, cs * 4, 0));
+            } else {
+                return load4_masked(wrow[tb], col, width, rok[tb]);
+            }
         };
         float4 w4[4];
 #pragma unroll
@@ -1799,12 +1816,8 @@ __global__ __launch_bounds__(kThreads) void widen_weights_kernel(const float* __
     const float v = g == 0 ? w_in[e & 65535] : w_rec[e & 65535];
     reinterpret_cast<double*>(wide + (long long)(2 * g + (u >> 7)) * N)[(u & 127) * kLarge + j] = (double)v;
 }
-// Buffer loads of the copy: a quarter is 128 unit rows of 256 doubles;
-// kBufferRsrcWord3 is the fourth word of a gfx9 buffer descriptor (raw,
-// untyped 32-bit elements: data format 32, no swizzle), as for every buffer
-// access below.
+// a quarter of the copy: 128 unit rows of 256 doubles
 constexpr int kWideQuarterBytes = 128 * kLarge * 8;
-constexpr int kBufferRsrcWord3 = 0x00020000;
 // unit row u of W_in (g = 0) or W_rec (g = 1) in the widened copy
 __device__ __forceinline__ const double* wide_row(const float* wide, long long N, int g, int u) {
     return reinterpret_cast<const double*>(wide + (long long)(2 * g + (u >> 7)) * N) + (u & 127) * kLarge;
@@ -1944,12 +1957,13 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large32_kernel(
                     return W4d{__builtin_bit_cast(double2, lo), __builtin_bit_cast(double2, hi)};
                 });
             } else {
-                const float* wbase = g == 0 ? w_in : w_rec;
-                const float* wrow[4];
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<float*>(g == 0 ? w_in : w_rec), (short)0, kLarge * kLarge * 4, kBufferRsrcWord3);
+                int voff[4];
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb) wrow[tb] = wbase + lunit(wave, tb, r) * H;
+                for (int tb = 0; tb < 4; ++tb) voff[tb] = (lunit(wave, tb, r) * kLarge + 4 * s) * 4;
                 half(g, [&](int tb, int jq) {
-                    return W4f{*reinterpret_cast<const float4*>(wrow[tb] + 16 * jq + 4 * s)};
+                    return W4f{__builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[tb], 64 * jq, 0))};
                 });
             }
         }
@@ -2210,9 +2224,13 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                 return;
             }
         }
+        const __amdgpu_buffer_rsrc_t rsm = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(wm), (short)0, kLarge * kLarge * 4, kBufferRsrcWord3);
         auto wld = [&](int ic) -> float4 {
             const int i = 64 * s + ic;
-            if constexpr (FULL) return *reinterpret_cast<const float4*>(wm + (long long)i * kLarge + jw);
+            if constexpr (FULL)  // lane's row 64 s and column jw in the vector offset, ic in the scalar one
+                return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rsm, (64 * s * kLarge + jw) * 4, ic * kLarge * 4, 0));
             else return load4_masked(wm + (long long)min(i, H - 1) * ld, jw, width, i < H);
         };
         auto chunks1 = [&](const float4 (&w4)[1], int icb) {
