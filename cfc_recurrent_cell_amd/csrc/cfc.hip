@@ -1911,7 +1911,10 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large32_kernel(
             decltype(load(0, 0)) w4[4];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) w4[tb] = load(tb, 0);
-#pragma unroll 4
+            // eight chunk groups per loop trip: the LDS operand offsets of the
+            // trip's groups are immediates (0.354 against 0.365 ms with four;
+            // all sixteen spill registers)
+#pragma unroll 8
             for (int jq = 0; jq < 16; ++jq) {
                 decltype(load(0, 0)) nw4[4];
                 const int jn = jq + 1 < 16 ? jq + 1 : jq;  // the next chunk group's weights
