@@ -2207,7 +2207,10 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
                 W4d va[PF], vb[PF];
 #pragma unroll
                 for (int u = 0; u < PF; ++u) va[u] = wld64(u);
-#pragma unroll 1
+                // two trips per loop iteration (phase 1 at B = 8192: 0.263
+                // against 0.274 ms with one; prefetching 2 or 8 chunks instead
+                // of 4 measured no better)
+#pragma unroll 2
                 for (int ic0 = 0; ic0 < 64 - 2 * PF; ic0 += 2 * PF) {
 #pragma unroll
                     for (int u = 0; u < PF; ++u) vb[u] = wld64(ic0 + PF + u);
