@@ -2758,7 +2758,7 @@ __global__ __launch_bounds__(kThreads) void reduce_axis0_kernel(const float* __r
     constexpr int TW = LPR * VEC;
     constexpr int kRowsPerWave = 64 / LPR;
     constexpr int kSlots = kRowsPerWave * (kThreads / 64);
-    constexpr int kUnroll = 8;
+    constexpr int kUnroll = LPR == 32 ? 16 : 8;
     __shared__ double part[kSlots][TW + 1];
 
     const int t = threadIdx.x;
@@ -3391,12 +3391,20 @@ extern "C" int reduce_axis0(const float* per_batch, long long B, long long N, fl
     if (!out || (B > 0 && !per_batch)) return CFC_ERR_NULL;
     if (B > 0 && overlap(span(out, N), span(per_batch, n))) return CFC_ERR_OVERLAP;
     const bool vec4 = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(per_batch) % 16 == 0);
-    // 256-byte row segments (16 lanes x float4) were as fast as or faster than
-    // 128- and 512-byte ones at every measured shape
-    const long long tw = 64;
+    // 256-byte row segments (16 lanes x float4, 8 rows' loads in flight per
+    // slot); above 256 MB of input (more than the MALL holds), 512-byte
+    // segments with 16 rows in flight: measured on MI355X at [8192, 131584]
+    // 0.696 against 0.711 ms after the large-batch backward, while at the
+    // training-scale scratch (34 MB) they were 0.5 us slower.  The two
+    // group the rows differently, so the result depends on (B, N) only.
+    const bool wide_tiles = vec4 && n > (64LL << 20);  // n floats: more than 256 MB
+    const long long tw = wide_tiles ? 128 : 64;
     const long long tiles = (N + tw - 1) / tw;
     if (tiles > INT_MAX) return CFC_ERR_DIM;
-    if (vec4)
+    if (wide_tiles)
+        hipLaunchKernelGGL((reduce_axis0_kernel<4, 32>), dim3((unsigned)tiles), dim3(kThreads), 0, stream,
+                           per_batch, B, N, out);
+    else if (vec4)
         hipLaunchKernelGGL((reduce_axis0_kernel<4, 16>), dim3((unsigned)tiles), dim3(kThreads), 0, stream,
                            per_batch, B, N, out);
     else

@@ -101,7 +101,11 @@ def test_profiled_kernel_duration_only_for_the_current_source(tmp_path, monkeypa
     assert bench.profiled_kernel_us("kernels_x", "reduce_axis0_kernel<4,16>", 526336) == 710.49
     assert bench.profiled_kernel_us("kernels_x", "reduce_axis0_kernel<4,16>", 163840) == 3.70
     assert bench.profiled_kernel_us("kernels_x", "reduce_axis0_kernel<4,16>", 1) is None
-    assert bench.REDUCE_GRID(40960) == 163840 and bench.REDUCE_GRID(131584) == 526336
+    # the instance and grid the library launches: 64 columns per workgroup,
+    # 128 above 256 MB of input
+    assert bench.reduce_kernel(32, 40960) == ("reduce_axis0_kernel<4,16>", 163840)
+    assert bench.reduce_kernel(256, 33024) == ("reduce_axis0_kernel<4,16>", 132096)
+    assert bench.reduce_kernel(8192, 131584) == ("reduce_axis0_kernel<4,32>", 263168)
     (tmp_path / "kernels_y.txt").write_text("t\ncommand: rocprofv3\nkernel source sha256[:16]: 0123456789abcdef\n"
                                             + rows)
     assert bench.profiled_kernel_us("kernels_y", "cfc_fb_small_kernel<true>") is None

@@ -343,3 +343,24 @@ def test_reduce_misaligned_rows():
     view = base[1:].view(6, 4096)
     out = C.reduce_axis0(view)
     assert np.array_equal(host(out).astype(np.int64), a.astype(np.int64).sum(0))
+
+
+@pytest.mark.parametrize("B,N", [(520, 131580), (70000, 964)])
+def test_reduce_inputs_above_256_mb(B, N):
+    """Inputs of more than 256 MB take 128-column tiles with 16 rows' loads in
+    flight per slot: exact integer sums (a ragged last tile: N % 128 != 0)
+    and, on real values, within one float32 ulp of the float64 sum, bitwise
+    repeatable."""
+    import torch
+    import cfc_recurrent_cell_amd as C
+    assert B * N * 4 > 256 * 1024 * 1024 and N % 128 != 0
+    say(f"[parity] reduce above 256 MB: B={B} N={N}")
+    a = W.make_random_matrix(B, N, seed=B + N, integer=True)
+    t = torch.from_numpy(a).cuda()
+    assert np.array_equal(host(C.reduce_axis0(t)).astype(np.int64), a.astype(np.int64).sum(axis=0))
+    del t
+    a = W.make_random_matrix(B, N, seed=B + 3 * N)
+    t = torch.from_numpy(a).cuda()
+    g = host(C.reduce_axis0(t)).copy()
+    _own_sum_check(g, a, f"reduce B={B} N={N}")
+    assert np.array_equal(g.view(np.uint32), host(C.reduce_axis0(t)).view(np.uint32))
