@@ -27,7 +27,7 @@ pytestmark = pytest.mark.gpu
 SHAPES = [
     # (B, K, n_in, H, dt, seed, note)
     (256, 64, 128, 128, 0.5, 901, "one kernel per row (training-scale shape)"),
-    (21, 6, 256, 256, 1.0, 902, "three launches: forward parking a_k, two backward stages"),
+    (21, 6, 256, 256, 1.0, 902, "four launches: weight widening, forward parking a_k, two backward stages"),
     (5, 30, 140, 160, 0.7, 903, "two launches: 16-row forward, general backward"),
 ]
 
