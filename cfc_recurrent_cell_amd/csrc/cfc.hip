@@ -2670,7 +2670,15 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
 // Inputs: dL/da parked in the head of the row's scratch by phase 1 (two 32-bit
 // halves per double, [k][unit]) and the dL/dw_tau sums in its last 2 H floats
 // (float64); both are read before the barrier that precedes the first store.
+// The launch reserves kGradsLdsReserve bytes of dynamic LDS that the kernel
+// never touches: with the 16 KB array below a workgroup then takes more than
+// half of a CU's 160 KB, so one row is written per CU at a time (256 rows in
+// flight instead of 1,024 at the register-bound four per CU).  Fewer
+// concurrent write streams keep HBM busier: 0.84 -> 0.81 ms for the 4.3 GB
+// of B = 8192, bitwise the same (two or three per CU measured 0.83 ms; a
+// persistent grid of 256 workgroups looping over rows, 0.84 ms).
 constexpr int kGradsMaxK = 8;
+constexpr size_t kGradsLdsReserve = 68 * 1024;
 __global__ __launch_bounds__(kThreads) void cfc_bwd_large_grads_kernel(
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq, int K,
     float* __restrict__ scratch, long long N) {
@@ -2974,6 +2982,8 @@ void set_kernel_attributes() {
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, true, false, 0, true>),
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, false, 0, true>)})
             (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_large_grads_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGradsLdsReserve);
     });
 }
 
@@ -3257,7 +3267,7 @@ int forward_backward(const cfc_params_t* params, const float* x, const float* h0
         const bool vgrads = full && K <= kGradsMaxK && al16(x) && al16(h0) && al16(h_seq) && al16(scratch);
         for (auto* bwd : {bwd1, bwd2}) {
             if (vgrads && bwd == bwd2) {
-                hipLaunchKernelGGL(cfc_bwd_large_grads_kernel, dim3((unsigned)B), dim3(kThreads), 0, stream, x, h0,
+                hipLaunchKernelGGL(cfc_bwd_large_grads_kernel, dim3((unsigned)B), dim3(kThreads), kGradsLdsReserve, stream, x, h0,
                                    h_seq, K, scratch, N);
                 break;
             }
