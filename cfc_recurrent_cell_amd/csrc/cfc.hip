@@ -2046,6 +2046,11 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large32_kernel(
 // the gradient, rounded to float32, is added in float32; dL/da is parked in
 // the caller's workspace `ws` (2 K H 32-bit words per row) instead of the
 // scratch tail, whose old values are still needed.
+// ACC with PARKED, STAGE 1 (accumulate mode at exactly 256 x 256, K <= 8): the
+// forward parked a_k in `ws` (the same 2 K H words per row, rows back to
+// back), dL/da_k replaces it there, and each row's dL/dw_tau, rounded to
+// float32, is added to its scratch element at once; the weight gradients and
+// db follow in cfc_bwd_large_grads_kernel<true>.
 template <bool FULL, bool TAU, bool PARKED, int STAGE = 0, bool ACC = false>
 __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
@@ -2053,7 +2058,8 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
     const float* __restrict__ y, double dt, int B, BwdWindow win, int n_in, int H, float* __restrict__ scratch,
     float* __restrict__ loss, float* __restrict__ grad_x, unsigned* __restrict__ ws, const float* __restrict__ wide) {
-    static_assert(!ACC || (!PARKED && STAGE == 0), "accumulate mode recomputes a_k and runs both phases");
+    static_assert(!ACC || (!PARKED && STAGE == 0) || (PARKED && STAGE == 1),
+                  "accumulate mode: both phases recomputing a_k, or the parked phase 1");
     constexpr int cell = TAU ? CFC_CELL_TAU_DECAY : CFC_CELL_GATED;
     const int K = win.Kw;  // steps of this launch; indices below are relative to win.k0
     const long long Kf = win.K, k0 = win.k0;
@@ -2137,8 +2143,8 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     dbl4 apre[4];
     auto fetch_a = [&](int k) {
         if constexpr (PARKED) {
-            const double* ap = reinterpret_cast<const double*>(scratch + b_own * N) + (k0 + k) * (long long)H;
-            if (FULL && (reinterpret_cast<uintptr_t>(scratch) & 15) == 0) {
+            const double* ap = reinterpret_cast<const double*>(park_row(b_own)) + (k0 + k) * (long long)H;
+            if (FULL && (reinterpret_cast<uintptr_t>(ACC ? static_cast<const void*>(ws) : scratch) & 15) == 0) {
                 // units lunit(wave, 0..3, m) are four consecutive doubles
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
@@ -2387,12 +2393,16 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
             }
     }
     if constexpr (STAGE == 1) {
-        // the rows' dL/dw_tau sums to the heads of their scratch rows
+        // the rows' dL/dw_tau sums to the last 2 H floats of their scratch
+        // rows (accumulate mode: added to the rows' dL/dw_tau elements)
         __syncthreads();
         for (int e = t; e < kLR * kLarge; e += kThreads) {
             const int rr = e / kLarge, u = e % kLarge;
             const long long b = r0 + rr;
-            if (b < B && u < H) reinterpret_cast<double*>(scratch + b * N + N - 2LL * H)[u] = gwt[zidx(u, rr)];
+            if (b < B && u < H) {
+                if constexpr (ACC) scratch[b * N + N - H + u] += (float)gwt[zidx(u, rr)];
+                else reinterpret_cast<double*>(scratch + b * N + N - 2LL * H)[u] = gwt[zidx(u, rr)];
+            }
         }
         return;
     }
@@ -2677,18 +2687,29 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
 // concurrent write streams keep HBM busier: 0.84 -> 0.81 ms for the 4.3 GB
 // of B = 8192, bitwise the same (two or three per CU measured 0.83 ms; a
 // persistent grid of 256 workgroups looping over rows, 0.84 ms).
+// ACC (accumulate mode): dL/da comes from the caller's workspace `ws` (rows of
+// 2 K H words, where the parked phase 1 left it), dL/dw_tau has already been
+// added by that phase, and each gradient element, rounded to float32, is added
+// to the scratch element in float32.  The old values are read with
+// non-temporal loads one block of eight loop trips (16 unit rows) ahead, and
+// the sums written through like the overwrite stores.  At B = 8192 this
+// kernel moves 8.6 GB: the whole one-call accumulate takes 2.29 ms, against
+// 2.93 ms for the forward and the recomputing backward (prefetching two or
+// four trips ahead, plain non-temporal stores, or four rows per CU measured
+// within 2 % of it).
 constexpr int kGradsMaxK = 8;
 constexpr size_t kGradsLdsReserve = 68 * 1024;
+template <bool ACC>
 __global__ __launch_bounds__(kThreads) void cfc_bwd_large_grads_kernel(
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq, int K,
-    float* __restrict__ scratch, long long N) {
+    float* __restrict__ scratch, long long N, const unsigned* __restrict__ ws) {
     constexpr int H = kLarge, NI = kLarge;
     __shared__ double das[kLarge][kGradsMaxK];  // dL/da of the row, unit-major
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const long long b = blockIdx.x;
     float* row = scratch + b * N;
     static_assert(kThreads == kLarge, "one thread per unit");
-    const unsigned* tq = reinterpret_cast<const unsigned*>(row);
+    const unsigned* tq = ACC ? ws + b * (2LL * K * H) : reinterpret_cast<const unsigned*>(row);
     double gb = 0.0;
     for (int kk = K - 1; kk >= 0; --kk) {  // db in the order of the per-step accumulation
         const long long q = 2 * ((long long)kk * H + t);
@@ -2697,7 +2718,7 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_grads_kernel(
         gb += dv;
     }
     for (int kk = K; kk < kGradsMaxK; ++kk) das[t][kk] = 0.0;
-    const double gw_t = reinterpret_cast<const double*>(row + N - 2LL * H)[t];
+    const double gw_t = ACC ? 0.0 : reinterpret_cast<const double*>(row + N - 2LL * H)[t];
     // this lane's four columns of [x_k | h_k-1] for every step: waves 0 and
     // 2 hold x (dW_in), waves 1 and 3 hold h_prev (dW_rec)
     const int part = wave & 1, c = 4 * lane;
@@ -2715,35 +2736,70 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_grads_kernel(
     }
     __syncthreads();  // every read of the row's head and tail precedes every store
     float* base = part == 0 ? row : row + (long long)H * NI;
-    // unit rows i = wave / 2 + 2 u, two per iteration
+    // gradient of unit row i for the lane's four columns, float32
+    auto grad4 = [&](int i) {
+        const double* d = das[i];
+        double dk[kGradsMaxK];
+#pragma unroll
+        for (int k = 0; k < kGradsMaxK; ++k) dk[k] = d[k];
+        f32x4 g;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            double a = dk[0] * z[0][m];
+#pragma unroll
+            for (int k = 1; k < kGradsMaxK; ++k) a = fma(dk[k], z[k][m], a);
+            g[m] = (float)a;
+        }
+        return g;
+    };
+    if constexpr (ACC) {
+        // unit rows i = wave / 2 + 2 u, eight per block of four loop trips;
+        // the next block's old values are loaded before this block's products
+        constexpr int kTrips = 8;
+        f32x4 old[kTrips][2], nxt[kTrips][2];
+        auto load_block = [&](int u0, f32x4 (&dst)[kTrips][2]) {
+#pragma unroll
+            for (int j = 0; j < kTrips; ++j)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const int i = (wave >> 1) + 2 * (u0 + 2 * j + p);
+                    dst[j][p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(base + (long long)i * H + c));
+                }
+        };
+        load_block(0, old);
 #pragma unroll 1
-    for (int u = 0; u < H / 2; u += 2) {
-        double acc[2][4];
+        for (int u0 = 0; u0 < H / 2; u0 += 2 * kTrips) {
+            if (u0 + 2 * kTrips < H / 2) load_block(u0 + 2 * kTrips, nxt);
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int i = (wave >> 1) + 2 * (u + p);
-            const double* d = das[i];
-            double dk[kGradsMaxK];
+            for (int j = 0; j < kTrips; ++j)
 #pragma unroll
-            for (int k = 0; k < kGradsMaxK; ++k) dk[k] = d[k];
+                for (int p = 0; p < 2; ++p) {
+                    const int i = (wave >> 1) + 2 * (u0 + 2 * j + p);
+                    store_stream_f32x4(base + (long long)i * H + c, old[j][p] + grad4(i));
+                }
+            if (u0 + 2 * kTrips < H / 2) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                double a = dk[0] * z[0][m];
+                for (int j = 0; j < kTrips; ++j)
 #pragma unroll
-                for (int k = 1; k < kGradsMaxK; ++k) a = fma(dk[k], z[k][m], a);
-                acc[p][m] = a;
+                    for (int p = 0; p < 2; ++p) old[j][p] = nxt[j][p];
             }
         }
+        // db of unit t (dL/dw_tau was added by phase 1)
+        row[(long long)H * (NI + H) + t] += (float)gb;
+    } else {
+        // unit rows i = wave / 2 + 2 u, two per iteration
+#pragma unroll 1
+        for (int u = 0; u < H / 2; u += 2) {
+            f32x4 g[2];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int i = (wave >> 1) + 2 * (u + p);
-            store_stream_f32x4(base + (long long)i * H + c,
-                               f32x4{(float)acc[p][0], (float)acc[p][1], (float)acc[p][2], (float)acc[p][3]});
+            for (int p = 0; p < 2; ++p) g[p] = grad4((wave >> 1) + 2 * (u + p));
+#pragma unroll
+            for (int p = 0; p < 2; ++p) store_stream_f32x4(base + (long long)((wave >> 1) + 2 * (u + p)) * H + c, g[p]);
         }
+        // db and dw_tau of unit t
+        row[(long long)H * (NI + H) + t] = (float)gb;
+        row[(long long)H * (NI + H) + H + t] = (float)gw_t;
     }
-    // db and dw_tau of unit t
-    row[(long long)H * (NI + H) + t] = (float)gb;
-    row[(long long)H * (NI + H) + H + t] = (float)gw_t;
 }
 
 // -------------------------------------------------------- reduce_axis0
@@ -2980,10 +3036,13 @@ void set_kernel_attributes() {
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, false, false, 0, true>),
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false, false, 0, true>),
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, true, false, 0, true>),
-                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, false, 0, true>)})
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, false, 0, true>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false, true, 1, true>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, true, 1, true>)})
             (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cfc_bwd_large_grads_kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGradsLdsReserve);
+        for (const void* f : {reinterpret_cast<const void*>(&cfc_bwd_large_grads_kernel<false>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_grads_kernel<true>)})
+            (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGradsLdsReserve);
     });
 }
 
@@ -3226,6 +3285,32 @@ int forward_backward(const cfc_params_t* params, const float* x, const float* h0
     const bool small_bwd = n_in <= kSmall && H <= kSmall && K <= kSmallBwdMaxK;
     const size_t lds = small_bwd ? small_bwd_lds_bytes() : large ? large_bwd_lds_bytes() : bwd_lds_bytes(K, n_in, H);
     if (lds > kLdsBytes) return CFC_ERR_UNSUPPORTED;
+    const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    // accumulate mode at exactly 256 x 256 and K <= 8 with a workspace: the
+    // forward parks a_k in the workspace (rows of 2 K H words), the parked
+    // phase 1 turns it into dL/da there and adds dL/dw_tau into the scratch,
+    // and the vector phase 2 adds the weight gradients and db
+    if (large && flags == CFC_ACCUMULATE && ws_used && large_full(params) && K <= kGradsMaxK && al16(x) &&
+        al16(h0) && al16(h_seq) && al16(scratch)) {
+        set_kernel_attributes();
+        const bool tau = params->cell == CFC_CELL_TAU_DECAY;
+        hipLaunchKernelGGL((cfc_fwd_large32_kernel<true, false>), dim3((unsigned)(((long long)B + kLR2 - 1) / kLR2)),
+                           dim3(kThreads), large32_fwd_lds_bytes(), stream, params->w_in, params->w_rec, params->b,
+                           params->w_tau, x, h0, (double)dt, B, K, h_seq, params->cell,
+                           reinterpret_cast<float*>(workspace), 2LL * K * H, nullptr);
+        rc = launch_status();
+        if (rc) return rc;
+        const BwdWindow win{K, 0, K, nullptr, grad_h0};
+        auto bwd1 = tau ? &cfc_bwd_large_kernel<true, true, true, 1, true> : &cfc_bwd_large_kernel<true, false, true, 1, true>;
+        hipLaunchKernelGGL(bwd1, dim3((unsigned)(((long long)B + kLR - 1) / kLR)), dim3(kThreads), large_bwd_lds_bytes(),
+                           stream, params->w_in, params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt,
+                           B, win, n_in, H, scratch, loss, grad_x, static_cast<unsigned*>(workspace), nullptr);
+        rc = launch_status();
+        if (rc) return rc;
+        hipLaunchKernelGGL(cfc_bwd_large_grads_kernel<true>, dim3((unsigned)B), dim3(kThreads), kGradsLdsReserve, stream,
+                           x, h0, h_seq, K, scratch, N, static_cast<const unsigned*>(workspace));
+        return launch_status();
+    }
     // 16-row kernels in overwrite mode: the forward parks a_k (float64) in the
     // head [0, 2KH) of each scratch row and the backward reads it back instead
     // of recomputing it, parking dL/da_k over a_k (needs 8-byte-aligned rows;
@@ -3236,7 +3321,6 @@ int forward_backward(const cfc_params_t* params, const float* x, const float* h0
         set_kernel_attributes();
         const long long groups = ((long long)B + kLR - 1) / kLR;
         const bool full = large_full(params), tau = params->cell == CFC_CELL_TAU_DECAY;
-        const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
         // float64 weights for the 256 x 256 products, in the middle of
         // scratch rows 0..3 (16-byte aligned for their double2 loads)
         const bool use_wide = full && B >= 4 && al16(scratch) && N % 4 == 0 && 4LL * K * H + kWideElems / 2 <= N;
@@ -3267,8 +3351,8 @@ int forward_backward(const cfc_params_t* params, const float* x, const float* h0
         const bool vgrads = full && K <= kGradsMaxK && al16(x) && al16(h0) && al16(h_seq) && al16(scratch);
         for (auto* bwd : {bwd1, bwd2}) {
             if (vgrads && bwd == bwd2) {
-                hipLaunchKernelGGL(cfc_bwd_large_grads_kernel, dim3((unsigned)B), dim3(kThreads), kGradsLdsReserve, stream, x, h0,
-                                   h_seq, K, scratch, N);
+                hipLaunchKernelGGL(cfc_bwd_large_grads_kernel<false>, dim3((unsigned)B), dim3(kThreads), kGradsLdsReserve,
+                                   stream, x, h0, h_seq, K, scratch, N, nullptr);
                 break;
             }
             hipLaunchKernelGGL(bwd, dim3((unsigned)groups), dim3(kThreads), large_bwd_lds_bytes(), stream, params->w_in,

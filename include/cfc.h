@@ -196,7 +196,8 @@ int cfc_backward_window(const cfc_params_t *params, const float *x, const float 
 /* Bytes of device workspace that cfc_backward_window_ws needs for a window of
  * Kw steps: 8 * B * Kw * n_hid (dL/da of every row-step, float64) where the
  * window runs the 16-row backward in accumulate mode (n_in or n_hid above
- * 128, Kw <= 20, flags = CFC_ACCUMULATE); 0 where no kernel uses one.
+ * 128, Kw <= 20, flags = CFC_ACCUMULATE); 0 where no kernel uses one.  The
+ * same size serves cfc_forward_backward_ws for B rows of K = Kw steps.
  * Returns -1 for a non-positive size, unknown flags or overflow. */
 long long cfc_backward_workspace(int B, int Kw, int n_in, int n_hid, int flags);
 
@@ -262,7 +263,14 @@ int cfc_forward_backward(const cfc_params_t *params, const float *x, const float
  * Implementation Plan", Task 5): with K <= 20 the backward then runs the
  * 16-row kernel, parking dL/da in the workspace, as cfc_backward_window_ws
  * does; otherwise the call is cfc_forward_backward and the workspace is
- * ignored.
+ * ignored.  At exactly 256 x 256 with K <= 8 (weights, x, h0, h_seq and the
+ * scratch 16-byte aligned) it is three launches, as in overwrite mode: the
+ * forward parks its float64 pre-activations in the workspace, the reverse
+ * pass reads them back, leaves dL/da there and adds dL/dw_tau to the scratch,
+ * and the last launch adds the weight gradients and db.  The gradient added is
+ * then the one cfc_forward_backward writes in overwrite mode, bitwise (rounded
+ * to float32, then added in float32); the other shapes add the gradient of
+ * cfc_forward followed by cfc_backward.
  *   arguments 1-13   as for cfc_forward_backward
  *   workspace        device memory, 8-byte aligned, or NULL; contents on entry
  *                    ignored, on return unspecified

@@ -92,36 +92,74 @@ def test_wide_accumulate_with_workspace(case):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"binding's own workspace: {name}"
 
 
-@pytest.mark.parametrize("cell", ["gated", "tau_decay"])
-def test_one_call_entry_with_workspace(cell):
-    """cfc_forward_backward_ws in accumulate mode: the forward's h_seq and the
-    backward's outputs bitwise equal to cfc_forward then the workspace
-    backward, and onto random values the float32 sum with the one-call
-    overwrite gradient (the parked path) within the backward's tolerance."""
+ONE_CALL = [
+    # (B, K, cell, dt, seed, note)
+    (21, 8, "gated", 1.0, 161, "parked path: two row groups of 16, a ragged one of 5"),
+    (21, 8, "tau_decay", 0.3, 163, "parked path, tau-decay cell"),
+    (1, 3, "gated", 0.6, 165, "parked path, one row"),
+    (37, 5, "gated", 0.8, 167, "parked path, three row groups"),
+    (21, 9, "gated", 1.0, 169, "K = 9: forward, then the recomputing backward"),
+]
+
+
+@pytest.mark.parametrize("case", ONE_CALL, ids=lambda c: "B{}_K{}_{}".format(*c[:3]))
+def test_one_call_entry_with_workspace(case):
+    """cfc_forward_backward_ws in accumulate mode at 256 x 256.  At K <= 8 the
+    forward parks a_k in the workspace and the parked backward follows, so the
+    result is the one-call overwrite path's gradient added to the old values
+    in float32, bitwise, with the same h_seq, loss, grad_x and grad_h0; onto
+    zeros it equals that path bitwise, and a workspace that is 8- but not
+    16-byte aligned gives the same bits.  At K = 9 the call is cfc_forward then
+    the workspace backward, bitwise.  Every case is checked against the oracle."""
     import torch
     import cfc_recurrent_cell_amd as C
-    B, K, n = 21, 8, 256
-    say(f"[wide accumulate] one-call entry with a workspace, {cell}")
-    inp = W.make_random_cfc_inputs(B, K, n, n, 0.3 if cell == "tau_decay" else 1.0, 161, cell=cell)
+    B, K, cell, dt, seed, note = case
+    n = 256
+    say(f"[wide accumulate] one-call entry with a workspace, B={B} K={K} {cell}: {note}")
+    inp = W.make_random_cfc_inputs(B, K, n, n, dt, seed, cell=cell)
     d = to_dev(inp)
     args = (d["w_in"], d["w_rec"], d["b"], d["w_tau"], d["x"], d["h0"])
     N = W.scratch_row_len(n, n)
-    ws = torch.empty((C.cfc_backward_workspace(B, K, n, n),), dtype=torch.uint8, device="cuda")
-    base = W.make_random_matrix(B, N, seed=162)
-    h1, s1, l1 = C.cfc_forward_backward(*args, d["y"], d["dt"], scratch=torch.from_numpy(base.copy()).cuda(),
-                                        accumulate=True, cell=cell, workspace=ws)
-    h2 = C.cfc_forward(*args, d["dt"], cell=cell)
-    s2, l2 = C.cfc_backward(*args, h2, d["y"], d["dt"], scratch=torch.from_numpy(base.copy()).cuda(),
-                            accumulate=True, cell=cell, workspace=ws)
-    for a, b_, name in ((h1, h2, "h_seq"), (s1, s2, "scratch"), (l1, l2, "loss")):
-        assert np.array_equal(host(a).view(np.uint32), host(b_).view(np.uint32)), name
-    _, over, _ = C.cfc_forward_backward(*args, d["y"], d["dt"], cell=cell)
-    assert_close(host(s1) - base, host(over), "accumulated one-call gradient")
+    need = C.cfc_backward_workspace(B, K, n, n)
+    ws_mem = torch.full(((need + 16) // 4,), float("nan"), device="cuda")   # contents on entry ignored
+    base = W.make_random_matrix(B, N, seed=seed + 1)
+
+    def run(start, ws):
+        out = C.cfc_forward_backward(*args, d["y"], d["dt"], scratch=start, accumulate=True, cell=cell,
+                                     workspace=ws, input_grads=True)
+        return [host(t).copy() for t in out]
+
+    acc = run(torch.from_numpy(base.copy()).cuda(), ws_mem.view(torch.uint8)[:need])
+    names = ("h_seq", "scratch", "loss", "grad_x", "grad_h0")
+    if K <= 8:
+        over = [host(t).copy() for t in C.cfc_forward_backward(*args, d["y"], d["dt"], cell=cell,
+                                                               input_grads=True)]
+        want = base.astype(np.float32) + over[1]
+        assert np.array_equal(acc[1].view(np.uint32), want.view(np.uint32)), "base + one-call gradient"
+        for i in (0, 2, 3, 4):
+            assert np.array_equal(acc[i].view(np.uint32), over[i].view(np.uint32)), names[i]
+        zero = run(torch.zeros((B, N), device="cuda"), ws_mem.view(torch.uint8)[:need])
+        for a, b_, name in zip(zero, over, names):
+            assert np.array_equal(a.view(np.uint32), b_.view(np.uint32)), f"onto zeros: {name}"
+        odd = run(torch.from_numpy(base.copy()).cuda(), ws_mem.view(torch.uint8)[8:8 + need])
+        for a, b_, name in zip(odd, acc, names):
+            assert np.array_equal(a.view(np.uint32), b_.view(np.uint32)), f"8-byte-aligned workspace: {name}"
+    else:
+        h2 = C.cfc_forward(*args, d["dt"], cell=cell)
+        s2, l2, gx2, gh2 = C.cfc_backward(*args, h2, d["y"], d["dt"],
+                                          scratch=torch.from_numpy(base.copy()).cuda(), accumulate=True,
+                                          cell=cell, workspace=ws_mem.view(torch.uint8)[:need], input_grads=True)
+        for a, b_, name in zip(acc, (h2, s2, l2, gx2, gh2), names):
+            assert np.array_equal(a.view(np.uint32), host(b_).view(np.uint32)), name
+    ref = O.cfc_step(inp, threads=oracle_threads(), input_grads=True)
+    assert_close(acc[1] - base.astype(np.float32), ref["scratch"], "accumulated one-call gradient")
+    assert_close(acc[2], ref["loss"], "loss")
+    assert_close(acc[3], ref["grad_x"], "grad_x")
+    assert_close(acc[4], ref["grad_h0"], "grad_h0")
     # no workspace given: the binding allocates one, same bits
-    h3, s3, l3 = C.cfc_forward_backward(*args, d["y"], d["dt"], scratch=torch.from_numpy(base.copy()).cuda(),
-                                        accumulate=True, cell=cell)
-    for a, b_, name in ((h3, h1, "h_seq"), (s3, s1, "scratch"), (l3, l1, "loss")):
-        assert np.array_equal(host(a).view(np.uint32), host(b_).view(np.uint32)), "binding's workspace: " + name
+    auto = run(torch.from_numpy(base.copy()).cuda(), None)
+    for a, b_, name in zip(auto, acc, names):
+        assert np.array_equal(a.view(np.uint32), b_.view(np.uint32)), "binding's workspace: " + name
 
 
 def test_workspace_reuse_over_calls_and_shapes():
