@@ -21,7 +21,9 @@ Families (each runs the kernels named):
   separate_16    cfc_forward + cfc_backward at 200 x 256: the 16-row kernels
   parked_16      cfc_forward_backward at 256 x 256: forward parking a_k, then
                  the two backward stages
-  accumulate_16  cfc_forward_backward_ws accumulating onto zeros at 256 x 256
+  accumulate_16  cfc_forward_backward_ws accumulating onto zeros at 256 x 256:
+                 the forward parking a_k in the workspace, then the two
+                 backward stages (the second adding into the scratch)
   general        cfc_forward + cfc_backward at K = 24, 140 x 160: the general
                  one-row-per-workgroup backward
 """
