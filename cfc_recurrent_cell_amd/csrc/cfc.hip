@@ -1840,8 +1840,11 @@ struct W4d {
 // instruction between two products adds 13 cycles or more), so the widenings
 // set the product loop's pace.  [x_k ; h_k] of the 32 rows is staged as in
 // the 16-row kernel, in [256][32] arrays swizzled within each row of 32.
-// PARK as in cfc_fwd_large_kernel.  W64: the weights come from the widened
-// float64 copy `wide` (scratch row 0 + 2 K H floats, see widen_weights_kernel).
+// PARK as in cfc_fwd_large_kernel: a_k of row b goes to a_park + b N, with
+// N the scratch row length (overwrite mode) or 2 K H (the caller's workspace
+// in accumulate mode).  W64: the weights come from the widened float64 copy
+// `wide` (scratch row 0 + 2 K H floats, quarters N floats apart, see
+// widen_weights_kernel).
 constexpr int kLR2 = 32;  // batch rows per workgroup of the 32-row forward
 __device__ __forceinline__ int zidx2(int j, int r) { return j * kLR2 + (r ^ (j & 31)); }
 __host__ __device__ constexpr size_t large32_fwd_lds_bytes() {
