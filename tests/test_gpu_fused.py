@@ -173,6 +173,7 @@ WIDE_PARKED = [
     # fewest rows that hold it, B = 3 reads the float32 weights
     (4, 5, 256, 256, 0.5, 58, "gated"),
     (3, 6, 256, 256, 0.5, 59, "tau_decay"),
+    (6, 1, 256, 256, 0.4, 60, "gated"),      # one step: no next x, h_prev = h0 only
 ]
 
 

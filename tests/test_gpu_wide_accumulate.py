@@ -98,6 +98,7 @@ ONE_CALL = [
     (21, 8, "tau_decay", 0.3, 163, "parked path, tau-decay cell"),
     (1, 3, "gated", 0.6, 165, "parked path, one row"),
     (37, 5, "gated", 0.8, 167, "parked path, three row groups"),
+    (6, 1, "tau_decay", 0.4, 171, "parked path, one step"),
     (21, 9, "gated", 1.0, 169, "K = 9: forward, then the recomputing backward"),
 ]
 
