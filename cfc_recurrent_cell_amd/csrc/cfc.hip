@@ -2049,11 +2049,16 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large32_kernel(
 // the gradient, rounded to float32, is added in float32; dL/da is parked in
 // the caller's workspace `ws` (2 K H 32-bit words per row) instead of the
 // scratch tail, whose old values are still needed.
-// ACC with PARKED, STAGE 1 (accumulate mode at exactly 256 x 256, K <= 8): the
-// forward parked a_k in `ws` (the same 2 K H words per row, rows back to
-// back), dL/da_k replaces it there, and each row's dL/dw_tau, rounded to
-// float32, is added to its scratch element at once; the weight gradients and
-// db follow in cfc_bwd_large_grads_kernel<true>.
+// ACC with STAGE 1 (accumulate mode at exactly 256 x 256, K <= 8): dL/da_k is
+// parked in `ws` (the same 2 K H words per row, rows back to back; PARKED:
+// over the a_k the forward parked there), and each row's dL/dw_tau, rounded
+// to float32, is added to its scratch element at once; the weight gradients
+// and db follow in cfc_bwd_large_grads_kernel<true>.
+// ACC, STAGE 1 without PARKED (cfc_backward accumulating over a whole
+// sequence at exactly 256 x 256, K <= 8): phase 1 recomputes a_k as STAGE 0
+// does.  In overwrite mode that split measured slower than STAGE 0 (1.48
+// against 1.45 ms at B = 8192), in accumulate mode faster (2.29 against 2.53
+// ms): there STAGE 0's phase 2 reads the old values on the matrix-core path.
 template <bool FULL, bool TAU, bool PARKED, int STAGE = 0, bool ACC = false>
 __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec,
@@ -2061,8 +2066,9 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
     const float* __restrict__ y, double dt, int B, BwdWindow win, int n_in, int H, float* __restrict__ scratch,
     float* __restrict__ loss, float* __restrict__ grad_x, unsigned* __restrict__ ws, const float* __restrict__ wide) {
-    static_assert(!ACC || (!PARKED && STAGE == 0) || (PARKED && STAGE == 1),
-                  "accumulate mode: both phases recomputing a_k, or the parked phase 1");
+    static_assert(!ACC || STAGE != 2, "accumulate mode: both phases in one launch, or phase 1 alone");
+    static_assert(PARKED || STAGE == 0 || (ACC && STAGE == 1),
+                  "the recomputing kernel runs both phases, or phase 1 alone in accumulate mode");
     constexpr int cell = TAU ? CFC_CELL_TAU_DECAY : CFC_CELL_GATED;
     const int K = win.Kw;  // steps of this launch; indices below are relative to win.k0
     const long long Kf = win.K, k0 = win.k0;
@@ -3041,7 +3047,9 @@ void set_kernel_attributes() {
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<false, true, false, 0, true>),
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, false, 0, true>),
                               reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false, true, 1, true>),
-                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, true, 1, true>)})
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, true, 1, true>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, false, false, 1, true>),
+                              reinterpret_cast<const void*>(&cfc_bwd_large_kernel<true, true, false, 1, true>)})
             (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
         for (const void* f : {reinterpret_cast<const void*>(&cfc_bwd_large_grads_kernel<false>),
                               reinterpret_cast<const void*>(&cfc_bwd_large_grads_kernel<true>)})
@@ -3193,6 +3201,23 @@ int backward_window(const cfc_params_t* params, const float* x, const float* h0,
     if (large) {
         const long long groups = ((long long)B + kLR - 1) / kLR;
         const bool tau = params->cell == CFC_CELL_TAU_DECAY, full = large_full(params);
+        auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+        // accumulating a whole sequence at exactly 256 x 256, K <= 8: phase 1
+        // alone (dL/da into the workspace, dL/dw_tau added to the scratch),
+        // then the vector phase 2's read-add-write
+        if (full && flags == CFC_ACCUMULATE && k_begin == 0 && Kw == K && !delta_in && K <= kGradsMaxK &&
+            al16(x) && al16(h0) && al16(h_seq) && al16(scratch)) {
+            auto st1 = tau ? &cfc_bwd_large_kernel<true, true, false, 1, true>
+                           : &cfc_bwd_large_kernel<true, false, false, 1, true>;
+            hipLaunchKernelGGL(st1, dim3((unsigned)groups), dim3(kThreads), lds, stream, params->w_in, params->w_rec,
+                               params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, win, n_in, H, scratch, loss,
+                               grad_x, static_cast<unsigned*>(workspace), nullptr);
+            const int rc = launch_status();
+            if (rc) return rc;
+            hipLaunchKernelGGL(cfc_bwd_large_grads_kernel<true>, dim3((unsigned)B), dim3(kThreads), kGradsLdsReserve,
+                               stream, x, h0, h_seq, K, scratch, N, static_cast<const unsigned*>(workspace));
+            return launch_status();
+        }
         auto kern = full ? (tau ? &cfc_bwd_large_kernel<true, true, false> : &cfc_bwd_large_kernel<true, false, false>)
                          : (tau ? &cfc_bwd_large_kernel<false, true, false> : &cfc_bwd_large_kernel<false, false, false>);
         if (flags == CFC_ACCUMULATE)
