@@ -222,7 +222,11 @@ long long cfc_backward_workspace(int B, int Kw, int n_in, int n_hid, int flags);
  * the summation order of the kernel that runs (the 16-row kernel's overwrite
  * and accumulate modes compute the same float32 gradient, bitwise).  The
  * workspace is ignored where the window does not use it (overwrite mode, or
- * n_in, n_hid <= 128, or more than 20 steps at the wider shapes). */
+ * n_in, n_hid <= 128, or more than 20 steps at the wider shapes).  A window
+ * over the whole sequence, seeded from y, at exactly 256 x 256 with K <= 8
+ * (x, h0, h_seq and the scratch 16-byte aligned) runs as two launches: the
+ * reverse pass, which leaves dL/da in the workspace and adds dL/dw_tau to the
+ * scratch, then the weight gradients and db, added on the vector units. */
 int cfc_backward_window_ws(const cfc_params_t *params, const float *x, const float *h0,
                            const float *h_seq, const float *y, const float *delta_in, float dt,
                            int B, int K, int k_begin, int k_end, float *scratch, float *loss,
