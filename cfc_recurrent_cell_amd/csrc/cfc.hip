@@ -1764,7 +1764,12 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
         }
         __syncthreads();  // every wave is done reading zx / zh of step k
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < 4; ++tb) {
+            // the four units' states first: read after a store to zh, each
+            // unit's read would wait for the previous unit's store
+            double hv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) hv[v] = zh[zidx(lunit(wave, tb, s + 4 * v), r)];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int i = lunit(wave, tb, s + 4 * v);
@@ -1777,9 +1782,9 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large_kernel(
                                      ? spdt_v[tb][v]
                                      : inv_one_plus_exp_exact(spdt_v[tb][v], spdt_v[tb][v] * kLog2e, a);
                 const double c = fma(-2.0, inv_one_plus_exp_exact(2.0, 2.0 * kLog2e, a), 1.0);
-                double* hp = zh + zidx(i, r);
-                *hp = fma(g, *hp - c, c);  // g*h + (1-g)*c
+                zh[zidx(i, r)] = fma(g, hv[v] - c, c);  // g*h + (1-g)*c
             }
+        }
 #pragma unroll
         for (int m = 0; m < kLR; ++m) {
             const int e = t + kThreads * m;
