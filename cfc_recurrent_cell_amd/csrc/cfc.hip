@@ -2731,8 +2731,9 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
 // concurrent write streams keep HBM busier: 0.84 -> 0.81 ms for the 4.3 GB
 // of B = 8192, bitwise the same (two or three per CU measured 0.83 ms; a
 // persistent grid of 256 workgroups looping over rows, 0.84 ms).
-// ACC (accumulate mode): dL/da comes from the caller's workspace `ws` (rows of
-// 2 K H words, where the parked phase 1 left it), dL/dw_tau has already been
+// ACC (accumulate mode, after the parked phase 1 of the one-call entry or the
+// recomputing one of cfc_backward): dL/da comes from the caller's workspace
+// `ws` (rows of 2 K H words, where phase 1 left it), dL/dw_tau has already been
 // added by that phase, and each gradient element, rounded to float32, is added
 // to the scratch element in float32.  The old values are read with
 // non-temporal loads one block of eight loop trips (16 unit rows) ahead, and
