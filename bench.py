@@ -327,8 +327,10 @@ def main():
         C.cfc_forward(w_in, w_rec, b, w_tau, x, h0, dt, h_seq=h_seq, cell=cell)
 
     # accumulate mode at widths above 128 (K <= 20): the 16-row backward parks
-    # dL/da in a caller workspace instead of the scratch tail
-    acc_ws_bytes = C.cfc_backward_workspace(B, K, n_in, H, accumulate=True)
+    # dL/da in a caller workspace instead of the scratch tail; the one-call
+    # entry's size also holds its float64 weight copy at 256 x 256 (the
+    # backward alone uses the leading part)
+    acc_ws_bytes = C.cfc_forward_backward_workspace(B, K, n_in, H, accumulate=True)
     acc_ws = torch.empty((acc_ws_bytes,), dtype=torch.uint8, device=dev) if acc_ws_bytes > 0 else None
 
     def bwd(ig=False, accumulate=False):

@@ -19,7 +19,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["cfc_forward", "cfc_backward", "cfc_backward_window", "cfc_backward_windows",
-           "cfc_backward_workspace", "cfc_forward_backward", "reduce_axis0", "reduce_axis0_noalloc",
+           "cfc_backward_workspace", "cfc_forward_backward_workspace", "cfc_forward_backward", "reduce_axis0", "reduce_axis0_noalloc",
            "reduce_axis0_split_workspace", "cfc_scratch_row_len", "CfcError", "load_library"]
 
 
@@ -98,14 +98,16 @@ def _workspace_arg(workspace):
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
-def _accumulate_workspace(x, p, K, accumulate, workspace):
+def _accumulate_workspace(x, p, K, accumulate, workspace, one_call=False):
     """The workspace accumulate mode needs at widths above 128 (K <= 20), allocated here when the
     caller passed none: without it that mode runs the general one-row-per-workgroup backward,
-    about 8x slower at B=8192, K=8, 256/256."""
+    about 8x slower at B=8192, K=8, 256/256.  The one-call entry gets its own size, which also
+    holds its float64 weight copy at 256 x 256."""
     import torch
     if workspace is not None or not accumulate:
         return workspace
-    need = cfc_backward_workspace(x.shape[0], K, p.n_in, p.n_hid, accumulate=True)
+    size = cfc_forward_backward_workspace if one_call else cfc_backward_workspace
+    need = size(x.shape[0], K, p.n_in, p.n_hid, accumulate=True)
     return torch.empty((need,), dtype=torch.uint8, device=x.device) if need > 0 else None
 
 
@@ -116,6 +118,16 @@ def cfc_backward_workspace(B: int, Kw: int, n_in: int, n_hid: int, accumulate: b
                                                    CFC_ACCUMULATE if accumulate else CFC_OVERWRITE))
     if n < 0:
         raise ValueError(f"invalid backward size B={B} Kw={Kw} n_in={n_in} n_hid={n_hid}")
+    return n
+
+
+def cfc_forward_backward_workspace(B: int, K: int, n_in: int, n_hid: int, accumulate: bool = True) -> int:
+    """Bytes of workspace cfc_forward_backward_ws runs best with: the backward's
+    size, plus its float64 weight copy at 256 x 256 with K <= 8."""
+    n = int(load_library().cfc_forward_backward_workspace(B, K, n_in, n_hid,
+                                                          CFC_ACCUMULATE if accumulate else CFC_OVERWRITE))
+    if n < 0:
+        raise ValueError(f"invalid size B={B} K={K} n_in={n_in} n_hid={n_hid}")
     return n
 
 
@@ -251,7 +263,8 @@ def cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt: float, h_seq=None,
     ``input_grads`` (or explicit buffers) grad_x and grad_h0 are appended.
     Accumulate mode at widths above 128 with K <= 20 runs the 16-row backward
     through cfc_forward_backward_ws with a device ``workspace`` of
-    cfc_backward_workspace bytes, allocated here unless given."""
+    cfc_forward_backward_workspace bytes (at least cfc_backward_workspace),
+    allocated here unless given."""
     import torch
     lib = load_library()
     p = _params(w_in, w_rec, b, w_tau, cell)
@@ -274,7 +287,7 @@ def cfc_forward_backward(w_in, w_rec, b, w_tau, x, h0, y, dt: float, h_seq=None,
     grad_x, grad_h0 = _input_grad_buffers(x, p, grad_x, grad_h0, input_grads)
     flags = CFC_ACCUMULATE if accumulate else CFC_OVERWRITE
     ptr = lambda t: t.data_ptr() if t is not None else None
-    workspace = _accumulate_workspace(x, p, K, accumulate, workspace)
+    workspace = _accumulate_workspace(x, p, K, accumulate, workspace, one_call=True)
     if workspace is not None:
         ws_ptr, ws_bytes = _workspace_arg(workspace)
         _check("cfc_forward_backward_ws", lib.cfc_forward_backward_ws(

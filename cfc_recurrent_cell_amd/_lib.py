@@ -66,6 +66,8 @@ def load_library(path: str = LIB_PATH):
                                         vp, i, vp]
     lib.cfc_backward_workspace.restype = ll
     lib.cfc_backward_workspace.argtypes = [i, i, i, i, i]
+    lib.cfc_forward_backward_workspace.restype = ll
+    lib.cfc_forward_backward_workspace.argtypes = [i, i, i, i, i]
     lib.cfc_backward_window_ws.restype = i
     lib.cfc_backward_window_ws.argtypes = [ctypes.POINTER(CfcParams), vp, vp, vp, vp, vp, f, i, i, i, i, vp, vp,
                                            vp, vp, i, vp, ll, vp]

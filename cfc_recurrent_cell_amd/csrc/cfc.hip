@@ -1823,10 +1823,7 @@ __global__ __launch_bounds__(kThreads) void widen_weights_kernel(const float* __
 }
 // a quarter of the copy: 128 unit rows of 256 doubles
 constexpr int kWideQuarterBytes = 128 * kLarge * 8;
-// unit row u of W_in (g = 0) or W_rec (g = 1) in the widened copy
-__device__ __forceinline__ const double* wide_row(const float* wide, long long N, int g, int u) {
-    return reinterpret_cast<const double*>(wide + (long long)(2 * g + (u >> 7)) * N) + (u & 127) * kLarge;
-}
+constexpr long long kWideQuarterFloats = kWideQuarterBytes / 4;
 // four consecutive weights of one unit row, as the products take them
 struct W4f {
     float4 v;
@@ -1848,8 +1845,9 @@ struct W4d {
 // PARK as in cfc_fwd_large_kernel: a_k of row b goes to a_park + b N, with
 // N the scratch row length (overwrite mode) or 2 K H (the caller's workspace
 // in accumulate mode).  W64: the weights come from the widened float64 copy
-// `wide` (scratch row 0 + 2 K H floats, quarters N floats apart, see
-// widen_weights_kernel).
+// `wide`, its quarters wstride floats apart (see widen_weights_kernel: in
+// scratch rows 0..3 in overwrite mode, after the parks in the workspace in
+// accumulate mode).
 constexpr int kLR2 = 32;  // batch rows per workgroup of the 32-row forward
 __device__ __forceinline__ int zidx2(int j, int r) { return j * kLR2 + (r ^ (j & 31)); }
 __host__ __device__ constexpr size_t large32_fwd_lds_bytes() {
@@ -1860,7 +1858,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large32_kernel(
     const float* __restrict__ w_in, const float* __restrict__ w_rec, const float* __restrict__ bias,
     const float* __restrict__ w_tau, const float* __restrict__ x, const float* __restrict__ h0, double dt, int B,
     int K, float* __restrict__ h_seq, int cell, float* __restrict__ a_park, long long N,
-    const float* __restrict__ wide) {
+    const float* __restrict__ wide, long long wstride) {
     constexpr int H = kLarge, NI = kLarge;
     extern __shared__ __align__(16) unsigned char smem[];
     float* zx = reinterpret_cast<float*>(smem);                          // [256][32] x_k
@@ -1957,7 +1955,7 @@ __global__ __launch_bounds__(kThreads) void cfc_fwd_large32_kernel(
                 // 0.37 against 0.41 ms for the forward at B = 8192.
                 const int wq = __builtin_amdgcn_readfirstlane(wave);
                 const __amdgpu_buffer_rsrc_t rs =
-                    __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(wide + (long long)(2 * g + (wq >> 1)) * N),
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(wide + (long long)(2 * g + (wq >> 1)) * wstride),
                                                       (short)0, kWideQuarterBytes, kBufferRsrcWord3);
                 int voff[4];
 #pragma unroll
@@ -2086,7 +2084,8 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
     const float* __restrict__ bias, const float* __restrict__ w_tau,
     const float* __restrict__ x, const float* __restrict__ h0, const float* __restrict__ h_seq,
     const float* __restrict__ y, double dt, int B, BwdWindow win, int n_in, int H, float* __restrict__ scratch,
-    float* __restrict__ loss, float* __restrict__ grad_x, unsigned* __restrict__ ws, const float* __restrict__ wide) {
+    float* __restrict__ loss, float* __restrict__ grad_x, unsigned* __restrict__ ws, const float* __restrict__ wide,
+    long long wstride) {
     static_assert(!ACC || STAGE != 2, "accumulate mode: both phases in one launch, or phase 1 alone");
     static_assert(PARKED || STAGE == 0 || (ACC && STAGE == 1),
                   "the recomputing kernel runs both phases, or phase 1 alone in accumulate mode");
@@ -2220,13 +2219,14 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
             if (wide) {
                 // chunk ic of k-slot s is unit row i = 64 s + ic: the lane's
                 // quarter of the copy is fixed (i >> 7 = s >> 1).  One buffer
-                // descriptor spans both quarters of the matrix (rows 2g and
-                // 2g + 1 of the scratch); the lane's offset selects its quarter
-                // and column, the chunk's row goes in the scalar offset.
+                // descriptor spans both quarters of the matrix (quarters 2g
+                // and 2g + 1, wstride floats apart); the lane's offset selects
+                // its quarter and column, the chunk's row goes in the scalar
+                // offset.
                 const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                    const_cast<float*>(wide + (long long)(2 * g) * N), (short)0,
-                    (int)(N * 4) + kWideQuarterBytes, kBufferRsrcWord3);
-                const int voff = (int)((s >> 1) * N * 4) + ((64 * (s & 1)) * kLarge + jw) * 8;
+                    const_cast<float*>(wide + (long long)(2 * g) * wstride), (short)0,
+                    (int)(wstride * 4) + kWideQuarterBytes, kBufferRsrcWord3);
+                const int voff = (int)((s >> 1) * wstride * 4) + ((64 * (s & 1)) * kLarge + jw) * 8;
                 auto wld64 = [&](int ic) -> W4d {
                     const auto lo = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, ic * kLarge * 8, 0);
                     const auto hi = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, ic * kLarge * 8, 0);
@@ -3152,7 +3152,7 @@ extern "C" int cfc_forward(const cfc_params_t* params, const float* x, const flo
         const long long groups = ((long long)B + kLR2 - 1) / kLR2;
         hipLaunchKernelGGL((cfc_fwd_large32_kernel<false, false>), dim3((unsigned)groups), dim3(kThreads),
                            large32_fwd_lds_bytes(), stream, params->w_in, params->w_rec, params->b, params->w_tau, x,
-                           h0, (double)dt, B, K, h_seq, params->cell, nullptr, 0LL, nullptr);
+                           h0, (double)dt, B, K, h_seq, params->cell, nullptr, 0LL, nullptr, 0LL);
         return launch_status();
     }
     const long long groups = ((long long)B + kLR - 1) / kLR;
@@ -3170,6 +3170,16 @@ extern "C" long long cfc_backward_workspace(int B, int Kw, int n_in, int n_hid, 
     if (!wide || Kw > kLargeBwdMaxK || flags != CFC_ACCUMULATE) return 0;
     long long n;  // dL/da of every row-step in float64
     if (!mul_ok(8LL * B * Kw, n_hid, &n)) return -1;
+    return n;
+}
+
+extern "C" long long cfc_forward_backward_workspace(int B, int K, int n_in, int n_hid, int flags) {
+    const long long n = cfc_backward_workspace(B, K, n_in, n_hid, flags);
+    if (n <= 0) return n;
+    // accumulate mode at 256 x 256 with K <= 8: the forward's float64 weight
+    // copy after the parked values
+    if (n_in == kLarge && n_hid == kLarge && K <= kGradsMaxK)
+        return n <= LLONG_MAX - kWideElems * 8 ? n + kWideElems * 8 : -1;
     return n;
 }
 
@@ -3247,7 +3257,7 @@ int backward_window(const cfc_params_t* params, const float* x, const float* h0,
                            : &cfc_bwd_large_kernel<true, false, false, 1, true>;
             hipLaunchKernelGGL(st1, dim3((unsigned)groups), dim3(kThreads), lds, stream, params->w_in, params->w_rec,
                                params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, win, n_in, H, scratch, loss,
-                               grad_x, static_cast<unsigned*>(workspace), nullptr);
+                               grad_x, static_cast<unsigned*>(workspace), nullptr, 0LL);
             const int rc = launch_status();
             if (rc) return rc;
             hipLaunchKernelGGL(cfc_bwd_large_grads_kernel<true>, dim3((unsigned)B), dim3(kThreads), kGradsLdsReserve,
@@ -3263,7 +3273,7 @@ int backward_window(const cfc_params_t* params, const float* x, const float* h0,
                                : &cfc_bwd_large_kernel<false, false, false, 0, true>);
         hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kThreads), lds, stream, params->w_in, params->w_rec,
                            params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, win, n_in, H, scratch, loss,
-                           grad_x, ws_used ? static_cast<unsigned*>(workspace) : nullptr, nullptr);
+                           grad_x, ws_used ? static_cast<unsigned*>(workspace) : nullptr, nullptr, 0LL);
         return launch_status();
     }
     hipLaunchKernelGGL(cfc_bwd_kernel, dim3(B), dim3(kThreads), lds, stream, params->w_in,
@@ -3340,9 +3350,14 @@ int forward_backward(const cfc_params_t* params, const float* x, const float* h0
     const long long ws_need = cfc_backward_workspace(B, K, n_in, H, flags);
     if (ws_need < 0) return CFC_ERR_DIM;
     const bool ws_used = workspace && ws_need > 0;
+    // a workspace of cfc_forward_backward_workspace bytes also holds the
+    // float64 weight copy of the accumulate path at 256 x 256
+    const long long ws_full = cfc_forward_backward_workspace(B, K, n_in, H, flags);
+    const bool ws_wide = ws_used && ws_full > ws_need && workspace_bytes >= ws_full;
     if (ws_used) {
         if (workspace_bytes < ws_need || (reinterpret_cast<uintptr_t>(workspace) & 7) != 0) return CFC_ERR_DIM;
-        const Range w{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + (uintptr_t)ws_need};
+        const Range w{reinterpret_cast<uintptr_t>(workspace),
+                      reinterpret_cast<uintptr_t>(workspace) + (uintptr_t)(ws_wide ? ws_full : ws_need)};
         if (!outputs_disjoint(&w, 1, outs, 5) || !outputs_disjoint(&w, 1, ins, 7)) return CFC_ERR_OVERLAP;
     }
     const bool large = (n_in > kSmall || H > kSmall) && K <= kLargeBwdMaxK && (flags == CFC_OVERWRITE || ws_used);
@@ -3358,17 +3373,27 @@ int forward_backward(const cfc_params_t* params, const float* x, const float* h0
         al16(h0) && al16(h_seq) && al16(scratch)) {
         set_kernel_attributes();
         const bool tau = params->cell == CFC_CELL_TAU_DECAY;
-        hipLaunchKernelGGL((cfc_fwd_large32_kernel<true, false>), dim3((unsigned)(((long long)B + kLR2 - 1) / kLR2)),
-                           dim3(kThreads), large32_fwd_lds_bytes(), stream, params->w_in, params->w_rec, params->b,
-                           params->w_tau, x, h0, (double)dt, B, K, h_seq, params->cell,
-                           reinterpret_cast<float*>(workspace), 2LL * K * H, nullptr);
+        // the float64 weight copy after the parks, where the workspace has
+        // room for it (cfc_forward_backward_workspace) and is 16-byte aligned
+        float* wide = nullptr;
+        if (ws_wide && al16(workspace)) {
+            wide = reinterpret_cast<float*>(workspace) + 2LL * B * K * H;
+            hipLaunchKernelGGL(widen_weights_kernel, dim3((unsigned)(kWideElems / kThreads)), dim3(kThreads), 0,
+                               stream, params->w_in, params->w_rec, wide, kWideQuarterFloats);
+        }
+        auto fwd = wide ? &cfc_fwd_large32_kernel<true, true> : &cfc_fwd_large32_kernel<true, false>;
+        hipLaunchKernelGGL(fwd, dim3((unsigned)(((long long)B + kLR2 - 1) / kLR2)), dim3(kThreads),
+                           large32_fwd_lds_bytes(), stream, params->w_in, params->w_rec, params->b, params->w_tau, x, h0,
+                           (double)dt, B, K, h_seq, params->cell, reinterpret_cast<float*>(workspace), 2LL * K * H,
+                           wide, kWideQuarterFloats);
         rc = launch_status();
         if (rc) return rc;
         const BwdWindow win{K, 0, K, nullptr, grad_h0};
         auto bwd1 = tau ? &cfc_bwd_large_kernel<true, true, true, 1, true> : &cfc_bwd_large_kernel<true, false, true, 1, true>;
         hipLaunchKernelGGL(bwd1, dim3((unsigned)(((long long)B + kLR - 1) / kLR)), dim3(kThreads), large_bwd_lds_bytes(),
                            stream, params->w_in, params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt,
-                           B, win, n_in, H, scratch, loss, grad_x, static_cast<unsigned*>(workspace), nullptr);
+                           B, win, n_in, H, scratch, loss, grad_x, static_cast<unsigned*>(workspace), wide,
+                           kWideQuarterFloats);
         rc = launch_status();
         if (rc) return rc;
         hipLaunchKernelGGL(cfc_bwd_large_grads_kernel<true>, dim3((unsigned)B), dim3(kThreads), kGradsLdsReserve, stream,
@@ -3394,11 +3419,11 @@ int forward_backward(const cfc_params_t* params, const float* x, const float* h0
                                stream, params->w_in, params->w_rec, wide, N);
             hipLaunchKernelGGL((cfc_fwd_large32_kernel<true, true>), dim3((unsigned)(((long long)B + kLR2 - 1) / kLR2)),
                                dim3(kThreads), large32_fwd_lds_bytes(), stream, params->w_in, params->w_rec, params->b,
-                               params->w_tau, x, h0, (double)dt, B, K, h_seq, params->cell, scratch, N, wide);
+                               params->w_tau, x, h0, (double)dt, B, K, h_seq, params->cell, scratch, N, wide, N);
         } else if (full) {
             hipLaunchKernelGGL((cfc_fwd_large32_kernel<true, false>), dim3((unsigned)(((long long)B + kLR2 - 1) / kLR2)),
                                dim3(kThreads), large32_fwd_lds_bytes(), stream, params->w_in, params->w_rec, params->b,
-                               params->w_tau, x, h0, (double)dt, B, K, h_seq, params->cell, scratch, N, nullptr);
+                               params->w_tau, x, h0, (double)dt, B, K, h_seq, params->cell, scratch, N, nullptr, 0LL);
         } else
             hipLaunchKernelGGL((cfc_fwd_large_kernel<false, true>), dim3((unsigned)groups), dim3(kThreads),
                                large_fwd_lds_bytes(), stream, params->w_in, params->w_rec, params->b, params->w_tau, x,
@@ -3421,7 +3446,7 @@ int forward_backward(const cfc_params_t* params, const float* x, const float* h0
             }
             hipLaunchKernelGGL(bwd, dim3((unsigned)groups), dim3(kThreads), large_bwd_lds_bytes(), stream, params->w_in,
                                params->w_rec, params->b, params->w_tau, x, h0, h_seq, y, (double)dt, B, win, n_in, H,
-                               scratch, loss, grad_x, nullptr, bwd == bwd1 ? wide : nullptr);
+                               scratch, loss, grad_x, nullptr, bwd == bwd1 ? wide : nullptr, N);
         }
         return launch_status();
     }

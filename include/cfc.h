@@ -201,6 +201,15 @@ int cfc_backward_window(const cfc_params_t *params, const float *x, const float 
  * Returns -1 for a non-positive size, unknown flags or overflow. */
 long long cfc_backward_workspace(int B, int Kw, int n_in, int n_hid, int flags);
 
+/* Bytes of device workspace for cfc_forward_backward_ws to run at its best:
+ * cfc_backward_workspace(B, K, n_in, n_hid, flags), plus 1 MiB at exactly
+ * 256 x 256 with K <= 8 in accumulate mode, where the call then also keeps a
+ * float64 copy of W_in and W_rec there (the forward and the reverse pass read
+ * it instead of converting the float32 weights; same results, bitwise).  A
+ * workspace of only cfc_backward_workspace bytes is still accepted there.
+ * Returns -1 for a non-positive size, unknown flags or overflow. */
+long long cfc_forward_backward_workspace(int B, int K, int n_in, int n_hid, int flags);
+
 /* cfc_backward_window with a caller-owned device workspace.  The pages' form
  * of the backward adds each call's gradient into the scratch ("K-loop
  * Parallelization Implementation Plan", Task 5: scratch zeroed once, the K
@@ -279,9 +288,13 @@ int cfc_forward_backward(const cfc_params_t *params, const float *x, const float
  *   workspace        device memory, 8-byte aligned, or NULL; contents on entry
  *                    ignored, on return unspecified
  *   workspace_bytes  at least cfc_backward_workspace(B, K, n_in, n_hid, flags)
- *                    where it is used (else CFC_ERR_DIM); a workspace that
- *                    overlaps another argument is CFC_ERR_OVERLAP.  Both are
- *                    checked before the forward is enqueued. */
+ *                    where it is used (else CFC_ERR_DIM);
+ *                    cfc_forward_backward_workspace(...) bytes let the
+ *                    256 x 256 accumulate path keep its float64 weight copy
+ *                    there too (the range checked for overlap is then that
+ *                    size).  A workspace that overlaps another argument is
+ *                    CFC_ERR_OVERLAP.  Both are checked before the forward is
+ *                    enqueued. */
 int cfc_forward_backward_ws(const cfc_params_t *params, const float *x, const float *h0,
                             const float *y, float dt, int B, int K, float *h_seq, float *scratch,
                             float *loss, float *grad_x, float *grad_h0, int flags,

@@ -29,7 +29,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"cfc_scratch_row_len", "cfc_forward", "cfc_backward", "cfc_backward_window",
                           "cfc_forward_backward", "reduce_axis0", "reduce_axis0_split",
                           "reduce_axis0_split_workspace", "cfc_status_string", "cfc_backward_workspace",
-                          "cfc_backward_window_ws", "cfc_forward_backward_ws", "reduce_axis0_split_noalloc"}
+                          "cfc_backward_window_ws", "cfc_forward_backward_ws", "reduce_axis0_split_noalloc",
+                          "cfc_forward_backward_workspace"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -184,6 +185,19 @@ def test_backward_workspace_sizes(lib):
     assert ws(2**31 - 1, 20, 256, 2**31 - 1, C.CFC_ACCUMULATE) == -1   # overflow
 
 
+def test_forward_backward_workspace_sizes(lib):
+    """The one-call entry's size: the backward's, plus the 1 MiB float64 weight
+    copy (2 x 256 x 256 doubles) at exactly 256 x 256 with K <= 8 in
+    accumulate mode."""
+    fb, bw = lib.cfc_forward_backward_workspace, lib.cfc_backward_workspace
+    A = C.CFC_ACCUMULATE
+    assert fb(8192, 8, 256, 256, A) == 8 * 8192 * 8 * 256 + 2 * 256 * 256 * 8
+    assert fb(3, 1, 256, 256, A) == bw(3, 1, 256, 256, A) + (1 << 20)
+    for args in ((3, 9, 256, 256, A), (3, 8, 200, 256, A), (3, 8, 256, 200, A), (3, 8, 256, 256, C.CFC_OVERWRITE),
+                 (3, 64, 128, 128, A), (3, 21, 256, 256, A), (0, 8, 256, 256, A), (3, 8, 256, 256, 7)):
+        assert fb(*args) == bw(*args), args
+
+
 def _win_ws(lib, p, ws, ws_bytes, k_begin=0, k_end=6, K=6, flags=C.CFC_ACCUMULATE, scratch=FAKE + 0x900000):
     return lib.cfc_backward_window_ws(ctypes.byref(p), FAKE + 0x400000, FAKE + 0x500000, FAKE + 0x600000,
                                       FAKE + 0x700000, None, 1.0, 2, K, k_begin, k_end, scratch, None, None, None,
@@ -222,6 +236,12 @@ def test_forward_backward_ws_validation(lib):
                                            ws, nbytes, None)
     assert fbw(WS, need - 1) == C.CFC_ERR_DIM
     assert fbw(WS + 4, need) == C.CFC_ERR_DIM
+    # with room for the float64 weight copy the whole size is checked for
+    # overlap: this workspace ends 32 KB before the scratch, its copy would not
+    full = lib.cfc_forward_backward_workspace(2, 6, 256, 256, C.CFC_ACCUMULATE)
+    assert full == need + (1 << 20)
+    near = FAKE + 0x900000 - 0x8000
+    assert fbw(near, full) == C.CFC_ERR_OVERLAP
     assert fbw(FAKE + 0x600000, need) == C.CFC_ERR_OVERLAP     # over h_seq
     assert fbw(FAKE + 0x900000, need) == C.CFC_ERR_OVERLAP     # over the scratch
     assert fbw(FAKE + 0x200000, need) == C.CFC_ERR_OVERLAP     # over b

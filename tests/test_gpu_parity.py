@@ -101,8 +101,9 @@ def test_large_workload_all_rows():
                   row, the backward's two stages read it back and park dL/da
                   in the row's tail);
       accumulate  cfc_forward_backward_ws accumulating onto a base that
-                  depends on row and column (dL/da parked in the workspace),
-                  compared as result - base.
+                  depends on row and column (a_k and dL/da parked in the
+                  workspace, the float64 weight copy after them), compared as
+                  result - base.
     Every h_seq element, every scratch row (block by block), the loss and the
     reduced gradient; each path is then run again and must repeat bitwise."""
     import torch
@@ -116,7 +117,7 @@ def test_large_workload_all_rows():
     # base[b, j] = (b % 7 - 3) + (j % 5 - 2): small integers, exact in float32
     rowval = (torch.arange(B, device="cuda") % 7 - 3).float()
     colval = (torch.arange(N, device="cuda") % 5 - 2).float()
-    ws = torch.empty((C.cfc_backward_workspace(B, K, n_in, H),), dtype=torch.uint8, device="cuda")
+    ws = torch.empty((C.cfc_forward_backward_workspace(B, K, n_in, H),), dtype=torch.uint8, device="cuda")
 
     def run(path):
         scratch = torch.empty((B, N), device="cuda")

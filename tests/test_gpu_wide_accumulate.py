@@ -145,6 +145,15 @@ def test_one_call_entry_with_workspace(case):
         odd = run(torch.from_numpy(base.copy()).cuda(), ws_mem.view(torch.uint8)[8:8 + need])
         for a, b_, name in zip(odd, acc, names):
             assert np.array_equal(a.view(np.uint32), b_.view(np.uint32)), f"8-byte-aligned workspace: {name}"
+        # room for the float64 weight copy: the widened weights give the same
+        # bits; 8- but not 16-byte aligned, the copy is skipped
+        full = C.cfc_forward_backward_workspace(B, K, n, n)
+        assert full == need + (1 << 20)
+        big = torch.full(((full + 16) // 4,), float("nan"), device="cuda").view(torch.uint8)
+        for off, what in ((0, "float64 weight copy"), (8, "8-byte-aligned full-size workspace")):
+            got = run(torch.from_numpy(base.copy()).cuda(), big[off:off + full])
+            for a, b_, name in zip(got, acc, names):
+                assert np.array_equal(a.view(np.uint32), b_.view(np.uint32)), f"{what}: {name}"
     else:
         h2 = C.cfc_forward(*args, d["dt"], cell=cell)
         s2, l2, gx2, gh2 = C.cfc_backward(*args, h2, d["y"], d["dt"],
