@@ -280,7 +280,9 @@ int cfc_forward_backward(const cfc_params_t *params, const float *x, const float
  * scratch 16-byte aligned) it is three launches, as in overwrite mode: the
  * forward parks its float64 pre-activations in the workspace, the reverse
  * pass reads them back, leaves dL/da there and adds dL/dw_tau to the scratch,
- * and the last launch adds the weight gradients and db.  The gradient added is
+ * and the last launch adds the weight gradients and db; with a 16-byte-aligned
+ * workspace of cfc_forward_backward_workspace bytes a fourth, first launch
+ * copies the weights to float64 there, as overwrite mode does in the scratch.  The gradient added is
  * then the one cfc_forward_backward writes in overwrite mode, bitwise (rounded
  * to float32, then added in float32); the other shapes add the gradient of
  * cfc_forward followed by cfc_backward.
