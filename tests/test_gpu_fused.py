@@ -280,11 +280,12 @@ def test_fused_256_dispatch_variants(cell):
     """At exactly 256 x 256, K <= 8 the one-call entry picks its kernels by
     alignment: the float64 weight copy needs a 16-byte-aligned scratch, the
     vector-unit weight-gradient phase also 16-byte-aligned x, h0 and h_seq.
-    With x one float off alignment (weight copy, matrix-core phase 2) and
-    with the scratch two floats off (float32 weights, matrix-core phase 2)
-    every output must be bitwise the same -- the widening is exact and the
-    phase-2 kernel is the same -- and each variant within tolerance of the
-    oracle, including the all-aligned one (weight copy, vector phase 2)."""
+    All aligned (weight copy, vector phase 2), with x one float off
+    alignment (weight copy, matrix-core phase 2) and with the scratch two
+    floats off (float32 weights, matrix-core phase 2) every output must be
+    bitwise the same -- the widening is exact, and both phase-2 forms sum each
+    element's K products in step order -- and within tolerance of the
+    oracle."""
     import torch
     import cfc_recurrent_cell_amd as C
     B, K, n = 37, 8, 256
@@ -303,8 +304,9 @@ def test_fused_256_dispatch_variants(cell):
         h, s, l, gx, gh = C.cfc_forward_backward(d["w_in"], d["w_rec"], d["b"], d["w_tau"], xx, d["h0"], d["y"],
                                                  d["dt"], scratch=sc, input_grads=True, cell=cell)
         outs[name] = [host(t) for t in (h, s, l, gx, gh)]
-    for name, a, b_ in zip(("h_seq", "scratch", "loss", "grad_x", "grad_h0"), outs["x_off"], outs["scratch_off"]):
-        assert np.array_equal(a.view(np.uint32), b_.view(np.uint32)), f"{cell}: {name} differs"
+    for other in ("x_off", "scratch_off"):
+        for name, a, b_ in zip(("h_seq", "scratch", "loss", "grad_x", "grad_h0"), outs["aligned"], outs[other]):
+            assert np.array_equal(a.view(np.uint32), b_.view(np.uint32)), f"{cell}: {name} differs ({other})"
     ref = O.cfc_step(inp, threads=oracle_threads(), input_grads=True)
     for variant, o in outs.items():
         assert np.isfinite(o[1]).all(), variant
