@@ -2401,13 +2401,23 @@ __global__ __launch_bounds__(kThreads) void cfc_bwd_large_kernel(
             dab_product(w_in, 0, n_in, n_in, acc3, k > 0, k);
             if (row_ok) {
                 float* gx = grad_x + (b_own * Kf + k0 + k) * n_in;
+                if (FULL && (reinterpret_cast<uintptr_t>(grad_x) & 15) == 0) {
+                    // columns lunit(wave, 0..3, m) are consecutive: one float4
+                    // per m (B = 8192 with input gradients: 1.591 -> 1.574 ms
+                    // for the one-call kernels, against 16 scalar stores)
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
+                    for (int v = 0; v < 4; ++v)
+                        *reinterpret_cast<f32x4*>(gx + lunit(wave, 0, s + 4 * v)) =
+                            f32x4{(float)acc3[0][v], (float)acc3[1][v], (float)acc3[2][v], (float)acc3[3][v]};
+                } else {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int j = lunit(wave, tb, s + 4 * v);
-                        if (j < n_in) gx[j] = (float)acc3[tb][v];
-                    }
+                    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int j = lunit(wave, tb, s + 4 * v);
+                            if (j < n_in) gx[j] = (float)acc3[tb][v];
+                        }
+                }
             }
         }
         // park dL/da_k of the 16 rows (PARKED: over a_k, in the heads; else in
