@@ -103,7 +103,11 @@ def test_large_workload_all_rows():
       accumulate  cfc_forward_backward_ws accumulating onto a base that
                   depends on row and column (a_k and dL/da parked in the
                   workspace, the float64 weight copy after them), compared as
-                  result - base.
+                  result - base;
+      bwd_accumulate  cfc_forward + cfc_backward accumulating onto the same
+                  base with the workspace (the recomputing reverse pass alone,
+                  then the vector weight-gradient phase adding into the
+                  scratch), compared as result - base.
     Every h_seq element, every scratch row (block by block), the loss and the
     reduced gradient; each path is then run again and must repeat bitwise."""
     import torch
@@ -127,13 +131,18 @@ def test_large_workload_all_rows():
         if path == "one_call":
             scratch.fill_(float("nan"))
             h_seq, scratch, loss = C.cfc_forward_backward(*args, d["y"], d["dt"], scratch=scratch)
-        else:
+        elif path == "accumulate":
             torch.add(rowval[:, None], colval[None, :], out=scratch)
             h_seq, scratch, loss = C.cfc_forward_backward(*args, d["y"], d["dt"], scratch=scratch,
                                                           accumulate=True, workspace=ws)
+        else:
+            torch.add(rowval[:, None], colval[None, :], out=scratch)
+            h_seq = C.cfc_forward(*args, d["dt"])
+            scratch, loss = C.cfc_backward(*args, h_seq, d["y"], d["dt"], scratch=scratch, accumulate=True,
+                                           workspace=ws)
         return h_seq, scratch, loss, C.reduce_axis0(scratch)
 
-    paths = ("separate", "one_call", "accumulate")
+    paths = ("separate", "one_call", "accumulate", "bwd_accumulate")
     res = {}
     for p in paths:
         say(f"[parity] {cfg.name}: GPU step, {p}")
@@ -157,7 +166,7 @@ def test_large_workload_all_rows():
         for p in paths:
             g = res[p][1][r0:r1].cpu().numpy()
             own_out[p] += O.reduce_axis0_f32(g)
-            if p == "accumulate":
+            if p in ("accumulate", "bwd_accumulate"):
                 base = (np.arange(r0, r1)[:, None] % 7 - 3) + (np.arange(N)[None, :] % 5 - 2)
                 g = g.astype(np.float64) - base
             assert_close(g, s, f"{cfg.name} {p} scratch rows {r0}..{r1}")
@@ -171,7 +180,7 @@ def test_large_workload_all_rows():
         own = own_out[p]
         diff = np.abs(g_out.astype(np.float64) - own)
         assert np.all(diff <= np.spacing(np.abs(own.astype(np.float32))).astype(np.float64) * 1.0001), p
-        if p == "accumulate":
+        if p in ("accumulate", "bwd_accumulate"):
             # the reduced base is an exact integer; the gradient part is checked
             # against the oracle at float32 resolution of the combined sum
             assert_close(g_out.astype(np.float64) - col_base, ref_out, f"{cfg.name} {p} out - base",
